@@ -1,0 +1,458 @@
+"""Pins of the CPU fp64 oracle against facts the pages and the mathematics fix.
+
+Each test names the passage it follows.  Page labels:
+[Latent] 'Latent 压缩' (zdszero.github.io/latent.html);
+[MLA] 'MLA：潜在表示压缩与解耦 RoPE' (lizn-zn.github.io/scholia-log);
+[MiniMind] 'MiniMind 学习笔记 10：Multi-Latent Attention…' (p-chao.com).
+"""
+import cmath
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as orc
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+BASE = 10000.0
+
+
+def rand_weights(rng, d, n_h, d_h, d_c, d_r, d_cq):
+    def w(o, i):
+        return rng.standard_normal((o, i)) / math.sqrt(i)
+    return dict(w_dkv=w(d_c, d), w_kr=w(d_r, d), w_dq=w(d_cq, d),
+                w_uq=w(n_h * d_h, d_cq), w_qr=w(n_h * d_r, d_cq),
+                w_uk=w(n_h * d_h, d_c), w_uv=w(n_h * d_h, d_c),
+                w_o=w(d, n_h * d_h))
+
+
+TINY = dict(d=64, n_h=4, d_h=16, d_c=32, d_r=8, d_cq=48)
+
+
+def tiny_case(seed=0, ctx=64, n_q=1, dims=TINY):
+    rng = np.random.default_rng(seed)
+    w = rand_weights(rng, **dims)
+    h_ctx = rng.standard_normal((ctx, dims["d"]))
+    h_new = rng.standard_normal((n_q, dims["d"]))
+    c_ctx, kr_ctx = orc.kv_latent(h_ctx, np.arange(ctx), w["w_dkv"],
+                                  w["w_kr"], BASE)
+    return w, h_ctx, h_new, c_ctx, kr_ctx
+
+
+def rel(a, b):
+    return np.linalg.norm(np.asarray(a) - np.asarray(b)) / np.linalg.norm(b)
+
+
+# ---------------------------------------------------------------- cache counts
+
+def test_cache_counts_match_pages():
+    """[Latent] MLA section; [MLA] sections 2 and 8; [MiniMind] sections 2
+    and 11: the printed per-token cache counts."""
+    g = json.load(open(os.path.join(HERE, "golden", "cache_counts.json")))
+    ds = g["deepseek_v2"]
+    dd = ds["dims"]
+    mla = orc.mla_cache_elements(dd["d_c"], dd["d_r"])
+    mha = orc.mha_cache_elements(dd["n_h"], dd["d_h"])
+    assert mla == ds["mla_elements"]
+    assert mha == ds["mha_elements"]
+    assert round(100.0 * mla / mha, 4) == ds["mla_over_mha_percent"]
+    assert mla / (2 * dd["d_h"]) == ds["equivalent_gqa_groups"]
+    assert round(mha / mla) == ds["mha_over_mla_approx"]
+    mm = g["minimind"]
+    gq = mm["gqa"]
+    assert gq["num_attention_heads"] * gq["head_dim"] == mm["q_width"]
+    assert gq["num_key_value_heads"] * gq["head_dim"] == mm["k_width"]
+    assert gq["num_key_value_heads"] * gq["head_dim"] == mm["v_width"]
+    g_el = orc.gqa_cache_elements(gq["num_key_value_heads"], gq["head_dim"])
+    assert g_el == mm["gqa_elements"]
+    m_el = orc.mla_cache_elements(mm["mla"]["kv_lora_rank"],
+                                  mm["mla"]["qk_rope_head_dim"])
+    assert m_el == mm["mla_elements"]
+    assert round(100.0 * m_el / g_el, 1) == mm["mla_over_gqa_percent"]
+    assert round(100.0 - 100.0 * m_el / g_el, 1) == mm["reduction_percent"]
+
+
+def test_cached_row_is_dc_plus_dr():
+    """[MLA] section 6: the cache holds c_KV (d_c) plus k_R (d_r), nothing
+    else."""
+    w, h_ctx, _, c, kr = tiny_case()
+    assert c.shape == (64, TINY["d_c"]) and kr.shape == (64, TINY["d_r"])
+    assert c.shape[1] + kr.shape[1] == orc.mla_cache_elements(TINY["d_c"],
+                                                              TINY["d_r"])
+
+
+# ------------------------------------------------------------ brute force
+
+def brute_force_layer(w, h_ctx, h_new, n_h, d_h, d_c, d_r, base):
+    """Whole layer with scalar loops, written from [MLA] section 7: every dot
+    product, rotation (as a complex multiplication), exponential and sum is
+    spelled out."""
+    ctx = len(h_ctx)
+    hs = [list(r) for r in h_ctx] + [list(r) for r in h_new]
+    S = len(hs)
+
+    def matvec(W, x):
+        return [sum(W[i][k] * x[k] for k in range(len(x)))
+                for i in range(len(W))]
+
+    def rot(v, p):
+        half = len(v) // 2
+        out = [0.0] * len(v)
+        for j in range(half):
+            theta = base ** (-2.0 * j / len(v))
+            z = complex(v[j], v[j + half]) * cmath.exp(1j * p * theta)
+            out[j], out[j + half] = z.real, z.imag
+        return out
+
+    c = [matvec(w["w_dkv"], hs[s]) for s in range(S)]
+    kr = [rot(matvec(w["w_kr"], hs[s]), s) for s in range(S)]
+    us, os_, lses = [], [], []
+    for i in range(len(h_new)):
+        P = ctx + i
+        cq = matvec(w["w_dq"], hs[P])
+        qc_all = matvec(w["w_uq"], cq)
+        qr_all = matvec(w["w_qr"], cq)
+        o_heads, lse_heads = [], []
+        for h in range(n_h):
+            qc = qc_all[h * d_h:(h + 1) * d_h]
+            qr = rot(qr_all[h * d_r:(h + 1) * d_r], P)
+            wk = w["w_uk"][h * d_h:(h + 1) * d_h]
+            wv = w["w_uv"][h * d_h:(h + 1) * d_h]
+            scores = []
+            for s in range(P + 1):
+                kc = matvec(wk, c[s])
+                sc = sum(qc[k] * kc[k] for k in range(d_h))
+                sc += sum(qr[k] * kr[s][k] for k in range(d_r))
+                scores.append(sc / math.sqrt(d_h + d_r))
+            m = max(scores)
+            ex = [math.exp(x - m) for x in scores]
+            den = sum(ex)
+            o = [0.0] * d_h
+            for s in range(P + 1):
+                vc = matvec(wv, c[s])
+                for k in range(d_h):
+                    o[k] += ex[s] / den * vc[k]
+            o_heads.append(o)
+            lse_heads.append(m + math.log(den))
+        flat = [x for o in o_heads for x in o]
+        us.append(matvec(w["w_o"], flat))
+        os_.append(o_heads)
+        lses.append(lse_heads)
+    return np.array(us), np.array(os_), np.array(lses), np.array(c), \
+        np.array(kr)
+
+
+@pytest.mark.parametrize("n_q", [1, 3])
+def test_brute_force_layer(n_q):
+    """The vectorised oracle equals a scalar evaluation of [MLA] section 7
+    (with the causal rule of [MiniMind] section 12 for several queries)."""
+    dims = dict(d=6, n_h=2, d_h=3, d_c=4, d_r=4, d_cq=5)
+    w, h_ctx, h_new, c_ctx, kr_ctx = tiny_case(seed=7, ctx=5, n_q=n_q,
+                                               dims=dims)
+    ref = orc.decode_step(w, dims["n_h"], BASE, h_new, c_ctx, kr_ctx)
+    u, o, lse, c, kr = brute_force_layer(
+        {k: v.tolist() for k, v in w.items()}, h_ctx, h_new, dims["n_h"],
+        dims["d_h"], dims["d_c"], dims["d_r"], BASE)
+    np.testing.assert_allclose(ref["u"], u, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ref["o"], o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ref["lse"], lse, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ref["c_kv"], c[5:], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ref["k_r"], kr[5:], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(c_ctx, c[:5], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(kr_ctx, kr[:5], rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------- absorption identities
+
+@pytest.mark.parametrize("n_q", [1, 4])
+def test_absorbed_equals_nonabsorbed(n_q):
+    """[Latent] MLA section, [MLA] section 4, [MiniMind] section 10:
+    <q, W_K c> = <W_K^T q, c> and sum_s a_s W_V c_s = W_V sum_s a_s c_s."""
+    w, _, h_new, c_ctx, kr_ctx = tiny_case(seed=1, n_q=n_q)
+    d = TINY
+    ref = orc.decode_step(w, d["n_h"], BASE, h_new, c_ctx, kr_ctx)
+    c_all = np.concatenate([c_ctx, ref["c_kv"]])
+    kr_all = np.concatenate([kr_ctx, ref["k_r"]])
+    q = orc.absorb_query(ref["q_c"], ref["q_r"], w["w_uk"])
+    assert q.shape == (n_q, d["n_h"], d["d_c"] + d["d_r"])
+    rows = np.concatenate([c_all, kr_all], axis=1)
+    o_lat, lse = orc.latent_attention(q, ref["q_pos"], rows, d["d_c"],
+                                      d["d_h"])
+    assert rel(lse, ref["lse"]) < 1e-12
+    o = orc.head_values(o_lat, w["w_uv"], d["d_h"])
+    assert rel(o, ref["o"]) < 1e-12
+    u = orc.deferred_output(o_lat, w["w_uv"], w["w_o"], d["d_h"])
+    assert rel(u, ref["u"]) < 1e-12
+
+
+def test_value_deferral_with_weights():
+    """[MLA] section 4: u = sum_i W_O_i W_UV_i (sum_s a_{s,i} c_s)."""
+    w, _, h_new, c_ctx, kr_ctx = tiny_case(seed=2)
+    d = TINY
+    ref = orc.decode_step(w, d["n_h"], BASE, h_new, c_ctx, kr_ctx)
+    c_all = np.concatenate([c_ctx, ref["c_kv"]])
+    kr_all = np.concatenate([kr_ctx, ref["k_r"]])
+    o, lse, a = orc.attention(ref["q_c"], ref["q_r"], ref["q_pos"], c_all,
+                              kr_all, w["w_uk"], w["w_uv"],
+                              return_weights=True)
+    u = np.zeros(d["d"])
+    for h in range(d["n_h"]):
+        sl = slice(h * d["d_h"], (h + 1) * d["d_h"])
+        latent_sum = a[0, h] @ c_all
+        u += w["w_o"][:, sl] @ (w["w_uv"][sl] @ latent_sum)
+    assert rel(u, ref["u"][0]) < 1e-12
+
+
+def test_softmax_rows_and_causal_zeros():
+    """[MLA] 'A Attention' softmax; [MiniMind] section 12 causal mask: each
+    row of weights sums to one and keys after the query's position get an
+    exact zero."""
+    w, _, h_new, c_ctx, kr_ctx = tiny_case(seed=3, ctx=10, n_q=5)
+    d = TINY
+    ref = orc.decode_step(w, d["n_h"], BASE, h_new, c_ctx, kr_ctx)
+    c_all = np.concatenate([c_ctx, ref["c_kv"]])
+    kr_all = np.concatenate([kr_ctx, ref["k_r"]])
+    _, _, a = orc.attention(ref["q_c"], ref["q_r"], ref["q_pos"], c_all,
+                            kr_all, w["w_uk"], w["w_uv"], return_weights=True)
+    np.testing.assert_allclose(a.sum(-1), 1.0, rtol=0, atol=1e-15)
+    for i in range(5):
+        P = 10 + i
+        assert np.all(a[i, :, P + 1:] == 0.0)
+        assert np.all(a[i, :, :P + 1] > 0.0)
+
+
+def test_rank_bound():
+    """[Latent] GEMM factorisation and MLA section: [K_nope V] = c_KV [W_UK
+    W_UV] has rank <= d_c, and rank(W_UK W_DKV) <= d_c."""
+    w, _, _, c, _ = tiny_case(seed=4, ctx=65)
+    d = TINY
+    blocks = []
+    for h in range(d["n_h"]):
+        k_c, v_c = orc.explicit_kv(c, w["w_uk"], w["w_uv"], h, d["d_h"])
+        blocks += [k_c, v_c]
+    kv = np.concatenate(blocks, axis=1)          # [65, 2 n_h d_h] = [65, 128]
+    s = np.linalg.svd(kv, compute_uv=False)
+    assert s[d["d_c"]] / s[0] < 1e-12
+    assert s[d["d_c"] - 1] / s[0] > 1e-6
+    s2 = np.linalg.svd(w["w_uk"] @ w["w_dkv"], compute_uv=False)
+    assert s2[d["d_c"]] / s2[0] < 1e-12
+
+
+# ------------------------------------------------------------------- RoPE
+
+def test_rope_identities():
+    """[MLA] section 5: R_t^T R_s = R_{s-t}; R_0 = I; rotations keep norms."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal(8)
+    k = rng.standard_normal(8)
+    np.testing.assert_array_equal(orc.apply_rope(q, 0, BASE), q)
+    for t, s in [(3, 10), (100, 50), (131072, 7)]:
+        np.testing.assert_allclose(
+            np.linalg.norm(orc.apply_rope(q, t, BASE)), np.linalg.norm(q),
+            rtol=1e-13)
+        lhs = orc.apply_rope(q, t, BASE) @ orc.apply_rope(k, s, BASE)
+        rhs = q @ orc.apply_rope(k, s - t, BASE)
+        assert abs(lhs - rhs) < 1e-12 * (1 + abs(rhs))
+
+
+def test_rope_frequencies_endpoints():
+    """Reading of RoPE(.) on d_r dims: theta_0 = 1 and the last frequency is
+    base**(-(d_r-2)/d_r); a quarter turn at theta_0 swaps the pair."""
+    th = orc.rope_frequencies(64, BASE)
+    assert th[0] == 1.0 and len(th) == 32
+    assert abs(th[-1] - BASE ** (-62 / 64)) < 1e-18
+    x = np.zeros(4)
+    x[0] = 1.0
+    y = orc.apply_rope(x, math.pi / 2, BASE)   # theta_0 = 1: angle pi/2
+    np.testing.assert_allclose(y, [0.0, 0.0, 1.0, 0.0], atol=1e-15)
+
+
+def test_position_shift_invariance():
+    """[MLA] section 5: only relative positions enter the scores, so
+    shifting every position by the same amount leaves o and u unchanged."""
+    w, h_ctx, h_new, _, _ = tiny_case(seed=6, ctx=20, n_q=3)
+    d = TINY
+    h_all = np.concatenate([h_ctx, h_new])
+    pos = np.arange(23)
+    outs = []
+    for shift in (0, 777, 100000):
+        c, kr = orc.kv_latent(h_all, pos + shift, w["w_dkv"], w["w_kr"], BASE)
+        qc, qr = orc.query(h_new, pos[20:] + shift, w["w_dq"], w["w_uq"],
+                           w["w_qr"], d["n_h"], BASE)
+        o, lse = orc.attention(qc, qr, pos[20:], c, kr, w["w_uk"], w["w_uv"])
+        outs.append((orc.output(o, w["w_o"]), lse))
+    for u, lse in outs[1:]:
+        assert rel(u, outs[0][0]) < 1e-10
+        assert rel(lse, outs[0][1]) < 1e-10
+
+
+# ---------------------------------------------------- library special cases
+
+def _sdpa(q, k, v, mask, scale):
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+        attn_mask=torch.from_numpy(mask), scale=scale).numpy()
+
+
+@pytest.mark.parametrize("n_q", [1, 4])
+def test_latent_attention_is_mqa_sdpa(n_q):
+    """[Latent] MLA section: after absorption decode is MQA (one shared key
+    head = the cache row, one shared value head = c_KV); compare with torch's
+    scaled_dot_product_attention on CPU in float64."""
+    rng = np.random.default_rng(8)
+    d = TINY
+    S = 70
+    q = rng.standard_normal((n_q, d["n_h"], d["d_c"] + d["d_r"]))
+    rows = rng.standard_normal((S, d["d_c"] + d["d_r"]))
+    q_pos = S - n_q + np.arange(n_q)
+    o_lat, _ = orc.latent_attention(q, q_pos, rows, d["d_c"], d["d_h"])
+    mask = orc.visibility(q_pos, S)
+    ref = _sdpa(q.transpose(1, 0, 2)[None],
+                np.broadcast_to(rows, (1, d["n_h"], S, rows.shape[1])).copy(),
+                np.broadcast_to(rows[:, :d["d_c"]],
+                                (1, d["n_h"], S, d["d_c"])).copy(),
+                mask, 1.0 / math.sqrt(d["d_h"] + d["d_r"]))
+    assert rel(o_lat, ref[0].transpose(1, 0, 2)) < 1e-12
+
+
+def test_mha_form_is_sdpa():
+    """[MLA] section 7 / [MiniMind] section 10 naive path: per-head attention
+    with k = [k_C ; k_R], v = v_C equals SDPA with scale 1/sqrt(d_h + d_r)."""
+    w, _, h_new, c_ctx, kr_ctx = tiny_case(seed=9, ctx=30, n_q=4)
+    d = TINY
+    ref = orc.decode_step(w, d["n_h"], BASE, h_new, c_ctx, kr_ctx)
+    c_all = np.concatenate([c_ctx, ref["c_kv"]])
+    kr_all = np.concatenate([kr_ctx, ref["k_r"]])
+    S = len(c_all)
+    ks, vs = [], []
+    for h in range(d["n_h"]):
+        k_c, v_c = orc.explicit_kv(c_all, w["w_uk"], w["w_uv"], h, d["d_h"])
+        ks.append(np.concatenate([k_c, kr_all], axis=1))
+        vs.append(v_c)
+    q = np.concatenate([ref["q_c"], ref["q_r"]], axis=-1)
+    out = _sdpa(q.transpose(1, 0, 2)[None], np.stack(ks)[None],
+                np.stack(vs)[None], orc.visibility(ref["q_pos"], S),
+                1.0 / math.sqrt(d["d_h"] + d["d_r"]))
+    assert rel(ref["o"], out[0].transpose(1, 0, 2)) < 1e-12
+
+
+def test_textbook_single_head():
+    """[MiniMind] section 4 structure without RoPE: with W_KR = W_QR = 0,
+    one head, d_c = d_h and W_UK = W_UV = I the layer is plain single-head
+    attention over c_KV (checked against SDPA)."""
+    rng = np.random.default_rng(10)
+    dh, dr, dd, dcq = 8, 4, 12, 6
+    w = rand_weights(rng, dd, 1, dh, dh, dr, dcq)
+    w["w_kr"][:] = 0.0
+    w["w_qr"][:] = 0.0
+    w["w_uk"] = np.eye(dh)
+    w["w_uv"] = np.eye(dh)
+    h_ctx = rng.standard_normal((9, dd))
+    h_new = rng.standard_normal((1, dd))
+    c_ctx, kr_ctx = orc.kv_latent(h_ctx, np.arange(9), w["w_dkv"], w["w_kr"],
+                                  BASE)
+    ref = orc.decode_step(w, 1, BASE, h_new, c_ctx, kr_ctx)
+    c_all = np.concatenate([c_ctx, ref["c_kv"]])
+    qc = ref["q_c"][:, 0]
+    out = _sdpa(qc[None, None], c_all[None, None], c_all[None, None],
+                np.ones((1, 10), bool), 1.0 / math.sqrt(dh + dr))
+    assert rel(ref["o"][:, 0], out[0, 0]) < 1e-12
+
+
+def test_latent_basis_invariance():
+    """[Latent] scale symmetry: (W_up S)(S^-1 W_down) is the same map, so
+    W_DKV -> S^-1 W_DKV, W_UK -> W_UK S, W_UV -> W_UV S leaves u unchanged."""
+    w, h_ctx, h_new, _, _ = tiny_case(seed=11, ctx=40, n_q=2)
+    d = TINY
+    rng = np.random.default_rng(12)
+    S = np.eye(d["d_c"]) + 0.3 * rng.standard_normal((d["d_c"], d["d_c"])) \
+        / math.sqrt(d["d_c"])
+    w2 = dict(w)
+    w2["w_dkv"] = np.linalg.solve(S, w["w_dkv"])
+    w2["w_uk"] = w["w_uk"] @ S
+    w2["w_uv"] = w["w_uv"] @ S
+    outs = []
+    for ww in (w, w2):
+        c, kr = orc.kv_latent(h_ctx, np.arange(40), ww["w_dkv"], ww["w_kr"],
+                              BASE)
+        outs.append(orc.decode_step(ww, d["n_h"], BASE, h_new, c, kr)["u"])
+    assert rel(outs[1], outs[0]) < 1e-10
+
+
+# -------------------------------------------------------------- closed forms
+
+def test_single_key_closed_form():
+    """With one visible key the softmax weight is 1: o_h = W_UV_h c_0 and
+    lse = the score."""
+    w, _, h_new, _, _ = tiny_case(seed=13, ctx=0)
+    d = TINY
+    ref = orc.decode_step(w, d["n_h"], BASE, h_new, np.zeros((0, d["d_c"])),
+                          np.zeros((0, d["d_r"])))
+    for h in range(d["n_h"]):
+        sl = slice(h * d["d_h"], (h + 1) * d["d_h"])
+        np.testing.assert_allclose(ref["o"][0, h], w["w_uv"][sl] @
+                                   ref["c_kv"][0], rtol=1e-13, atol=1e-14)
+        k = np.concatenate([w["w_uk"][sl] @ ref["c_kv"][0], ref["k_r"][0]])
+        q = np.concatenate([ref["q_c"][0, h], ref["q_r"][0, h]])
+        s = q @ k / math.sqrt(d["d_h"] + d["d_r"])
+        assert abs(ref["lse"][0, h] - s) < 1e-12
+
+
+def test_equal_keys_closed_form():
+    """S identical keys (no rotary part): uniform weights, lse = s + log S."""
+    rng = np.random.default_rng(14)
+    d = TINY
+    S = 37
+    row = rng.standard_normal(d["d_c"] + d["d_r"])
+    row[d["d_c"]:] = 0.0
+    rows = np.tile(row, (S, 1))
+    q = rng.standard_normal((1, d["n_h"], d["d_c"] + d["d_r"]))
+    o_lat, lse = orc.latent_attention(q, [S - 1], rows, d["d_c"], d["d_h"])
+    s = q[0] @ row / math.sqrt(d["d_h"] + d["d_r"])
+    np.testing.assert_allclose(lse[0], s + math.log(S), rtol=1e-13)
+    np.testing.assert_allclose(o_lat[0], np.tile(row[:d["d_c"]],
+                                                 (d["n_h"], 1)), rtol=1e-13)
+
+
+def test_causal_last_row_is_plain_decode():
+    """[MiniMind] section 12 (bottom-right alignment): in a chunk of new
+    tokens, the last query equals a decode of one query at the full length
+    and the first equals a decode that has not seen the later new tokens."""
+    w, h_ctx, h_new, c_ctx, kr_ctx = tiny_case(seed=15, ctx=25, n_q=4)
+    d = TINY
+    chunk = orc.decode_step(w, d["n_h"], BASE, h_new, c_ctx, kr_ctx)
+    c_all = np.concatenate([c_ctx, chunk["c_kv"][:3]])
+    kr_all = np.concatenate([kr_ctx, chunk["k_r"][:3]])
+    last = orc.decode_step(w, d["n_h"], BASE, h_new[3:], c_all, kr_all)
+    assert rel(last["u"][0], chunk["u"][3]) < 1e-12
+    first = orc.decode_step(w, d["n_h"], BASE, h_new[:1], c_ctx, kr_ctx)
+    assert rel(first["u"][0], chunk["u"][0]) < 1e-12
+
+
+def test_head_subset_matches_full():
+    """Computing a subset of heads gives the same per-head outputs."""
+    w, _, h_new, c_ctx, kr_ctx = tiny_case(seed=16)
+    d = TINY
+    full = orc.decode_step(w, d["n_h"], BASE, h_new, c_ctx, kr_ctx)
+    part = orc.decode_step(w, d["n_h"], BASE, h_new, c_ctx, kr_ctx,
+                           heads=[1, 3])
+    np.testing.assert_array_equal(part["o"][:, [1, 3]], full["o"][:, [1, 3]])
+    assert "u" not in part
+
+
+# ---------------------------------------------------------- independence
+
+def test_oracle_is_independent_of_product_path():
+    """The oracle imports nothing from the HIP path and vice versa."""
+    root = os.path.dirname(HERE)
+    src = open(os.path.join(root, "oracle", "mla_oracle.py")).read()
+    assert "mla_latent_kv_33_amd" not in src
+    pkg = os.path.join(root, "mla_latent_kv_33_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h", ".hpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text
