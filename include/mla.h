@@ -1,0 +1,214 @@
+/*
+ * mla.h - C ABI of the MI355X (gfx950) MLA decode library, libmla.so.
+ *
+ * Multi-head Latent Attention decode over a paged latent cache.  Each cached
+ * token keeps only its latent c_KV (d_c values) and the RoPE key k_R shared by
+ * every head (d_r values), one row of d_c + d_r elements
+ * ('MLA：潜在表示压缩与解耦 RoPE', sections 3, 6 and 7).  A decode step is four
+ * calls, enqueued in this order on one HIP stream:
+ *
+ *   mla_append_cache  c_KV = W_DKV h, k_R = RoPE(W_KR h), written to the cache
+ *   mla_absorb_q      c_Q = W_DQ h, q_C = W_UQ c_Q, q_R = RoPE(W_QR c_Q),
+ *                     q_lat_h = W_UK_h^T q_C_h  -> q = [q_lat | q_R] per head
+ *   mla_decode        scores q . row / sqrt(d_h + d_r), softmax, o_lat =
+ *                     sum_s a_s c_KV_s (split over the keys, then combined)
+ *   mla_out           v_h = W_UV_h o_lat_h, u = W_O [v_0; ...; v_{n_h-1}]
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers are device memory unless a parameter says "host".  The caller
+ *   allocates and frees every buffer (weights, cache pool, block table,
+ *   lengths, outputs, workspace); the library allocates nothing and keeps no
+ *   state between calls.  Every call only enqueues work on `stream` and
+ *   returns; results are ready once the caller synchronises the stream.
+ * - Weights are row-major [out, in] (y = W x), in the activation dtype.
+ *   Head h owns rows h*d_h .. h*d_h+d_h-1 of W_UQ, W_UK, W_UV and rows
+ *   h*d_r .. of W_QR.
+ * - Activations, weights and the cache share `dims->dtype`; accumulation is
+ *   fp32.  o_lat and lse are always fp32.
+ * - Cache pool: `cache[num_blocks][block_size][d_c + d_r]`, each row the
+ *   token's c_KV followed by its k_R.  Token at position p of sequence b lives
+ *   in row p % block_size of block `block_table[b * max_blocks + p /
+ *   block_size]`.  Positions are 0-based.
+ * - RoPE tables: `rope_cos/rope_sin[max_pos][d_r / 2]` fp32, entry (p, j) =
+ *   cos/sin(p * base^(-2j/d_r)); the pair (x_j, x_{j + d_r/2}) is rotated by
+ *   that angle.  mla_rope_tables_host builds them.
+ * - Errors are returned, never printed or thrown.  Host-checkable arguments
+ *   (null pointers, sizes, dims, workspace) are validated before anything is
+ *   enqueued.  Values that live on the device (block ids, lengths, positions,
+ *   sequence indices) are trusted: they must be in range, as documented per
+ *   call.  MLA_ERR_DEVICE reports a failed launch.
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* mla_stream_t; /* a hipStream_t; NULL = default */
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = 1,        /* a required pointer is NULL */
+  MLA_ERR_SHAPE = 2,       /* inconsistent or non-positive sizes */
+  MLA_ERR_UNSUPPORTED = 3, /* dims/dtype this build has no kernel for */
+  MLA_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+  MLA_ERR_RANGE = 5,       /* a host-checkable value out of range */
+  MLA_ERR_DEVICE = 6       /* a kernel launch failed */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+/* Layer dimensions.  Bracketed names are the usual hyper-parameter names
+ * ('MiniMind 学习笔记 10', section 8).  Requirements: all positive, d_r even,
+ * block_size a power of two; for BF16 also d, d_h, d_c, d_r and d_cq
+ * multiples of 8 (else MLA_ERR_UNSUPPORTED).  The matrix-core decode kernel
+ * takes BF16 with d_c = 512, d_r = 64, block_size 64 and n_h = 64, 96 or a
+ * multiple of 128; other dims run on the general (SIMT) decode kernel. */
+typedef struct {
+  int32_t d;          /* hidden size */
+  int32_t n_h;        /* attention heads */
+  int32_t d_h;        /* per-head content dim [qk_nope_head_dim = v_head_dim] */
+  int32_t d_c;        /* KV latent dim [kv_lora_rank] */
+  int32_t d_r;        /* decoupled RoPE dim [qk_rope_head_dim] */
+  int32_t d_cq;       /* query latent dim [q_lora_rank] */
+  int32_t block_size; /* tokens per cache block */
+  int32_t dtype;      /* mla_dtype of activations, weights and cache */
+} mla_dims;
+
+/* Human-readable name of a status code (static string). */
+const char* mla_status_string(mla_status s);
+
+/* Library version string (static). */
+const char* mla_version(void);
+
+/* Host helper: fill host arrays cos_out/sin_out[max_pos][d_r/2] with
+ * cos/sin(p * base^(-2j/d_r)), angles computed in double and rounded once to
+ * float.  RoPE as used for q_R and k_R ('MLA：潜在表示压缩与解耦 RoPE',
+ * sections 5-6; the frequency and half-split pairing are this library's
+ * convention).  Errors: MLA_ERR_NULL, MLA_ERR_SHAPE (d_r odd or <= 0,
+ * max_pos <= 0, base <= 0). */
+mla_status mla_rope_tables_host(int32_t d_r, double base, int32_t max_pos,
+                                float* cos_out, float* sin_out);
+
+/* ------------------------------------------------------------------------
+ * mla_append_cache - write the latent rows of T new tokens into the cache.
+ *
+ * For token t (0 <= t < T) with hidden state h[t][d], sequence seq_idx[t]
+ * and position pos[t]:  c = W_DKV h  (d_c values), r = RoPE_{pos}(W_KR h)
+ * (d_r values), rounded once to the cache dtype and stored as the row of that
+ * position ('MLA：潜在表示压缩与解耦 RoPE', sections 3 and 6: only c_KV and k_R
+ * are cached).
+ *
+ *   h            [T][d]                  activation dtype
+ *   seq_idx, pos [T] int32 (device)      0 <= seq_idx < num_seqs (trusted),
+ *                                        0 <= pos < max_pos and
+ *                                        pos / block_size < max_blocks
+ *   w_dkv        [d_c][d], w_kr [d_r][d]
+ *   rope_cos/sin [max_pos][d_r/2] fp32
+ *   block_table  [num_seqs][max_blocks] int32, entries < num_blocks
+ *   cache        [num_blocks][block_size][d_c + d_r]
+ *   ws           workspace of at least mla_append_workspace_bytes(dims, T)
+ * Rows of distinct tokens must not coincide.  T = 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+size_t mla_append_workspace_bytes(const mla_dims* dims, int32_t T);
+mla_status mla_append_cache(const mla_dims* dims, int32_t T, const void* h,
+                            const int32_t* seq_idx, const int32_t* pos,
+                            const void* w_dkv, const void* w_kr,
+                            const float* rope_cos, const float* rope_sin,
+                            int32_t max_pos, const int32_t* block_table,
+                            int32_t max_blocks, void* cache,
+                            int32_t num_blocks, void* ws, size_t ws_bytes,
+                            mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mla_absorb_q - query path and absorption of W_UK into the query.
+ *
+ * c_Q = W_DQ h (kept fp32, not rounded), q_C = W_UQ c_Q, q_R = RoPE_{pos}(W_QR
+ * c_Q) per head, q_lat_h = W_UK_h^T q_C_h ('MLA：潜在表示压缩与解耦 RoPE',
+ * sections 3, 4 and 6; 'Latent 压缩', MLA section: <q, W_K c> = <W_K^T q, c>).
+ * Output q[t][h] = [q_lat_h (d_c) | q_R_h (d_r)], rounded once to the
+ * activation dtype.
+ *
+ *   h      [T][d];  pos [T] int32 (device), 0 <= pos < max_pos (trusted)
+ *   w_dq [d_cq][d], w_uq [n_h*d_h][d_cq], w_qr [n_h*d_r][d_cq],
+ *   w_uk [n_h*d_h][d_c]
+ *   q_out  [T][n_h][d_c + d_r]
+ *   ws     at least mla_absorb_workspace_bytes(dims, T)
+ * ---------------------------------------------------------------------- */
+size_t mla_absorb_workspace_bytes(const mla_dims* dims, int32_t T);
+mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
+                        const int32_t* pos, const void* w_dq,
+                        const void* w_uq, const void* w_qr, const void* w_uk,
+                        const float* rope_cos, const float* rope_sin,
+                        int32_t max_pos, void* q_out, void* ws,
+                        size_t ws_bytes, mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * mla_decode - attention of absorbed queries over the latent cache.
+ *
+ * Sequence b has kv_lens[b] cached rows (positions 0 .. kv_lens[b]-1) and
+ * n_q queries, the last n_q positions: query i sits at position
+ * P = kv_lens[b] - n_q + i and sees rows 0..P (causal, bottom-right aligned:
+ * 'MiniMind 学习笔记 10', section 12).  Per head h:
+ *   score_s = (q_lat_h . c_KV_s + q_R_h . k_R_s) / sqrt(d_h + d_r)
+ *   o_lat_h = sum_s softmax(score)_s c_KV_s,   lse_h = log sum_s e^score_s
+ * ('MLA：潜在表示压缩与解耦 RoPE', sections 4, 6, 7; 'Latent 压缩', MLA
+ * section: decode in the latent is MQA with one shared key/value head).
+ * The keys of each (b, query) are cut into n_split chunks whose partial
+ * softmax states are merged by a log-sum-exp combine.
+ *
+ *   q           [B][n_q][n_h][d_c + d_r]
+ *   cache, block_table, max_blocks, num_blocks as in mla_append_cache
+ *   kv_lens     [B] int32 (device), n_q <= kv_lens[b] <= max_kv_len and
+ *               ceil(kv_lens[b] / block_size) <= max_blocks (trusted)
+ *   max_kv_len  host upper bound of kv_lens (sizes the split plan)
+ *   causal      must be 1 when n_q > 1 (the only defined rule); ignored for
+ *               n_q = 1
+ *   n_split     key chunks per (b, query); 0 lets the library choose;
+ *               must not exceed ceil(max_kv_len / block_size)
+ *   o_lat       [B][n_q][n_h][d_c] fp32 output
+ *   lse         [B][n_q][n_h] fp32 output, may be NULL
+ *   ws          at least mla_decode_workspace_bytes(dims, B, n_q,
+ *               max_kv_len, n_split)
+ * ---------------------------------------------------------------------- */
+size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t B,
+                                  int32_t n_q, int32_t max_kv_len,
+                                  int32_t n_split);
+mla_status mla_decode(const mla_dims* dims, int32_t B, int32_t n_q,
+                      const void* q, const void* cache, int32_t num_blocks,
+                      const int32_t* block_table, int32_t max_blocks,
+                      const int32_t* kv_lens, int32_t max_kv_len,
+                      int32_t causal, int32_t n_split, float* o_lat,
+                      float* lse, void* ws, size_t ws_bytes,
+                      mla_stream_t stream);
+
+/* The split count mla_decode uses for n_split = 0 (host only). */
+int32_t mla_decode_auto_splits(const mla_dims* dims, int32_t B, int32_t n_q,
+                               int32_t max_kv_len);
+
+/* ------------------------------------------------------------------------
+ * mla_out - value up-projection after the weighted sum, then W_O.
+ *
+ * v_h = W_UV_h o_lat_h (kept fp32), u = W_O [v_0; ...; v_{n_h-1}] rounded
+ * once to the activation dtype ('MLA：潜在表示压缩与解耦 RoPE', section 4
+ * per-head output formula and section 7).
+ *
+ *   o_lat [T][n_h][d_c] fp32;  w_uv [n_h*d_h][d_c];  w_o [d][n_h*d_h]
+ *   u     [T][d]
+ *   ws    at least mla_out_workspace_bytes(dims, T)
+ * ---------------------------------------------------------------------- */
+size_t mla_out_workspace_bytes(const mla_dims* dims, int32_t T);
+mla_status mla_out(const mla_dims* dims, int32_t T, const float* o_lat,
+                   const void* w_uv, const void* w_o, void* u, void* ws,
+                   size_t ws_bytes, mla_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H */

@@ -1,0 +1,206 @@
+"""Thin ctypes binding of libmla.so (include/mla.h).
+
+Every function here only marshals torch tensors into pointers, sizes and the
+current HIP stream, and turns status codes into exceptions; all arithmetic
+of the decode path runs in the library's HIP kernels.  Functions carry the
+C names.  There is no fallback: if the library is missing or fails to load,
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+MLA_F32 = 0
+MLA_BF16 = 1
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+        self.status = status
+
+
+class MlaDims(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("n_h", ctypes.c_int32),
+                ("d_h", ctypes.c_int32), ("d_c", ctypes.c_int32),
+                ("d_r", ctypes.c_int32), ("d_cq", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_S = ctypes.c_size_t
+_DP = ctypes.POINTER(MlaDims)
+
+_SIGNATURES = {
+    "mla_status_string": (ctypes.c_char_p, [_I]),
+    "mla_version": (ctypes.c_char_p, []),
+    "mla_rope_tables_host": (_I, [_I, ctypes.c_double, _I, _P, _P]),
+    "mla_append_workspace_bytes": (_S, [_DP, _I]),
+    "mla_append_cache": (_I, [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I,
+                              _P, _I, _P, _S, _P]),
+    "mla_absorb_workspace_bytes": (_S, [_DP, _I]),
+    "mla_absorb_q": (_I, [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                          _S, _P]),
+    "mla_decode_workspace_bytes": (_S, [_DP, _I, _I, _I, _I]),
+    "mla_decode_auto_splits": (_I, [_DP, _I, _I, _I]),
+    "mla_decode": (_I, [_DP, _I, _I, _P, _P, _I, _P, _I, _P, _I, _I, _I, _P,
+                        _P, _P, _S, _P]),
+    "mla_out_workspace_bytes": (_S, [_DP, _I]),
+    "mla_out": (_I, [_DP, _I, _P, _P, _P, _P, _P, _S, _P]),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                "python -m mla_latent_kv_33_amd.build")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def make_dims(dims, dtype: str, block_size: int = 64) -> MlaDims:
+    """mla_dims from an object with d, n_h, d_h, d_c, d_r, d_cq."""
+    return MlaDims(dims.d, dims.n_h, dims.d_h, dims.d_c, dims.d_r, dims.d_cq,
+                   block_size, MLA_BF16 if dtype == "bf16" else MLA_F32)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MlaError(fn, status, lib().mla_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmla must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return ws, 0 if ws is None else ws.numel() * ws.element_size()
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def mla_status_string(status: int) -> str:
+    return lib().mla_status_string(status).decode()
+
+
+def mla_version() -> str:
+    return lib().mla_version().decode()
+
+
+def mla_rope_tables_host(d_r: int, base: float, max_pos: int):
+    """Host cos/sin tables [max_pos, d_r/2] (float32 numpy)."""
+    cos = np.empty((max_pos, d_r // 2), np.float32)
+    sin = np.empty((max_pos, d_r // 2), np.float32)
+    _check("mla_rope_tables_host", lib().mla_rope_tables_host(
+        d_r, float(base), max_pos, cos.ctypes.data_as(_P),
+        sin.ctypes.data_as(_P)))
+    return cos, sin
+
+
+def mla_append_workspace_bytes(dims: MlaDims, T: int) -> int:
+    return lib().mla_append_workspace_bytes(ctypes.byref(dims), T)
+
+
+def mla_absorb_workspace_bytes(dims: MlaDims, T: int) -> int:
+    return lib().mla_absorb_workspace_bytes(ctypes.byref(dims), T)
+
+
+def mla_decode_workspace_bytes(dims: MlaDims, B: int, n_q: int,
+                               max_kv_len: int, n_split: int) -> int:
+    return lib().mla_decode_workspace_bytes(ctypes.byref(dims), B, n_q,
+                                            max_kv_len, n_split)
+
+
+def mla_decode_auto_splits(dims: MlaDims, B: int, n_q: int,
+                           max_kv_len: int) -> int:
+    return lib().mla_decode_auto_splits(ctypes.byref(dims), B, n_q,
+                                        max_kv_len)
+
+
+def mla_out_workspace_bytes(dims: MlaDims, T: int) -> int:
+    return lib().mla_out_workspace_bytes(ctypes.byref(dims), T)
+
+
+def mla_append_cache(dims: MlaDims, h, seq_idx, pos, w_dkv, w_kr, rope_cos,
+                     rope_sin, block_table, cache, ws=None, stream=None):
+    """c_KV = W_DKV h and k_R = RoPE(W_KR h) for T = h.shape[0] tokens,
+    written into the paged cache (see include/mla.h)."""
+    T = h.shape[0]
+    ws, wsb = _workspace(mla_append_workspace_bytes(dims, T) if T else 0,
+                         h.device, ws)
+    _check("mla_append_cache", lib().mla_append_cache(
+        ctypes.byref(dims), T, _ptr(h), _ptr(seq_idx), _ptr(pos), _ptr(w_dkv),
+        _ptr(w_kr), _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
+        _ptr(block_table), block_table.shape[1], _ptr(cache), cache.shape[0],
+        _ptr(ws), wsb, _stream(stream)))
+
+
+def mla_absorb_q(dims: MlaDims, h, pos, w_dq, w_uq, w_qr, w_uk, rope_cos,
+                 rope_sin, q_out, ws=None, stream=None):
+    """q_out[t, h] = [W_UK_h^T q_C | RoPE(W_QR c_Q)_h] (see include/mla.h)."""
+    T = h.shape[0]
+    ws, wsb = _workspace(mla_absorb_workspace_bytes(dims, T) if T else 0,
+                         h.device, ws)
+    _check("mla_absorb_q", lib().mla_absorb_q(
+        ctypes.byref(dims), T, _ptr(h), _ptr(pos), _ptr(w_dq), _ptr(w_uq),
+        _ptr(w_qr), _ptr(w_uk), _ptr(rope_cos), _ptr(rope_sin),
+        rope_cos.shape[0], _ptr(q_out), _ptr(ws), wsb, _stream(stream)))
+
+
+def mla_decode(dims: MlaDims, q, cache, block_table, kv_lens, max_kv_len: int,
+               o_lat, lse=None, causal: int = 1, n_split: int = 0, ws=None,
+               stream=None):
+    """Latent attention of q [B, n_q, n_h, d_c + d_r] over the cache
+    (see include/mla.h); writes o_lat [B, n_q, n_h, d_c] fp32 and lse."""
+    B, n_q = q.shape[0], q.shape[1]
+    ws, wsb = _workspace(
+        mla_decode_workspace_bytes(dims, B, n_q, max_kv_len, n_split),
+        q.device, ws)
+    _check("mla_decode", lib().mla_decode(
+        ctypes.byref(dims), B, n_q, _ptr(q), _ptr(cache), cache.shape[0],
+        _ptr(block_table), block_table.shape[1], _ptr(kv_lens), max_kv_len,
+        causal, n_split, _ptr(o_lat), _ptr(lse), _ptr(ws), wsb,
+        _stream(stream)))
+
+
+def mla_out(dims: MlaDims, o_lat, w_uv, w_o, u, ws=None, stream=None):
+    """u = W_O [W_UV_h o_lat_h]_h for T = o_lat.shape[0] rows."""
+    T = o_lat.shape[0]
+    ws, wsb = _workspace(mla_out_workspace_bytes(dims, T) if T else 0,
+                         o_lat.device, ws)
+    _check("mla_out", lib().mla_out(
+        ctypes.byref(dims), T, _ptr(o_lat), _ptr(w_uv), _ptr(w_o), _ptr(u),
+        _ptr(ws), wsb, _stream(stream)))

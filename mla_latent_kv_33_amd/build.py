@@ -1,0 +1,38 @@
+"""Build libmla.so (the HIP kernels and the C ABI of include/mla.h) in-tree
+with hipcc for gfx950."""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libmla.so")
+SOURCES = ["mla_api.hip", "gemm.hip", "elementwise.hip", "decode_simt.hip",
+           "decode_mfma.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+         "-Wno-inline-asm",
+         # no packed-fp32 VALU forms (v_pk_*_f32) anywhere in device code
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I", os.path.join(ROOT, "include")]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libmla.so next to this file; returns the
+    library path.  Always recompiles."""
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    proc = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(l for l in (proc.stdout + proc.stderr).splitlines()
+                    if "packed-fp32-ops" not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{out}")
+    if verbose and out.strip():
+        print(out, file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,206 @@
+// General split-KV latent decode (any d_c, d_r, block size; fp32 or bf16)
+// and the split combine shared by both decode kernels.
+//
+// Same computation as the matrix-core kernel ('MLA：潜在表示压缩与解耦 RoPE',
+// sections 4, 6 and 7): per (sequence, query, head, split), scores against
+// the shared cache rows, an online softmax in base 2 and the weighted sum of
+// the c_KV columns.  One workgroup handles one head; its threads score one
+// key each per round, then share the weights through LDS to accumulate the
+// d_c output columns.  Used for dims the matrix-core kernel does not cover
+// (including fp32 layers).
+//
+// Combine: for splits j with states (acc_j, m_j, l_j) in log2 units,
+//   M = max_j m_j,  w_j = 2^(m_j - M),  o = sum_j w_j acc_j / sum_j w_j l_j,
+//   lse = (M + log2 sum_j w_j l_j) * ln 2.
+// Splits with no keys carry m = -inf and are skipped.
+
+#include "mla_common.hpp"
+#include "mla_kernels.hpp"
+
+namespace mla {
+namespace {
+
+constexpr int NT = 128;
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(NT) void decode_simt_kernel(
+    const T* __restrict__ q, const T* __restrict__ cache,
+    const int32_t* __restrict__ block_table, int max_blocks,
+    const int32_t* __restrict__ kv_lens, int n_q, int n_h, int d_c, int d_r,
+    int bs, int n_split, float scale_log2,
+    float* __restrict__ o_part, float* __restrict__ m_part,
+    float* __restrict__ l_part, float* __restrict__ o_final,
+    float* __restrict__ lse_final) {
+  extern __shared__ float sh[];
+  const int width = d_c + d_r;
+  float* qs = sh;             // [width]
+  float* acc = qs + width;    // [d_c]
+  float* ps = acc + d_c;      // [NT]
+  int* rows = (int*)(ps + NT);  // [NT] cache row index of each key
+  __shared__ float red[NT / 64];
+
+  const int tid = threadIdx.x;
+  const int bq = blockIdx.x, split = blockIdx.y, h = blockIdx.z;
+  const int b = bq / n_q, qi = bq - b * n_q;
+  const int visible = kv_lens[b] - n_q + qi + 1;
+  // Split j covers blocks [j nblk / n_split, (j + 1) nblk / n_split).
+  const int nblk = (visible + bs - 1) / bs;
+  const int tok0 = (int)((long)split * nblk / n_split) * bs;
+  const int tok1 = min(visible, (int)((long)(split + 1) * nblk / n_split) * bs);
+  const size_t row_id = ((size_t)bq * n_split + split) * n_h + h;
+  if (tok0 >= tok1) {
+    if (tid == 0) {
+      m_part[row_id] = -INFINITY;
+      l_part[row_id] = 0.0f;
+    }
+    return;
+  }
+  const T* qrow = q + ((size_t)bq * n_h + h) * width;
+  for (int k = tid; k < width; k += NT) qs[k] = DT<T>::load(qrow, k);
+  for (int j = tid; j < d_c; j += NT) acc[j] = 0.0f;
+  const int32_t* bt = block_table + (size_t)b * max_blocks;
+  float m_run = -INFINITY, l_run = 0.0f;
+  __syncthreads();
+
+  for (int start = tok0; start < tok1; start += NT) {
+    const int t = start + tid;
+    float s = -INFINITY;
+    if (t < tok1) {
+      const int r = bt[t / bs] * bs + (t % bs);
+      rows[tid] = r;
+      const T* kr = cache + (size_t)r * width;
+      float dot = 0.0f;
+      for (int k = 0; k < width; ++k) dot = fmaf(qs[k], DT<T>::load(kr, k), dot);
+      s = dot * scale_log2;
+    }
+    float cmax = wave_max(s);
+    if ((tid & 63) == 0) red[tid >> 6] = cmax;
+    __syncthreads();
+    cmax = red[0];
+    for (int w = 1; w < NT / 64; ++w) cmax = fmaxf(cmax, red[w]);
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = exp2f(m_run - m_new);
+    const float p = t < tok1 ? exp2f(s - m_new) : 0.0f;
+    ps[tid] = p;
+    __syncthreads();  // red[] reads done, ps/rows visible
+    float psum = wave_sum(p);
+    if ((tid & 63) == 0) red[tid >> 6] = psum;
+    __syncthreads();
+    psum = 0.0f;
+    for (int w = 0; w < NT / 64; ++w) psum += red[w];
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    const int cnt = min(NT, tok1 - start);
+    for (int j = tid; j < d_c; j += NT) {
+      float a = acc[j] * alpha;
+      for (int u = 0; u < cnt; ++u)
+        a = fmaf(ps[u], DT<T>::load(cache + (size_t)rows[u] * width, j), a);
+      acc[j] = a;
+    }
+    __syncthreads();
+  }
+
+  if (n_split == 1) {
+    float* dst = o_final + ((size_t)bq * n_h + h) * d_c;
+    const float inv = 1.0f / l_run;
+    for (int j = tid; j < d_c; j += NT) dst[j] = acc[j] * inv;
+    if (tid == 0 && lse_final)
+      lse_final[(size_t)bq * n_h + h] =
+          (m_run + log2f(l_run)) * 0.69314718055994531f;
+  } else {
+    float* dst = o_part + row_id * d_c;
+    for (int j = tid; j < d_c; j += NT) dst[j] = acc[j];
+    if (tid == 0) {
+      m_part[row_id] = m_run;
+      l_part[row_id] = l_run;
+    }
+  }
+}
+
+// One workgroup per (row, head); threads over the d_c columns.
+__global__ __launch_bounds__(256) void combine_kernel(
+    int n_h, int d_c, int n_split, const float* __restrict__ o_part,
+    const float* __restrict__ m_part, const float* __restrict__ l_part,
+    float* __restrict__ o_lat, float* __restrict__ lse) {
+  extern __shared__ float wsh[];  // [n_split] weights
+  __shared__ float scal[2];
+  const int bq = blockIdx.x, h = blockIdx.y;
+  const size_t base = (size_t)bq * n_split * n_h + h;
+  if (threadIdx.x == 0) {
+    float M = -INFINITY;
+    for (int j = 0; j < n_split; ++j) M = fmaxf(M, m_part[base + (size_t)j * n_h]);
+    float L = 0.0f;
+    for (int j = 0; j < n_split; ++j) {
+      const float m = m_part[base + (size_t)j * n_h];
+      const float w = m == -INFINITY ? 0.0f : exp2f(m - M);
+      wsh[j] = w;
+      L += w * l_part[base + (size_t)j * n_h];
+    }
+    scal[0] = M;
+    scal[1] = L;
+  }
+  __syncthreads();
+  const float inv = 1.0f / scal[1];
+  for (int c = threadIdx.x; c < d_c; c += blockDim.x) {
+    float v = 0.0f;
+    for (int j = 0; j < n_split; ++j) {
+      const float w = wsh[j];
+      if (w != 0.0f) v = fmaf(w, o_part[(base + (size_t)j * n_h) * d_c + c], v);
+    }
+    o_lat[((size_t)bq * n_h + h) * d_c + c] = v * inv;
+  }
+  if (threadIdx.x == 0 && lse)
+    lse[(size_t)bq * n_h + h] = (scal[0] + log2f(scal[1])) * 0.69314718055994531f;
+}
+
+}  // namespace
+
+hipError_t launch_decode_simt(const mla_dims& d, int B, int n_q,
+                              const void* q, const void* cache,
+                              const int32_t* block_table, int max_blocks,
+                              const int32_t* kv_lens, int n_split,
+                              float* o_part, float* m_part,
+                              float* l_part, float* o_final, float* lse_final,
+                              hipStream_t stream) {
+  const float scale_log2 =
+      (float)(1.4426950408889634 / __builtin_sqrt((double)(d.d_h + d.d_r)));
+  const size_t lds = (size_t)(d.d_c + d.d_r + d.d_c + NT) * sizeof(float) +
+                     NT * sizeof(int);
+  dim3 grid(B * n_q, n_split, d.n_h);
+  if (d.dtype == MLA_BF16)
+    hipLaunchKernelGGL(decode_simt_kernel<uint16_t>, grid, dim3(NT), lds,
+                       stream, (const uint16_t*)q, (const uint16_t*)cache,
+                       block_table, max_blocks, kv_lens, n_q, d.n_h, d.d_c,
+                       d.d_r, d.block_size, n_split, scale_log2, o_part,
+                       m_part, l_part, o_final, lse_final);
+  else
+    hipLaunchKernelGGL(decode_simt_kernel<float>, grid, dim3(NT), lds, stream,
+                       (const float*)q, (const float*)cache, block_table,
+                       max_blocks, kv_lens, n_q, d.n_h, d.d_c, d.d_r,
+                       d.block_size, n_split, scale_log2, o_part, m_part,
+                       l_part, o_final, lse_final);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
+                          const float* o_part, const float* m_part,
+                          const float* l_part, float* o_lat, float* lse,
+                          hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  dim3 grid(rows, d.n_h);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256),
+                     (size_t)n_split * sizeof(float), stream, d.n_h, d.d_c,
+                     n_split, o_part, m_part, l_part, o_lat, lse);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,171 @@
+// Element-wise epilogues of the projections: summing K-chunk partials,
+// RoPE, rounding to the layer dtype and the scatter of latent rows into the
+// paged cache.
+//
+// RoPE ('MLA：潜在表示压缩与解耦 RoPE', sections 5-6): position p rotates the
+// pair (x_j, x_{j + d_r/2}) by the angle p * theta_j, with cos/sin taken
+// from host-built fp32 tables [max_pos][d_r/2].  A position outside the
+// table (a caller error) yields NaN in the rotated columns instead of a read
+// past the table.
+
+#include "mla_common.hpp"
+#include "mla_kernels.hpp"
+
+namespace mla {
+namespace {
+
+__device__ __forceinline__ float sum_parts(const float* p, int nparts,
+                                           long stride, long i) {
+  float v = p[i];
+  for (int k = 1; k < nparts; ++k) v += p[k * stride + i];
+  return v;
+}
+
+__global__ void reduce_parts_kernel(const float* __restrict__ src, int nparts,
+                                    long part_stride, long n,
+                                    float* __restrict__ dst) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n;
+       i += (long)gridDim.x * blockDim.x)
+    dst[i] = sum_parts(src, nparts, part_stride, i);
+}
+
+// One workgroup per token.  Columns j < d_c are copied, the d_r RoPE columns
+// are rotated in pairs; the row goes to its paged cache slot.
+template <typename T>
+__global__ void append_scatter_kernel(
+    const float* __restrict__ acc, int nparts, long part_stride, int d_c,
+    int d_r, const int32_t* __restrict__ seq_idx,
+    const int32_t* __restrict__ pos, const float* __restrict__ rcos,
+    const float* __restrict__ rsin, int max_pos,
+    const int32_t* __restrict__ block_table, int max_blocks, int block_size,
+    T* __restrict__ cache) {
+  const int t = blockIdx.x;
+  const int width = d_c + d_r;
+  const int half = d_r / 2;
+  const int p = pos[t];
+  const int blk = block_table[(long)seq_idx[t] * max_blocks + p / block_size];
+  T* row = cache + ((long)blk * block_size + (p % block_size)) * width;
+  const long base = (long)t * width;
+  for (int j = threadIdx.x; j < d_c + half; j += blockDim.x) {
+    if (j < d_c) {
+      DT<T>::store(row, j, sum_parts(acc, nparts, part_stride, base + j));
+    } else {
+      const int jj = j - d_c;
+      const float x1 = sum_parts(acc, nparts, part_stride, base + d_c + jj);
+      const float x2 =
+          sum_parts(acc, nparts, part_stride, base + d_c + jj + half);
+      const bool ok = p >= 0 && p < max_pos;
+      const float c = ok ? rcos[(long)p * half + jj] : NAN;
+      const float s = ok ? rsin[(long)p * half + jj] : NAN;
+      DT<T>::store(row, d_c + jj, x1 * c - x2 * s);
+      DT<T>::store(row, d_c + jj + half, x1 * s + x2 * c);
+    }
+  }
+}
+
+template <typename T>
+__global__ void query_rope_kernel(const float* __restrict__ qr, long ld_qr,
+                                  int n_h, int d_c, int d_r,
+                                  const int32_t* __restrict__ pos,
+                                  const float* __restrict__ rcos,
+                                  const float* __restrict__ rsin, int max_pos,
+                                  T* __restrict__ q_out) {
+  const int t = blockIdx.x;
+  const int half = d_r / 2;
+  const int p = pos[t];
+  const float* src = qr + (long)t * ld_qr;
+  for (int i = threadIdx.x; i < n_h * half; i += blockDim.x) {
+    const int h = i / half, jj = i - h * half;
+    const float x1 = src[h * d_r + jj], x2 = src[h * d_r + jj + half];
+    const bool ok = p >= 0 && p < max_pos;
+    const float c = ok ? rcos[(long)p * half + jj] : NAN;
+    const float s = ok ? rsin[(long)p * half + jj] : NAN;
+    T* dst = q_out + ((long)t * n_h + h) * (d_c + d_r) + d_c;
+    DT<T>::store(dst, jj, x1 * c - x2 * s);
+    DT<T>::store(dst, jj + half, x1 * s + x2 * c);
+  }
+}
+
+template <typename T>
+__global__ void convert_kernel(const float* __restrict__ src, long lds,
+                               int nparts, long part_stride, int rows,
+                               int cols, T* __restrict__ dst, long ldd) {
+  const long n = (long)rows * cols;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n;
+       i += (long)gridDim.x * blockDim.x) {
+    const long r = i / cols, c = i - r * cols;
+    DT<T>::store(dst, r * ldd + c,
+                 sum_parts(src, nparts, part_stride, r * lds + c));
+  }
+}
+
+inline int grid_for(long n, int threads) {
+  long g = (n + threads - 1) / threads;
+  return (int)(g < 8192 ? (g < 1 ? 1 : g) : 8192);
+}
+
+}  // namespace
+
+hipError_t launch_reduce_parts(const float* src, int nparts, long part_stride,
+                               long n, float* dst, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(reduce_parts_kernel, dim3(grid_for(n, 256)), dim3(256), 0,
+                     stream, src, nparts, part_stride, n, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_scatter(const mla_dims& d, int T, const float* acc,
+                                 int nparts, long part_stride,
+                                 const int32_t* seq_idx, const int32_t* pos,
+                                 const float* rope_cos, const float* rope_sin,
+                                 int max_pos, const int32_t* block_table,
+                                 int max_blocks, void* cache,
+                                 hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  if (d.dtype == MLA_BF16)
+    hipLaunchKernelGGL(append_scatter_kernel<uint16_t>, dim3(T), dim3(256), 0,
+                       stream, acc, nparts, part_stride, d.d_c, d.d_r, seq_idx,
+                       pos, rope_cos, rope_sin, max_pos, block_table,
+                       max_blocks, d.block_size, (uint16_t*)cache);
+  else
+    hipLaunchKernelGGL(append_scatter_kernel<float>, dim3(T), dim3(256), 0,
+                       stream, acc, nparts, part_stride, d.d_c, d.d_r, seq_idx,
+                       pos, rope_cos, rope_sin, max_pos, block_table,
+                       max_blocks, d.block_size, (float*)cache);
+  return hipGetLastError();
+}
+
+hipError_t launch_query_rope(const mla_dims& d, int T, const float* qr,
+                             long ld_qr, const int32_t* pos,
+                             const float* rope_cos, const float* rope_sin,
+                             int max_pos, void* q_out, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  if (d.dtype == MLA_BF16)
+    hipLaunchKernelGGL(query_rope_kernel<uint16_t>, dim3(T), dim3(256), 0,
+                       stream, qr, ld_qr, d.n_h, d.d_c, d.d_r, pos, rope_cos,
+                       rope_sin, max_pos, (uint16_t*)q_out);
+  else
+    hipLaunchKernelGGL(query_rope_kernel<float>, dim3(T), dim3(256), 0,
+                       stream, qr, ld_qr, d.n_h, d.d_c, d.d_r, pos, rope_cos,
+                       rope_sin, max_pos, (float*)q_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_convert(const mla_dims& d, int rows, int cols,
+                          const float* src, long lds, int nparts,
+                          long part_stride, void* dst, long ldd,
+                          hipStream_t stream) {
+  const long n = (long)rows * cols;
+  if (n <= 0) return hipSuccess;
+  if (d.dtype == MLA_BF16)
+    hipLaunchKernelGGL(convert_kernel<uint16_t>, dim3(grid_for(n, 256)),
+                       dim3(256), 0, stream, src, lds, nparts, part_stride,
+                       rows, cols, (uint16_t*)dst, ldd);
+  else
+    hipLaunchKernelGGL(convert_kernel<float>, dim3(grid_for(n, 256)),
+                       dim3(256), 0, stream, src, lds, nparts, part_stride,
+                       rows, cols, (float*)dst, ldd);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,437 @@
+// C ABI of libmla.so: argument checks, workspace layout and the launch
+// sequence of each step.  Declarations and contracts: include/mla.h.
+
+#include <math.h>
+#include <string.h>
+
+#include "mla_common.hpp"
+#include "mla_kernels.hpp"
+
+using namespace mla;
+
+namespace {
+
+constexpr size_t WS_ALIGN = 256;
+
+inline size_t align_up(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
+
+// Bump allocator over the caller's workspace.
+struct Carve {
+  char* base;
+  size_t used = 0;
+  explicit Carve(void* p) : base((char*)p) {}
+  float* take(size_t floats) {
+    float* p = (float*)(base + used);
+    used += align_up(floats * sizeof(float));
+    return p;
+  }
+};
+
+bool dims_ok(const mla_dims* d) {
+  if (!d) return false;
+  if (d->d <= 0 || d->n_h <= 0 || d->d_h <= 0 || d->d_c <= 0 || d->d_r <= 0 ||
+      d->d_cq <= 0 || d->block_size <= 0)
+    return false;
+  if (d->d_r % 2) return false;
+  if (d->block_size & (d->block_size - 1)) return false;
+  if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return false;
+  return true;
+}
+
+// The bf16 kernels move 8 elements (16 bytes) at a time along every row.
+bool dims_supported(const mla_dims* d) {
+  if (d->dtype != MLA_BF16) return true;
+  return d->d % 8 == 0 && d->d_h % 8 == 0 && d->d_c % 8 == 0 &&
+         d->d_r % 8 == 0 && d->d_cq % 8 == 0;
+}
+
+mla_status dev(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_DEVICE; }
+
+#define MLA_TRY(expr)                          \
+  do {                                         \
+    hipError_t e_ = (expr);                    \
+    if (e_ != hipSuccess) return MLA_ERR_DEVICE; \
+  } while (0)
+
+// ---- GEMM argument builders (shared by sizing and launching) ----
+GemmArgs append_gemm(const mla_dims& d, int T) {
+  GemmArgs g;
+  g.lda = d.d;
+  g.nb1 = d.d_c;
+  g.ldb = d.d;
+  g.ldc = d.d_c + d.d_r;
+  g.c_ks = (long)T * (d.d_c + d.d_r);
+  g.M = T;
+  g.N = d.d_c + d.d_r;
+  g.K = d.d;
+  g.k_split = gemm_pick_k_split(d, g);
+  return g;
+}
+GemmArgs cq_gemm(const mla_dims& d, int T) {
+  GemmArgs g;
+  g.lda = d.d;
+  g.ldb = d.d;
+  g.ldc = d.d_cq;
+  g.c_ks = (long)T * d.d_cq;
+  g.M = T;
+  g.N = d.d_cq;
+  g.K = d.d;
+  g.k_split = gemm_pick_k_split(d, g);
+  return g;
+}
+GemmArgs qcr_gemm(const mla_dims& d, int T) {
+  GemmArgs g;
+  g.a_f32 = 1;
+  g.lda = d.d_cq;
+  g.nb1 = d.n_h * d.d_h;
+  g.ldb = d.d_cq;
+  g.ldc = (long)d.n_h * (d.d_h + d.d_r);
+  g.c_ks = (long)T * g.ldc;
+  g.M = T;
+  g.N = d.n_h * (d.d_h + d.d_r);
+  g.K = d.d_cq;
+  g.k_split = gemm_pick_k_split(d, g);
+  return g;
+}
+GemmArgs absorb_gemm(const mla_dims& d, int T) {
+  GemmArgs g;
+  g.a_f32 = 1;
+  g.lda = (long)d.n_h * (d.d_h + d.d_r);
+  g.a_bs = d.d_h;
+  g.b_nn = 1;
+  g.ldb = d.d_c;
+  g.b_bs = (long)d.d_h * d.d_c;
+  g.ldc = (long)d.n_h * d.d_c;
+  g.c_bs = d.d_c;
+  g.M = T;
+  g.N = d.d_c;
+  g.K = d.d_h;
+  g.batch = d.n_h;
+  g.k_split = 1;
+  return g;
+}
+GemmArgs uv_gemm(const mla_dims& d, int T) {
+  GemmArgs g;
+  g.a_f32 = 1;
+  g.lda = (long)d.n_h * d.d_c;
+  g.a_bs = d.d_c;
+  g.ldb = d.d_c;
+  g.b_bs = (long)d.d_h * d.d_c;
+  g.ldc = (long)d.n_h * d.d_h;
+  g.c_bs = d.d_h;
+  g.M = T;
+  g.N = d.d_h;
+  g.K = d.d_c;
+  g.batch = d.n_h;
+  g.k_split = 1;
+  return g;
+}
+GemmArgs o_gemm(const mla_dims& d, int T) {
+  GemmArgs g;
+  g.a_f32 = 1;
+  g.lda = (long)d.n_h * d.d_h;
+  g.ldb = (long)d.n_h * d.d_h;
+  g.ldc = d.d;
+  g.c_ks = (long)T * d.d;
+  g.M = T;
+  g.N = d.d;
+  g.K = d.n_h * d.d_h;
+  g.k_split = gemm_pick_k_split(d, g);
+  return g;
+}
+
+size_t parts_floats(const GemmArgs& g) { return (size_t)g.k_split * g.M * g.N * g.batch; }
+
+int decode_nblk(const mla_dims& d, int max_kv_len) {
+  return (max_kv_len + d.block_size - 1) / d.block_size;
+}
+
+int auto_splits(const mla_dims& d, int B, int n_q, int max_kv_len) {
+  const int nblk = decode_nblk(d, max_kv_len);
+  long groups = (long)B * n_q;
+  long target;
+  if (decode_mfma_supported(d)) {
+    groups *= (d.n_h + 127) / 128;
+    target = 256;   // one workgroup per CU (LDS-bound occupancy)
+  } else {
+    groups *= d.n_h;
+    target = 1024;
+  }
+  long s = (target + groups - 1) / groups;
+  const long cap = nblk / 4 > 0 ? nblk / 4 : 1;  // >= 4 blocks per split
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+// Effective split count for a requested one (at most one block per split).
+int split_count(const mla_dims& d, int max_kv_len, int want) {
+  const int nblk = decode_nblk(d, max_kv_len);
+  if (want < 1) want = 1;
+  return want > nblk ? nblk : want;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "null pointer argument";
+    case MLA_ERR_SHAPE: return "inconsistent or invalid sizes";
+    case MLA_ERR_UNSUPPORTED: return "dims or dtype not supported";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_RANGE: return "argument out of range";
+    case MLA_ERR_DEVICE: return "device launch failed";
+  }
+  return "unknown status";
+}
+
+const char* mla_version(void) { return "mla-gfx950 0.1"; }
+
+mla_status mla_rope_tables_host(int32_t d_r, double base, int32_t max_pos,
+                                float* cos_out, float* sin_out) {
+  if (!cos_out || !sin_out) return MLA_ERR_NULL;
+  if (d_r <= 0 || d_r % 2 || max_pos <= 0 || !(base > 0.0)) return MLA_ERR_SHAPE;
+  const int half = d_r / 2;
+  for (int j = 0; j < half; ++j) {
+    const double theta = pow(base, -2.0 * j / (double)d_r);
+    for (int p = 0; p < max_pos; ++p) {
+      const double a = (double)p * theta;
+      cos_out[(size_t)p * half + j] = (float)cos(a);
+      sin_out[(size_t)p * half + j] = (float)sin(a);
+    }
+  }
+  return MLA_OK;
+}
+
+// ------------------------------------------------------------------ append
+size_t mla_append_workspace_bytes(const mla_dims* dims, int32_t T) {
+  if (!dims_ok(dims) || T <= 0) return 0;
+  return align_up(parts_floats(append_gemm(*dims, T)) * sizeof(float));
+}
+
+mla_status mla_append_cache(const mla_dims* dims, int32_t T, const void* h,
+                            const int32_t* seq_idx, const int32_t* pos,
+                            const void* w_dkv, const void* w_kr,
+                            const float* rope_cos, const float* rope_sin,
+                            int32_t max_pos, const int32_t* block_table,
+                            int32_t max_blocks, void* cache,
+                            int32_t num_blocks, void* ws, size_t ws_bytes,
+                            mla_stream_t stream) {
+  if (!dims) return MLA_ERR_NULL;
+  if (!dims_ok(dims) || T < 0 || max_pos <= 0 || max_blocks <= 0 ||
+      num_blocks <= 0)
+    return MLA_ERR_SHAPE;
+  if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  if (T == 0) return MLA_OK;
+  if (!h || !seq_idx || !pos || !w_dkv || !w_kr || !rope_cos || !rope_sin ||
+      !block_table || !cache)
+    return MLA_ERR_NULL;
+  const mla_dims& d = *dims;
+  const size_t need = mla_append_workspace_bytes(dims, T);
+  if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs g = append_gemm(d, T);
+  g.A = h;
+  g.B = w_dkv;
+  g.B2 = w_kr;
+  g.C = (float*)ws;
+  MLA_TRY(launch_gemm(d, g, s));
+  MLA_TRY(launch_append_scatter(d, T, g.C, g.k_split, g.c_ks, seq_idx, pos,
+                                rope_cos, rope_sin, max_pos, block_table,
+                                max_blocks, cache, s));
+  return MLA_OK;
+}
+
+// ------------------------------------------------------------------ absorb
+namespace {
+struct AbsorbWs {
+  float *cq_parts, *cq, *qcr_parts, *qcr, *qlat;
+  size_t bytes;
+};
+AbsorbWs absorb_layout(const mla_dims& d, int T, void* base) {
+  Carve c(base);
+  AbsorbWs w;
+  const GemmArgs g1 = cq_gemm(d, T), g2 = qcr_gemm(d, T), g3 = absorb_gemm(d, T);
+  w.cq_parts = c.take(parts_floats(g1));
+  w.cq = g1.k_split > 1 ? c.take((size_t)T * d.d_cq) : w.cq_parts;
+  w.qcr_parts = c.take(parts_floats(g2));
+  w.qcr = g2.k_split > 1 ? c.take((size_t)T * g2.N) : w.qcr_parts;
+  w.qlat = c.take(parts_floats(g3));
+  w.bytes = c.used;
+  return w;
+}
+}  // namespace
+
+size_t mla_absorb_workspace_bytes(const mla_dims* dims, int32_t T) {
+  if (!dims_ok(dims) || T <= 0) return 0;
+  return absorb_layout(*dims, T, nullptr).bytes;
+}
+
+mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
+                        const int32_t* pos, const void* w_dq,
+                        const void* w_uq, const void* w_qr, const void* w_uk,
+                        const float* rope_cos, const float* rope_sin,
+                        int32_t max_pos, void* q_out, void* ws,
+                        size_t ws_bytes, mla_stream_t stream) {
+  if (!dims) return MLA_ERR_NULL;
+  if (!dims_ok(dims) || T < 0 || max_pos <= 0) return MLA_ERR_SHAPE;
+  if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  if (T == 0) return MLA_OK;
+  if (!h || !pos || !w_dq || !w_uq || !w_qr || !w_uk || !rope_cos ||
+      !rope_sin || !q_out)
+    return MLA_ERR_NULL;
+  const mla_dims& d = *dims;
+  if (!ws) return MLA_ERR_WORKSPACE;
+  const AbsorbWs w = absorb_layout(d, T, ws);
+  if (ws_bytes < w.bytes) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+
+  GemmArgs g1 = cq_gemm(d, T);
+  g1.A = h;
+  g1.B = w_dq;
+  g1.C = w.cq_parts;
+  MLA_TRY(launch_gemm(d, g1, s));
+  if (g1.k_split > 1)
+    MLA_TRY(launch_reduce_parts(w.cq_parts, g1.k_split, g1.c_ks,
+                                (long)T * d.d_cq, w.cq, s));
+
+  GemmArgs g2 = qcr_gemm(d, T);
+  g2.A = w.cq;
+  g2.B = w_uq;
+  g2.B2 = w_qr;
+  g2.C = w.qcr_parts;
+  MLA_TRY(launch_gemm(d, g2, s));
+  if (g2.k_split > 1)
+    MLA_TRY(launch_reduce_parts(w.qcr_parts, g2.k_split, g2.c_ks,
+                                (long)T * g2.N, w.qcr, s));
+
+  MLA_TRY(launch_query_rope(d, T, w.qcr + (long)d.n_h * d.d_h, g2.ldc, pos,
+                            rope_cos, rope_sin, max_pos, q_out, s));
+
+  GemmArgs g3 = absorb_gemm(d, T);
+  g3.A = w.qcr;
+  g3.B = w_uk;
+  g3.C = w.qlat;
+  MLA_TRY(launch_gemm(d, g3, s));
+  MLA_TRY(launch_convert(d, T * d.n_h, d.d_c, w.qlat, d.d_c, 1, 0, q_out,
+                         d.d_c + d.d_r, s));
+  return MLA_OK;
+}
+
+// ------------------------------------------------------------------ decode
+int32_t mla_decode_auto_splits(const mla_dims* dims, int32_t B, int32_t n_q,
+                               int32_t max_kv_len) {
+  if (!dims_ok(dims) || B <= 0 || n_q <= 0 || max_kv_len <= 0) return 1;
+  return split_count(*dims, max_kv_len, auto_splits(*dims, B, n_q, max_kv_len));
+}
+
+size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t B, int32_t n_q,
+                                  int32_t max_kv_len, int32_t n_split) {
+  if (!dims_ok(dims) || B <= 0 || n_q <= 0 || max_kv_len <= 0 || n_split < 0)
+    return 0;
+  const mla_dims& d = *dims;
+  const int ns = split_count(
+      d, max_kv_len, n_split ? n_split : auto_splits(d, B, n_q, max_kv_len));
+  if (ns <= 1) return 0;
+  const size_t rows = (size_t)B * n_q * ns * d.n_h;
+  return align_up(rows * d.d_c * sizeof(float)) + 2 * align_up(rows * sizeof(float));
+}
+
+mla_status mla_decode(const mla_dims* dims, int32_t B, int32_t n_q,
+                      const void* q, const void* cache, int32_t num_blocks,
+                      const int32_t* block_table, int32_t max_blocks,
+                      const int32_t* kv_lens, int32_t max_kv_len,
+                      int32_t causal, int32_t n_split, float* o_lat,
+                      float* lse, void* ws, size_t ws_bytes,
+                      mla_stream_t stream) {
+  if (!dims) return MLA_ERR_NULL;
+  if (!dims_ok(dims) || B <= 0 || n_q <= 0 || max_kv_len <= 0 ||
+      num_blocks <= 0 || max_blocks <= 0 || n_split < 0)
+    return MLA_ERR_SHAPE;
+  if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  if (!q || !cache || !block_table || !kv_lens || !o_lat) return MLA_ERR_NULL;
+  const mla_dims& d = *dims;
+  if (n_q > max_kv_len) return MLA_ERR_SHAPE;
+  if (n_q > 1 && causal != 1) return MLA_ERR_UNSUPPORTED;
+  const int nblk = decode_nblk(d, max_kv_len);
+  if (nblk > max_blocks) return MLA_ERR_RANGE;
+  if (n_split > nblk) return MLA_ERR_RANGE;
+  const int ns = split_count(
+      d, max_kv_len, n_split ? n_split : auto_splits(d, B, n_q, max_kv_len));
+  const size_t need = mla_decode_workspace_bytes(dims, B, n_q, max_kv_len, n_split);
+  if (need && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  float *o_part = nullptr, *m_part = nullptr, *l_part = nullptr;
+  if (ns > 1) {
+    Carve c(ws);
+    const size_t rows = (size_t)B * n_q * ns * d.n_h;
+    o_part = c.take(rows * d.d_c);
+    m_part = c.take(rows);
+    l_part = c.take(rows);
+  }
+  if (decode_mfma_supported(d))
+    MLA_TRY(launch_decode_mfma(d, B, n_q, q, cache, block_table, max_blocks,
+                               kv_lens, ns, o_part, m_part, l_part, o_lat,
+                               lse, s));
+  else
+    MLA_TRY(launch_decode_simt(d, B, n_q, q, cache, block_table, max_blocks,
+                               kv_lens, ns, o_part, m_part, l_part, o_lat,
+                               lse, s));
+  if (ns > 1)
+    MLA_TRY(launch_combine(d, B * n_q, ns, o_part, m_part, l_part, o_lat, lse, s));
+  return MLA_OK;
+}
+
+// --------------------------------------------------------------------- out
+namespace {
+struct OutWs {
+  float *v, *u_parts;
+  size_t bytes;
+};
+OutWs out_layout(const mla_dims& d, int T, void* base) {
+  Carve c(base);
+  OutWs w;
+  w.v = c.take(parts_floats(uv_gemm(d, T)));
+  w.u_parts = c.take(parts_floats(o_gemm(d, T)));
+  w.bytes = c.used;
+  return w;
+}
+}  // namespace
+
+size_t mla_out_workspace_bytes(const mla_dims* dims, int32_t T) {
+  if (!dims_ok(dims) || T <= 0) return 0;
+  return out_layout(*dims, T, nullptr).bytes;
+}
+
+mla_status mla_out(const mla_dims* dims, int32_t T, const float* o_lat,
+                   const void* w_uv, const void* w_o, void* u, void* ws,
+                   size_t ws_bytes, mla_stream_t stream) {
+  if (!dims) return MLA_ERR_NULL;
+  if (!dims_ok(dims) || T < 0) return MLA_ERR_SHAPE;
+  if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  if (T == 0) return MLA_OK;
+  if (!o_lat || !w_uv || !w_o || !u) return MLA_ERR_NULL;
+  const mla_dims& d = *dims;
+  if (!ws) return MLA_ERR_WORKSPACE;
+  const OutWs w = out_layout(d, T, ws);
+  if (ws_bytes < w.bytes) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs g1 = uv_gemm(d, T);
+  g1.A = o_lat;
+  g1.B = w_uv;
+  g1.C = w.v;
+  MLA_TRY(launch_gemm(d, g1, s));
+  GemmArgs g2 = o_gemm(d, T);
+  g2.A = w.v;
+  g2.B = w_o;
+  g2.C = w.u_parts;
+  MLA_TRY(launch_gemm(d, g2, s));
+  MLA_TRY(launch_convert(d, T, d.d, w.u_parts, d.d, g2.k_split, g2.c_ks, u,
+                         d.d, s));
+  return MLA_OK;
+}
+
+}  // extern "C"

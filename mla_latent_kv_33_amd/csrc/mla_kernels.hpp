@@ -1,0 +1,91 @@
+// Internal launchers shared by the C ABI (mla_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mla.h"
+
+namespace mla {
+
+// ---- split-KV decode ---------------------------------------------------
+// Split j of a (sequence, query) whose visible keys span nblk blocks covers
+// blocks [j nblk / n_split, (j + 1) nblk / n_split).
+// Partials: o_part [B*n_q][n_split][n_h][d_c] (unnormalised), m_part/l_part
+// [B*n_q][n_split][n_h] with m in log2 units.  With n_split == 1 the kernels
+// write o_final [B*n_q][n_h][d_c] and lse_final (natural log) directly.
+bool decode_mfma_supported(const mla_dims& d);
+hipError_t launch_decode_mfma(const mla_dims& d, int B, int n_q,
+                              const void* q, const void* cache,
+                              const int32_t* block_table, int max_blocks,
+                              const int32_t* kv_lens, int n_split,
+                              float* o_part, float* m_part,
+                              float* l_part, float* o_final, float* lse_final,
+                              hipStream_t stream);
+hipError_t launch_decode_simt(const mla_dims& d, int B, int n_q,
+                              const void* q, const void* cache,
+                              const int32_t* block_table, int max_blocks,
+                              const int32_t* kv_lens, int n_split,
+                              float* o_part, float* m_part,
+                              float* l_part, float* o_final, float* lse_final,
+                              hipStream_t stream);
+hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
+                          const float* o_part, const float* m_part,
+                          const float* l_part, float* o_lat, float* lse,
+                          hipStream_t stream);
+
+// ---- GEMM C = A . B^T --------------------------------------------------
+// A [M][K] (row stride lda, batch stride a_bs), fp32 or the layer dtype.
+// B (layer dtype) is either [N][K] ("NT", row stride ldb), optionally in two
+// parts - rows n < nb1 from B and rows n >= nb1 from B2 (row n - nb1) - or
+// [K][N] ("NN", row stride ldb, no second part).  C is fp32 [M][N] (row
+// stride ldc).  Batch index z offsets A, B (and B2) and C by their batch
+// strides.  With k_split > 1 the K range is cut into k_split chunks and
+// chunk kz writes its own partial product at C + kz * c_ks; the consumer
+// sums the parts (deterministic, no atomics).
+struct GemmArgs {
+  const void* A = nullptr;
+  int a_f32 = 0;  // A is fp32 (else the layer dtype)
+  long lda = 0, a_bs = 0;
+  const void* B = nullptr;
+  const void* B2 = nullptr;
+  int nb1 = 1 << 30;
+  int b_nn = 0;  // B stored [K][N]
+  long ldb = 0, b_bs = 0;
+  float* C = nullptr;
+  long ldc = 0, c_bs = 0, c_ks = 0;
+  int M = 0, N = 0, K = 0, batch = 1;
+  int k_split = 1;
+};
+hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
+                       hipStream_t stream);
+int gemm_pick_k_split(const mla_dims& d, const GemmArgs& g);
+
+// ---- element-wise kernels ----------------------------------------------
+// Inputs given as (pointer, nparts, part_stride) are the sum of nparts fp32
+// arrays spaced part_stride floats apart (the K chunks of a GEMM).
+// dst[i] = sum of the parts at i, for i < n.
+hipError_t launch_reduce_parts(const float* src, int nparts, long part_stride,
+                               long n, float* dst, hipStream_t stream);
+// acc [T][d_c + d_r] fp32 -> RoPE on the last d_r columns -> cache rows.
+hipError_t launch_append_scatter(const mla_dims& d, int T, const float* acc,
+                                 int nparts, long part_stride,
+                                 const int32_t* seq_idx, const int32_t* pos,
+                                 const float* rope_cos, const float* rope_sin,
+                                 int max_pos, const int32_t* block_table,
+                                 int max_blocks, void* cache,
+                                 hipStream_t stream);
+// qr rows of ld_qr floats, the [n_h][d_r] block of token t at
+// qr + t * ld_qr -> RoPE -> q_out[t][h][d_c ..] (layer dtype).
+hipError_t launch_query_rope(const mla_dims& d, int T, const float* qr,
+                             long ld_qr, const int32_t* pos,
+                             const float* rope_cos, const float* rope_sin,
+                             int max_pos, void* q_out, hipStream_t stream);
+// src fp32 [rows][cols] (row stride lds, parts) -> dst layer dtype (row
+// stride ldd).
+hipError_t launch_convert(const mla_dims& d, int rows, int cols,
+                          const float* src, long lds, int nparts,
+                          long part_stride, void* dst, long ldd,
+                          hipStream_t stream);
+
+}  // namespace mla

@@ -241,7 +241,7 @@ def workload(name: str) -> Workload:
                         True)
     if name == "b64_ctx8k":
         return Workload("b64_ctx8k", DEEPSEEK_V2, "bf16", 64, (8192,) * 64, 1,
-                        6, True)
+                        6, True, synthetic_context=True)
     if name == "b4_ctx128k":
         return Workload("b4_ctx128k", DEEPSEEK_V2, "bf16", 4, (131072,) * 4, 1,
                         4, False, n_split=64, synthetic_context=True)

@@ -1,0 +1,72 @@
+"""Shared helpers of the GPU parity tests: error metrics and oracle
+references for sampled sequences of a workload."""
+import sys
+import time
+
+import numpy as np
+
+from mla_latent_kv_33_amd import workloads as W
+from oracle import mla_oracle as orc
+
+# Parity bars: bf16 inputs: relative Frobenius 5e-3 and max-abs 2e-2;
+# fp32 inputs: 1e-5 for both.
+TOL = {"bf16": (5e-3, 2e-2), "f32": (1e-5, 1e-5)}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def errors(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    diff = got - ref
+    rel = np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-300)
+    return float(rel), float(np.abs(diff).max()) if diff.size else 0.0
+
+
+def assert_close(name, got, ref, dtype, tol=None):
+    rel_tol, abs_tol = TOL[dtype] if tol is None else tol
+    rel, mx = errors(got, ref)
+    log(f"  {name}: rel_frob={rel:.3e} max_abs={mx:.3e} "
+        f"(bars {rel_tol:g}, {abs_tol:g})")
+    assert np.all(np.isfinite(np.asarray(got, np.float64))), f"{name}: non-finite"
+    assert rel <= rel_tol and mx <= abs_tol, f"{name}: rel {rel} max {mx}"
+
+
+def context_latents(wl: W.Workload, weights, b: int):
+    """Oracle-side latents (c_kv, k_r) of sequence b's context: recomputed
+    from its hidden states, or the seeded rows for a given cache."""
+    d = wl.dims
+    c = wl.ctx[b]
+    if wl.synthetic_context:
+        rows = W.latent_rows(d, wl.dtype, wl.seed, b, 0, c).astype(np.float64)
+        return rows[:, :d.d_c], rows[:, d.d_c:]
+    h = W.hidden_states(d, wl.dtype, wl.seed, b, 0, c)
+    return orc.kv_latent(h, np.arange(c), weights["w_dkv"], weights["w_kr"],
+                         W.ROPE_BASE)
+
+
+def oracle_sequence(wl: W.Workload, weights, b: int, q_rows=None, heads=None):
+    """Oracle step of sequence b: non-absorbed attention (all heads unless
+    `heads`), plus the absorbed-form latent output for the same queries."""
+    t0 = time.time()
+    d = wl.dims
+    c_kv, k_r = context_latents(wl, weights, b)
+    h_new = W.hidden_states(d, wl.dtype, wl.seed, b, wl.ctx[b], wl.n_q)
+    ref = orc.decode_step(weights, d.n_h, W.ROPE_BASE, h_new, c_kv, k_r,
+                          heads=heads, q_rows=q_rows)
+    rows = np.concatenate([np.concatenate([c_kv, ref["c_kv"]]),
+                           np.concatenate([k_r, ref["k_r"]])], axis=1)
+    q = orc.absorb_query(ref["q_c"], ref["q_r"], weights["w_uk"])
+    o_lat, lse = orc.latent_attention(q, ref["q_pos"], rows, d.d_c, d.d_h)
+    ref["q"] = q
+    ref["o_lat"] = o_lat
+    ref["lse_lat"] = lse
+    if "u" not in ref:
+        ref["u_lat"] = orc.deferred_output(o_lat, weights["w_uv"],
+                                           weights["w_o"], d.d_h)
+    log(f"  oracle seq {b} (ctx {wl.ctx[b]}, queries "
+        f"{'all' if q_rows is None else len(q_rows)}): {time.time() - t0:.1f}s")
+    return ref

@@ -1,0 +1,227 @@
+"""Properties of the HIP path that hold at any size: bit-exact cache
+indexing, split-count and block-table invariance, determinism, the
+causal/decode consistency of a chunk, and degenerate sizes."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from mla_latent_kv_33_amd import binding as B
+from mla_latent_kv_33_amd import flow
+from mla_latent_kv_33_amd import workloads as W
+from mla_latent_kv_33_amd.layer import MlaLayer, to_device
+from oracle import mla_oracle as orc
+from tests.gpu_common import assert_close, log, oracle_sequence
+
+pytestmark = pytest.mark.gpu
+DS = W.DEEPSEEK_V2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+_cache = {}
+
+
+def ds_layer(seed=2):
+    if seed not in _cache:
+        _cache.clear()
+        w = W.make_weights(DS, "bf16", seed)
+        _cache[seed] = (MlaLayer(DS, "bf16", w, 20000), w)
+    return _cache[seed]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_cache_indexing_bit_exact(dtype):
+    """Integer-valued inputs make every product and sum exact, so each
+    cached c_KV row and the k_R of position-0 tokens must equal the oracle
+    bit for bit; every row must sit at its block-table slot."""
+    dims = DS if dtype == "bf16" else W.TINY
+    rng = np.random.default_rng(123)
+    w = {k: np.zeros(s, np.float32) for k, s in W.weight_shapes(dims).items()}
+    for k in ("w_dkv", "w_kr"):
+        o, i = w[k].shape
+        for r in range(o):   # 8 entries of +-1 per row
+            cols = rng.choice(i, 8, replace=False)
+            w[k][r, cols] = rng.choice([-1.0, 1.0], 8)
+    layer = MlaLayer(dims, dtype, w, 4096)
+    lens = np.array([1, 64, 65, 200, 130])
+    table_np, nb = W.block_table(lens, True, 9)
+    cache = layer.new_cache(nb)
+    cache.fill_(float("nan"))
+    table = torch.from_numpy(table_np).cuda()
+    T = int(lens.sum())
+    h = rng.integers(-3, 4, size=(T, dims.d)).astype(np.float32)
+    seq = np.repeat(np.arange(len(lens)), lens).astype(np.int32)
+    pos = np.concatenate([np.arange(n) for n in lens]).astype(np.int32)
+    perm = rng.permutation(T)    # token order does not matter
+    layer.append(to_device(h[perm], dtype), torch.from_numpy(seq[perm]).cuda(),
+                 torch.from_numpy(pos[perm]).cuda(), table, cache)
+    torch.cuda.synchronize()
+    host = cache.float().cpu().numpy()
+    c_kv, k_r = orc.kv_latent(h, pos, w["w_dkv"], w["w_kr"], W.ROPE_BASE)
+    for t in range(T):
+        b, p = seq[t], pos[t]
+        row = host[table_np[b, p // 64], p % 64]
+        np.testing.assert_array_equal(row[:dims.d_c], c_kv[t])
+        if p == 0:
+            np.testing.assert_array_equal(row[dims.d_c:], k_r[t])
+        else:
+            np.testing.assert_allclose(row[dims.d_c:], k_r[t], rtol=1e-2,
+                                       atol=1e-2 * (1 + np.abs(k_r[t]).max()))
+    # slots no token owns stay untouched (NaN)
+    owned = np.zeros(host.shape[:2], bool)
+    for b, n in enumerate(lens):
+        for p in range(n):
+            owned[table_np[b, p // 64], p % 64] = True
+    assert np.isnan(host[~owned]).all()
+    log(f"  {T} rows bit-exact ({dtype})")
+
+
+def _decode_once(layer, q, cache, table, kv, max_kv, n_split):
+    o, lse = layer.decode(q, cache, table, kv, max_kv, n_split=n_split)
+    torch.cuda.synchronize()
+    return o.clone(), lse.clone()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_split_count_invariance_and_determinism(dtype):
+    """Any split count gives the same result: exactly up to fp32 rounding for
+    fp32 layers; for bf16 layers the weights P are rounded to bf16 against
+    each split's own reference maximum, so splits agree to that rounding.
+    A fixed split count is bitwise deterministic."""
+    # bf16: each P carries up to 2^-9 relative rounding, so o agrees to
+    # ~1e-3 and l (hence lse) to ~2^-9 / sqrt(keys) relative.
+    if dtype == "bf16":
+        layer, _ = ds_layer()
+        dims, tol, lse_tol = DS, (3e-3, 2e-2), (1e-4, 4e-3)
+    else:
+        dims, tol, lse_tol = W.TINY, (2e-6, 1e-5), (1e-6, 2e-5)
+        layer = MlaLayer(dims, "f32", W.make_weights(dims, "f32", 1), 5000)
+    width = dims.d_c + dims.d_r
+    rng = np.random.default_rng(5)
+    lens = np.array([4097, 1000, 64, 1, 3333])
+    table_np, nb = W.block_table(lens, True, 11)
+    cache = layer.new_cache(nb)
+    cache.copy_(to_device(rng.standard_normal((nb, 64, width)).astype(
+        np.float32), dtype))
+    table = torch.from_numpy(table_np).cuda()
+    kv = torch.from_numpy(lens.astype(np.int32)).cuda()
+    q = to_device(0.5 * rng.standard_normal((5, 1, dims.n_h, width)).astype(
+        np.float32), dtype)
+    base, base_lse = _decode_once(layer, q, cache, table, kv, 4097, 1)
+    for ns in (2, 7, 16, 65):
+        o, lse = _decode_once(layer, q, cache, table, kv, 4097, ns)
+        assert_close(f"n_split={ns} vs 1", o.cpu().numpy(),
+                     base.cpu().numpy(), "f32", tol=tol)
+        assert_close(f"lse n_split={ns}", lse.cpu().numpy(),
+                     base_lse.cpu().numpy(), "f32", tol=lse_tol)
+        o2, lse2 = _decode_once(layer, q, cache, table, kv, 4097, ns)
+        assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def test_block_table_permutation_invariance():
+    """The same rows under a different physical block order give bitwise
+    the same output."""
+    layer, _ = ds_layer()
+    rng = np.random.default_rng(6)
+    lens = np.array([700, 2000])
+    rows = [rng.standard_normal((n, 576)).astype(np.float32) for n in lens]
+    q = to_device(0.5 * rng.standard_normal((2, 1, 128, 576)).astype(
+        np.float32), "bf16")
+    kv = torch.from_numpy(lens.astype(np.int32)).cuda()
+    outs = []
+    for permuted in (False, True):
+        table_np, nb = W.block_table(lens, permuted, 21)
+        img = np.zeros((nb, 64, 576), np.float32)
+        for b in range(2):
+            flow.scatter_rows_host(img, table_np, b, 0, rows[b], 64)
+        cache = to_device(img, "bf16")
+        outs.append(_decode_once(layer, q, cache,
+                                 torch.from_numpy(table_np).cuda(), kv, 2000,
+                                 3))
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+
+
+def test_chunk_last_row_equals_decode():
+    """In a causal chunk the last query sees the whole cache, the first only
+    the context and itself: they equal plain decodes at those lengths."""
+    layer, w = ds_layer()
+    rng = np.random.default_rng(7)
+    ctx, n_q = 1000, 77
+    kvl = ctx + n_q
+    table_np, nb = W.block_table(np.array([kvl]), False, 1)
+    img = np.zeros((nb, 64, 576), np.float32)
+    flow.scatter_rows_host(img, table_np, 0, 0,
+                           rng.standard_normal((kvl, 576)).astype(np.float32),
+                           64)
+    cache = to_device(img, "bf16")
+    table = torch.from_numpy(table_np).cuda()
+    q = to_device(0.5 * rng.standard_normal((1, n_q, 128, 576)).astype(
+        np.float32), "bf16")
+    o, lse = _decode_once(layer, q, cache, table,
+                          torch.tensor([kvl], dtype=torch.int32).cuda(), kvl,
+                          1)
+    o_last, _ = _decode_once(layer, q[:, -1:].contiguous(), cache, table,
+                             torch.tensor([kvl], dtype=torch.int32).cuda(),
+                             kvl, 1)
+    o_first, _ = _decode_once(layer, q[:, :1].contiguous(), cache, table,
+                              torch.tensor([ctx + 1], dtype=torch.int32).cuda(),
+                              kvl, 1)
+    assert torch.equal(o[:, -1], o_last[:, 0])
+    assert torch.equal(o[:, 0], o_first[:, 0])
+
+
+def test_single_key_and_zero_tokens():
+    """kv_len = 1 (the softmax weight is 1: o_lat is the row itself) and
+    T = 0 calls (no-ops)."""
+    layer, _ = ds_layer()
+    rng = np.random.default_rng(8)
+    row = rng.standard_normal(576).astype(np.float32)
+    img = np.zeros((1, 64, 576), np.float32)
+    img[0, 0] = row
+    cache = to_device(img, "bf16")
+    q = to_device(rng.standard_normal((1, 1, 128, 576)).astype(np.float32),
+                  "bf16")
+    o, lse = _decode_once(layer, q, cache,
+                          torch.zeros((1, 1), dtype=torch.int32).cuda(),
+                          torch.ones(1, dtype=torch.int32).cuda(), 1, 0)
+    rowq = W.round_bf16(row)
+    np.testing.assert_array_equal(o[0, 0].cpu().numpy(),
+                                  np.tile(rowq[:512], (128, 1)))
+    s = (q[0, 0].float().cpu().numpy().astype(np.float64) @ rowq) / np.sqrt(192)
+    assert_close("lse single key", lse[0, 0].cpu().numpy(), s, "f32",
+                 tol=(1e-5, 1e-4))
+    empty = torch.empty((0, DS.d), dtype=torch.bfloat16, device="cuda")
+    e32 = torch.empty(0, dtype=torch.int32, device="cuda")
+    layer.append(empty, e32, e32, torch.zeros((1, 1), dtype=torch.int32,
+                                              device="cuda"), cache)
+    B.mla_out(layer.cdims, torch.empty((0, 128, 512), device="cuda"),
+              layer.w["w_uv"], layer.w["w_o"],
+              torch.empty((0, DS.d), dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+
+
+def test_simt_path_bf16_odd_heads():
+    """Dims the matrix-core kernel does not take (n_h = 16) run on the
+    general kernels and still meet the bf16 bar end to end."""
+    dims = dataclasses.replace(DS, n_h=16)
+    wl = W.Workload("ds_h16", dims, "bf16", 2, (300, 1000), 1, 12, True)
+    w = W.make_weights(dims, "bf16", wl.seed)
+    layer = flow.make_layer(wl, w)
+    st = flow.prepare(wl, layer)
+    out = flow.run_step(st, n_split=3)
+    torch.cuda.synchronize()
+    for b in range(2):
+        ref = oracle_sequence(wl, w, b)
+        assert_close(f"h16 seq{b} u",
+                     out.u.view(2, 1, dims.d)[b].float().cpu().numpy(),
+                     ref["u"], "bf16")
+        assert_close(f"h16 seq{b} o_lat", out.o_lat[b].cpu().numpy(),
+                     ref["o_lat"], "bf16")
