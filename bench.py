@@ -1,0 +1,229 @@
+"""Benchmark of one MLA decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: append the 64 new
+tokens' latents to the paged cache, build their absorbed queries, split-KV
+decode over the 8192 + 1 cached rows of every sequence (plus the combine),
+and the output projection.  Workload: B = 64 sequences, context 8192 each,
+one query token per sequence, DeepSeek-V2 dimensions, bf16, 64-token blocks
+under a random-permutation block table; synthetic seeded inputs, resident in
+HBM before timing starts.
+
+Prints one JSON line (see the keys below).  `--gpus N` with N > 1 exits: this
+build measures one GPU.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("MLA decode queries/sec + latent-cache GB/s & MFMA util vs peak "
+          "(B=64,S=8K)")
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+DECODE_KERNEL = "decode_mfma_kernel"
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_b64_ctx8k_pmc.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "mla_latent_kv_33_amd", "csrc", f)
+                  for f in ("decode_mfma.hip", "decode_simt.hip")]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="b64_ctx8k")
+    ap.add_argument("--cpu-sample", type=int, default=24,
+                    help="sequences of the workload the CPU oracle times")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device copy of known size (for "
+                         "scaling HBM byte counters)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of 1 GiB, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": n, "launches": 3}))
+
+
+def cpu_baseline(wl, sample):
+    """Time the CPU fp64 oracle (non-absorbed MLA) on `sample` sequences of
+    the workload; queries/s scaled from the sample."""
+    import numpy as np
+    from mla_latent_kv_33_amd import workloads as W
+    from oracle import mla_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 0) for i in threadpool_info()] or
+                    [os.cpu_count()])
+    except Exception:   # threadpoolctl missing: report the visible CPUs
+        cores = os.cpu_count()
+    d = wl.dims
+    w = {k: v.astype(np.float64) for k, v in
+         W.make_weights(d, wl.dtype, wl.seed).items()}
+    total = 0.0
+    for b in range(sample):
+        rows = W.latent_rows(d, wl.dtype, wl.seed, b, 0, wl.ctx[b]).astype(
+            np.float64)
+        h_new = W.hidden_states(d, wl.dtype, wl.seed, b, wl.ctx[b], wl.n_q)
+        t0 = time.perf_counter()
+        orc.decode_step(w, d.n_h, W.ROPE_BASE, h_new, rows[:, :d.d_c],
+                        rows[:, d.d_c:])
+        total += time.perf_counter() - t0
+    return {"value": sample * wl.n_q / total, "unit": "queries/s",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"{sample} of {wl.batch} sequences (context "
+                      f"{wl.ctx[0]} + {wl.n_q} query), full non-absorbed "
+                      f"layer step per sequence, fp64 numpy; {total:.1f} s"}
+
+
+def stored_traffic(bytes_per_launch_alg):
+    """HBM traffic of the decode kernel from the committed counter summary,
+    if it was taken on the current kernel source."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    s = json.load(open(PMC_SUMMARY))
+    if s.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return s.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not "
+              "supported by this build (one process, one MI355X).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import numpy as np
+    from mla_latent_kv_33_amd import binding as B
+    from mla_latent_kv_33_amd import flow
+    from mla_latent_kv_33_amd import workloads as W
+
+    B.lib()   # fail loudly if the library is not built
+    wl = W.workload(args.workload)
+    d = wl.dims
+    torch.cuda.set_device(0)
+    layer = flow.make_layer(wl)
+    st = flow.prepare(wl, layer)
+    stream = torch.cuda.current_stream()
+    n_split = B.mla_decode_auto_splits(layer.cdims, wl.batch, wl.n_q,
+                                       st.max_kv_len) if not wl.n_split \
+        else wl.n_split
+    out = flow.run_step(st)   # allocates outputs and workspaces once
+    torch.cuda.synchronize()
+
+    names = ("append", "absorb", "decode", "out")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+          for _ in range(args.steps)]
+
+    def step(i=None):
+        e = ev[i] if i is not None else None
+        q2 = out.q.view(-1, d.n_h, d.d_c + d.d_r)
+        if e: e[0].record(stream)
+        layer.append(st.h_new, st.seq_idx, st.pos, st.table, st.cache)
+        if e: e[1].record(stream)
+        layer.absorb(st.h_new, st.pos, q_out=q2)
+        if e: e[2].record(stream)
+        layer.decode(out.q, st.cache, st.table, st.kv_lens, st.max_kv_len,
+                     n_split=n_split, o_lat=out.o_lat, lse=out.lse)
+        if e: e[3].record(stream)
+        layer.out(out.o_lat.view(-1, d.n_h, d.d_c), u=out.u)
+        if e: e[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    stage_ms = {n: float(np.mean([ev[i][k].elapsed_time(ev[i][k + 1])
+                                  for i in range(args.steps)]))
+                for k, n in enumerate(names)}
+    ms_per_step = wall * 1e3 / args.steps
+    queries = wl.batch * wl.n_q
+    kv = wl.kv_lens
+    cache_bytes = float(kv.sum()) * (d.d_c + d.d_r) * 2
+    q_bytes = queries * d.n_h * (d.d_c + d.d_r) * 2
+    olat_bytes = queries * d.n_h * d.d_c * 4
+    alg_bytes = cache_bytes + q_bytes + olat_bytes
+    flops = d.n_h * float(kv.sum()) * (2 * (d.d_c + d.d_r) + 2 * d.d_c)
+    t_dec = stage_ms["decode"] * 1e-3
+    achieved = alg_bytes / t_dec / 1e9
+    traffic = stored_traffic(alg_bytes)
+    result = {
+        "metric": METRIC,
+        "value": queries / (ms_per_step * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) hidden states and latent cache "
+                "rows, N(0,1/fan_in) weights)",
+        "config": {
+            "workload": "MLA decode step, B=64, context 8192 + 1 query token "
+                        "per sequence, DeepSeek-V2 dims (d 5120, n_h 128, "
+                        "d_h 128, d_c 512, d_r 64, d_c' 1536), paged latent "
+                        "cache of 64-token blocks, random-permutation block "
+                        "table",
+            "batch": wl.batch, "context": wl.ctx[0], "kv_len": int(kv[0]),
+            "n_q": wl.n_q, "n_split": int(n_split), "block_size": 64,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "mla_decode: " + DECODE_KERNEL + " + combine_kernel",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+            "alg_bytes_per_launch": alg_bytes,
+            "flops_per_launch": flops,
+            "mfma_tflops": flops / t_dec / 1e12,
+            "mfma_frac": flops / t_dec / 1e12 / BF16_PEAK_TFLOPS,
+            "decode_us": t_dec * 1e6,
+        },
+        "decode_queries_per_s": queries / t_dec,
+        "latent_cache_GBps": cache_bytes / t_dec / 1e9,
+        "stage_us": {k: v * 1e3 for k, v in stage_ms.items()},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
