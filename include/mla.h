@@ -67,7 +67,7 @@ typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
  * ('MiniMind 学习笔记 10', section 8).  Requirements: all positive, d_r even,
  * block_size a power of two; for BF16 also d, d_h, d_c, d_r and d_cq
  * multiples of 8 (else MLA_ERR_UNSUPPORTED).  The matrix-core decode kernel
- * takes BF16 with d_c = 512, d_r = 64, block_size 64 and n_h = 64, 96 or a
+ * takes BF16 with d_c = 512, d_r = 64, block_size 64 and n_h = 32, 64 or a
  * multiple of 128; other dims run on the general (SIMT) decode kernel. */
 typedef struct {
   int32_t d;          /* hidden size */

@@ -6,40 +6,40 @@
 //   o_lat_h = sum_s softmax(score)_s c_KV_s
 // over the key range of one split.  In the latent space every head uses the
 // same key (the 576-wide cache row) and the same value (its first 512
-// columns), so one workgroup serves all heads and each cache tile crosses
+// columns), so one workgroup serves all heads and each cache row crosses
 // HBM once.
 //
 // Work decomposition (one workgroup = NW waves, NW * 32 heads):
-//   * wave w owns heads 32w .. 32w+31.  Its query slice Q[32][576] lives in
-//     VGPRs as 36 MFMA B-operands; its output O^T[512][32] fp32 is 16
-//     32x32 accumulators (the whole accumulation register file).
-//   * keys stream in 64-token tiles (one cache block).  A tile is copied
-//     HBM -> LDS by direct-to-LDS loads (no VGPR staging) into one of two
-//     buffers, so tile k+1 is in flight while tile k is consumed.
-//   * LDS tile layout: 16-byte chunk c (of 72 per row) of token t lives in
-//     group (c / 8, t / 8) of 64 chunks (1 KiB), at position
-//     8 (t % 8) + ((c % 8) ^ swz(t % 8)).  One DMA instruction fills one
-//     group, i.e. 8 tokens x 128 contiguous bytes; the XOR makes both read
-//     patterns below bank-conflict free.
-//   * each tile is processed as two 32-token halves:
-//       scores S^T[32 tok][32 heads] = K . Q^T: 36 MFMA 32x32x16 (A = K rows
-//       from LDS, B = Q from VGPRs; accumulators in VGPRs);
-//       softmax in base 2 against a reference maximum m_ref per head, taken
-//       from the split's first half-tile: P = 2^(s - m_ref), rounded to
-//       bf16; l and O accumulate with no rescaling, so O is never touched by
-//       vector ALU code inside the loop.  Keys far below m_ref underflow to
-//       0 as in any softmax; a half-tile whose maximum exceeds m_ref by more
-//       than 2^64 (still finite, but beyond the range trusted for P and the
-//       sums) makes the workgroup restart the split with a raised m_ref.
-//       Real scores never span that range; the restart keeps the result
-//       exact for inputs that do;
-//       values O^T[512][32] += V^T[512][32 tok] . P^T: 16 x 2 MFMA.  The A
-//       operand (V^T) comes straight from the LDS tile through
-//       ds_read_b64_tr_b16 transposing loads; P^T is already in the right
-//       lanes because the MFMA k-slots are mapped to tokens the way the
-//       score accumulator lays them out.
+//   * keys stream in half tiles of 32 tokens (half a 64-token cache block),
+//     copied HBM -> LDS by direct-to-LDS loads into a ring of four buffers:
+//     while a wave computes on halves j and j+1, halves j+2 and j+3 are in
+//     flight.
+//   * scores: wave w owns heads 32w .. 32w+31.  Its query slice Q[32][576]
+//     lives in VGPRs as 36 MFMA B operands; the scores S^T[32 tok][32 heads]
+//     of a half are 36 MFMA 32x32x16 (A = key rows from LDS) accumulated in
+//     two independent chains.
+//   * softmax in base 2 against a reference maximum m_ref per head, taken
+//     from the split's first half tile: P = 2^(s - m_ref), rounded to bf16;
+//     l and O accumulate with no rescaling, so O is never touched by vector
+//     ALU code inside the loop.  Keys far below m_ref underflow to 0 as in
+//     any softmax; a half tile whose maximum exceeds m_ref by more than 2^64
+//     (still finite, but beyond the range trusted for P and the sums) makes
+//     the workgroup restart the split with a raised m_ref.  Real scores never
+//     span that range; the restart keeps the result exact for inputs that do.
+//   * values: the owner wave writes its P^T to LDS, and wave w accumulates
+//     O^T[latent tiles of wave w][all heads of the workgroup] += V^T P^T,
+//     32 MFMAs per half, so each value element is read from LDS once per
+//     workgroup (through ds_read_b64_tr_b16 transposing loads) rather than
+//     once per wave.  The MFMA k slots are mapped to tokens the way the score
+//     accumulator lays them out, so P needs no transposition on its way.
+//   * software pipeline, one barrier per half: step j computes the scores of
+//     half j+1, then the values of half j with the softmax of half j+1
+//     spread over those MFMAs, then stores P of half j+1.
 //   * the workgroup writes its unnormalised O, m_ref (log2 units) and l, or
 //     the final o_lat and lse when there is one split.
+//
+// LDS (NW = 4): 4 half-tile buffers of 36 KiB, then two P buffers of
+// 128 heads x 32 tokens bf16 (8 KiB each): 160 KiB, the whole LDS.
 
 #include "mla_common.hpp"
 #include "mla_kernels.hpp"
@@ -51,13 +51,31 @@ constexpr int DC = 512;
 constexpr int DR = 64;
 constexpr int ROW = DC + DR;          // elements per cache row
 constexpr int ROWB = ROW * 2;         // bytes per cache row
-constexpr int BS = 64;                // tokens per block (= tile)
-constexpr int CHUNKS = ROWB / 16;     // 72 sixteen-byte chunks per row
-constexpr int TILE_BYTES = BS * ROWB; // 73728
-constexpr int GROUPS = CHUNKS / 8 * BS / 8;  // 72 DMA groups per tile
+constexpr int BS = 64;                // tokens per cache block
+constexpr int BLOCK_BYTES = BS * ROWB;
+constexpr int HT = 32;                // tokens per half tile
+constexpr int HALF_BYTES = HT * ROWB; // 36864
+constexpr int HGROUPS = HALF_BYTES / 1024;  // 36 DMA groups per half tile
+constexpr int NBUF = 4;               // half-tile ring
 constexpr int KSTEPS = ROW / 16;      // 36 k-steps of the score MFMA
 constexpr int MT_LAT = DC / 32;       // 16 latent tiles of the value MFMA
 constexpr float REF_SLACK = 64.0f;    // log2 headroom above m_ref
+constexpr int SDEPTH = 4;             // score fragments in flight
+
+template <int NW>
+struct Cfg {
+  static constexpr int HEADS = 32 * NW;
+  static constexpr int MTW = MT_LAT / NW;          // latent tiles per wave
+  static constexpr int PER_HALF = HGROUPS / NW;    // copies per wave per half
+  static constexpr int PBYTES = HEADS * HT * 2;    // P of one half tile
+  static constexpr int P_OFF = NBUF * HALF_BYTES;
+  static constexpr int LDS = P_OFF + 2 * PBYTES;
+  static constexpr int AR = NW == 4 ? 3 : NW == 2 ? 4 : 8;  // V^T ring
+  static_assert(HGROUPS % NW == 0, "half-tile groups must split evenly");
+  static_assert(PER_HALF <= 63, "outstanding copies must fit vmcnt");
+  static_assert(MTW % 2 == 0, "latent tiles per wave must be even");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
 
 // Value of lane l ^ 32.  permlane32_swap(x, x) returns {[x_lo, x_lo],
 // [x_hi, x_hi]} (upper half of the first operand exchanged with the lower
@@ -78,9 +96,9 @@ __device__ __forceinline__ int swz(int t8) { return ((2 * t8) & 7) | (t8 >> 2); 
 // live in the other register file; the compiler picks one file for every
 // MFMA of a function, so these few are written out.  Hazards the compiler
 // cannot see through the asm: the first MFMA of a chain takes a literal 0 as
-// accumulator (no VALU write feeds it), back-to-back accumulation into the
-// same registers needs no wait states, and mfma_v_drain adds the wait
-// states a 32x32x16 result needs before VALU reads it (>= 18).
+// accumulator (no VALU write feeds it), accumulation into exactly the same
+// registers as an earlier MFMA needs no wait states, and mfma_v_drain adds
+// the wait states a 32x32x16 result needs before VALU reads it (>= 18).
 __device__ __forceinline__ f32x16 mfma_v_first(bf16x8 a, bf16x8 b) {
   f32x16 d;
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
@@ -97,12 +115,12 @@ __device__ __forceinline__ void mfma_v_drain(f32x16& d) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d));
 }
 
-// Tile copies, their waits and the tile barriers are written out: the
-// compiler tracks direct-to-LDS loads conservatively and would wait for the
-// whole prefetch before every transposing LDS read, serialising copy and
-// compute.  None of these statements returns a register, and each is a
-// compiler memory barrier ("memory" clobber), so LDS reads stay between the
-// waits and barriers they are written between.
+// Copies, their waits and the barriers are written out: the compiler tracks
+// direct-to-LDS loads conservatively and would wait for every copy in flight
+// before each LDS read, serialising copy and compute.  None of these
+// statements returns a register, and each is a compiler memory barrier
+// ("memory" clobber), so LDS accesses stay between the waits and barriers
+// they are written between.
 //
 // dma16: the wave's 64 lanes copy 16 bytes each from sbase + voff (lane's
 // offset) to LDS address lds_addr + 16 * lane.  M0 carries the LDS address;
@@ -138,42 +156,49 @@ __device__ __forceinline__ void barrier() {
   asm volatile("s_barrier" : : : "memory");
 }
 
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+  return (uint32_t)(uintptr_t)(const lds_char*)p;
 }
 
-// Copy one 64-token block into an LDS tile.  Wave `wave` issues groups
-// k = wave, wave + NW, ...; group k = (chunk group k / 8, token group k % 8).
-// Lane l fetches token 8 (k % 8) + l / 8, chunk 8 (k / 8) + ((l % 8) ^
-// swz(l / 8)).  Rows at or past `nvalid` are filled from the last valid row:
-// their scores are masked, and finite data keeps 0 * value at zero.
+// Copy half `hf` (tokens 32 hf .. 32 hf + 31) of a cache block into an LDS
+// half-tile buffer.  LDS layout: 16-byte chunk c (of 72 per row) of token t
+// lives in group (c / 8, t / 8) of 64 chunks (1 KiB) at 1024 (4 (c / 8) +
+// t / 8), position 8 (t % 8) + ((c % 8) ^ swz(t % 8)).  One copy fills one
+// group, i.e. 8 tokens x 128 contiguous bytes; the XOR makes the score and
+// the value read patterns bank-conflict free.  Wave `wave` issues groups
+// k = wave, wave + NW, ...; lane l fetches token 8 (k % 4) + l / 8, chunk
+// 8 (k / 4) + ((l % 8) ^ swz(l / 8)).  Rows at or past `nvalid` are filled
+// from the last valid row: their scores are masked, and finite data keeps
+// 0 * value at zero.
 template <int NW>
-__device__ __forceinline__ void issue_tile(const char* __restrict__ blk,
-                                           char* lds_tile, int nvalid,
-                                           int wave, int lane) {
-  constexpr int PER_WAVE = GROUPS / NW;
-  static_assert(GROUPS % NW == 0, "tile groups must split evenly over waves");
-  static_assert(PER_WAVE <= 63, "outstanding loads must fit the vmcnt field");
+__device__ __forceinline__ void issue_half(const char* __restrict__ blk,
+                                           int hf, uint32_t lds_buf,
+                                           int nvalid, int wave, int lane) {
+  constexpr int PER = Cfg<NW>::PER_HALF;
   const int tl = lane >> 3;
-  uint32_t lane_off = tl * ROWB + ((lane & 7) ^ swz(tl)) * 16;
-  // Opaque per tile, so the per-copy offsets below are recomputed (one add
-  // each) instead of being hoisted into long-lived registers.
-  asm volatile("" : "+v"(lane_off));
-  const uint32_t lds0 = lds_u32(lds_tile);
-  if (nvalid == BS) {
+  const uint32_t ch = ((lane & 7) ^ swz(tl)) * 16;
+  if (nvalid == HT) {
+    uint32_t lane_off = (HT * hf + tl) * ROWB + ch;
+    // Opaque, so the per-copy offsets below are recomputed (one add each)
+    // instead of being hoisted into long-lived registers.
+    asm volatile("" : "+v"(lane_off));
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
+    for (int j = 0; j < PER; ++j) {
       const int k = j * NW + wave;
-      dma16(lds0 + k * 1024, blk,
-            lane_off + 8 * (k & 7) * ROWB + (k >> 3) * 128);
+      dma16(lds_buf + k * 1024, blk,
+            lane_off + 8 * (k & 3) * ROWB + (k >> 2) * 128);
     }
-  } else {  // the last, partial block of a sequence
-    const uint32_t ch = lane_off - tl * ROWB;
+  } else {  // the last, partial half of a sequence
 #pragma unroll 1
-    for (int j = 0; j < PER_WAVE; ++j) {
+    for (int j = 0; j < PER; ++j) {
       const int k = j * NW + wave;
-      const int t = min(8 * (k & 7) + tl, nvalid - 1);
-      dma16(lds0 + k * 1024, blk, t * ROWB + (k >> 3) * 128 + ch);
+      const int t = min(8 * (k & 3) + tl, nvalid - 1);
+      dma16(lds_buf + k * 1024, blk, (HT * hf + t) * ROWB + (k >> 2) * 128 + ch);
     }
   }
 }
@@ -184,20 +209,24 @@ __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
 decode_mfma_kernel(
     const uint16_t* __restrict__ q, const char* __restrict__ cache,
     const int32_t* __restrict__ block_table, int max_blocks,
-    const int32_t* __restrict__ kv_lens, int n_q, int n_h, int n_split, float scale_log2, float* __restrict__ o_part,
-    float* __restrict__ m_part, float* __restrict__ l_part,
-    float* __restrict__ o_final, float* __restrict__ lse_final) {
+    const int32_t* __restrict__ kv_lens, int n_q, int n_h, int n_split,
+    float scale_log2, float* __restrict__ o_part, float* __restrict__ m_part,
+    float* __restrict__ l_part, float* __restrict__ o_final,
+    float* __restrict__ lse_final) {
+  using C = Cfg<NW>;
+  constexpr int MTW = C::MTW;
+  constexpr int PER = C::PER_HALF;
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  constexpr int PER_WAVE = GROUPS / NW;
-  typedef __attribute__((address_space(3))) char lds_char;
+  lds_char* const L = (lds_char*)lds;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5;     // lane half
-  const int col = lane & 31;   // head within the wave
+  const int col = lane & 31;   // head within a 32-head tile
   const int bq = blockIdx.x;   // b * n_q + i
   const int split = blockIdx.y;
-  const int head = blockIdx.z * NW * 32 + wave * 32 + col;
+  const int hbase = blockIdx.z * C::HEADS;
+  const int head = hbase + wave * 32 + col;  // head whose scores this lane owns
   const int b = bq / n_q;
   const int qi = bq - b * n_q;
 
@@ -207,19 +236,26 @@ decode_mfma_kernel(
   // Split j covers blocks [j nblk / n_split, (j + 1) nblk / n_split).
   const int blk0 = (int)((long)split * nblk / n_split);
   const int blk1 = (int)((long)(split + 1) * nblk / n_split);
-  const size_t row_id = ((size_t)bq * n_split + split) * n_h + head;
+  const size_t row_base = ((size_t)bq * n_split + split) * n_h;
 
   if (blk0 >= blk1) {  // empty split: no keys, weight zero in the combine
     if (g == 0) {
-      m_part[row_id] = -INFINITY;
-      l_part[row_id] = 0.0f;
+      m_part[row_base + head] = -INFINITY;
+      l_part[row_base + head] = 0.0f;
     }
     return;
   }
+  const int tok0 = blk0 * BS;
+  const int n_half = (min(blk1 * BS, visible) - tok0 + HT - 1) / HT;
 
   const int32_t* bt = block_table + (size_t)b * max_blocks;
-  issue_tile<NW>(cache + (size_t)bt[blk0] * TILE_BYTES, lds,
-                 min(BS, visible - blk0 * BS), wave, lane);
+  const uint32_t lds0 = lds_u32(lds);
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    const int ts = tok0 + HT * j;
+    issue_half<NW>(cache + (size_t)bt[ts / BS] * BLOCK_BYTES, j & 1,
+                   lds0 + (j & (NBUF - 1)) * HALF_BYTES,
+                   min(HT, visible - ts), wave, lane);
+  };
 
   // Query slice: lane holds Q[head][16ks + 8g .. +7] for every k-step.
   bf16x8 qreg[KSTEPS];
@@ -229,44 +265,32 @@ decode_mfma_kernel(
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = qp[2 * ks];
   }
-  // The first tile is needed before any compute anyway; waiting for every
-  // load here also tells the compiler that no query load is outstanding
-  // inside the loop, where vmcnt only tracks the prefetch of the next tile.
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  wait_vm<0>();
 
-  f32x16 o[MT_LAT];
-#pragma unroll
-  for (int i = 0; i < MT_LAT; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
-  float m_ref = -INFINITY;  // per head, log2 units
+  f32x16 o[MTW][NW];
+  float m_ref = -INFINITY;  // per owned head, log2 units
   float l_run = 0.0f;
-  int* restart_flag = (int*)(lds + 2 * TILE_BYTES);  // [2][NW]
+  bool pass_ovf = false;    // a score exceeded m_ref + REF_SLACK this pass
 
-  // Per-lane LDS byte offsets; every read is one of these plus an
-  // immediate.  Group (cg, tg) starts at 1024 (8 cg + tg).
-  //  Scores, half hf, k-step ks: token t = 32 hf + col, chunk c = 2 ks + g:
-  //  cg = ks / 4, tg = 4 hf + col / 8, c % 8 = 2 (ks % 4) + g, so
-  //  a_s[ks % 4] + 8192 (ks / 4) + 4096 hf; for ks / 4 >= 4 the first
-  //  32 KiB of that offset sits in a_s[4 + ks % 4] so that immediates stay
-  //  below 64 KiB.
-  int a_s[8];
+  // Per-lane LDS byte offsets; every read is a buffer base plus one of these
+  // plus an immediate.
+  //  Scores, k-step ks: token t = col, chunk c = 2 ks + g, group (ks / 4,
+  //  col / 8), c % 8 = 2 (ks % 4) + g:  a_s[ks % 4] + 4096 (ks / 4).
+  int a_s[4];
   {
     const int t8 = col & 7;
-    const int base = (col >> 3) * 1024 + t8 * 128;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      a_s[j] = base + 16 * ((2 * j + g) ^ swz(t8));
-      a_s[4 + j] = a_s[j] + 32768;
-    }
+    for (int j = 0; j < 4; ++j)
+      a_s[j] = (col >> 3) * 1024 + t8 * 128 + 16 * ((2 * j + g) ^ swz(t8));
   }
-  //  Values, half hf, k-step kk (16 tokens), read h in {0,1}, latent tile
-  //  mtl: the 16-lane group q16 supplies rows t = 32 hf + 16 kk + 8 h + vt
-  //  (vt = 4 (q16 / 2) + s16 / 4) and the 4 bf16 at chunk c = 4 mtl + vc
-  //  (vc = 2 (q16 % 2) + (s16 % 4) / 2), byte 8 (s16 % 2).  cg = mtl / 2,
-  //  tg = 4 hf + 2 kk + h, c % 8 = 4 (mtl % 2) + vc:
-  //  a_v[mtl % 2] + 8192 (mtl / 2) + 1024 (4 hf + 2 kk + h).
+  //  Values, k-step kk (16 tokens), read h in {0,1}, latent tile mt of the
+  //  wave (global tile MTW w + mt): the 16-lane group q16 supplies rows
+  //  t = 16 kk + 8 h + vt (vt = 4 (q16 / 2) + s16 / 4) and the 4 bf16 at
+  //  chunk c = 4 (MTW w + mt) + vc (vc = 2 (q16 % 2) + (s16 % 4) / 2), byte
+  //  8 (s16 % 2).  After the transposing read, lane L holds latent column
+  //  L % 32 of the tile for tokens 16 kk + 8 h + 4 (L / 32) + 0..3, i.e. MFMA
+  //  k slot 8 g + e <-> token 16 kk + 8 (e / 4) + 4 g + e % 4, the order of
+  //  the score accumulator rows.  Group (c / 8, t / 8):
+  //  a_v[mt % 2] + 4096 (mt / 2) + 1024 (2 kk + h).
   int a_v[2];
   {
     const int q16 = lane >> 4, s16 = lane & 15;
@@ -274,149 +298,277 @@ decode_mfma_kernel(
     const int vc = 2 * (q16 & 1) + ((s16 & 3) >> 1);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-      a_v[e] = vt * 128 + 16 * ((4 * e + vc) ^ swz(vt)) + 8 * (s16 & 1);
+      a_v[e] = vt * 128 + 16 * ((4 * e + vc) ^ swz(vt)) + 8 * (s16 & 1) +
+               4096 * (MTW / 2) * wave;
   }
+  //  P of a half: head-major rows of 64 bytes, chunk 2 kk + g holding k slots
+  //  8 g .. 8 g + 7 of k-step kk (bf16), at position (2 kk + g) ^ ((h / 2) % 4)
+  //  so that 8 consecutive heads hit 8 distinct bank groups.  Head 32 nt +
+  //  col: a_p[kk] + 2048 nt.
+  int a_p[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+    a_p[kk] = 64 * col + 16 * ((2 * kk + g) ^ ((col >> 1) & 3));
+  int* const flags = (int*)(lds + C::P_OFF);
 
-  int first = blk0;  // first tile of the current pass over the split
-  for (int kb = blk0; kb < blk1; ++kb) {
-    const int cur_off = ((kb - first) & 1) * TILE_BYTES;
-    char* cur = lds + cur_off;
-    lds_char* curl = (lds_char*)cur;
-    const bool more = kb + 1 < blk1;
-    if (more) {
-      issue_tile<NW>(cache + (size_t)bt[kb + 1] * TILE_BYTES,
-                     lds + (TILE_BYTES - cur_off),
-                     min(BS, visible - (kb + 1) * BS), wave, lane);
-      wait_vm<PER_WAVE>();  // this tile landed, the next one is in flight
-    } else {
-      wait_vm<0>();
+  // Scores of half j: two interleaved accumulation chains (even / odd k
+  // steps), so consecutive MFMAs never wait on each other's results.
+  auto s_phase = [&](int j) __attribute__((always_inline)) {
+    const lds_char* kb = L + (j & (NBUF - 1)) * HALF_BYTES;
+    const lds_char* sp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sp[i] = kb + a_s[i];
+    auto frag = [&](int ks) __attribute__((always_inline)) {
+      return *(const lds_bf16x8*)(sp[ks & 3] + 4096 * (ks >> 2));
+    };
+    bf16x8 af[SDEPTH];
+#pragma unroll
+    for (int i = 0; i < SDEPTH; ++i) af[i] = frag(i);
+    f32x16 sa = mfma_v_first(af[0], qreg[0]);
+    af[0] = frag(SDEPTH);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 sb = mfma_v_first(af[1], qreg[1]);
+    af[1] = frag(SDEPTH + 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 2; ks < KSTEPS; ++ks) {
+      mfma_v_acc((ks & 1) ? sb : sa, af[ks % SDEPTH], qreg[ks]);
+      if (ks + SDEPTH < KSTEPS) af[ks % SDEPTH] = frag(ks + SDEPTH);
+      __builtin_amdgcn_sched_barrier(0);  // keep the ring depth as written
     }
+    mfma_v_drain(sb);  // sa's last MFMA is one MFMA further back
+    return sa + sb;
+  };
+
+  // Softmax of one half tile, split in steps so that it can be spread over
+  // the value MFMAs:
+  //   step r = 0..15  : scale score r, running max
+  //   step 16         : per-head max over both lane halves, reference update
+  //   step 17..24     : P = 2^(s - m_ref) for a pair, bf16 pack, row sum
+  struct Half {
+    f32x16 s;
+    float tmax;
+    uint32_t pw[8];
+  };
+  auto softmax_step = [&](Half& H, int step) __attribute__((always_inline)) {
+    if (step < 16) {
+      const int r = step;
+      const float v = H.s[r] * scale_log2;
+      H.s[r] = v;
+      H.tmax = r == 0 ? v : fmaxf(H.tmax, v);
+    } else if (step == 16) {
+      const float t = fmaxf(H.tmax, lane_xor32(H.tmax, g));
+      if (m_ref == -INFINITY) m_ref = t;  // first half tile of the split
+      const bool ovf = t > m_ref + REF_SLACK;
+      m_ref = ovf ? t : m_ref;            // raised reference, next pass
+      pass_ovf |= ovf;
+    } else if (step < 25) {
+      const int e = step - 17;
+      const float p0 = __builtin_amdgcn_exp2f(H.s[2 * e] - m_ref);
+      const float p1 = __builtin_amdgcn_exp2f(H.s[2 * e + 1] - m_ref);
+      const uint32_t pk = __builtin_bit_cast(
+          uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
+      H.pw[e] = pk;
+      // The sum uses the same bf16 weights as the value product.
+      l_run += __uint_as_float(pk << 16) + __uint_as_float(pk & 0xFFFF0000u);
+      // Materialise here, between the MFMAs this step is spread over,
+      // instead of being sunk towards its use.
+      asm volatile("" : "+v"(H.pw[e]), "+v"(l_run));
+    }
+  };
+  // Keys at or past `lim` (only in the last half tile of a sequence) get
+  // score -inf, hence weight 0.  Accumulator row r of lane half g is token
+  // 8 (r / 4) + 4 g + r % 4.
+  auto mask = [&](Half& H, int lim) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = 8 * (r >> 2) + 4 * g + (r & 3);
+      H.s[r] = t < lim ? H.s[r] : -INFINITY;
+    }
+  };
+  // P of half j (already in k-slot order: pw[4 kk .. 4 kk + 3] are k slots
+  // 8 g .. 8 g + 7 of k-step kk) to the P buffer of j.
+  auto store_p = [&](int j, const Half& H) __attribute__((always_inline)) {
+    lds_char* pb = L + C::P_OFF + (j & 1) * C::PBYTES + 2048 * wave;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      *(lds_u32x4*)(pb + a_p[kk]) = (u32x4){H.pw[4 * kk], H.pw[4 * kk + 1],
+                                            H.pw[4 * kk + 2], H.pw[4 * kk + 3]};
+  };
+
+  // Values of half j: O^T[tile mt][head tile nt] += V^T(mt, kk) P(nt, kk)
+  // for kk = 0, 1, every mt of the wave and every head tile; hook(i) after
+  // the i-th of the 32 MFMAs.  All P fragments are read up front; the V^T
+  // fragments go through a ring of AR.
+  auto pv_phase = [&](int j, auto hook) __attribute__((always_inline)) {
+    constexpr int AR = C::AR;
+    constexpr int NP = 2 * MTW;  // (kk, mt) pairs
+    const lds_char* vb = L + (j & (NBUF - 1)) * HALF_BYTES;
+    const lds_char* pb = L + C::P_OFF + (j & 1) * C::PBYTES;
+    const lds_char* vp0 = vb + a_v[0];
+    const lds_char* vp1 = vb + a_v[1];
+    auto vfrag = [&](int p) __attribute__((always_inline)) {
+      const int kk = p / MTW, mt = p % MTW;
+      const lds_char* base = ((mt & 1) ? vp1 : vp0) + 4096 * (mt >> 1) +
+                             2048 * kk;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)base);
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(base + 1024));
+      const s16x8 lohi =
+          __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_bit_cast(bf16x8, lohi);
+    };
+    bf16x8 pf[2][NW];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int nt = 0; nt < NW; ++nt)
+        pf[kk][nt] = *(const lds_bf16x8*)(pb + a_p[kk] + 2048 * nt);
+    bf16x8 vf[AR];
+#pragma unroll
+    for (int p = 0; p < AR; ++p) vf[p] = vfrag(p);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int kk = p / MTW, mt = p % MTW;
+      const bf16x8 a = vf[p % AR];
+#pragma unroll
+      for (int nt = 0; nt < NW; ++nt) {
+        o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            a, pf[kk][nt], o[mt][nt], 0, 0, 0);
+        if (nt == NW - 1 && p + AR < NP) vf[p % AR] = vfrag(p + AR);
+        hook(p * NW + nt);
+        __builtin_amdgcn_sched_barrier(0);  // keep the ring depth as written
+      }
+    }
+  };
+
+  // Passes over the split: a second one only after an overflow.  m_ref only
+  // rises, and after the first pass every half tile's maximum is at most
+  // m_ref + REF_SLACK, so the second pass cannot overflow; the loop stops
+  // there regardless.
+  bool first_pass = true;
+  for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NW; ++nt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[mt][nt][r] = 0.0f;
+    // Prologue: halves 0 and 1 landed, half 2 in flight; P of half 0.
+    issue(0);
+    if (n_half > 1) issue(1);
+    if (first_pass) {
+      // Also retires the query loads, so that inside the loop vmcnt only
+      // tracks the copies.
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      first_pass = false;
+    }
+    wait_vm<0>();
+    if (n_half > 2) issue(2);
     barrier();
-
-    bool wave_ovf = false;
+    {
+      Half h;
+      h.s = s_phase(0);
+      const int lim = visible - tok0;
+      if (lim < HT) mask(h, lim);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      // ---- scores S^T = K Q^T for tokens 32 hf .. 32 hf + 31 ----------
-      f32x16 s;
-      s = mfma_v_first(*(const bf16x8*)(cur + a_s[0] + 4096 * hf), qreg[0]);
-#pragma unroll
-      for (int ks = 1; ks < KSTEPS; ++ks) {
-        const int ka = ks >> 2;  // chunk group 0 .. 8
-        const int hi = ka >= 4 ? 4 : 0;
-        const bf16x8 a = *(const bf16x8*)(cur + a_s[hi + (ks & 3)] +
-                                          8192 * (ka - hi) + 4096 * hf);
-        mfma_v_acc(s, a, qreg[ks]);
-      }
-      mfma_v_drain(s);
-
-      // ---- softmax against m_ref ----------------------------------------
-      const int tok0 = kb * BS + 32 * hf;
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tok = tok0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        float v = s[r] * scale_log2;
-        v = tok < visible ? v : -INFINITY;
-        s[r] = v;
-        tmax = fmaxf(tmax, v);
-      }
-      tmax = fmaxf(tmax, lane_xor32(tmax, g));
-      if (m_ref == -INFINITY) m_ref = tmax;  // first half-tile of the split
-      const bool ovf = tmax > m_ref + REF_SLACK;
-      if (ovf) m_ref = tmax;  // raised reference for the next pass
-      wave_ovf |= __builtin_amdgcn_ballot_w64(ovf) != 0;
-      if (wave_ovf) continue;
-
-      // P^T as MFMA B operands: k-step kk covers registers 8 kk .. 8 kk + 7.
-      bf16x8 pb[2];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        uint32_t w4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = exp2f(s[8 * kk + 2 * e] - m_ref);
-          const float p1 = exp2f(s[8 * kk + 2 * e + 1] - m_ref);
-          const uint32_t pk = pack_bf2(p0, p1);
-          l_run +=
-              __uint_as_float(pk << 16) + __uint_as_float(pk & 0xFFFF0000u);
-          w4[e] = pk;
-        }
-        pb[kk] = __builtin_bit_cast(bf16x8, (u32x4){w4[0], w4[1], w4[2], w4[3]});
-      }
-
-      // ---- values O^T += V^T P^T ----------------------------------------
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int mtl = 0; mtl < MT_LAT; ++mtl) {
-          const int imm = 8192 * (mtl >> 1) + 1024 * (4 * hf + 2 * kk);
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (s16x4 __attribute__((address_space(3)))*)(
-                  curl + a_v[mtl & 1] + imm));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (s16x4 __attribute__((address_space(3)))*)(
-                  curl + a_v[mtl & 1] + imm + 1024));
-          const s16x8 lohi =
-              __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[mtl] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, lohi), pb[kk], o[mtl], 0, 0, 0);
-        }
-      }
+      for (int st = 0; st < 25; ++st) softmax_step(h, st);
+      store_p(0, h);
     }
-    if (lane == 0) restart_flag[(kb & 1) * NW + wave] = wave_ovf;
-    // Every read of `cur` (and the flag write) has landed before any wave
-    // may refill the buffer.
     wait_lgkm0();
-    barrier();
+
+    // Step j: entry state (after the barrier) is P of half j and the
+    // copies of halves j and j+1 visible, half j+2 in flight, and every
+    // wave done with half j-1; so half j+3 goes into j-1's buffer.
+    // The last step has no next half: its scores are skipped and a fully
+    // masked softmax (lim = 0) leaves m_ref, l and the flags alone (P = 0,
+    // maximum -inf), so one body serves every step.
+    for (int j = 0; j < n_half; ++j) {
+      barrier();
+      if (j + 3 < n_half) issue(j + 3);
+      const bool next = j + 1 < n_half;
+      Half h;
+      if (next) h.s = s_phase(j + 1);
+      const int lim = next ? visible - (tok0 + HT * (j + 1)) : 0;
+      if (lim < HT) mask(h, lim);
+      pv_phase(j, [&](int i) __attribute__((always_inline)) {
+        softmax_step(h, i);
+      });
+      if (next) store_p(j + 1, h);
+      // Half j+2 must have landed by the next barrier; j+3 may stay in
+      // flight.
+      if (j + 3 < n_half)
+        wait_vm<PER>();
+      else
+        wait_vm<0>();
+      wait_lgkm0();
+    }
 
     // Restart the split when any wave saw a score beyond its reference.
+    // The flags use the P buffer that the last step did not read (P of
+    // half n_half - 1 sits in buffer (n_half - 1) % 2).
+    int* fl = flags + (n_half & 1) * (C::PBYTES / 4);
+    if (lane == 0) fl[wave] = __builtin_amdgcn_ballot_w64(pass_ovf) != 0;
+    wait_lgkm0();
+    barrier();
     int any = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) any |= restart_flag[(kb & 1) * NW + w];
-    if (any) {
-      wait_vm<0>();  // drain the prefetch
-      barrier();
-#pragma unroll
-      for (int i = 0; i < MT_LAT; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][r] = 0.0f;
-      l_run = 0.0f;
-      first = blk0;
-      kb = blk0 - 1;
-      issue_tile<NW>(cache + (size_t)bt[blk0] * TILE_BYTES, lds,
-                     min(BS, visible - blk0 * BS), wave, lane);
-    }
+    for (int w = 0; w < NW; ++w) any |= fl[w];
+    if (!any || pass > 0) break;
+    l_run = 0.0f;
+    pass_ovf = false;
   }
 
   // ---- epilogue ----------------------------------------------------------
+  // l of every head of the workgroup, through the P buffer the last step
+  // read (free after the flag barrier, and apart from the flags).
   l_run += lane_xor32(l_run, g);
+  float* lsh = (float*)(lds + C::P_OFF + ((n_half - 1) & 1) * C::PBYTES);
+  if (g == 0) lsh[wave * 32 + col] = l_run;
+  wait_lgkm0();
+  barrier();
+  float l_nt[NW];
+#pragma unroll
+  for (int nt = 0; nt < NW; ++nt) l_nt[nt] = lsh[nt * 32 + col];
+
+  // O^T accumulator (mt, nt), register r: head hbase + 32 nt + col, latent
+  // 32 (MTW w + mt) + 8 (r / 4) + 4 g + r % 4.
   if (n_split == 1) {
-    const float inv = 1.0f / l_run;
-    float* dst = o_final + ((size_t)bq * n_h + head) * DC;
 #pragma unroll
-    for (int mtl = 0; mtl < MT_LAT; ++mtl)
+    for (int nt = 0; nt < NW; ++nt) {
+      const float inv = 1.0f / l_nt[nt];
+      float* dst = o_final + ((size_t)bq * n_h + hbase + 32 * nt + col) * DC +
+                   32 * MTW * wave;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 v = {o[mtl][4 * i] * inv, o[mtl][4 * i + 1] * inv,
-                   o[mtl][4 * i + 2] * inv, o[mtl][4 * i + 3] * inv};
-        *(f32x4*)(dst + 32 * mtl + 8 * i + 4 * g) = v;
-      }
+      for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4 v = {o[mt][nt][4 * i] * inv, o[mt][nt][4 * i + 1] * inv,
+                     o[mt][nt][4 * i + 2] * inv, o[mt][nt][4 * i + 3] * inv};
+          *(f32x4*)(dst + 32 * mt + 8 * i + 4 * g) = v;
+        }
+    }
     if (g == 0 && lse_final)
       lse_final[(size_t)bq * n_h + head] =
           (m_ref + __log2f(l_run)) * 0.69314718055994531f;
   } else {
-    float* dst = o_part + row_id * DC;
 #pragma unroll
-    for (int mtl = 0; mtl < MT_LAT; ++mtl)
+    for (int nt = 0; nt < NW; ++nt) {
+      float* dst = o_part + (row_base + hbase + 32 * nt + col) * DC +
+                   32 * MTW * wave;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 v = {o[mtl][4 * i], o[mtl][4 * i + 1], o[mtl][4 * i + 2],
-                   o[mtl][4 * i + 3]};
-        *(f32x4*)(dst + 32 * mtl + 8 * i + 4 * g) = v;
-      }
+      for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f32x4 v = {o[mt][nt][4 * i], o[mt][nt][4 * i + 1],
+                     o[mt][nt][4 * i + 2], o[mt][nt][4 * i + 3]};
+          *(f32x4*)(dst + 32 * mt + 8 * i + 4 * g) = v;
+        }
+    }
     if (g == 0) {
-      m_part[row_id] = m_ref;
-      l_part[row_id] = l_run;
+      m_part[row_base + head] = m_ref;
+      l_part[row_base + head] = l_run;
     }
   }
 }
@@ -425,12 +577,11 @@ template <int NW>
 hipError_t launch_nw(const mla_dims& d, int B, int n_q, const void* q,
                      const void* cache, const int32_t* block_table,
                      int max_blocks, const int32_t* kv_lens, int n_split,
-                     float* o_part,
-                     float* m_part, float* l_part, float* o_final,
-                     float* lse_final, hipStream_t stream) {
+                     float* o_part, float* m_part, float* l_part,
+                     float* o_final, float* lse_final, hipStream_t stream) {
   const float scale_log2 =
       (float)(1.4426950408889634 / __builtin_sqrt((double)(d.d_h + d.d_r)));
-  const size_t lds = 2 * TILE_BYTES + 2 * NW * sizeof(int);
+  constexpr size_t lds = Cfg<NW>::LDS;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
@@ -442,8 +593,8 @@ hipError_t launch_nw(const mla_dims& d, int B, int n_q, const void* q,
   dim3 grid(B * n_q, n_split, d.n_h / (NW * 32));
   hipLaunchKernelGGL(decode_mfma_kernel<NW>, grid, dim3(NW * 64), lds, stream,
                      (const uint16_t*)q, (const char*)cache, block_table,
-                     max_blocks, kv_lens, n_q, d.n_h, n_split, scale_log2, o_part, m_part, l_part, o_final,
-                     lse_final);
+                     max_blocks, kv_lens, n_q, d.n_h, n_split, scale_log2,
+                     o_part, m_part, l_part, o_final, lse_final);
   return hipGetLastError();
 }
 
@@ -451,8 +602,8 @@ hipError_t launch_nw(const mla_dims& d, int B, int n_q, const void* q,
 
 bool decode_mfma_supported(const mla_dims& d) {
   return d.dtype == MLA_BF16 && d.d_c == DC && d.d_r == DR &&
-         d.block_size == BS && d.n_h % 32 == 0 &&
-         (d.n_h % 128 == 0 || d.n_h == 64 || d.n_h == 96);
+         d.block_size == BS &&
+         (d.n_h % 128 == 0 || d.n_h == 64 || d.n_h == 32);
 }
 
 hipError_t launch_decode_mfma(const mla_dims& d, int B, int n_q,
@@ -466,8 +617,8 @@ hipError_t launch_decode_mfma(const mla_dims& d, int B, int n_q,
   d, B, n_q, q, cache, block_table, max_blocks, kv_lens, n_split, o_part, \
       m_part, l_part, o_final, lse_final, stream
   if (d.n_h % 128 == 0) return launch_nw<4>(MLA_DECODE_ARGS);
-  if (d.n_h == 96) return launch_nw<3>(MLA_DECODE_ARGS);
   if (d.n_h == 64) return launch_nw<2>(MLA_DECODE_ARGS);
+  if (d.n_h == 32) return launch_nw<1>(MLA_DECODE_ARGS);
 #undef MLA_DECODE_ARGS
   return hipErrorInvalidValue;
 }

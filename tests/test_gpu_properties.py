@@ -208,11 +208,14 @@ def test_single_key_and_zero_tokens():
     torch.cuda.synchronize()
 
 
-def test_simt_path_bf16_odd_heads():
-    """Dims the matrix-core kernel does not take (n_h = 16) run on the
-    general kernels and still meet the bf16 bar end to end."""
-    dims = dataclasses.replace(DS, n_h=16)
-    wl = W.Workload("ds_h16", dims, "bf16", 2, (300, 1000), 1, 12, True)
+@pytest.mark.parametrize("n_h", [16, 32, 64])
+def test_head_counts_end_to_end(n_h):
+    """n_h = 32 and 64 run the matrix-core kernel with one and two waves per
+    workgroup; n_h = 16 (which it does not take) runs the general kernels.
+    Each meets the bf16 bar end to end, with ragged lengths that end inside
+    a half block and splits."""
+    dims = dataclasses.replace(DS, n_h=n_h)
+    wl = W.Workload(f"ds_h{n_h}", dims, "bf16", 2, (300, 1000), 1, 12, True)
     w = W.make_weights(dims, "bf16", wl.seed)
     layer = flow.make_layer(wl, w)
     st = flow.prepare(wl, layer)
@@ -220,8 +223,36 @@ def test_simt_path_bf16_odd_heads():
     torch.cuda.synchronize()
     for b in range(2):
         ref = oracle_sequence(wl, w, b)
-        assert_close(f"h16 seq{b} u",
+        assert_close(f"h{n_h} seq{b} u",
                      out.u.view(2, 1, dims.d)[b].float().cpu().numpy(),
                      ref["u"], "bf16")
-        assert_close(f"h16 seq{b} o_lat", out.o_lat[b].cpu().numpy(),
+        assert_close(f"h{n_h} seq{b} o_lat", out.o_lat[b].cpu().numpy(),
                      ref["o_lat"], "bf16")
+
+
+@pytest.mark.parametrize("n_split", [1, 3])
+def test_score_jump_restart(n_split):
+    """Keys whose scores jump far above the first keys' maximum (more than
+    2^64 in weight) make the matrix-core kernel redo a split with a raised
+    reference maximum; the result still matches the softmax definition.
+    Two jumps, the second above the first, also exercise a second raise
+    within one pass."""
+    layer, _ = ds_layer()
+    rng = np.random.default_rng(31)
+    kvl = 700
+    rows = 0.1 * rng.standard_normal((kvl, 576)).astype(np.float32)
+    rows[100] = 5.0      # score ~ 5 * sum(q) / sqrt(192): about 90 in log2
+    rows[450] = 12.0     # above the first jump by more than 64 in log2
+    rows = W.round_bf16(rows)
+    q = (0.5 * rng.standard_normal((1, 1, 128, 576)) + 0.3).astype(np.float32)
+    q = W.round_bf16(q)
+    table_np, nb = W.block_table(np.array([kvl]), True, 3)
+    img = np.zeros((nb, 64, 576), np.float32)
+    flow.scatter_rows_host(img, table_np, 0, 0, rows, 64)
+    o, lse = _decode_once(layer, to_device(q, "bf16"), to_device(img, "bf16"),
+                          torch.from_numpy(table_np).cuda(),
+                          torch.tensor([kvl], dtype=torch.int32).cuda(), kvl,
+                          n_split)
+    ref_o, ref_lse = orc.latent_attention(q[0], [kvl - 1], rows, 512, 128)
+    assert_close("o_lat after restart", o[0].cpu().numpy(), ref_o, "bf16")
+    assert_close("lse after restart", lse[0].cpu().numpy(), ref_lse, "bf16")
