@@ -127,39 +127,100 @@ __global__ __launch_bounds__(NT) void decode_simt_kernel(
 }
 
 // One workgroup per (row, head); threads over the d_c columns.
+// Split combine ('MLA：潜在表示压缩与解耦 RoPE', section 7: the softmax over
+// the whole key range from per-split maxima and sums).  For each head,
+// M = max_j m_j, w_j = 2^(m_j - M) (0 for an empty split, m_j = -inf),
+// L = sum_j w_j l_j, o_lat = sum_j w_j o_j / L, lse = (M + log2 L) ln 2.
+// Workgroup = (query row, ch heads).  The weights of its heads are computed
+// in parallel (one thread per head), then each thread owns CB float4
+// columns and reads their partials CS splits at a time, so that CB * CS
+// 16-byte loads per lane are in flight.  Splits of weight 0 are not read:
+// an empty split never wrote its partial.
+constexpr int CMB_CH = 16, CMB_CB = 8, CMB_CS = 4;
+constexpr size_t CMB_LDS_MAX = 160 * 1024;
+
 __global__ __launch_bounds__(256) void combine_kernel(
-    int n_h, int d_c, int n_split, const float* __restrict__ o_part,
+    int n_h, int d_c, int n_split, int ch, const float* __restrict__ o_part,
     const float* __restrict__ m_part, const float* __restrict__ l_part,
     float* __restrict__ o_lat, float* __restrict__ lse) {
-  extern __shared__ float wsh[];  // [n_split] weights
-  __shared__ float scal[2];
-  const int bq = blockIdx.x, h = blockIdx.y;
-  const size_t base = (size_t)bq * n_split * n_h + h;
-  if (threadIdx.x == 0) {
+  extern __shared__ float wsh[];  // [ch][n_split] weights, [ch] 1/L
+  float* inv_l = wsh + ch * n_split;
+  const int bq = blockIdx.x;
+  const int h0 = blockIdx.y * ch;
+  const int nh = min(ch, n_h - h0);
+  const size_t rows = (size_t)bq * n_split * n_h + h0;  // + j n_h + h
+  // weights: one thread per head
+  for (int h = threadIdx.x; h < nh; h += blockDim.x) {
     float M = -INFINITY;
-    for (int j = 0; j < n_split; ++j) M = fmaxf(M, m_part[base + (size_t)j * n_h]);
+    for (int j = 0; j < n_split; ++j)
+      M = fmaxf(M, m_part[rows + (size_t)j * n_h + h]);
     float L = 0.0f;
     for (int j = 0; j < n_split; ++j) {
-      const float m = m_part[base + (size_t)j * n_h];
+      const float m = m_part[rows + (size_t)j * n_h + h];
       const float w = m == -INFINITY ? 0.0f : exp2f(m - M);
-      wsh[j] = w;
-      L += w * l_part[base + (size_t)j * n_h];
+      wsh[h * n_split + j] = w;
+      L += w * l_part[rows + (size_t)j * n_h + h];
     }
-    scal[0] = M;
-    scal[1] = L;
+    inv_l[h] = 1.0f / L;
+    if (lse)
+      lse[(size_t)bq * n_h + h0 + h] = (M + log2f(L)) * 0.69314718055994531f;
   }
   __syncthreads();
-  const float inv = 1.0f / scal[1];
-  for (int c = threadIdx.x; c < d_c; c += blockDim.x) {
-    float v = 0.0f;
-    for (int j = 0; j < n_split; ++j) {
-      const float w = wsh[j];
-      if (w != 0.0f) v = fmaf(w, o_part[(base + (size_t)j * n_h) * d_c + c], v);
+  if (d_c % 4) {  // rows not float4-aligned: plain loop
+    for (int idx = threadIdx.x; idx < nh * d_c; idx += blockDim.x) {
+      const int h = idx / d_c, c = idx - h * d_c;
+      float acc = 0.0f;
+      for (int j = 0; j < n_split; ++j) {
+        const float w = wsh[h * n_split + j];
+        if (w != 0.0f)
+          acc += w * o_part[(rows + (size_t)j * n_h + h) * d_c + c];
+      }
+      o_lat[((size_t)bq * n_h + h0 + h) * d_c + c] = acc * inv_l[h];
     }
-    o_lat[((size_t)bq * n_h + h) * d_c + c] = v * inv;
+    return;
   }
-  if (threadIdx.x == 0 && lse)
-    lse[(size_t)bq * n_h + h] = (scal[0] + log2f(scal[1])) * 0.69314718055994531f;
+  const int c4n = d_c / 4;
+  const int total = nh * c4n;
+  for (int base = threadIdx.x; base < total; base += blockDim.x * CMB_CB) {
+    f32x4 acc[CMB_CB];
+#pragma unroll
+    for (int b = 0; b < CMB_CB; ++b) acc[b] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j0 = 0; j0 < n_split; j0 += CMB_CS) {
+      f32x4 v[CMB_CS][CMB_CB];
+      float w[CMB_CS][CMB_CB];
+#pragma unroll
+      for (int u = 0; u < CMB_CS; ++u)
+#pragma unroll
+        for (int b = 0; b < CMB_CB; ++b) {
+          const int idx = base + b * blockDim.x;
+          const int h = idx / c4n, c4 = idx - h * c4n;
+          const int j = j0 + u;
+          w[u][b] = (j < n_split && idx < total) ? wsh[h * n_split + j] : 0.0f;
+          v[u][b] = w[u][b] != 0.0f
+                        ? *(const f32x4*)(o_part +
+                                          (rows + (size_t)j * n_h + h) * d_c +
+                                          4 * c4)
+                        : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        }
+#pragma unroll
+      for (int u = 0; u < CMB_CS; ++u)
+#pragma unroll
+        for (int b = 0; b < CMB_CB; ++b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[b][e] += w[u][b] * v[u][b][e];
+    }
+#pragma unroll
+    for (int b = 0; b < CMB_CB; ++b) {
+      const int idx = base + b * blockDim.x;
+      if (idx < total) {
+        const int h = idx / c4n, c4 = idx - h * c4n;
+        const float il = inv_l[h];
+        *(f32x4*)(o_lat + ((size_t)bq * n_h + h0 + h) * d_c + 4 * c4) =
+            (f32x4){acc[b][0] * il, acc[b][1] * il, acc[b][2] * il,
+                    acc[b][3] * il};
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -196,10 +257,23 @@ hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
                           const float* l_part, float* o_lat, float* lse,
                           hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  dim3 grid(rows, d.n_h);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(256),
-                     (size_t)n_split * sizeof(float), stream, d.n_h, d.d_c,
-                     n_split, o_part, m_part, l_part, o_lat, lse);
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(
+        (const void*)combine_kernel,
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)CMB_LDS_MAX);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  // heads per workgroup: their weights must fit the LDS
+  const size_t per_head = (size_t)(n_split + 1) * sizeof(float);
+  int ch = (int)(CMB_LDS_MAX / per_head);
+  if (ch > CMB_CH) ch = CMB_CH;
+  if (ch < 1) return hipErrorInvalidValue;
+  dim3 grid(rows, (d.n_h + ch - 1) / ch);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), ch * per_head, stream,
+                     d.n_h, d.d_c, n_split, ch, o_part, m_part, l_part, o_lat,
+                     lse);
   return hipGetLastError();
 }
 

@@ -14,11 +14,20 @@
 namespace mla {
 namespace {
 
+// Sum of the parts at i; four independent loads in flight per round.
 __device__ __forceinline__ float sum_parts(const float* p, int nparts,
                                            long stride, long i) {
-  float v = p[i];
-  for (int k = 1; k < nparts; ++k) v += p[k * stride + i];
-  return v;
+  const float* q = p + i;
+  float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
+  int k = 0;
+  for (; k + 4 <= nparts; k += 4) {
+    v0 += q[k * stride];
+    v1 += q[(k + 1) * stride];
+    v2 += q[(k + 2) * stride];
+    v3 += q[(k + 3) * stride];
+  }
+  for (; k < nparts; ++k) v0 += q[k * stride];
+  return (v0 + v1) + (v2 + v3);
 }
 
 __global__ void reduce_parts_kernel(const float* __restrict__ src, int nparts,
@@ -29,8 +38,9 @@ __global__ void reduce_parts_kernel(const float* __restrict__ src, int nparts,
     dst[i] = sum_parts(src, nparts, part_stride, i);
 }
 
-// One workgroup per token.  Columns j < d_c are copied, the d_r RoPE columns
-// are rotated in pairs; the row goes to its paged cache slot.
+// Workgroup (token, slice of 256 items): items j < d_c are copied columns,
+// the rest rotate the d_r RoPE columns in pairs; the row goes to its paged
+// cache slot.
 template <typename T>
 __global__ void append_scatter_kernel(
     const float* __restrict__ acc, int nparts, long part_stride, int d_c,
@@ -46,7 +56,8 @@ __global__ void append_scatter_kernel(
   const int blk = block_table[(long)seq_idx[t] * max_blocks + p / block_size];
   T* row = cache + ((long)blk * block_size + (p % block_size)) * width;
   const long base = (long)t * width;
-  for (int j = threadIdx.x; j < d_c + half; j += blockDim.x) {
+  for (int j = blockIdx.y * blockDim.x + threadIdx.x; j < d_c + half;
+       j += gridDim.y * blockDim.x) {
     if (j < d_c) {
       DT<T>::store(row, j, sum_parts(acc, nparts, part_stride, base + j));
     } else {
@@ -74,7 +85,8 @@ __global__ void query_rope_kernel(const float* __restrict__ qr, long ld_qr,
   const int half = d_r / 2;
   const int p = pos[t];
   const float* src = qr + (long)t * ld_qr;
-  for (int i = threadIdx.x; i < n_h * half; i += blockDim.x) {
+  for (int i = blockIdx.y * blockDim.x + threadIdx.x; i < n_h * half;
+       i += gridDim.y * blockDim.x) {
     const int h = i / half, jj = i - h * half;
     const float x1 = src[h * d_r + jj], x2 = src[h * d_r + jj + half];
     const bool ok = p >= 0 && p < max_pos;
@@ -122,13 +134,14 @@ hipError_t launch_append_scatter(const mla_dims& d, int T, const float* acc,
                                  int max_blocks, void* cache,
                                  hipStream_t stream) {
   if (T <= 0) return hipSuccess;
+  const dim3 grid(T, (d.d_c + d.d_r / 2 + 255) / 256);
   if (d.dtype == MLA_BF16)
-    hipLaunchKernelGGL(append_scatter_kernel<uint16_t>, dim3(T), dim3(256), 0,
+    hipLaunchKernelGGL(append_scatter_kernel<uint16_t>, grid, dim3(256), 0,
                        stream, acc, nparts, part_stride, d.d_c, d.d_r, seq_idx,
                        pos, rope_cos, rope_sin, max_pos, block_table,
                        max_blocks, d.block_size, (uint16_t*)cache);
   else
-    hipLaunchKernelGGL(append_scatter_kernel<float>, dim3(T), dim3(256), 0,
+    hipLaunchKernelGGL(append_scatter_kernel<float>, grid, dim3(256), 0,
                        stream, acc, nparts, part_stride, d.d_c, d.d_r, seq_idx,
                        pos, rope_cos, rope_sin, max_pos, block_table,
                        max_blocks, d.block_size, (float*)cache);
@@ -140,12 +153,13 @@ hipError_t launch_query_rope(const mla_dims& d, int T, const float* qr,
                              const float* rope_cos, const float* rope_sin,
                              int max_pos, void* q_out, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
+  const dim3 grid(T, (d.n_h * (d.d_r / 2) + 255) / 256);
   if (d.dtype == MLA_BF16)
-    hipLaunchKernelGGL(query_rope_kernel<uint16_t>, dim3(T), dim3(256), 0,
+    hipLaunchKernelGGL(query_rope_kernel<uint16_t>, grid, dim3(256), 0,
                        stream, qr, ld_qr, d.n_h, d.d_c, d.d_r, pos, rope_cos,
                        rope_sin, max_pos, (uint16_t*)q_out);
   else
-    hipLaunchKernelGGL(query_rope_kernel<float>, dim3(T), dim3(256), 0,
+    hipLaunchKernelGGL(query_rope_kernel<float>, grid, dim3(256), 0,
                        stream, qr, ld_qr, d.n_h, d.d_c, d.d_r, pos, rope_cos,
                        rope_sin, max_pos, (float*)q_out);
   return hipGetLastError();

@@ -160,6 +160,204 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
   }
 }
 
+// ---------------------------------------------------------------- stream
+// Weight-streaming kernel for M <= 64 (decode batches), NT, K % 16 == 0.
+// Workgroup = 4 waves over 32 NTW output columns; wave w takes a contiguous
+// quarter of the workgroup's K chunk, so its consecutive k-steps read each
+// weight row in 128-byte runs, and every activation fragment it loads feeds
+// NTW column tiles.  Weight fragments are loaded straight from HBM into
+// registers PFB k-steps ahead (a ring of PFB x NTW fragments), activation
+// fragments PFA k-steps ahead.  The four partial tiles are summed through LDS
+// one column tile at a time; each K chunk writes its own partial C.  Rows
+// past M or N read a valid row and are dropped at the store.
+__device__ __forceinline__ void split_hi_lo_hw(const f32x4& a, const f32x4& b,
+                                               bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t hp = __builtin_bit_cast(
+        uint32_t, __builtin_convertvector((f32x2){x[2 * e], x[2 * e + 1]},
+                                          bf16x2));
+    const float r0 = x[2 * e] - __uint_as_float(hp << 16);
+    const float r1 = x[2 * e + 1] - __uint_as_float(hp & 0xFFFF0000u);
+    h[e] = hp;
+    l[e] = __builtin_bit_cast(
+        uint32_t, __builtin_convertvector((f32x2){r0, r1}, bf16x2));
+  }
+  hi = __builtin_bit_cast(bf16x8, (u32x4){h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]});
+}
+
+// Prefetch depth in k-steps, the same for weights and activations: loads
+// retire in order, so the shallower ring would set the depth of both.
+// About 144 VGPRs of ring: per step NTW weight fragments (4 VGPRs each) and
+// MT activation fragments (8 VGPRs fp32, 4 bf16).
+template <int MT, int NTW, bool AF32>
+struct StreamCfg {
+  static constexpr int PER_STEP = 4 * NTW + MT * (AF32 ? 8 : 4);
+  static constexpr int PF0 = 144 / PER_STEP;
+  static constexpr int PF = PF0 < 2 ? 2 : PF0 > 16 ? 16 : PF0;
+};
+
+template <int MT, int NTW, bool AF32>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(
+    const void* __restrict__ Av, long lda, long a_bs,
+    const uint16_t* __restrict__ B, const uint16_t* __restrict__ B2, int nb1,
+    long ldb, long b_bs, float* __restrict__ C, long ldc, long c_bs, long c_ks,
+    int M, int N, int K, int k_chunk) {
+  constexpr int PFB = StreamCfg<MT, NTW, AF32>::PF;
+  constexpr int PFA = PFB;
+  constexpr int R = PFB;
+  __shared__ float red[4][MT][16][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5;
+  const int col = lane & 31;
+  const int n_base = blockIdx.x * 32 * NTW;
+  const int kz = blockIdx.y;
+  const int z = blockIdx.z;
+  const int kbeg = kz * k_chunk;
+  const int kend = min(K, kbeg + k_chunk);
+  const int steps = max(0, (kend - kbeg) / 16);
+  const int per = (steps + 3) / 4;
+  const int s0 = min(steps, wave * per);
+  const int nsteps = min(steps, s0 + per) - s0;
+  const int kw = kbeg + 16 * s0 + 8 * g;  // this lane's first k
+
+  const uint16_t* brow_p[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int n = min(n_base + 32 * nt + col, N - 1);
+    brow_p[nt] = (n < nb1 ? B + z * b_bs + (long)n * ldb
+                          : B2 + z * b_bs + (long)(n - nb1) * ldb) + kw;
+  }
+  const char* arow_p[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = min(32 * mt + col, M - 1);
+    arow_p[mt] = AF32 ? (const char*)((const float*)Av + z * a_bs +
+                                      (long)m * lda + kw)
+                      : (const char*)((const uint16_t*)Av + z * a_bs +
+                                      (long)m * lda + kw);
+  }
+
+  struct AFrag {
+    f32x4 x0, x1;   // fp32 activations (AF32)
+    bf16x8 h;       // bf16 activations
+  };
+  auto load_b = [&](int j, bf16x8 (&dst)[NTW]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+      dst[nt] = *(const bf16x8*)(brow_p[nt] + 16 * j);
+  };
+  auto load_a = [&](int j, AFrag (&dst)[MT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (AF32) {
+        const float* p = (const float*)arow_p[mt] + 16 * j;
+        dst[mt].x0 = *(const f32x4*)p;
+        dst[mt].x1 = *(const f32x4*)(p + 4);
+      } else {
+        dst[mt].h = *(const bf16x8*)((const uint16_t*)arow_p[mt] + 16 * j);
+      }
+    }
+  };
+
+  f32x16 acc[MT][NTW];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.0f;
+
+  bf16x8 bq[PFB][NTW];
+  AFrag aq[PFA][MT];
+  // One k-step: consume ring slot u % PFB (weights) and u % PFA
+  // (activations), refill them with steps j + PFB and j + PFA (only those
+  // below nsteps when `guard`).
+  auto step = [&](int u, int j, bool guard) __attribute__((always_inline)) {
+    bf16x8 ahi[MT], alo[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (AF32)
+        split_hi_lo_hw(aq[u % PFA][mt].x0, aq[u % PFA][mt].x1, ahi[mt],
+                       alo[mt]);
+      else
+        ahi[mt] = aq[u % PFA][mt].h;
+    }
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            ahi[mt], bq[u % PFB][nt], acc[mt][nt], 0, 0, 0);
+        if (AF32)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              alo[mt], bq[u % PFB][nt], acc[mt][nt], 0, 0, 0);
+      }
+    if (!guard || j + PFA < nsteps) load_a(j + PFA, aq[u % PFA]);
+    if (!guard || j + PFB < nsteps) load_b(j + PFB, bq[u % PFB]);
+    // Keep each step's loads in that step: the scheduler would otherwise
+    // sink the prefetches next to their uses and wait for them at once.
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Prologue in the loop's own issue order (step i issues A(i + PFA), then
+  // B(i + PFB)).  When the steady-state loop runs, its prologue is
+  // unconditional and is its only entry, so the loads outstanding at the
+  // loop entry line up with those at its back edge and the waits stay
+  // exact; the steady-state body has no branches.  The last < R + PFB steps
+  // run in an unrolled, guarded tail.
+  int jb = 0;
+  if (nsteps >= R + PFB) {
+#pragma unroll
+    for (int i = -PFB; i < 0; ++i) {
+      if (i + PFA >= 0) load_a(i + PFA, aq[i + PFA]);
+      load_b(i + PFB, bq[i + PFB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (; jb + R + PFB <= nsteps; jb += R) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) step(u, jb + u, false);
+    }
+  } else {
+#pragma unroll
+    for (int i = -PFB; i < 0; ++i) {
+      if (i + PFA >= 0 && i + PFA < nsteps) load_a(i + PFA, aq[i + PFA]);
+      if (i + PFB < nsteps) load_b(i + PFB, bq[i + PFB]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < R + PFB; ++u)
+    if (jb + u < nsteps) step(u, jb + u, true);
+
+  // Sum the four waves' tiles, one column tile at a time.  Accumulator
+  // register r of lane (col, g) is row 32 mt + 8 (r / 4) + 4 g + r % 4,
+  // column 32 nt + col.
+  float* cz = C + z * c_bs + kz * c_ks;
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[wave][mt][r][lane] = acc[mt][nt][r];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MT * 4; ++i) {
+      const int idx = threadIdx.x + 256 * i;
+      const int mt = idx >> 10, r = (idx >> 6) & 15, l = idx & 63;
+      const float v = red[0][mt][r][l] + red[1][mt][r][l] + red[2][mt][r][l] +
+                      red[3][mt][r][l];
+      const int m = 32 * mt + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+      const int n = n_base + 32 * nt + (l & 31);
+      if (m < M && n < N) cz[(long)m * ldc + n] = v;
+    }
+    __syncthreads();
+  }
+}
+
 // ----------------------------------------------------------------- tiled
 constexpr int TB_M = 128, TB_N = 128, TB_K = 32;
 constexpr int A_LD = TB_K + 8;     // bf16 elements per LDS row of A / NT B
@@ -170,7 +368,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
     const void* __restrict__ Av, long lda, long a_bs,
     const uint16_t* __restrict__ B, const uint16_t* __restrict__ B2, int nb1,
     long ldb, long b_bs, float* __restrict__ C, long ldc, long c_bs, long c_ks,
-    int M, int N, int K, int k_chunk, int tiles_n) {
+    int M, int N, int K, int k_chunk, int tiles_n,
+    uint16_t* __restrict__ C16) {
   __shared__ __attribute__((aligned(16))) uint16_t a_hi[TB_M * A_LD];
   __shared__ __attribute__((aligned(16))) uint16_t a_lo[AF32 ? TB_M * A_LD : 8];
   __shared__ __attribute__((aligned(16)))
@@ -303,7 +502,10 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
     __syncthreads();
   }
 
-  float* cz = C + z * c_bs + kz * c_ks;
+  // fp32 partial per K chunk, or (C16, one K chunk) the result rounded to
+  // bf16 straight into its destination.
+  float* cz = C16 ? nullptr : C + z * c_bs + kz * c_ks;
+  uint16_t* cz16 = C16 ? C16 + z * c_bs : nullptr;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -312,7 +514,12 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
         const int nn = n0 + wn * 64 + 32 * j + col;
-        if (m < M && nn < N) cz[(long)m * ldc + nn] = acc[i][j][r];
+        if (m < M && nn < N) {
+          if (C16)
+            cz16[(long)m * ldc + nn] = f2bf(acc[i][j][r]);
+          else
+            cz[(long)m * ldc + nn] = acc[i][j][r];
+        }
       }
 }
 
@@ -342,13 +549,54 @@ __global__ void gemm_simt_kernel(const float* __restrict__ A, long lda,
 
 }  // namespace
 
-int gemm_pick_k_split(const mla_dims& d, const GemmArgs& g) {
-  if (d.dtype != MLA_BF16 || g.b_nn || g.M > 64) return 1;
-  // Skinny path: aim for >= ~1024 workgroups, each with >= 512 of K.
-  const long tiles = (long)((g.N + 31) / 32) * g.batch;
-  int ks = 1;
-  while (tiles * ks < 1024 && (long)g.K / (ks * 2) >= 512) ks *= 2;
-  return ks;
+void gemm_plan(const mla_dims& d, GemmArgs& g, int max_split) {
+  g.ntw = 0;
+  g.k_split = 1;
+  if (d.dtype != MLA_BF16 || g.b_nn || g.M > 64 || g.M <= 0 || g.N <= 0 ||
+      g.K <= 0)
+    return;
+  if (g.K % 16) {
+    // Older skinny kernel: aim for >= ~1024 workgroups, >= 512 of K each.
+    const long tiles = (long)((g.N + 31) / 32) * g.batch;
+    int ks = 1;
+    while (tiles * ks < 1024 && (long)g.K / (ks * 2) >= 512 &&
+           ks * 2 <= max_split)
+      ks *= 2;
+    g.k_split = ks;
+    return;
+  }
+  // Streaming kernel: pick column tiles per wave and the K split that
+  // minimise the bytes moved (weights once, padded to whole column tiles;
+  // activations per column slice,
+  // mostly from L2; partial tiles written and read back) divided by the
+  // fraction of the 256 compute units the grid keeps busy.
+  const double a_el = g.a_f32 ? 4.0 : 2.0;
+  double best = 1e300;
+  for (int ntw = 4; ntw >= 1; --ntw) {
+    const long slices = (long)((g.N + 32 * ntw - 1) / (32 * ntw)) * g.batch;
+    // weight rows streamed, counting the padding of the last column tile
+    const double wbytes = 2.0 * slices * 32.0 * ntw * (double)g.K;
+    for (int s = 1; s <= max_split; ++s) {
+      const int kc = (g.K + s - 1) / s;
+      const int kc16 = (kc + 63) / 64 * 64;
+      if (s > 1 && kc16 < 256) break;   // at least 4 k-steps per wave
+      const int se = (g.K + kc16 - 1) / kc16;
+      if (se != s) continue;
+      const long wgs = slices * se;
+      const long rounds = (wgs + 255) / 256;
+      const double eff = (double)wgs / (rounds * 256.0);
+      const double parts = se > 1 ? 2.0 * se * g.M * (double)g.N * 4.0 *
+                                        g.batch
+                                  : 0.0;
+      const double abytes = 0.25 * slices * g.M * (double)g.K * a_el;
+      const double cost = (wbytes + parts + abytes) / eff;
+      if (cost < best * 0.999) {
+        best = cost;
+        g.ntw = ntw;
+        g.k_split = se;
+      }
+    }
+  }
 }
 
 hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
@@ -366,6 +614,32 @@ hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
   }
   const uint16_t* B = (const uint16_t*)g.B;
   const uint16_t* B2 = (const uint16_t*)g.B2;
+  if (g.c16 && (ks != 1 || g.ntw > 0 || (!g.b_nn && g.M <= 64)))
+    return hipErrorInvalidValue;  // bf16 output: tiled kernel, one K chunk
+  if (g.ntw > 0) {
+    const int kc = (g.K + ks - 1) / ks;
+    k_chunk = (kc + 63) / 64 * 64;
+    dim3 grid((g.N + 32 * g.ntw - 1) / (32 * g.ntw), ks, g.batch);
+#define MLA_ST(MT, NTW, AF)                                                   \
+  hipLaunchKernelGGL((gemm_stream_kernel<MT, NTW, AF>), grid, dim3(256), 0,   \
+                     stream, g.A, g.lda, g.a_bs, B, B2, g.nb1, g.ldb, g.b_bs, \
+                     g.C, g.ldc, g.c_bs, g.c_ks, g.M, g.N, g.K, (int)k_chunk)
+#define MLA_ST_NTW(MT, AF)                          \
+  switch (g.ntw) {                                  \
+    case 1: MLA_ST(MT, 1, AF); break;               \
+    case 2: MLA_ST(MT, 2, AF); break;               \
+    case 3: MLA_ST(MT, 3, AF); break;               \
+    default: MLA_ST(MT, 4, AF); break;              \
+  }
+    if (g.M <= 32) {
+      if (g.a_f32) { MLA_ST_NTW(1, true) } else { MLA_ST_NTW(1, false) }
+    } else {
+      if (g.a_f32) { MLA_ST_NTW(2, true) } else { MLA_ST_NTW(2, false) }
+    }
+#undef MLA_ST_NTW
+#undef MLA_ST
+    return hipGetLastError();
+  }
   if (!g.b_nn && g.M <= 64) {
     k_chunk = (k_chunk + 63) / 64 * 64;
     dim3 grid((g.N + 31) / 32, ks, g.batch);
@@ -389,7 +663,7 @@ hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
   hipLaunchKernelGGL((gemm_tiled_kernel<AF, NN>), grid, dim3(256), 0, stream, \
                      g.A, g.lda, g.a_bs, B, B2, g.nb1, g.ldb, g.b_bs, g.C,    \
                      g.ldc, g.c_bs, g.c_ks, g.M, g.N, g.K, (int)k_chunk,      \
-                     tiles_n)
+                     tiles_n, (uint16_t*)g.c16)
   if (g.a_f32) {
     if (g.b_nn) MLA_TL(true, true); else MLA_TL(true, false);
   } else {

@@ -64,7 +64,7 @@ GemmArgs append_gemm(const mla_dims& d, int T) {
   g.M = T;
   g.N = d.d_c + d.d_r;
   g.K = d.d;
-  g.k_split = gemm_pick_k_split(d, g);
+  gemm_plan(d, g);
   return g;
 }
 GemmArgs cq_gemm(const mla_dims& d, int T) {
@@ -76,7 +76,7 @@ GemmArgs cq_gemm(const mla_dims& d, int T) {
   g.M = T;
   g.N = d.d_cq;
   g.K = d.d;
-  g.k_split = gemm_pick_k_split(d, g);
+  gemm_plan(d, g);
   return g;
 }
 GemmArgs qcr_gemm(const mla_dims& d, int T) {
@@ -90,7 +90,7 @@ GemmArgs qcr_gemm(const mla_dims& d, int T) {
   g.M = T;
   g.N = d.n_h * (d.d_h + d.d_r);
   g.K = d.d_cq;
-  g.k_split = gemm_pick_k_split(d, g);
+  gemm_plan(d, g);
   return g;
 }
 GemmArgs absorb_gemm(const mla_dims& d, int T) {
@@ -123,7 +123,7 @@ GemmArgs uv_gemm(const mla_dims& d, int T) {
   g.N = d.d_h;
   g.K = d.d_c;
   g.batch = d.n_h;
-  g.k_split = 1;
+  gemm_plan(d, g, 1);  // its consumer reads one C
   return g;
 }
 GemmArgs o_gemm(const mla_dims& d, int T) {
@@ -136,7 +136,7 @@ GemmArgs o_gemm(const mla_dims& d, int T) {
   g.M = T;
   g.N = d.d;
   g.K = d.n_h * d.d_h;
-  g.k_split = gemm_pick_k_split(d, g);
+  gemm_plan(d, g);
   return g;
 }
 
@@ -248,18 +248,17 @@ mla_status mla_append_cache(const mla_dims* dims, int32_t T, const void* h,
 // ------------------------------------------------------------------ absorb
 namespace {
 struct AbsorbWs {
-  float *cq_parts, *cq, *qcr_parts, *qcr, *qlat;
+  float *cq_parts, *cq, *qcr_parts, *qcr;
   size_t bytes;
 };
 AbsorbWs absorb_layout(const mla_dims& d, int T, void* base) {
   Carve c(base);
   AbsorbWs w;
-  const GemmArgs g1 = cq_gemm(d, T), g2 = qcr_gemm(d, T), g3 = absorb_gemm(d, T);
+  const GemmArgs g1 = cq_gemm(d, T), g2 = qcr_gemm(d, T);
   w.cq_parts = c.take(parts_floats(g1));
   w.cq = g1.k_split > 1 ? c.take((size_t)T * d.d_cq) : w.cq_parts;
   w.qcr_parts = c.take(parts_floats(g2));
   w.qcr = g2.k_split > 1 ? c.take((size_t)T * g2.N) : w.qcr_parts;
-  w.qlat = c.take(parts_floats(g3));
   w.bytes = c.used;
   return w;
 }
@@ -311,13 +310,18 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
   MLA_TRY(launch_query_rope(d, T, w.qcr + (long)d.n_h * d.d_h, g2.ldc, pos,
                             rope_cos, rope_sin, max_pos, q_out, s));
 
+  // q_lat_h = W_UK_h^T q_C_h straight into the first d_c columns of each
+  // head's q row (rounded to bf16 by the GEMM for bf16 layers).
   GemmArgs g3 = absorb_gemm(d, T);
   g3.A = w.qcr;
   g3.B = w_uk;
-  g3.C = w.qlat;
+  g3.ldc = (long)d.n_h * (d.d_c + d.d_r);
+  g3.c_bs = d.d_c + d.d_r;
+  if (d.dtype == MLA_BF16)
+    g3.c16 = q_out;
+  else
+    g3.C = (float*)q_out;
   MLA_TRY(launch_gemm(d, g3, s));
-  MLA_TRY(launch_convert(d, T * d.n_h, d.d_c, w.qlat, d.d_c, 1, 0, q_out,
-                         d.d_c + d.d_r, s));
   return MLA_OK;
 }
 
