@@ -41,6 +41,7 @@
 // LDS (NW = 4): 4 half-tile buffers of 36 KiB, then two P buffers of
 // 128 heads x 32 tokens bf16 (8 KiB each): 160 KiB, the whole LDS.
 
+#include "lds_dma.hpp"
 #include "mla_common.hpp"
 #include "mla_kernels.hpp"
 
@@ -88,8 +89,6 @@ __device__ __forceinline__ float lane_xor32(float x, int g) {
   return __uint_as_float(g ? sw[0] : sw[1]);
 }
 
-// Swizzle of the chunk position inside a row of 8 chunks, keyed by t % 8.
-__device__ __forceinline__ int swz(int t8) { return ((2 * t8) & 7) | (t8 >> 2); }
 
 // Score MFMAs with the accumulator pinned to VGPRs.  The output O^T of a
 // wave fills all 256 accumulation registers, so the score accumulators must
@@ -115,55 +114,10 @@ __device__ __forceinline__ void mfma_v_drain(f32x16& d) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d));
 }
 
-// Copies, their waits and the barriers are written out: the compiler tracks
-// direct-to-LDS loads conservatively and would wait for every copy in flight
-// before each LDS read, serialising copy and compute.  None of these
-// statements returns a register, and each is a compiler memory barrier
-// ("memory" clobber), so LDS accesses stay between the waits and barriers
-// they are written between.
-//
-// dma16: the wave's 64 lanes copy 16 bytes each from sbase + voff (lane's
-// offset) to LDS address lds_addr + 16 * lane.  M0 carries the LDS address;
-// one wait state separates its write from the load that reads it.
-__device__ __forceinline__ void dma16(uint32_t lds_addr, const char* sbase,
-                                      uint32_t voff) {
-  // Both addresses are wave-uniform; readfirstlane makes that explicit so
-  // they can sit in scalar registers.
-  // readfirstlane returns a signed int: convert through uint32_t so the
-  // low word is zero-extended, not sign-extended, into the 64-bit address.
-  const uint64_t b = (uint64_t)sbase;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-  const uint32_t hi =
-      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %1"
-      :
-      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"((const char*)sb),
-        "v"(voff)
-      : "memory", "m0");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lgkm0() {
-  asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
-}
-__device__ __forceinline__ void barrier() {
-  asm volatile("s_barrier" : : : "memory");
-}
-
-typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_char*)p;
-}
 
 // Copy half `hf` (tokens 32 hf .. 32 hf + 31) of a cache block into an LDS
 // half-tile buffer.  LDS layout: 16-byte chunk c (of 72 per row) of token t

@@ -21,6 +21,7 @@
 //     MFMA still sees k-contiguous B fragments.
 // fp32 layers use a plain SIMT kernel (small shapes only).
 
+#include "lds_dma.hpp"
 #include "mla_common.hpp"
 #include "mla_kernels.hpp"
 
@@ -214,8 +215,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5;
   const int col = lane & 31;
-  const int n_base = blockIdx.x * 32 * NTW;
-  const int kz = blockIdx.y;
+  // K chunk fastest in the launch order: workgroups are dealt to the XCDs
+  // round-robin, so with a power-of-two split each XCD works on the same
+  // chunk(s) and keeps their activation slice in its own L2.
+  const int kz = blockIdx.x;
+  const int n_base = blockIdx.y * 32 * NTW;
   const int z = blockIdx.z;
   const int kbeg = kz * k_chunk;
   const int kend = min(K, kbeg + k_chunk);
@@ -355,6 +359,191 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
       if (m < M && n < N) cz[(long)m * ldc + n] = v;
     }
     __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ ldsk
+// LDS-staged weight-streaming kernel for M <= 64, NT, K % 64 == 0 (and the
+// B / B2 boundary at a multiple of 32 rows).  Workgroup = 4 waves over
+// 128 NTW output columns, wave w owning column tiles w NTW .. w NTW + NTW-1;
+// all waves walk the workgroup's K chunk together in super-steps of 64 k.
+// Each super-step's activation rows (shared by the waves) and weight rows
+// are copied HBM -> LDS by direct-to-LDS loads, whole 128-byte line runs per
+// instruction, into a ring of NBUF slots, so that NBUF - 1 super-steps are
+// in flight while one is consumed; MFMA operands are read back with
+// ds_read_b128 from swizzled positions (conflict free).  No cross-wave
+// reduction: each wave writes its own tiles; each K chunk writes its own
+// partial C.
+template <int MT, int NTW, bool AF32>
+struct LdsCfg {
+  static constexpr int MROWS = 32 * MT;
+  static constexpr int RB = AF32 ? 256 : 128;      // A bytes per row per 64 k
+  static constexpr int PPR = RB / 16;              // 16-byte pieces per row
+  static constexpr int RPI = 64 / PPR;             // A rows per copy
+  static constexpr int A_BYTES = MROWS * RB;
+  static constexpr int A_PER = A_BYTES / 1024 / 4; // A copies per wave
+  static constexpr int B_PER = 4 * NTW;            // B copies per wave
+  static constexpr int D_PER = A_PER + B_PER;      // copies per wave per step
+  static constexpr int B_OFF = A_BYTES;
+  static constexpr int SLOT = A_BYTES + 4 * NTW * 4096;
+  static constexpr int NB0 = (160 * 1024) / SLOT;
+  static constexpr int NBUF = NB0 > 4 ? 4 : NB0;
+  static_assert(A_PER >= 1 && A_BYTES % 4096 == 0, "A copy split");
+  static_assert(NBUF >= 2, "LDS ring");
+  static_assert((NBUF - 2) * D_PER <= 63, "vmcnt range");
+  static constexpr int LDS = NBUF * SLOT;
+};
+
+template <int MT, int NTW, bool AF32>
+__global__ __launch_bounds__(256) void gemm_lds_kernel(
+    const void* __restrict__ Av, long lda, long a_bs,
+    const uint16_t* __restrict__ B, const uint16_t* __restrict__ B2, int nb1,
+    long ldb, long b_bs, float* __restrict__ C, long ldc, long c_bs, long c_ks,
+    int M, int N, int K, int k_chunk) {
+  using L = LdsCfg<MT, NTW, AF32>;
+  constexpr int NBUF = L::NBUF;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5;
+  const int col = lane & 31;
+  // K chunk fastest in the launch order (see gemm_stream_kernel).
+  const int kz = blockIdx.x;
+  const int n_wg = blockIdx.y * 128 * NTW;
+  const int z = blockIdx.z;
+  const int kbeg = kz * k_chunk;
+  const int kend = min(K, kbeg + k_chunk);
+  const int nss = max(0, (kend - kbeg) / 64);
+  const int esz = AF32 ? 4 : 2;
+
+  // ---- per-lane copy offsets (bytes from the per-super-step scalar base)
+  // A: copy i (= wave A_PER + a) covers rows i RPI .. i RPI + RPI - 1; lane l
+  // takes row r = i RPI + l / PPR and piece (l % PPR) ^ (r % 8) of it, so
+  // that LDS position p of row r holds piece p ^ (r % 8).
+  const char* a_base =
+      (const char*)Av + (size_t)z * a_bs * esz + (size_t)kbeg * esz;
+  uint32_t a_off[L::A_PER];
+#pragma unroll
+  for (int a = 0; a < L::A_PER; ++a) {
+    const int r = (wave * L::A_PER + a) * L::RPI + lane / L::PPR;
+    const int pos = lane % L::PPR;
+    a_off[a] = (uint32_t)((size_t)min(r, M - 1) * lda * esz) +
+               16 * (pos ^ (r & 7));
+  }
+  // B: column tile t = wave NTW + nt (32 rows), copies q = 0..3 of 8 rows;
+  // lane l takes row 8 q + l / 8 and chunk (l % 8) ^ swz(l / 8).
+  const char* b_base[NTW];
+  uint32_t b_off[NTW][4];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int row0 = min(n_wg + 32 * (wave * NTW + nt), N - 1);
+    const uint16_t* bb = row0 < nb1 ? B + z * b_bs + (long)row0 * ldb
+                                    : B2 + z * b_bs + (long)(row0 - nb1) * ldb;
+    b_base[nt] = (const char*)(bb + kbeg);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = min(row0 + 8 * q + (lane >> 3), N - 1) - row0;
+      b_off[nt][q] = (uint32_t)(rr * ldb * 2) +
+                     16 * ((lane & 7) ^ swz(lane >> 3));
+    }
+  }
+  const uint32_t lds0 = lds_u32(lds);
+  auto issue = [&](int ss) __attribute__((always_inline)) {
+    const uint32_t slot = lds0 + (ss % NBUF) * L::SLOT;
+#pragma unroll
+    for (int a = 0; a < L::A_PER; ++a)
+      dma16(slot + (wave * L::A_PER + a) * 1024, a_base + (size_t)ss * L::RB,
+            a_off[a]);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        dma16(slot + L::B_OFF + (wave * NTW + nt) * 4096 + q * 1024,
+              b_base[nt] + (size_t)ss * 128, b_off[nt][q]);
+  };
+
+  // ---- per-lane read offsets inside a slot
+  // A operand (mt, ks): row m = 32 mt + col; fp32 pieces 4 ks + 2 g and
+  // 4 ks + 2 g + 1, bf16 piece 2 ks + g.
+  // B operand (nt, ks): row col of tile (wave NTW + nt), chunk 2 ks + g.
+  const int ar = col;  // row within an M tile; (32 mt + col) % 8 == col % 8
+  auto a_read = [&](const lds_char* sl, int mt, int piece) __attribute__((always_inline)) {
+    const int m = 32 * mt + ar;
+    return *(const __attribute__((address_space(3))) u32x4*)(
+        sl + m * L::RB + 16 * (piece ^ (m & 7)));
+  };
+  const int b_row_off = (col >> 3) * 1024 + (col & 7) * 128;
+  auto b_read = [&](const lds_char* sl, int nt, int ks) __attribute__((always_inline)) {
+    const int c = 2 * ks + g;
+    return *(const __attribute__((address_space(3))) bf16x8*)(
+        sl + L::B_OFF + (wave * NTW + nt) * 4096 + b_row_off +
+        16 * (c ^ swz(col & 7)));
+  };
+
+  f32x16 acc[MT][NTW];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.0f;
+
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (i < nss) issue(i);
+  for (int ss = 0; ss < nss; ++ss) {
+    // Own copies of super-step ss done (later ones may stay in flight),
+    // then everybody's; the slot of ss - 1 is free after the barrier.
+    const int later = min(NBUF - 2, nss - 1 - ss);
+    if (later >= 2 && NBUF >= 4) wait_vm<(NBUF >= 4 ? 2 : 0) * L::D_PER>();
+    else if (later >= 1 && NBUF >= 3) wait_vm<(NBUF >= 3 ? 1 : 0) * L::D_PER>();
+    else wait_vm<0>();
+    barrier();
+    if (ss + NBUF - 1 < nss) issue(ss + NBUF - 1);
+    const lds_char* sl = (const lds_char*)lds + (ss % NBUF) * L::SLOT;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 ahi[MT], alo[MT], bf[NTW];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (AF32) {
+          const u32x4 x0 = a_read(sl, mt, 4 * ks + 2 * g);
+          const u32x4 x1 = a_read(sl, mt, 4 * ks + 2 * g + 1);
+          split_hi_lo_hw(__builtin_bit_cast(f32x4, x0),
+                         __builtin_bit_cast(f32x4, x1), ahi[mt], alo[mt]);
+        } else {
+          ahi[mt] = __builtin_bit_cast(bf16x8, a_read(sl, mt, 2 * ks + g));
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) bf[nt] = b_read(sl, nt, ks);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              ahi[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+          if (AF32)
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                alo[mt], bf[nt], acc[mt][nt], 0, 0, 0);
+        }
+    }
+    wait_lgkm0();  // this slot's reads returned before the next barrier
+  }
+
+  // Accumulator register r of lane (col, g): row 32 mt + 8 (r / 4) + 4 g +
+  // r % 4, column 32 (wave NTW + nt) + col.
+  float* cz = C + z * c_bs + kz * c_ks;
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int n = n_wg + 32 * (wave * NTW + nt) + col;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (m < M && n < N) cz[(long)m * ldc + n] = acc[mt][nt][r];
+      }
   }
 }
 
@@ -547,6 +736,25 @@ __global__ void gemm_simt_kernel(const float* __restrict__ A, long lda,
   C[z * c_bs + (long)m * ldc + n] = acc;
 }
 
+template <int MT, int NTW, bool AF>
+hipError_t launch_lds(const GemmArgs& g, dim3 grid, int k_chunk,
+                      hipStream_t stream) {
+  constexpr int lds = LdsCfg<MT, NTW, AF>::LDS;
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute(
+        (const void*)gemm_lds_kernel<MT, NTW, AF>,
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((gemm_lds_kernel<MT, NTW, AF>), grid, dim3(256), lds,
+                     stream, g.A, g.lda, g.a_bs, (const uint16_t*)g.B,
+                     (const uint16_t*)g.B2, g.nb1, g.ldb, g.b_bs, g.C, g.ldc,
+                     g.c_bs, g.c_ks, g.M, g.N, g.K, k_chunk);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 void gemm_plan(const mla_dims& d, GemmArgs& g, int max_split) {
@@ -555,6 +763,40 @@ void gemm_plan(const mla_dims& d, GemmArgs& g, int max_split) {
   if (d.dtype != MLA_BF16 || g.b_nn || g.M > 64 || g.M <= 0 || g.N <= 0 ||
       g.K <= 0)
     return;
+  if (g.K % 64 == 0 && (g.nb1 >= g.N || g.nb1 % 32 == 0)) {
+    // LDS-staged kernel: 128 or 256 columns per workgroup and a K split
+    // (64-multiple chunks) with at most one workgroup per compute unit.
+    // Cost = weights (padded to whole column slices) + half the activation
+    // bytes (one chunk per workgroup, mostly L2 hits) + half the partial
+    // tiles written and read back, over the fraction of the 256 compute
+    // units the grid occupies (weights fitted to measured decode shapes).
+    const double a_el = g.a_f32 ? 4.0 : 2.0;
+    double best = 1e300;
+    for (int ntw = 2; ntw >= 1; --ntw) {
+      const long slices =
+          (long)((g.N + 128 * ntw - 1) / (128 * ntw)) * g.batch;
+      for (int s = 1; s <= max_split; ++s) {
+        const int kc = ((g.K + s - 1) / s + 63) / 64 * 64;
+        const int se = (g.K + kc - 1) / kc;
+        if (se != s) continue;
+        const long wgs = slices * se;
+        if (wgs > 256 && s > 1) break;
+        const double eff = wgs <= 256 ? wgs / 256.0
+                                      : wgs / (((wgs + 255) / 256) * 256.0);
+        const double wbytes = 2.0 * slices * 128.0 * ntw * g.K;
+        const double abytes = 0.5 * slices * g.M * (double)g.K * a_el;
+        const double parts =
+            se > 1 ? 0.5 * 2.0 * se * g.M * (double)g.N * 4.0 * g.batch : 0.0;
+        const double cost = (wbytes + abytes + parts) / eff;
+        if (cost < best * 0.999) {
+          best = cost;
+          g.ntw = -ntw;
+          g.k_split = se;
+        }
+      }
+    }
+    return;
+  }
   if (g.K % 16) {
     // Older skinny kernel: aim for >= ~1024 workgroups, >= 512 of K each.
     const long tiles = (long)((g.N + 31) / 32) * g.batch;
@@ -614,12 +856,30 @@ hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
   }
   const uint16_t* B = (const uint16_t*)g.B;
   const uint16_t* B2 = (const uint16_t*)g.B2;
-  if (g.c16 && (ks != 1 || g.ntw > 0 || (!g.b_nn && g.M <= 64)))
+  if (g.c16 && (ks != 1 || g.ntw != 0 || (!g.b_nn && g.M <= 64)))
     return hipErrorInvalidValue;  // bf16 output: tiled kernel, one K chunk
+  if (g.ntw < 0) {  // LDS-staged kernel, -ntw column tiles per wave
+    const int kc = (g.K + ks - 1) / ks;
+    k_chunk = (kc + 63) / 64 * 64;
+    const int ntw = -g.ntw;
+    dim3 grid(ks, (g.N + 128 * ntw - 1) / (128 * ntw), g.batch);
+#define MLA_LK(MT, NTW, AF) \
+  return launch_lds<MT, NTW, AF>(g, grid, (int)k_chunk, stream)
+#define MLA_LK_NTW(MT, AF)                    \
+  if (ntw == 1) MLA_LK(MT, 1, AF);            \
+  else MLA_LK(MT, 2, AF);
+    if (g.M <= 32) {
+      if (g.a_f32) { MLA_LK_NTW(1, true) } else { MLA_LK_NTW(1, false) }
+    } else {
+      if (g.a_f32) { MLA_LK_NTW(2, true) } else { MLA_LK_NTW(2, false) }
+    }
+#undef MLA_LK_NTW
+#undef MLA_LK
+  }
   if (g.ntw > 0) {
     const int kc = (g.K + ks - 1) / ks;
     k_chunk = (kc + 63) / 64 * 64;
-    dim3 grid((g.N + 32 * g.ntw - 1) / (32 * g.ntw), ks, g.batch);
+    dim3 grid(ks, (g.N + 32 * g.ntw - 1) / (32 * g.ntw), g.batch);
 #define MLA_ST(MT, NTW, AF)                                                   \
   hipLaunchKernelGGL((gemm_stream_kernel<MT, NTW, AF>), grid, dim3(256), 0,   \
                      stream, g.A, g.lda, g.a_bs, B, B2, g.nb1, g.ldb, g.b_bs, \
@@ -629,7 +889,8 @@ hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
     case 1: MLA_ST(MT, 1, AF); break;               \
     case 2: MLA_ST(MT, 2, AF); break;               \
     case 3: MLA_ST(MT, 3, AF); break;               \
-    default: MLA_ST(MT, 4, AF); break;              \
+    case 4: MLA_ST(MT, 4, AF); break;               \
+    default: MLA_ST(MT, 5, AF); break;              \
   }
     if (g.M <= 32) {
       if (g.a_f32) { MLA_ST_NTW(1, true) } else { MLA_ST_NTW(1, false) }

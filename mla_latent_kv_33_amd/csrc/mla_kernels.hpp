@@ -56,14 +56,16 @@ struct GemmArgs {
   long ldc = 0, c_bs = 0, c_ks = 0;
   int M = 0, N = 0, K = 0, batch = 1;
   int k_split = 1;
-  int ntw = 0;    // streaming kernel: 32-column tiles per wave (0: other)
+  // > 0: register-streaming kernel with ntw 32-column tiles per wave;
+  // < 0: LDS-staged kernel with -ntw tiles per wave; 0: skinny / tiled.
+  int ntw = 0;
   void* c16 = nullptr;  // bf16 output instead of C (tiled kernel, k_split 1)
 };
 hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
                        hipStream_t stream);
 // Chooses the kernel shape (k_split <= max_split, ntw) of a GEMM; call after
 // M, N, K, batch, a_f32 and b_nn are set.
-void gemm_plan(const mla_dims& d, GemmArgs& g, int max_split = 64);
+void gemm_plan(const mla_dims& d, GemmArgs& g, int max_split = 16);
 
 // ---- element-wise kernels ----------------------------------------------
 // Inputs given as (pointer, nparts, part_stride) are the sum of nparts fp32
