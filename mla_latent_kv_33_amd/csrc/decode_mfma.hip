@@ -126,34 +126,92 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 // group, i.e. 8 tokens x 128 contiguous bytes; the XOR makes the score and
 // the value read patterns bank-conflict free.  Wave `wave` issues groups
 // k = wave, wave + NW, ...; lane l fetches token 8 (k % 4) + l / 8, chunk
-// 8 (k / 4) + ((l % 8) ^ swz(l / 8)).  Rows at or past `nvalid` are filled
-// from the last valid row: their scores are masked, and finite data keeps
-// 0 * value at zero.
+// 8 (k / 4) + ((l % 8) ^ swz(l / 8)).  Rows at or past `nvalid` (only in the
+// last, partial half of a sequence) are filled from the last valid row:
+// their scores are masked, and finite data keeps 0 * value at zero.
+//
+// The lane's byte offset depends on k only through k % 4 (the token group)
+// and k / 4 (128 bytes per chunk group, the copy's immediate offset), so a
+// half needs at most four lane offsets, computed once per half.
 template <int NW>
-__device__ __forceinline__ void issue_half(const char* __restrict__ blk,
-                                           int hf, uint32_t lds_buf,
-                                           int nvalid, int wave, int lane) {
-  constexpr int PER = Cfg<NW>::PER_HALF;
-  const int tl = lane >> 3;
-  const uint32_t ch = ((lane & 7) ^ swz(tl)) * 16;
-  if (nvalid == HT) {
-    uint32_t lane_off = (HT * hf + tl) * ROWB + ch;
-    // Opaque, so the per-copy offsets below are recomputed (one add each)
-    // instead of being hoisted into long-lived registers.
-    asm volatile("" : "+v"(lane_off));
+struct HalfCopy {
+  static constexpr int PER = Cfg<NW>::PER_HALF;
+  static constexpr int NQ = NW >= 4 ? 1 : 4 / NW;  // distinct k % 4 per wave
+  uint32_t lane_off[NQ];
+  uint32_t lds_buf;
+  const char* blk;
+
+  __device__ __forceinline__ HalfCopy(const char* blk_, int hf, uint32_t buf,
+                                      int nvalid, int wave, int lane)
+      : lds_buf(buf), blk(blk_) {
+    int tl = lane >> 3;
+    // Opaque, so that the offsets are computed here, once per half, and not
+    // hoisted into long-lived registers.
+    asm volatile("" : "+v"(tl));
+    const uint32_t ch = ((lane & 7) ^ swz(tl)) * 16;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int k = j * NW + wave;
-      dma16(lds_buf + k * 1024, blk,
-            lane_off + 8 * (k & 3) * ROWB + (k >> 2) * 128);
-    }
-  } else {  // the last, partial half of a sequence
-#pragma unroll 1
-    for (int j = 0; j < PER; ++j) {
-      const int k = j * NW + wave;
+    for (int q = 0; q < NQ; ++q) {
+      const int k = q * NW + wave;  // k % 4 for copies i = q, q + NQ, ...
       const int t = min(8 * (k & 3) + tl, nvalid - 1);
-      dma16(lds_buf + k * 1024, blk, (HT * hf + t) * ROWB + (k >> 2) * 128 + ch);
+      lane_off[q] = (HT * hf + t) * ROWB + ch;
     }
+  }
+  // Copy i (0 .. PER - 1) of this wave: group k = i NW + wave.
+  template <int I>
+  __device__ __forceinline__ void copy(int wave) const {
+    static_assert(I < PER, "copy index");
+    constexpr int Q = I % NQ;
+    // group k = I NW + wave; k / 4 = (I NW) / 4 since wave < NW <= 4 and
+    // (I NW) % 4 + wave < 4 for every wave when NW divides 4.
+    constexpr int CG = (I * NW) / 4;
+    dma16_off<CG * 128>(lds_buf + (I * NW + wave) * 1024, blk, lane_off[Q]);
+  }
+};
+
+// Copy number `i` (a constant after unrolling) of a half.
+template <int PER>
+struct CopyOne {
+  template <class HC>
+  static __device__ __forceinline__ void run(const HC& hc, int wave, int i) {
+    run_from<0>(hc, wave, i);
+  }
+  template <int I, class HC>
+  static __device__ __forceinline__ void run_from(const HC& hc, int wave,
+                                                  int i) {
+    if constexpr (I < PER) {
+      if (i == I)
+        hc.template copy<I>(wave);
+      else
+        run_from<I + 1>(hc, wave, i);
+    }
+  }
+};
+
+// All PER copies of a half, in order (the offsets are template arguments).
+template <int I, int N>
+struct CopyAll {
+  template <class HC>
+  static __device__ __forceinline__ void run(const HC& hc, int wave) {
+    hc.template copy<I>(wave);
+    CopyAll<I + 1, N>::run(hc, wave);
+  }
+};
+template <int N>
+struct CopyAll<N, N> {
+  template <class HC>
+  static __device__ __forceinline__ void run(const HC&, int) {}
+};
+
+// Copy slot of value MFMA i (0 .. 31): copies 0 .. min(PER, 32) - 1 at an
+// even stride over the 32 MFMAs (the rest, if PER > 32, after the phase).
+template <int PER, class HC>
+__device__ __forceinline__ void copy_slot(const HC& hc, int wave, int i,
+                                          bool on) {
+  constexpr int NC = PER < 32 ? PER : 32;
+  constexpr int STRIDE = 32 / NC;
+  if (i % STRIDE == 0 && i / STRIDE < NC && on) {
+    // i is a constant here (the value phase is fully unrolled).
+    CopyOne<PER>::run(hc, wave, i / STRIDE);
   }
 }
 
@@ -204,11 +262,19 @@ decode_mfma_kernel(
 
   const int32_t* bt = block_table + (size_t)b * max_blocks;
   const uint32_t lds0 = lds_u32(lds);
-  auto issue = [&](int j) __attribute__((always_inline)) {
+  // The copies of half j from cache block `bid`.
+  auto half_copy = [&](int j, int bid) __attribute__((always_inline)) {
     const int ts = tok0 + HT * j;
-    issue_half<NW>(cache + (size_t)bt[ts / BS] * BLOCK_BYTES, j & 1,
-                   lds0 + (j & (NBUF - 1)) * HALF_BYTES,
-                   min(HT, visible - ts), wave, lane);
+    return HalfCopy<NW>(cache + (size_t)bid * BLOCK_BYTES, j & 1,
+                        lds0 + (j & (NBUF - 1)) * HALF_BYTES,
+                        min(HT, visible - ts), wave, lane);
+  };
+  auto block_of = [&](int j) __attribute__((always_inline)) {
+    return bt[(tok0 + HT * j) / BS];
+  };
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    const HalfCopy<NW> hc = half_copy(j, block_of(j));
+    CopyAll<0, PER>::run(hc, wave);
   };
 
   // Query slice: lane holds Q[head][16ks + 8g .. +7] for every k-step.
@@ -267,7 +333,7 @@ decode_mfma_kernel(
 
   // Scores of half j: two interleaved accumulation chains (even / odd k
   // steps), so consecutive MFMAs never wait on each other's results.
-  auto s_phase = [&](int j) __attribute__((always_inline)) {
+  auto s_phase = [&](int j, auto hook) __attribute__((always_inline)) {
     const lds_char* kb = L + (j & (NBUF - 1)) * HALF_BYTES;
     const lds_char* sp[4];
 #pragma unroll
@@ -280,14 +346,17 @@ decode_mfma_kernel(
     for (int i = 0; i < SDEPTH; ++i) af[i] = frag(i);
     f32x16 sa = mfma_v_first(af[0], qreg[0]);
     af[0] = frag(SDEPTH);
+    hook(0);
     __builtin_amdgcn_sched_barrier(0);
     f32x16 sb = mfma_v_first(af[1], qreg[1]);
     af[1] = frag(SDEPTH + 1);
+    hook(1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 2; ks < KSTEPS; ++ks) {
       mfma_v_acc((ks & 1) ? sb : sa, af[ks % SDEPTH], qreg[ks]);
       if (ks + SDEPTH < KSTEPS) af[ks % SDEPTH] = frag(ks + SDEPTH);
+      hook(ks);
       __builtin_amdgcn_sched_barrier(0);  // keep the ring depth as written
     }
     mfma_v_drain(sb);  // sa's last MFMA is one MFMA further back
@@ -295,10 +364,12 @@ decode_mfma_kernel(
   };
 
   // Softmax of one half tile, split in steps so that it can be spread over
-  // the value MFMAs:
-  //   step r = 0..15  : scale score r, running max
-  //   step 16         : per-head max over both lane halves, reference update
-  //   step 17..24     : P = 2^(s - m_ref) for a pair, bf16 pack, row sum
+  // the value MFMAs (scores s are raw dot products; scale_log2 > 0 turns
+  // them into log2 units, so the maximum can be taken before scaling):
+  //   step r = 0..15  : running max of the raw scores
+  //   step 16         : per-head max over both lane halves, scaled;
+  //                     reference update
+  //   step 17..24     : P = 2^(s scale - m_ref) for a pair, bf16 pack, row sum
   struct Half {
     f32x16 s;
     float tmax;
@@ -307,24 +378,24 @@ decode_mfma_kernel(
   auto softmax_step = [&](Half& H, int step) __attribute__((always_inline)) {
     if (step < 16) {
       const int r = step;
-      const float v = H.s[r] * scale_log2;
-      H.s[r] = v;
-      H.tmax = r == 0 ? v : fmaxf(H.tmax, v);
+      H.tmax = r == 0 ? H.s[0] : fmaxf(H.tmax, H.s[r]);
     } else if (step == 16) {
-      const float t = fmaxf(H.tmax, lane_xor32(H.tmax, g));
+      const float t = fmaxf(H.tmax, lane_xor32(H.tmax, g)) * scale_log2;
       if (m_ref == -INFINITY) m_ref = t;  // first half tile of the split
       const bool ovf = t > m_ref + REF_SLACK;
       m_ref = ovf ? t : m_ref;            // raised reference, next pass
       pass_ovf |= ovf;
     } else if (step < 25) {
       const int e = step - 17;
-      const float p0 = __builtin_amdgcn_exp2f(H.s[2 * e] - m_ref);
-      const float p1 = __builtin_amdgcn_exp2f(H.s[2 * e + 1] - m_ref);
-      const uint32_t pk = __builtin_bit_cast(
-          uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
-      H.pw[e] = pk;
+      const float p0 =
+          __builtin_amdgcn_exp2f(__builtin_fmaf(H.s[2 * e], scale_log2, -m_ref));
+      const float p1 = __builtin_amdgcn_exp2f(
+          __builtin_fmaf(H.s[2 * e + 1], scale_log2, -m_ref));
+      const bf16x2 pb = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+      H.pw[e] = __builtin_bit_cast(uint32_t, pb);
       // The sum uses the same bf16 weights as the value product.
-      l_run += __uint_as_float(pk << 16) + __uint_as_float(pk & 0xFFFF0000u);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(
+          pb, __builtin_bit_cast(bf16x2, 0x3F803F80u), l_run, false);
       // Materialise here, between the MFMAs this step is spread over,
       // instead of being sunk towards its use.
       asm volatile("" : "+v"(H.pw[e]), "+v"(l_run));
@@ -423,7 +494,7 @@ decode_mfma_kernel(
     barrier();
     {
       Half h;
-      h.s = s_phase(0);
+      h.s = s_phase(0, [](int) __attribute__((always_inline)) {});
       const int lim = visible - tok0;
       if (lim < HT) mask(h, lim);
 #pragma unroll
@@ -438,17 +509,27 @@ decode_mfma_kernel(
     // The last step has no next half: its scores are skipped and a fully
     // masked softmax (lim = 0) leaves m_ref, l and the flags alone (P = 0,
     // maximum -inf), so one body serves every step.
+    // The block id of the half copied in step j is loaded one step ahead
+    // (a scalar load, complete by the end-of-step lgkm wait).  The copies
+    // are spread over the value MFMAs: issued together, the workgroup's 36
+    // copies queue at the address unit (16 cycles each per CU) and block
+    // the issuing waves; spread out, the queue drains while they compute.
+    int bid_next = n_half > 3 ? block_of(3) : 0;
     for (int j = 0; j < n_half; ++j) {
       barrier();
-      if (j + 3 < n_half) issue(j + 3);
+      const bool copying = j + 3 < n_half;
+      const HalfCopy<NW> hc = half_copy(j + 3, bid_next);
+      if (j + 4 < n_half) bid_next = block_of(j + 4);
       const bool next = j + 1 < n_half;
       Half h;
-      if (next) h.s = s_phase(j + 1);
+      if (next) h.s = s_phase(j + 1, [](int) __attribute__((always_inline)) {});
       const int lim = next ? visible - (tok0 + HT * (j + 1)) : 0;
       if (lim < HT) mask(h, lim);
       pv_phase(j, [&](int i) __attribute__((always_inline)) {
         softmax_step(h, i);
+        copy_slot<PER>(hc, wave, i, copying);
       });
+      if (copying) CopyAll<32, (PER > 32 ? PER : 32)>::run(hc, wave);
       if (next) store_p(j + 1, h);
       // Half j+2 must have landed by the next barrier; j+3 may stay in
       // flight.

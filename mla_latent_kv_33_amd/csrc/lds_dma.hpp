@@ -41,6 +41,29 @@ __device__ __forceinline__ void dma16(uint32_t lds_addr, const void* sbase,
         "v"(voff)
       : "memory", "m0");
 }
+// dma16 with a constant added to the global address through the
+// instruction's offset field (0 .. 4095).  The offset field is added to the
+// LDS destination as well, so it is subtracted from M0 here: the data still
+// lands at lds_addr + 16 * lane.
+template <int IMM>
+__device__ __forceinline__ void dma16_off(uint32_t lds_addr, const void* sbase,
+                                          uint32_t voff) {
+  static_assert(IMM >= 0 && IMM < 4096, "offset field range");
+  lds_addr -= IMM;
+  const uint64_t b = (uint64_t)sbase;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %1 offset:%3"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"((const char*)sb),
+        "v"(voff), "n"(IMM)
+      : "memory", "m0");
+}
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
