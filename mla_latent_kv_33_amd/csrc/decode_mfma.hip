@@ -32,9 +32,10 @@
 //     workgroup (through ds_read_b64_tr_b16 transposing loads) rather than
 //     once per wave.  The MFMA k slots are mapped to tokens the way the score
 //     accumulator lays them out, so P needs no transposition on its way.
-//   * software pipeline, one barrier per half: step j computes the scores of
-//     half j+1, then the values of half j with the softmax of half j+1
-//     spread over those MFMAs, then stores P of half j+1.
+//   * software pipeline, one barrier per half: step j interleaves the score
+//     MFMAs of half j+1 with the first half of the value MFMAs of half j,
+//     then runs the rest of the value MFMAs with the softmax of half j+1
+//     spread over them, then stores P of half j+1.
 //   * the workgroup writes its unnormalised O, m_ref (log2 units) and l, or
 //     the final o_lat and lse when there is one split.
 //
@@ -61,7 +62,7 @@ constexpr int NBUF = 4;               // half-tile ring
 constexpr int KSTEPS = ROW / 16;      // 36 k-steps of the score MFMA
 constexpr int MT_LAT = DC / 32;       // 16 latent tiles of the value MFMA
 constexpr float REF_SLACK = 64.0f;    // log2 headroom above m_ref
-constexpr int SDEPTH = 4;             // score fragments in flight
+constexpr int SDEPTH = 3;             // score fragments in flight
 
 template <int NW>
 struct Cfg {
@@ -122,11 +123,16 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 // Copy half `hf` (tokens 32 hf .. 32 hf + 31) of a cache block into an LDS
 // half-tile buffer.  LDS layout: 16-byte chunk c (of 72 per row) of token t
 // lives in group (c / 8, t / 8) of 64 chunks (1 KiB) at 1024 (4 (c / 8) +
-// t / 8), position 8 (t % 8) + ((c % 8) ^ swz(t % 8)).  One copy fills one
-// group, i.e. 8 tokens x 128 contiguous bytes; the XOR makes the score and
-// the value read patterns bank-conflict free.  Wave `wave` issues groups
-// k = wave, wave + NW, ...; lane l fetches token 8 (k % 4) + l / 8, chunk
-// 8 (k / 4) + ((l % 8) ^ swz(l / 8)).  Rows at or past `nvalid` (only in the
+// t / 8), position 8 (t % 8) + x, x = (c % 8) ^ swz(t % 8) ^ 2 ((t / 8) % 2).
+// One copy fills one group, i.e. 8 tokens x 128 contiguous bytes.  The LDS
+// has 64 four-byte banks and serves 16 lanes of a 16-byte read (32 of an
+// 8-byte read) per cycle; the score reads take tokens 0..15 in one such
+// step, so swz spreads the 8 tokens of a group over all chunk positions of
+// two bank rows and the parity term moves the next group onto the other
+// half of each row.  Every score, value and copy access is conflict free.
+// Wave `wave` issues groups k = wave, wave + NW, ...; lane l fetches token
+// 8 (k % 4) + l / 8, chunk 8 (k / 4) + ((l % 8) ^ swz(l / 8) ^ 2 (k % 2)).
+// Rows at or past `nvalid` (only in the
 // last, partial half of a sequence) are filled from the last valid row:
 // their scores are masked, and finite data keeps 0 * value at zero.
 //
@@ -153,7 +159,7 @@ struct HalfCopy {
     for (int q = 0; q < NQ; ++q) {
       const int k = q * NW + wave;  // k % 4 for copies i = q, q + NQ, ...
       const int t = min(8 * (k & 3) + tl, nvalid - 1);
-      lane_off[q] = (HT * hf + t) * ROWB + ch;
+      lane_off[q] = (HT * hf + t) * ROWB + (ch ^ (32 * (k & 1)));
     }
   }
   // Copy i (0 .. PER - 1) of this wave: group k = i NW + wave.
@@ -165,25 +171,6 @@ struct HalfCopy {
     // (I NW) % 4 + wave < 4 for every wave when NW divides 4.
     constexpr int CG = (I * NW) / 4;
     dma16_off<CG * 128>(lds_buf + (I * NW + wave) * 1024, blk, lane_off[Q]);
-  }
-};
-
-// Copy number `i` (a constant after unrolling) of a half.
-template <int PER>
-struct CopyOne {
-  template <class HC>
-  static __device__ __forceinline__ void run(const HC& hc, int wave, int i) {
-    run_from<0>(hc, wave, i);
-  }
-  template <int I, class HC>
-  static __device__ __forceinline__ void run_from(const HC& hc, int wave,
-                                                  int i) {
-    if constexpr (I < PER) {
-      if (i == I)
-        hc.template copy<I>(wave);
-      else
-        run_from<I + 1>(hc, wave, i);
-    }
   }
 };
 
@@ -202,16 +189,15 @@ struct CopyAll<N, N> {
   static __device__ __forceinline__ void run(const HC&, int) {}
 };
 
-// Copy slot of value MFMA i (0 .. 31): copies 0 .. min(PER, 32) - 1 at an
-// even stride over the 32 MFMAs (the rest, if PER > 32, after the phase).
-template <int PER, class HC>
-__device__ __forceinline__ void copy_slot(const HC& hc, int wave, int i,
-                                          bool on) {
-  constexpr int NC = PER < 32 ? PER : 32;
-  constexpr int STRIDE = 32 / NC;
-  if (i % STRIDE == 0 && i / STRIDE < NC && on) {
-    // i is a constant here (the value phase is fully unrolled).
-    CopyOne<PER>::run(hc, wave, i / STRIDE);
+// The copies that go with group g (0 .. NG - 1) of a step: copy c is issued
+// in group (c NG) / PER, so the PER copies spread evenly over the groups.
+template <int PER, int NG, int C = 0, class HC>
+__device__ __forceinline__ void copy_group(const HC& hc, int wave, int g,
+                                           bool on) {
+  if constexpr (C < PER) {
+    // g is a constant here (the step is fully unrolled).
+    if ((C * NG) / PER == g && on) hc.template copy<C>(wave);
+    copy_group<PER, NG, C + 1>(hc, wave, g, on);
   }
 }
 
@@ -298,9 +284,11 @@ decode_mfma_kernel(
   int a_s[4];
   {
     const int t8 = col & 7;
+    const int par = 2 * ((col >> 3) & 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      a_s[j] = (col >> 3) * 1024 + t8 * 128 + 16 * ((2 * j + g) ^ swz(t8));
+      a_s[j] = (col >> 3) * 1024 + t8 * 128 +
+               16 * ((2 * j + g) ^ swz(t8) ^ par);
   }
   //  Values, k-step kk (16 tokens), read h in {0,1}, latent tile mt of the
   //  wave (global tile MTW w + mt): the 16-lane group q16 supplies rows
@@ -310,7 +298,8 @@ decode_mfma_kernel(
   //  L % 32 of the tile for tokens 16 kk + 8 h + 4 (L / 32) + 0..3, i.e. MFMA
   //  k slot 8 g + e <-> token 16 kk + 8 (e / 4) + 4 g + e % 4, the order of
   //  the score accumulator rows.  Group (c / 8, t / 8):
-  //  a_v[mt % 2] + 4096 (mt / 2) + 1024 (2 kk + h).
+  //  a_v[mt % 2] + 4096 (mt / 2) + 2048 kk, then for h = 1 the chunk parity
+  //  term (byte offset ^ 32) and + 1024.
   int a_v[2];
   {
     const int q16 = lane >> 4, s16 = lane & 15;
@@ -322,13 +311,13 @@ decode_mfma_kernel(
                4096 * (MTW / 2) * wave;
   }
   //  P of a half: head-major rows of 64 bytes, chunk 2 kk + g holding k slots
-  //  8 g .. 8 g + 7 of k-step kk (bf16), at position (2 kk + g) ^ ((h / 2) % 4)
-  //  so that 8 consecutive heads hit 8 distinct bank groups.  Head 32 nt +
-  //  col: a_p[kk] + 2048 nt.
+  //  8 g .. 8 g + 7 of k-step kk (bf16), at position (2 kk + g) ^ ((h / 4) % 4)
+  //  so that 16 consecutive heads hit 16 distinct 16-byte bank groups.
+  //  Head 32 nt + col: a_p[kk] + 2048 nt.
   int a_p[2];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
-    a_p[kk] = 64 * col + 16 * ((2 * kk + g) ^ ((col >> 1) & 3));
+    a_p[kk] = 64 * col + 16 * ((2 * kk + g) ^ ((col >> 2) & 3));
   int* const flags = (int*)(lds + C::P_OFF);
 
   // Scores of half j: two interleaved accumulation chains (even / odd k
@@ -421,49 +410,107 @@ decode_mfma_kernel(
                                             H.pw[4 * kk + 2], H.pw[4 * kk + 3]};
   };
 
-  // Values of half j: O^T[tile mt][head tile nt] += V^T(mt, kk) P(nt, kk)
-  // for kk = 0, 1, every mt of the wave and every head tile; hook(i) after
-  // the i-th of the 32 MFMAs.  All P fragments are read up front; the V^T
-  // fragments go through a ring of AR.
-  auto pv_phase = [&](int j, auto hook) __attribute__((always_inline)) {
+  // Step j, one instruction stream: the scores of half j+1 (36 MFMAs on the
+  // keys in buffer (j+1) % 4) and the values of half j (32 MFMAs,
+  // O^T[tile mt][head tile nt] += V^T(mt, kk) P(nt, kk), value MFMA
+  // i = NW (MTW kk + mt) + nt).  Part A (16 groups): group g issues the score
+  // MFMAs (36 g / 16) .. (36 (g+1) / 16) - 1 and value MFMA g, so the key
+  // reads of the score MFMAs and the value/P reads share the LDS evenly and
+  // neither kind of MFMA waits for a whole phase of reads.  Part B: value
+  // MFMAs 16 .. 31, with the softmax of half j+1 spread over them.  The
+  // copies of half j+3 go with the groups of part A.  Scores of the step
+  // after the last half are computed on stale buffer contents and fully
+  // masked by the caller's lim (0 there).
+  auto step = [&](int j, Half& H, int lim, const HalfCopy<NW>& hc,
+                  bool copying) __attribute__((always_inline)) {
     constexpr int AR = C::AR;
-    constexpr int NP = 2 * MTW;  // (kk, mt) pairs
-    const lds_char* vb = L + (j & (NBUF - 1)) * HALF_BYTES;
+    constexpr int NPV = 2 * MTW * NW;  // value MFMAs per half: 32
+    constexpr int NG = NPV / 2;        // groups of part A (kk = 0)
+    static_assert(NPV == 32, "value MFMAs per half");
+    // keys of half j+1
+    const lds_char* kb = L + ((j + 1) & (NBUF - 1)) * HALF_BYTES;
+    const lds_char* sp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sp[i] = kb + a_s[i];
+    auto frag = [&](int ks) __attribute__((always_inline)) {
+      return *(const lds_bf16x8*)(sp[ks & 3] + 4096 * (ks >> 2));
+    };
+    // values and P of half j
+    const int vb = (j & (NBUF - 1)) * HALF_BYTES;
     const lds_char* pb = L + C::P_OFF + (j & 1) * C::PBYTES;
-    const lds_char* vp0 = vb + a_v[0];
-    const lds_char* vp1 = vb + a_v[1];
+    const int vp0 = vb + a_v[0];
+    const int vp1 = vb + a_v[1];
     auto vfrag = [&](int p) __attribute__((always_inline)) {
       const int kk = p / MTW, mt = p % MTW;
-      const lds_char* base = ((mt & 1) ? vp1 : vp0) + 4096 * (mt >> 1) +
-                             2048 * kk;
+      // Bit 5 of every other term is 0, so ^ 32 flips the chunk parity.
+      const int off = ((mt & 1) ? vp1 : vp0) + 4096 * (mt >> 1) + 2048 * kk;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)base);
+          (lds_s16x4*)(L + off));
       const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(base + 1024));
+          (lds_s16x4*)(L + ((off ^ 32) + 1024)));
       const s16x8 lohi =
           __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       return __builtin_bit_cast(bf16x8, lohi);
     };
-    bf16x8 pf[2][NW];
+    auto pfrag = [&](int kk, int nt) __attribute__((always_inline)) {
+      return *(const lds_bf16x8*)(pb + a_p[kk] + 2048 * nt);
+    };
+    bf16x8 pf[NW];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-      for (int nt = 0; nt < NW; ++nt)
-        pf[kk][nt] = *(const lds_bf16x8*)(pb + a_p[kk] + 2048 * nt);
+    for (int nt = 0; nt < NW; ++nt) pf[nt] = pfrag(0, nt);
     bf16x8 vf[AR];
 #pragma unroll
     for (int p = 0; p < AR; ++p) vf[p] = vfrag(p);
+    bf16x8 af[SDEPTH];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int kk = p / MTW, mt = p % MTW;
-      const bf16x8 a = vf[p % AR];
+    for (int i = 0; i < SDEPTH; ++i) af[i] = frag(i);
+
+    f32x16 sa, sb;
+    auto s_mfma = [&](int ks) __attribute__((always_inline)) {
+      if (ks == 0)
+        sa = mfma_v_first(af[0], qreg[0]);
+      else if (ks == 1)
+        sb = mfma_v_first(af[1], qreg[1]);
+      else
+        mfma_v_acc((ks & 1) ? sb : sa, af[ks % SDEPTH], qreg[ks]);
+      if (ks + SDEPTH < KSTEPS) af[ks % SDEPTH] = frag(ks + SDEPTH);
+      __builtin_amdgcn_sched_barrier(0);  // keep the ring depth as written
+    };
+    auto v_mfma = [&](int i) __attribute__((always_inline)) {
+      const int p = i / NW, nt = i % NW, mt = p % MTW;
+      o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[p % AR], pf[nt],
+                                                          o[mt][nt], 0, 0, 0);
+      // P of kk = 1 replaces that of kk = 0 after its last use.
+      if (p == MTW - 1) pf[nt] = pfrag(1, nt);
+      if (nt == NW - 1 && p + AR < 2 * MTW) vf[p % AR] = vfrag(p + AR);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Part A
 #pragma unroll
-      for (int nt = 0; nt < NW; ++nt) {
-        o[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            a, pf[kk][nt], o[mt][nt], 0, 0, 0);
-        if (nt == NW - 1 && p + AR < NP) vf[p % AR] = vfrag(p + AR);
-        hook(p * NW + nt);
-        __builtin_amdgcn_sched_barrier(0);  // keep the ring depth as written
+    for (int g = 0; g < NG; ++g) {
+#pragma unroll
+      for (int ks = (KSTEPS * g) / NG; ks < (KSTEPS * (g + 1)) / NG; ++ks)
+        s_mfma(ks);
+      v_mfma(g);
+      copy_group<PER, NG>(hc, wave, g, copying);
+    }
+    mfma_v_drain(sb);  // sa's last MFMA is one MFMA further back
+    H.s = sa + sb;
+    if (lim < HT) mask(H, lim);
+    // Part B: softmax steps 0..7, 8..15, 16, then one exponent pair each.
+#pragma unroll
+    for (int i = NG; i < NPV; ++i) {
+      v_mfma(i);
+      const int k = i - NG;
+      if (k == 0) {
+#pragma unroll
+        for (int st = 0; st < 8; ++st) softmax_step(H, st);
+      } else if (k == 1) {
+#pragma unroll
+        for (int st = 8; st < 16; ++st) softmax_step(H, st);
+      } else if (k < 11) {
+        softmax_step(H, k + 14);
       }
     }
   };
@@ -522,14 +569,7 @@ decode_mfma_kernel(
       if (j + 4 < n_half) bid_next = block_of(j + 4);
       const bool next = j + 1 < n_half;
       Half h;
-      if (next) h.s = s_phase(j + 1, [](int) __attribute__((always_inline)) {});
-      const int lim = next ? visible - (tok0 + HT * (j + 1)) : 0;
-      if (lim < HT) mask(h, lim);
-      pv_phase(j, [&](int i) __attribute__((always_inline)) {
-        softmax_step(h, i);
-        copy_slot<PER>(hc, wave, i, copying);
-      });
-      if (copying) CopyAll<32, (PER > 32 ? PER : 32)>::run(hc, wave);
+      step(j, h, next ? visible - (tok0 + HT * (j + 1)) : 0, hc, copying);
       if (next) store_p(j + 1, h);
       // Half j+2 must have landed by the next barrier; j+3 may stay in
       // flight.
