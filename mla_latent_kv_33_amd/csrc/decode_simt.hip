@@ -131,12 +131,91 @@ __global__ __launch_bounds__(NT) void decode_simt_kernel(
 // the whole key range from per-split maxima and sums).  For each head,
 // M = max_j m_j, w_j = 2^(m_j - M) (0 for an empty split, m_j = -inf),
 // L = sum_j w_j l_j, o_lat = sum_j w_j o_j / L, lse = (M + log2 L) ln 2.
-// Workgroup = (query row, ch heads).  The weights of its heads are computed
-// in parallel (one thread per head), then each thread owns CB float4
-// columns and reads their partials CS splits at a time, so that CB * CS
-// 16-byte loads per lane are in flight.  Splits of weight 0 are not read:
-// an empty split never wrote its partial.
-constexpr int CMB_CH = 16, CMB_CB = 8, CMB_CS = 4;
+//
+// combine_rows_kernel (d_c a multiple of 4, at most 512 wide): workgroup =
+// (query row, 16 heads), 16 threads per head, thread q of a head owning the
+// float4 columns q, q + 16, ... (NB of them).  Every thread loads the m and
+// l of its head with its partial columns, CS splits at a time, so the
+// workgroup has no barrier and one round of load latency per split chunk;
+// the chunks merge online (running maximum, earlier sums rescaled).  An
+// empty split never wrote its partial, so its columns enter through a
+// select on w = 0, never a product.
+constexpr int CMB_TPH = 16, CMB_CS = 4;
+
+template <int NB>
+__global__ __launch_bounds__(256) void combine_rows_kernel(
+    int n_h, int d_c, int n_split, const float* __restrict__ o_part,
+    const float* __restrict__ m_part, const float* __restrict__ l_part,
+    float* __restrict__ o_lat, float* __restrict__ lse) {
+  const int bq = blockIdx.x;
+  const int h = blockIdx.y * (256 / CMB_TPH) + (threadIdx.x / CMB_TPH);
+  const int q = threadIdx.x % CMB_TPH;
+  if (h >= n_h) return;
+  const int c4n = d_c / 4;
+  const size_t row0 = (size_t)bq * n_split * n_h + h;  // + j n_h
+  float M = -INFINITY, L = 0.0f;
+  f32x4 acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) acc[b] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j0 = 0; j0 < n_split; j0 += CMB_CS) {
+    float m[CMB_CS], l[CMB_CS];
+    f32x4 v[CMB_CS][NB];
+#pragma unroll
+    for (int u = 0; u < CMB_CS; ++u) {
+      const int j = j0 + u;
+      const bool ok = j < n_split;
+      const size_t r = row0 + (size_t)(ok ? j : 0) * n_h;
+      m[u] = ok ? m_part[r] : -INFINITY;
+      l[u] = ok ? l_part[r] : 0.0f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const int c4 = q + CMB_TPH * b;
+        v[u][b] = (ok && c4 < c4n) ? *(const f32x4*)(o_part + r * d_c + 4 * c4)
+                                   : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+      }
+    }
+    float mc = M;
+#pragma unroll
+    for (int u = 0; u < CMB_CS; ++u) mc = fmaxf(mc, m[u]);
+    if (mc == -INFINITY) continue;  // only empty splits so far
+    const float sc = M == -INFINITY ? 0.0f : exp2f(M - mc);
+    L *= sc;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[b][e] *= sc;
+#pragma unroll
+    for (int u = 0; u < CMB_CS; ++u) {
+      const bool live = m[u] != -INFINITY;
+      const float w = live ? exp2f(m[u] - mc) : 0.0f;
+      L += live ? w * l[u] : 0.0f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[b][e] = live ? __builtin_fmaf(w, v[u][b][e], acc[b][e])
+                           : acc[b][e];
+    }
+    M = mc;
+  }
+  const float il = 1.0f / L;
+  float* dst = o_lat + ((size_t)bq * n_h + h) * d_c;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int c4 = q + CMB_TPH * b;
+    if (c4 < c4n)
+      *(f32x4*)(dst + 4 * c4) = (f32x4){acc[b][0] * il, acc[b][1] * il,
+                                        acc[b][2] * il, acc[b][3] * il};
+  }
+  if (q == 0 && lse)
+    lse[(size_t)bq * n_h + h] = (M + log2f(L)) * 0.69314718055994531f;
+}
+
+// Other widths: workgroup = (query row, ch heads).  The weights of its
+// heads are computed in parallel (one thread per head), then each thread
+// owns CB float4 columns and reads their partials CS splits at a time.
+// Splits of weight 0 are not read: an empty split never wrote its partial.
+constexpr int CMB_CH = 16, CMB_CB = 8;
 constexpr size_t CMB_LDS_MAX = 160 * 1024;
 
 __global__ __launch_bounds__(256) void combine_kernel(
@@ -257,6 +336,24 @@ hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
                           const float* l_part, float* o_lat, float* lse,
                           hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
+  if (d.d_c % 4 == 0 && d.d_c <= 4 * CMB_TPH * 8) {
+    const int c4n = d.d_c / 4;
+    const int nb = (c4n + CMB_TPH - 1) / CMB_TPH;
+    dim3 grid(rows, (d.n_h + 256 / CMB_TPH - 1) / (256 / CMB_TPH));
+#define MLA_CMB(NB)                                                          \
+  hipLaunchKernelGGL(combine_rows_kernel<NB>, grid, dim3(256), 0, stream,     \
+                     d.n_h, d.d_c, n_split, o_part, m_part, l_part, o_lat, lse)
+    if (nb <= 1)
+      MLA_CMB(1);
+    else if (nb <= 2)
+      MLA_CMB(2);
+    else if (nb <= 4)
+      MLA_CMB(4);
+    else
+      MLA_CMB(8);
+#undef MLA_CMB
+    return hipGetLastError();
+  }
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
