@@ -75,7 +75,8 @@ __global__ void append_scatter_kernel(
 }
 
 template <typename T>
-__global__ void query_rope_kernel(const float* __restrict__ qr, long ld_qr,
+__global__ void query_rope_kernel(const float* __restrict__ qr, int nparts,
+                                  long part_stride, long ld_qr,
                                   int n_h, int d_c, int d_r,
                                   const int32_t* __restrict__ pos,
                                   const float* __restrict__ rcos,
@@ -88,7 +89,8 @@ __global__ void query_rope_kernel(const float* __restrict__ qr, long ld_qr,
   for (int i = blockIdx.y * blockDim.x + threadIdx.x; i < n_h * half;
        i += gridDim.y * blockDim.x) {
     const int h = i / half, jj = i - h * half;
-    const float x1 = src[h * d_r + jj], x2 = src[h * d_r + jj + half];
+    const float x1 = sum_parts(src, nparts, part_stride, h * d_r + jj);
+    const float x2 = sum_parts(src, nparts, part_stride, h * d_r + jj + half);
     const bool ok = p >= 0 && p < max_pos;
     const float c = ok ? rcos[(long)p * half + jj] : NAN;
     const float s = ok ? rsin[(long)p * half + jj] : NAN;
@@ -149,19 +151,22 @@ hipError_t launch_append_scatter(const mla_dims& d, int T, const float* acc,
 }
 
 hipError_t launch_query_rope(const mla_dims& d, int T, const float* qr,
-                             long ld_qr, const int32_t* pos,
-                             const float* rope_cos, const float* rope_sin,
-                             int max_pos, void* q_out, hipStream_t stream) {
+                             int nparts, long part_stride, long ld_qr,
+                             const int32_t* pos, const float* rope_cos,
+                             const float* rope_sin, int max_pos, void* q_out,
+                             hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   const dim3 grid(T, (d.n_h * (d.d_r / 2) + 255) / 256);
   if (d.dtype == MLA_BF16)
     hipLaunchKernelGGL(query_rope_kernel<uint16_t>, grid, dim3(256), 0,
-                       stream, qr, ld_qr, d.n_h, d.d_c, d.d_r, pos, rope_cos,
-                       rope_sin, max_pos, (uint16_t*)q_out);
+                       stream, qr, nparts, part_stride, ld_qr, d.n_h, d.d_c,
+                       d.d_r, pos, rope_cos, rope_sin, max_pos,
+                       (uint16_t*)q_out);
   else
     hipLaunchKernelGGL(query_rope_kernel<float>, grid, dim3(256), 0,
-                       stream, qr, ld_qr, d.n_h, d.d_c, d.d_r, pos, rope_cos,
-                       rope_sin, max_pos, (float*)q_out);
+                       stream, qr, nparts, part_stride, ld_qr, d.n_h, d.d_c,
+                       d.d_r, pos, rope_cos, rope_sin, max_pos,
+                       (float*)q_out);
   return hipGetLastError();
 }
 

@@ -44,6 +44,29 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
 }
 
+// fp32 x -> bf16 hi + bf16 lo with hi + lo = x to about 16 significant bits
+// (hi rounded to nearest by the hardware conversion, lo the rounded
+// remainder): eight values a[0..3], b[0..3] into hi[0..7], lo[0..7].  Two
+// bf16 products against the same weight then reproduce an fp32 activation.
+__device__ __forceinline__ void split_hi_lo_hw(const f32x4& a, const f32x4& b,
+                                               bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t hp = __builtin_bit_cast(
+        uint32_t, __builtin_convertvector((f32x2){x[2 * e], x[2 * e + 1]},
+                                          bf16x2));
+    const float r0 = x[2 * e] - __uint_as_float(hp << 16);
+    const float r1 = x[2 * e + 1] - __uint_as_float(hp & 0xFFFF0000u);
+    h[e] = hp;
+    l[e] = __builtin_bit_cast(
+        uint32_t, __builtin_convertvector((f32x2){r0, r1}, bf16x2));
+  }
+  hi = __builtin_bit_cast(bf16x8, (u32x4){h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]});
+}
+
 template <typename T>
 struct DT;
 template <>

@@ -34,6 +34,18 @@ hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
                           const float* l_part, float* o_lat, float* lse,
                           hipStream_t stream);
 
+// ---- query absorption (absorb.hip) -------------------------------------
+// q_lat[t, h, :] = W_UK_h^T (sum of nparts fp32 parts of q_C[t, h, :]) into
+// the first d_c columns of q_out's rows (bf16), for the shapes accepted by
+// absorb_fast_supported (bf16, d_h = 128, d_c % 256 == 0, T <= 64, at most
+// two parts).  parts: T rows of stride lda floats, head h at column h d_h,
+// part p at parts + p part_stride.
+bool absorb_fast_supported(const mla_dims& d, int T, int nparts);
+hipError_t launch_absorb_fast(const mla_dims& d, int T, const float* parts,
+                              int nparts, long part_stride, long lda,
+                              const void* w_uk, void* q_out,
+                              hipStream_t stream);
+
 // ---- GEMM C = A . B^T --------------------------------------------------
 // A [M][K] (row stride lda, batch stride a_bs), fp32 or the layer dtype.
 // B (layer dtype) is either [N][K] ("NT", row stride ldb), optionally in two
@@ -83,10 +95,12 @@ hipError_t launch_append_scatter(const mla_dims& d, int T, const float* acc,
                                  hipStream_t stream);
 // qr rows of ld_qr floats, the [n_h][d_r] block of token t at
 // qr + t * ld_qr -> RoPE -> q_out[t][h][d_c ..] (layer dtype).
+// qr: the sum of nparts fp32 parts spaced part_stride floats apart.
 hipError_t launch_query_rope(const mla_dims& d, int T, const float* qr,
-                             long ld_qr, const int32_t* pos,
-                             const float* rope_cos, const float* rope_sin,
-                             int max_pos, void* q_out, hipStream_t stream);
+                             int nparts, long part_stride, long ld_qr,
+                             const int32_t* pos, const float* rope_cos,
+                             const float* rope_sin, int max_pos, void* q_out,
+                             hipStream_t stream);
 // src fp32 [rows][cols] (row stride lds, parts) -> dst layer dtype (row
 // stride ldd).
 hipError_t launch_convert(const mla_dims& d, int rows, int cols,
