@@ -36,8 +36,10 @@
 //     MFMAs of half j+1 with the first half of the value MFMAs of half j,
 //     then runs the rest of the value MFMAs with the softmax of half j+1
 //     spread over them, then stores P of half j+1.
-//   * the workgroup writes its unnormalised O, m_ref (log2 units) and l, or
-//     the final o_lat and lse when there is one split.
+//   * the workgroup writes its partial O / l as fp16 under a power-of-two
+//     scale per head (half the bytes of fp32, 11 significant bits), with
+//     m_ref (log2 units), l and the scale, or the final o_lat and lse when
+//     there is one split.
 //
 // LDS (NW = 4): 4 half-tile buffers of 36 KiB, then two P buffers of
 // 128 heads x 32 tokens bf16 (8 KiB each): 160 KiB, the whole LDS.
@@ -628,18 +630,56 @@ decode_mfma_kernel(
       lse_final[(size_t)bq * n_h + head] =
           (m_ref + __log2f(l_run)) * 0.69314718055994531f;
   } else {
+    // fp16 partials: row (query row, split, head) of DC elements holding
+    // O / (l s), s = 2^e per head with e chosen so that the head's largest
+    // |O / l| lands in [2^14, 2^15): any input range fits fp16 (max 65504)
+    // and every value keeps 11 significant bits.  The rows' scales follow
+    // the fp16 rows in the same buffer.  Per-head maxima cross the waves
+    // through the first half-tile buffer: no copy is in flight and every
+    // wave is past its last read of it (flag barrier above).
+    uint16_t* const o16 = (uint16_t*)o_part;
+    float* const sc_part =
+        (float*)(o16 + (size_t)gridDim.x * n_split * n_h * DC);
+    float* const mx = (float*)lds;  // [NW][HEADS]
+    float inv[NW];
 #pragma unroll
     for (int nt = 0; nt < NW; ++nt) {
-      float* dst = o_part + (row_base + hbase + 32 * nt + col) * DC +
-                   32 * MTW * wave;
+      inv[nt] = 1.0f / l_nt[nt];  // l >= 1: the maximum key has P = 1
+      float a = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a = fmaxf(a, fabsf(o[mt][nt][r]));
+      a = fmaxf(a, lane_xor32(a, g)) * inv[nt];
+      if (g == 0) mx[wave * C::HEADS + 32 * nt + col] = a;
+    }
+    wait_lgkm0();
+    barrier();
+#pragma unroll
+    for (int nt = 0; nt < NW; ++nt) {
+      float hm = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) hm = fmaxf(hm, mx[w * C::HEADS + 32 * nt + col]);
+      const int e = hm > 0.0f
+                        ? min(max(__builtin_amdgcn_frexp_expf(hm) - 15, -100), 120)
+                        : 0;
+      const float mul = inv[nt] * __builtin_amdgcn_ldexpf(1.0f, -e);
+      uint16_t* dst = o16 + (row_base + hbase + 32 * nt + col) * DC +
+                      32 * MTW * wave;
 #pragma unroll
       for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          f32x4 v = {o[mt][nt][4 * i], o[mt][nt][4 * i + 1],
-                     o[mt][nt][4 * i + 2], o[mt][nt][4 * i + 3]};
-          *(f32x4*)(dst + 32 * mt + 8 * i + 4 * g) = v;
+          const f16x4 h = __builtin_convertvector(
+              ((f32x4){o[mt][nt][4 * i], o[mt][nt][4 * i + 1],
+                       o[mt][nt][4 * i + 2], o[mt][nt][4 * i + 3]}) * mul,
+              f16x4);
+          *(uint2*)(dst + 32 * mt + 8 * i + 4 * g) =
+              __builtin_bit_cast(uint2, h);
         }
+      if (g == 0 && wave == 0)
+        sc_part[row_base + hbase + 32 * nt + col] =
+            __builtin_amdgcn_ldexpf(1.0f, e);
     }
     if (g == 0) {
       m_part[row_base + head] = m_ref;

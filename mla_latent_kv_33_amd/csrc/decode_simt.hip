@@ -132,34 +132,46 @@ __global__ __launch_bounds__(NT) void decode_simt_kernel(
 // M = max_j m_j, w_j = 2^(m_j - M) (0 for an empty split, m_j = -inf),
 // L = sum_j w_j l_j, o_lat = sum_j w_j o_j / L, lse = (M + log2 L) ln 2.
 //
-// combine_rows_kernel (d_c a multiple of 4, at most 512 wide): workgroup =
-// (query row, 16 heads), 16 threads per head, thread q of a head owning the
-// float4 columns q, q + 16, ... (NB of them).  Every thread loads the m and
-// l of its head with its partial columns, CS splits at a time, so the
-// workgroup has no barrier and one round of load latency per split chunk;
-// the chunks merge online (running maximum, earlier sums rescaled).  An
-// empty split never wrote its partial, so its columns enter through a
-// select on w = 0, never a product.
+// combine_rows_kernel (d_c a multiple of 4, at most 512 wide; with fp16
+// partials a multiple of 8): workgroup = (query row, 16 heads), 16 threads
+// per head, thread q of a head owning the column vectors q, q + 16, ...
+// (NB of them; 4 fp32 columns, or 8 fp16 columns for fp16 partials).  Every
+// thread loads the m and l of its head with its partial columns, CS splits
+// at a time, so the workgroup has no barrier and one round of load latency
+// per split chunk; the chunks merge online (running maximum, earlier sums
+// rescaled).  An empty split never wrote its partial, so its columns enter
+// through a select on w = 0, never a product.
+//
+// fp32 partials hold the unnormalised O_j (weight w_j); fp16 partials hold
+// O_j / (l_j s_j) with s_j the row's scale stored after the fp16 rows
+// (weight w_j l_j s_j), as the matrix-core decode writes them.
 constexpr int CMB_TPH = 16, CMB_CS = 4;
 
-template <int NB>
+template <int NB, bool P16>
 __global__ __launch_bounds__(256) void combine_rows_kernel(
     int n_h, int d_c, int n_split, const float* __restrict__ o_part,
     const float* __restrict__ m_part, const float* __restrict__ l_part,
     float* __restrict__ o_lat, float* __restrict__ lse) {
+  constexpr int VW = P16 ? 8 : 4;  // columns per vector
   const int bq = blockIdx.x;
   const int h = blockIdx.y * (256 / CMB_TPH) + (threadIdx.x / CMB_TPH);
   const int q = threadIdx.x % CMB_TPH;
   if (h >= n_h) return;
-  const int c4n = d_c / 4;
+  const int cvn = d_c / VW;
   const size_t row0 = (size_t)bq * n_split * n_h + h;  // + j n_h
+  const uint16_t* const p16 = (const uint16_t*)o_part;
+  const float* const sc_part =
+      (const float*)(p16 + (size_t)gridDim.x * n_split * n_h * d_c);
   float M = -INFINITY, L = 0.0f;
-  f32x4 acc[NB];
+  f32x4 acc[NB][VW / 4];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) acc[b] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int hh = 0; hh < VW / 4; ++hh)
+      acc[b][hh] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
   for (int j0 = 0; j0 < n_split; j0 += CMB_CS) {
-    float m[CMB_CS], l[CMB_CS];
-    f32x4 v[CMB_CS][NB];
+    float m[CMB_CS], l[CMB_CS], ps[CMB_CS];
+    f32x4 v[CMB_CS][NB][VW / 4];
 #pragma unroll
     for (int u = 0; u < CMB_CS; ++u) {
       const int j = j0 + u;
@@ -167,11 +179,24 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
       const size_t r = row0 + (size_t)(ok ? j : 0) * n_h;
       m[u] = ok ? m_part[r] : -INFINITY;
       l[u] = ok ? l_part[r] : 0.0f;
+      ps[u] = (P16 && ok) ? sc_part[r] : 1.0f;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const int c4 = q + CMB_TPH * b;
-        v[u][b] = (ok && c4 < c4n) ? *(const f32x4*)(o_part + r * d_c + 4 * c4)
-                                   : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        const int cv = q + CMB_TPH * b;
+        const bool in = ok && cv < cvn;
+        if (P16) {
+          const uint4 x = in ? *(const uint4*)(p16 + r * d_c + 8 * cv)
+                             : make_uint4(0, 0, 0, 0);
+          const f32x8 f =
+              __builtin_convertvector(__builtin_bit_cast(f16x8, x), f32x8);
+#pragma unroll
+          for (int hh = 0; hh < VW / 4; ++hh)
+            v[u][b][hh] = (f32x4){f[4 * hh], f[4 * hh + 1], f[4 * hh + 2],
+                                  f[4 * hh + 3]};
+        } else {
+          v[u][b][0] = in ? *(const f32x4*)(o_part + r * d_c + 4 * cv)
+                          : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        }
       }
     }
     float mc = M;
@@ -183,18 +208,25 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[b][e] *= sc;
+      for (int hh = 0; hh < VW / 4; ++hh)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[b][hh][e] *= sc;
 #pragma unroll
     for (int u = 0; u < CMB_CS; ++u) {
       const bool live = m[u] != -INFINITY;
       const float w = live ? exp2f(m[u] - mc) : 0.0f;
-      L += live ? w * l[u] : 0.0f;
+      const float wl = w * l[u];
+      L += live ? wl : 0.0f;
+      const float wv = P16 ? wl * ps[u] : w;  // weight of the stored partial
 #pragma unroll
       for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[b][e] = live ? __builtin_fmaf(w, v[u][b][e], acc[b][e])
-                           : acc[b][e];
+        for (int hh = 0; hh < VW / 4; ++hh)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[b][hh][e] =
+                live ? __builtin_fmaf(wv, v[u][b][hh][e], acc[b][hh][e])
+                     : acc[b][hh][e];
     }
     M = mc;
   }
@@ -202,10 +234,13 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
   float* dst = o_lat + ((size_t)bq * n_h + h) * d_c;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int c4 = q + CMB_TPH * b;
-    if (c4 < c4n)
-      *(f32x4*)(dst + 4 * c4) = (f32x4){acc[b][0] * il, acc[b][1] * il,
-                                        acc[b][2] * il, acc[b][3] * il};
+    const int cv = q + CMB_TPH * b;
+    if (cv < cvn)
+#pragma unroll
+      for (int hh = 0; hh < VW / 4; ++hh)
+        *(f32x4*)(dst + VW * cv + 4 * hh) =
+            (f32x4){acc[b][hh][0] * il, acc[b][hh][1] * il,
+                    acc[b][hh][2] * il, acc[b][hh][3] * il};
   }
   if (q == 0 && lse)
     lse[(size_t)bq * n_h + h] = (M + log2f(L)) * 0.69314718055994531f;
@@ -332,28 +367,34 @@ hipError_t launch_decode_simt(const mla_dims& d, int B, int n_q,
 }
 
 hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
-                          const float* o_part, const float* m_part,
-                          const float* l_part, float* o_lat, float* lse,
-                          hipStream_t stream) {
+                          const float* o_part, bool f16_parts,
+                          const float* m_part, const float* l_part,
+                          float* o_lat, float* lse, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
+  const dim3 rgrid(rows, (d.n_h + 256 / CMB_TPH - 1) / (256 / CMB_TPH));
+#define MLA_CMB(NB, P16)                                                      \
+  hipLaunchKernelGGL((combine_rows_kernel<NB, P16>), rgrid, dim3(256), 0,      \
+                     stream, d.n_h, d.d_c, n_split, o_part, m_part, l_part,   \
+                     o_lat, lse)
+  if (f16_parts) {
+    if (d.d_c % 8 != 0 || d.d_c > 8 * CMB_TPH * 4) return hipErrorInvalidValue;
+    MLA_CMB(4, true);
+    return hipGetLastError();
+  }
   if (d.d_c % 4 == 0 && d.d_c <= 4 * CMB_TPH * 8) {
     const int c4n = d.d_c / 4;
     const int nb = (c4n + CMB_TPH - 1) / CMB_TPH;
-    dim3 grid(rows, (d.n_h + 256 / CMB_TPH - 1) / (256 / CMB_TPH));
-#define MLA_CMB(NB)                                                          \
-  hipLaunchKernelGGL(combine_rows_kernel<NB>, grid, dim3(256), 0, stream,     \
-                     d.n_h, d.d_c, n_split, o_part, m_part, l_part, o_lat, lse)
     if (nb <= 1)
-      MLA_CMB(1);
+      MLA_CMB(1, false);
     else if (nb <= 2)
-      MLA_CMB(2);
+      MLA_CMB(2, false);
     else if (nb <= 4)
-      MLA_CMB(4);
+      MLA_CMB(4, false);
     else
-      MLA_CMB(8);
-#undef MLA_CMB
+      MLA_CMB(8, false);
     return hipGetLastError();
   }
+#undef MLA_CMB
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(

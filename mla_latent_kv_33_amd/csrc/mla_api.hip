@@ -385,7 +385,8 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, int32_t n_q,
     m_part = c.take(rows);
     l_part = c.take(rows);
   }
-  if (decode_mfma_supported(d))
+  const bool mfma = decode_mfma_supported(d);
+  if (mfma)
     MLA_TRY(launch_decode_mfma(d, B, n_q, q, cache, block_table, max_blocks,
                                kv_lens, ns, o_part, m_part, l_part, o_lat,
                                lse, s));
@@ -394,7 +395,8 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, int32_t n_q,
                                kv_lens, ns, o_part, m_part, l_part, o_lat,
                                lse, s));
   if (ns > 1)
-    MLA_TRY(launch_combine(d, B * n_q, ns, o_part, m_part, l_part, o_lat, lse, s));
+    MLA_TRY(launch_combine(d, B * n_q, ns, o_part, mfma, m_part, l_part,
+                           o_lat, lse, s));
   return MLA_OK;
 }
 

@@ -11,8 +11,10 @@ namespace mla {
 // ---- split-KV decode ---------------------------------------------------
 // Split j of a (sequence, query) whose visible keys span nblk blocks covers
 // blocks [j nblk / n_split, (j + 1) nblk / n_split).
-// Partials: o_part [B*n_q][n_split][n_h][d_c] (unnormalised), m_part/l_part
-// [B*n_q][n_split][n_h] with m in log2 units.  With n_split == 1 the kernels
+// Partials: o_part [B*n_q][n_split][n_h][d_c] (fp32 unnormalised from the
+// SIMT kernel; from the matrix-core kernel fp16 O / (l s) in the first half
+// of the same buffer, followed by the per-row scales s as fp32),
+// m_part/l_part [B*n_q][n_split][n_h] with m in log2 units.  With n_split == 1 the kernels
 // write o_final [B*n_q][n_h][d_c] and lse_final (natural log) directly.
 bool decode_mfma_supported(const mla_dims& d);
 hipError_t launch_decode_mfma(const mla_dims& d, int B, int n_q,
@@ -29,10 +31,12 @@ hipError_t launch_decode_simt(const mla_dims& d, int B, int n_q,
                               float* o_part, float* m_part,
                               float* l_part, float* o_final, float* lse_final,
                               hipStream_t stream);
+// o_part: fp32 unnormalised partials (decode_simt_kernel), or with
+// f16_parts the scaled fp16 partials of decode_mfma_kernel.
 hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
-                          const float* o_part, const float* m_part,
-                          const float* l_part, float* o_lat, float* lse,
-                          hipStream_t stream);
+                          const float* o_part, bool f16_parts,
+                          const float* m_part, const float* l_part,
+                          float* o_lat, float* lse, hipStream_t stream);
 
 // ---- query absorption (absorb.hip) -------------------------------------
 // q_lat[t, h, :] = W_UK_h^T (sum of nparts fp32 parts of q_C[t, h, :]) into
