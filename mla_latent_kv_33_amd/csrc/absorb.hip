@@ -6,9 +6,13 @@
 // with W_UK_h stored [d_h][d_c] (row k holds the d_c latent weights of
 // query feature k), and q_C[m, h, :] the sum of the K-split parts of the
 // query up-projection (fp32).  The result is rounded to bf16 into the first
-// d_c columns of the head's query row.
+// d_c columns of the head's query row.  The same launch rotates the head's
+// decoupled RoPE query (section 5: q_R = RoPE(W_QR c_Q), half-split pairs
+// (j, j + d_r / 2) at angle pos theta_j from the cos / sin tables) into the
+// last d_r columns: the workgroups of a head share its query rows, after
+// their MFMA work.
 //
-// Shape this kernel serves: bf16 weights, d_h = 128, d_c a multiple of 256,
+// Shape this kernel serves: bf16 weights, d_h = 128, d_r = 64, d_c a multiple of 256,
 // at most 64 query rows and at most two fp32 parts.  Workgroup = (head,
 // 256 latent columns), 4 waves; wave w owns latent columns 64 w .. 64 w + 63
 // and every query row.  The transposed product C^T[n][m] is accumulated, so
@@ -41,11 +45,14 @@ constexpr int AB_W_BYTES = AB_K * AB_N * 2;  // 64 KiB
 constexpr int AB_ROWS = 64;                // query rows held
 constexpr int AB_A_BYTES = AB_ROWS * AB_K * 4;  // 32 KiB per part
 constexpr int AB_MAX_PARTS = 2;
+constexpr int AB_DR = 64;                  // d_r
 
 __global__ __launch_bounds__(256) void absorb_kernel(
     const float* __restrict__ parts, int nparts, long part_stride, long lda,
     const uint16_t* __restrict__ w_uk, int d_c, int row_elems, int M,
-    uint16_t* __restrict__ q_out, long ldq) {
+    uint16_t* __restrict__ q_out, long ldq, long qr_col,
+    const int32_t* __restrict__ pos, const float* __restrict__ rcos,
+    const float* __restrict__ rsin, int max_pos) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -195,19 +202,52 @@ __global__ __launch_bounds__(256) void absorb_kernel(
                        __builtin_bit_cast(uint32_t, p1));
       }
   }
+
+  // ---- RoPE query of head h: rows [r0, r1) of this workgroup, 4 pairs per
+  // item.  Every copy has landed (vmcnt 0 above), so these loads are the
+  // only ones in flight.  An out-of-range position yields NaN, as for the
+  // cache rows.
+  constexpr int HALF = AB_DR / 2;
+  const int rows_per = (AB_ROWS + gridDim.y - 1) / gridDim.y;
+  const int r0 = ns * rows_per, r1 = min(M, r0 + rows_per);
+  for (int it = threadIdx.x; it < (r1 - r0) * (HALF / 4); it += 256) {
+    const int m = r0 + it / (HALF / 4);
+    const int j0 = 4 * (it % (HALF / 4));
+    const int p = pos[m];
+    const bool ok = p >= 0 && p < max_pos;
+    const size_t src = (size_t)m * lda + qr_col + (size_t)h * AB_DR + j0;
+    f32x4 x1 = *(const f32x4*)(parts + src);
+    f32x4 x2 = *(const f32x4*)(parts + src + HALF);
+    for (int pp = 1; pp < nparts; ++pp) {
+      x1 += *(const f32x4*)(parts + pp * part_stride + src);
+      x2 += *(const f32x4*)(parts + pp * part_stride + src + HALF);
+    }
+    const f32x4 c = ok ? *(const f32x4*)(rcos + (size_t)p * HALF + j0)
+                       : (f32x4){NAN, NAN, NAN, NAN};
+    const f32x4 s = ok ? *(const f32x4*)(rsin + (size_t)p * HALF + j0)
+                       : (f32x4){NAN, NAN, NAN, NAN};
+    uint16_t* dst = q_out + (size_t)m * ldq + (size_t)h * row_elems + d_c + j0;
+    const f32x4 y1 = x1 * c - x2 * s;
+    const f32x4 y2 = x1 * s + x2 * c;
+    *(uint2*)dst = make_uint2(pack_bf2(y1[0], y1[1]), pack_bf2(y1[2], y1[3]));
+    *(uint2*)(dst + HALF) =
+        make_uint2(pack_bf2(y2[0], y2[1]), pack_bf2(y2[2], y2[3]));
+  }
 }
 
 }  // namespace
 
 bool absorb_fast_supported(const mla_dims& d, int T, int nparts) {
   return d.dtype == MLA_BF16 && d.d_h == AB_K && d.d_c % AB_N == 0 &&
-         T >= 1 && T <= AB_ROWS && nparts >= 1 && nparts <= AB_MAX_PARTS;
+         d.d_r == AB_DR && T >= 1 && T <= AB_ROWS && nparts >= 1 &&
+         nparts <= AB_MAX_PARTS;
 }
 
 hipError_t launch_absorb_fast(const mla_dims& d, int T, const float* parts,
                               int nparts, long part_stride, long lda,
-                              const void* w_uk, void* q_out,
-                              hipStream_t stream) {
+                              const void* w_uk, const int32_t* pos,
+                              const float* rope_cos, const float* rope_sin,
+                              int max_pos, void* q_out, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
@@ -222,7 +262,8 @@ hipError_t launch_absorb_fast(const mla_dims& d, int T, const float* parts,
   hipLaunchKernelGGL(absorb_kernel, grid, dim3(256), lds, stream, parts,
                      nparts, part_stride, lda, (const uint16_t*)w_uk, d.d_c,
                      row_elems, T, (uint16_t*)q_out,
-                     (long)d.n_h * row_elems);
+                     (long)d.n_h * row_elems, (long)d.n_h * d.d_h, pos,
+                     rope_cos, rope_sin, max_pos);
   return hipGetLastError();
 }
 

@@ -303,15 +303,12 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
   g2.B2 = w_qr;
   g2.C = w.qcr_parts;
   MLA_TRY(launch_gemm(d, g2, s));
-  // Decode batches: the RoPE and absorption kernels read the K-split parts
-  // of q_C / q_R themselves.
-  if (absorb_fast_supported(d, T, g2.k_split)) {
-    MLA_TRY(launch_query_rope(d, T, w.qcr_parts + (long)d.n_h * d.d_h,
-                              g2.k_split, g2.c_ks, g2.ldc, pos, rope_cos,
-                              rope_sin, max_pos, q_out, s));
+  // Decode batches: one kernel reads the K-split parts of q_C / q_R and
+  // writes both halves of every query row.
+  if (absorb_fast_supported(d, T, g2.k_split))
     return dev(launch_absorb_fast(d, T, w.qcr_parts, g2.k_split, g2.c_ks,
-                                  g2.ldc, w_uk, q_out, s));
-  }
+                                  g2.ldc, w_uk, pos, rope_cos, rope_sin,
+                                  max_pos, q_out, s));
   if (g2.k_split > 1)
     MLA_TRY(launch_reduce_parts(w.qcr_parts, g2.k_split, g2.c_ks,
                                 (long)T * g2.N, w.qcr, s));

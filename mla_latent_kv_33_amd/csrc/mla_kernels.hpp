@@ -40,15 +40,17 @@ hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
 
 // ---- query absorption (absorb.hip) -------------------------------------
 // q_lat[t, h, :] = W_UK_h^T (sum of nparts fp32 parts of q_C[t, h, :]) into
-// the first d_c columns of q_out's rows (bf16), for the shapes accepted by
-// absorb_fast_supported (bf16, d_h = 128, d_c % 256 == 0, T <= 64, at most
-// two parts).  parts: T rows of stride lda floats, head h at column h d_h,
-// part p at parts + p part_stride.
+// the first d_c columns of q_out's rows (bf16), and RoPE(q_R[t, h, :]) into
+// the last d_r, for the shapes accepted by absorb_fast_supported (bf16,
+// d_h = 128, d_c % 256 == 0, d_r = 64, T <= 64, at most two parts).
+// parts: T rows of stride lda floats, q_C of head h at column h d_h, q_R of
+// head h at column n_h d_h + h d_r, part p at parts + p part_stride.
 bool absorb_fast_supported(const mla_dims& d, int T, int nparts);
 hipError_t launch_absorb_fast(const mla_dims& d, int T, const float* parts,
                               int nparts, long part_stride, long lda,
-                              const void* w_uk, void* q_out,
-                              hipStream_t stream);
+                              const void* w_uk, const int32_t* pos,
+                              const float* rope_cos, const float* rope_sin,
+                              int max_pos, void* q_out, hipStream_t stream);
 
 // ---- GEMM C = A . B^T --------------------------------------------------
 // A [M][K] (row stride lda, batch stride a_bs), fp32 or the layer dtype.
