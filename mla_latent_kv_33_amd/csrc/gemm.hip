@@ -347,7 +347,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
 // ------------------------------------------------------------------ ldsk
 // LDS-staged weight-streaming kernel for M <= 64, NT, K % 64 == 0 (and the
 // B / B2 boundary at a multiple of 32 rows).  Workgroup = 4 waves over
-// 128 NTW output columns, wave w owning column tiles w NTW .. w NTW + NTW-1;
+// 128 NTW output columns and 32 MT rows (row block gridDim.z / batch of a
+// row split: a small grid can run each half of the rows in its own
+// workgroup, the pair sharing the weights through L2),
+// wave w owning column tiles w NTW .. w NTW + NTW-1;
 // all waves walk the workgroup's K chunk together in super-steps of 64 k.
 // Each super-step's activation rows (shared by the waves) and weight rows
 // are copied HBM -> LDS by direct-to-LDS loads, whole 128-byte line runs per
@@ -381,7 +384,7 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
     const void* __restrict__ Av, long lda, long a_bs,
     const uint16_t* __restrict__ B, const uint16_t* __restrict__ B2, int nb1,
     long ldb, long b_bs, float* __restrict__ C, long ldc, long c_bs, long c_ks,
-    int M, int N, int K, int k_chunk) {
+    int M, int N, int K, int k_chunk, int m_split) {
   using L = LdsCfg<MT, NTW, AF32>;
   constexpr int NBUF = L::NBUF;
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -392,7 +395,12 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
   // K chunk fastest in the launch order (see gemm_stream_kernel).
   const int kz = blockIdx.x;
   const int n_wg = blockIdx.y * 128 * NTW;
-  const int z = blockIdx.z;
+  const int nbatch = gridDim.z / m_split;
+  const int z = blockIdx.z % nbatch;
+  const int m0 = (blockIdx.z / nbatch) * L::MROWS;  // first row of the block
+  M = min(L::MROWS, M - m0);
+  if (M <= 0) return;  // empty row block (whole workgroup, before any barrier)
+  C += (size_t)m0 * ldc;
   const int kbeg = kz * k_chunk;
   const int kend = min(K, kbeg + k_chunk);
   const int nss = max(0, (kend - kbeg) / 64);
@@ -402,8 +410,8 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
   // A: copy i (= wave A_PER + a) covers rows i RPI .. i RPI + RPI - 1; lane l
   // takes row r = i RPI + l / PPR and piece (l % PPR) ^ (r % 8) of it, so
   // that LDS position p of row r holds piece p ^ (r % 8).
-  const char* a_base =
-      (const char*)Av + (size_t)z * a_bs * esz + (size_t)kbeg * esz;
+  const char* a_base = (const char*)Av + (size_t)z * a_bs * esz +
+                       (size_t)m0 * lda * esz + (size_t)kbeg * esz;
   uint32_t a_off[L::A_PER];
 #pragma unroll
   for (int a = 0; a < L::A_PER; ++a) {
@@ -733,7 +741,7 @@ hipError_t launch_lds(const GemmArgs& g, dim3 grid, int k_chunk,
   hipLaunchKernelGGL((gemm_lds_kernel<MT, NTW, AF>), grid, dim3(256), lds,
                      stream, g.A, g.lda, g.a_bs, (const uint16_t*)g.B,
                      (const uint16_t*)g.B2, g.nb1, g.ldb, g.b_bs, g.C, g.ldc,
-                     g.c_bs, g.c_ks, g.M, g.N, g.K, k_chunk);
+                     g.c_bs, g.c_ks, g.M, g.N, g.K, k_chunk, g.m_split);
   return hipGetLastError();
 }
 
@@ -742,6 +750,7 @@ hipError_t launch_lds(const GemmArgs& g, dim3 grid, int k_chunk,
 void gemm_plan(const mla_dims& d, GemmArgs& g, int max_split) {
   g.ntw = 0;
   g.k_split = 1;
+  g.m_split = 1;
   if (d.dtype != MLA_BF16 || g.b_nn || g.M > 64 || g.M <= 0 || g.N <= 0 ||
       g.K <= 0)
     return;
@@ -777,6 +786,11 @@ void gemm_plan(const mla_dims& d, GemmArgs& g, int max_split) {
         }
       }
     }
+    // A grid that leaves half the compute units idle runs its two 32-row
+    // blocks in separate workgroups (same XCD, weights shared through L2).
+    const long wgs = (long)((g.N + 128 * -g.ntw - 1) / (128 * -g.ntw)) *
+                     g.batch * g.k_split;
+    g.m_split = (g.M > 32 && 2 * wgs <= 256) ? 2 : 1;
     return;
   }
   if (g.K % 16) {
@@ -844,13 +858,13 @@ hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
     const int kc = (g.K + ks - 1) / ks;
     k_chunk = (kc + 63) / 64 * 64;
     const int ntw = -g.ntw;
-    dim3 grid(ks, (g.N + 128 * ntw - 1) / (128 * ntw), g.batch);
+    dim3 grid(ks, (g.N + 128 * ntw - 1) / (128 * ntw), g.batch * g.m_split);
 #define MLA_LK(MT, NTW, AF) \
   return launch_lds<MT, NTW, AF>(g, grid, (int)k_chunk, stream)
 #define MLA_LK_NTW(MT, AF)                    \
   if (ntw == 1) MLA_LK(MT, 1, AF);            \
   else MLA_LK(MT, 2, AF);
-    if (g.M <= 32) {
+    if (g.M <= 32 || g.m_split > 1) {
       if (g.a_f32) { MLA_LK_NTW(1, true) } else { MLA_LK_NTW(1, false) }
     } else {
       if (g.a_f32) { MLA_LK_NTW(2, true) } else { MLA_LK_NTW(2, false) }

@@ -77,6 +77,8 @@ struct GemmArgs {
   // > 0: register-streaming kernel with ntw 32-column tiles per wave;
   // < 0: LDS-staged kernel with -ntw tiles per wave; 0: skinny / tiled.
   int ntw = 0;
+  // LDS-staged kernel: rows in blocks of 32, one workgroup per block (1 or 2)
+  int m_split = 1;
   void* c16 = nullptr;  // bf16 output instead of C (tiled kernel, k_split 1)
 };
 hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
