@@ -21,6 +21,9 @@
  *   lengths, outputs, workspace); the library allocates nothing and keeps no
  *   state between calls.  Every call only enqueues work on `stream` and
  *   returns; results are ready once the caller synchronises the stream.
+ * - The calls never allocate, clear memory or synchronise, so a caller may
+ *   capture a whole step into a HIP graph and replay it (after one eager
+ *   call of each entry point in the process, which sets kernel attributes).
  * - Weights are row-major [out, in] (y = W x), in the activation dtype.
  *   Head h owns rows h*d_h .. h*d_h+d_h-1 of W_UQ, W_UK, W_UV and rows
  *   h*d_r .. of W_QR.

@@ -1,0 +1,71 @@
+"""HIP graph capture of the whole decode step.
+
+No API call allocates, clears memory or synchronises inside, so a caller
+can capture a step (append, absorb, decode with the split combine, out)
+into a HIP graph.  The graph is replayed several times, with eager work and
+synchronisations in between, and every replay must reproduce the eager
+step's outputs bit for bit (same kernels, same inputs, no atomics)."""
+import dataclasses
+
+import pytest
+import torch
+
+from mla_latent_kv_33_amd import flow
+from mla_latent_kv_33_amd import workloads as W
+from tests.gpu_common import log
+
+pytestmark = pytest.mark.gpu
+
+
+def _workload():
+    # 16 sequences, ragged contexts (partial last blocks), permuted table,
+    # library-chosen splits (several per sequence, so the combine runs).
+    base = W.workload("b64_ctx8k")
+    return dataclasses.replace(
+        base, name="graph_b16", batch=16,
+        ctx=tuple(700 + 131 * i for i in range(16)), seed=11)
+
+
+def _snapshot(st, out):
+    return {"q": out.q.clone(), "o_lat": out.o_lat.clone(),
+            "lse": out.lse.clone(), "u": out.u.clone(),
+            "cache": st.cache.clone()}
+
+
+def test_step_graph_replays_match_eager():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    wl = _workload()
+    layer = flow.make_layer(wl)
+    st = flow.prepare(wl, layer)
+    out = flow.run_step(st)           # eager: outputs and workspaces
+    torch.cuda.synchronize()
+    ref = _snapshot(st, out)
+
+    # capture on a side stream after one warm pass there
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        flow.run_step(st, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        flow.run_step(st, out=out)
+    torch.cuda.synchronize()
+
+    for rep in range(4):
+        # eager work between replays: clobber the outputs, run an eager step
+        # into separate buffers
+        for k in ("q", "o_lat", "lse", "u"):
+            getattr(out, k).fill_(float("nan"))
+        other = flow.run_step(st)
+        torch.cuda.synchronize()
+        assert torch.equal(other.u, ref["u"]), "eager step changed"
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ("q", "o_lat", "lse", "u"):
+            same = torch.equal(getattr(out, k), ref[k])
+            log(f"  replay {rep}: {k} {'identical' if same else 'DIFFERS'}")
+            assert same, f"replay {rep}: {k} differs from the eager step"
+        assert torch.equal(st.cache, ref["cache"]), \
+            f"replay {rep}: cache differs from the eager step"
