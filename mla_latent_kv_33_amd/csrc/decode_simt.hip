@@ -172,30 +172,45 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
   for (int j0 = 0; j0 < n_split; j0 += CMB_CS) {
     float m[CMB_CS], l[CMB_CS], ps[CMB_CS];
     f32x4 v[CMB_CS][NB][VW / 4];
+    // Every load is issued unconditionally from an in-range address (split
+    // and column clamped) and masked afterwards, so that all of them are in
+    // flight together: a load under a condition becomes a branch that waits
+    // for it on the spot.
+    uint4 raw[CMB_CS][NB];
+    f32x4 rawf[CMB_CS][NB];
 #pragma unroll
     for (int u = 0; u < CMB_CS; ++u) {
-      const int j = j0 + u;
-      const bool ok = j < n_split;
-      const size_t r = row0 + (size_t)(ok ? j : 0) * n_h;
-      m[u] = ok ? m_part[r] : -INFINITY;
-      l[u] = ok ? l_part[r] : 0.0f;
-      ps[u] = (P16 && ok) ? sc_part[r] : 1.0f;
+      const size_t r = row0 + (size_t)min(j0 + u, n_split - 1) * n_h;
+      m[u] = m_part[r];
+      l[u] = l_part[r];
+      ps[u] = P16 ? sc_part[r] : 1.0f;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const int cv = q + CMB_TPH * b;
-        const bool in = ok && cv < cvn;
+        const int cv = min(q + CMB_TPH * b, cvn - 1);
+        if (P16)
+          raw[u][b] = *(const uint4*)(p16 + r * d_c + 8 * cv);
+        else
+          rawf[u][b] = *(const f32x4*)(o_part + r * d_c + 4 * cv);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < CMB_CS; ++u) {
+      const bool ok = j0 + u < n_split;
+      m[u] = ok ? m[u] : -INFINITY;
+      l[u] = ok ? l[u] : 0.0f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const bool in = ok && q + CMB_TPH * b < cvn;
         if (P16) {
-          const uint4 x = in ? *(const uint4*)(p16 + r * d_c + 8 * cv)
-                             : make_uint4(0, 0, 0, 0);
-          const f32x8 f =
-              __builtin_convertvector(__builtin_bit_cast(f16x8, x), f32x8);
+          const f32x8 f = __builtin_convertvector(
+              __builtin_bit_cast(f16x8, raw[u][b]), f32x8);
 #pragma unroll
           for (int hh = 0; hh < VW / 4; ++hh)
-            v[u][b][hh] = (f32x4){f[4 * hh], f[4 * hh + 1], f[4 * hh + 2],
-                                  f[4 * hh + 3]};
+            v[u][b][hh] = in ? (f32x4){f[4 * hh], f[4 * hh + 1],
+                                       f[4 * hh + 2], f[4 * hh + 3]}
+                             : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
         } else {
-          v[u][b][0] = in ? *(const f32x4*)(o_part + r * d_c + 4 * cv)
-                          : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+          v[u][b][0] = in ? rawf[u][b] : (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
         }
       }
     }
