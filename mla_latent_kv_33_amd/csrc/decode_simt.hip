@@ -145,17 +145,19 @@ __global__ __launch_bounds__(NT) void decode_simt_kernel(
 // fp32 partials hold the unnormalised O_j (weight w_j); fp16 partials hold
 // O_j / (l_j s_j) with s_j the row's scale stored after the fp16 rows
 // (weight w_j l_j s_j), as the matrix-core decode writes them.
-constexpr int CMB_TPH = 16, CMB_CS = 4;
-
-template <int NB, bool P16>
+// Shapes: TPH = 16 threads per head and CS = 4 splits per chunk for many
+// query rows; for few rows (a grid of a few dozen workgroups) TPH = 64 and
+// CS = 16 give each head four times the threads and each thread four times
+// the loads in flight.
+template <int NB, bool P16, int TPH, int CS>
 __global__ __launch_bounds__(256) void combine_rows_kernel(
     int n_h, int d_c, int n_split, const float* __restrict__ o_part,
     const float* __restrict__ m_part, const float* __restrict__ l_part,
     float* __restrict__ o_lat, float* __restrict__ lse) {
   constexpr int VW = P16 ? 8 : 4;  // columns per vector
   const int bq = blockIdx.x;
-  const int h = blockIdx.y * (256 / CMB_TPH) + (threadIdx.x / CMB_TPH);
-  const int q = threadIdx.x % CMB_TPH;
+  const int h = blockIdx.y * (256 / TPH) + (threadIdx.x / TPH);
+  const int q = threadIdx.x % TPH;
   if (h >= n_h) return;
   const int cvn = d_c / VW;
   const size_t row0 = (size_t)bq * n_split * n_h + h;  // + j n_h
@@ -169,24 +171,24 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
 #pragma unroll
     for (int hh = 0; hh < VW / 4; ++hh)
       acc[b][hh] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j0 = 0; j0 < n_split; j0 += CMB_CS) {
-    float m[CMB_CS], l[CMB_CS], ps[CMB_CS];
-    f32x4 v[CMB_CS][NB][VW / 4];
+  for (int j0 = 0; j0 < n_split; j0 += CS) {
+    float m[CS], l[CS], ps[CS];
+    f32x4 v[CS][NB][VW / 4];
     // Every load is issued unconditionally from an in-range address (split
     // and column clamped) and masked afterwards, so that all of them are in
     // flight together: a load under a condition becomes a branch that waits
     // for it on the spot.
-    uint4 raw[CMB_CS][NB];
-    f32x4 rawf[CMB_CS][NB];
+    uint4 raw[CS][NB];
+    f32x4 rawf[CS][NB];
 #pragma unroll
-    for (int u = 0; u < CMB_CS; ++u) {
+    for (int u = 0; u < CS; ++u) {
       const size_t r = row0 + (size_t)min(j0 + u, n_split - 1) * n_h;
       m[u] = m_part[r];
       l[u] = l_part[r];
       ps[u] = P16 ? sc_part[r] : 1.0f;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const int cv = min(q + CMB_TPH * b, cvn - 1);
+        const int cv = min(q + TPH * b, cvn - 1);
         if (P16)
           raw[u][b] = *(const uint4*)(p16 + r * d_c + 8 * cv);
         else
@@ -194,13 +196,13 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
       }
     }
 #pragma unroll
-    for (int u = 0; u < CMB_CS; ++u) {
+    for (int u = 0; u < CS; ++u) {
       const bool ok = j0 + u < n_split;
       m[u] = ok ? m[u] : -INFINITY;
       l[u] = ok ? l[u] : 0.0f;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const bool in = ok && q + CMB_TPH * b < cvn;
+        const bool in = ok && q + TPH * b < cvn;
         if (P16) {
           const f32x8 f = __builtin_convertvector(
               __builtin_bit_cast(f16x8, raw[u][b]), f32x8);
@@ -216,7 +218,7 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
     }
     float mc = M;
 #pragma unroll
-    for (int u = 0; u < CMB_CS; ++u) mc = fmaxf(mc, m[u]);
+    for (int u = 0; u < CS; ++u) mc = fmaxf(mc, m[u]);
     if (mc == -INFINITY) continue;  // only empty splits so far
     const float sc = M == -INFINITY ? 0.0f : exp2f(M - mc);
     L *= sc;
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[b][hh][e] *= sc;
 #pragma unroll
-    for (int u = 0; u < CMB_CS; ++u) {
+    for (int u = 0; u < CS; ++u) {
       const bool live = m[u] != -INFINITY;
       const float w = live ? exp2f(m[u] - mc) : 0.0f;
       const float wl = w * l[u];
@@ -249,7 +251,7 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
   float* dst = o_lat + ((size_t)bq * n_h + h) * d_c;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    const int cv = q + CMB_TPH * b;
+    const int cv = q + TPH * b;
     if (cv < cvn)
 #pragma unroll
       for (int hh = 0; hh < VW / 4; ++hh)
@@ -263,9 +265,9 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
 
 // Other widths: workgroup = (query row, ch heads).  The weights of its
 // heads are computed in parallel (one thread per head), then each thread
-// owns CB float4 columns and reads their partials CS splits at a time.
+// owns CB float4 columns and reads their partials CMB_CS splits at a time.
 // Splits of weight 0 are not read: an empty split never wrote its partial.
-constexpr int CMB_CH = 16, CMB_CB = 8;
+constexpr int CMB_CH = 16, CMB_CB = 8, CMB_CS = 4;
 constexpr size_t CMB_LDS_MAX = 160 * 1024;
 
 __global__ __launch_bounds__(256) void combine_kernel(
@@ -386,27 +388,34 @@ hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
                           const float* m_part, const float* l_part,
                           float* o_lat, float* lse, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  const dim3 rgrid(rows, (d.n_h + 256 / CMB_TPH - 1) / (256 / CMB_TPH));
-#define MLA_CMB(NB, P16)                                                      \
-  hipLaunchKernelGGL((combine_rows_kernel<NB, P16>), rgrid, dim3(256), 0,      \
-                     stream, d.n_h, d.d_c, n_split, o_part, m_part, l_part,   \
-                     o_lat, lse)
+  // Many rows: 16 threads per head (16 heads per workgroup), 4 splits per
+  // chunk.  Few rows: 64 threads per head, 16 splits per chunk, so that a
+  // small batch still spreads over a few hundred waves.
+  const bool wide = (long)rows * ((d.n_h + 15) / 16) < 256;
+#define MLA_CMB(NB, P16, TPH, CS)                                             \
+  hipLaunchKernelGGL((combine_rows_kernel<NB, P16, TPH, CS>),                  \
+                     dim3(rows, (d.n_h + 256 / TPH - 1) / (256 / TPH)),        \
+                     dim3(256), 0, stream, d.n_h, d.d_c, n_split, o_part,     \
+                     m_part, l_part, o_lat, lse)
   if (f16_parts) {
-    if (d.d_c % 8 != 0 || d.d_c > 8 * CMB_TPH * 4) return hipErrorInvalidValue;
-    MLA_CMB(4, true);
+    if (d.d_c % 8 != 0 || d.d_c > 8 * 16 * 4) return hipErrorInvalidValue;
+    if (wide)
+      MLA_CMB(1, true, 64, 16);
+    else
+      MLA_CMB(4, true, 16, 4);
     return hipGetLastError();
   }
-  if (d.d_c % 4 == 0 && d.d_c <= 4 * CMB_TPH * 8) {
+  if (d.d_c % 4 == 0 && d.d_c <= 4 * 16 * 8) {
     const int c4n = d.d_c / 4;
-    const int nb = (c4n + CMB_TPH - 1) / CMB_TPH;
+    const int nb = (c4n + 15) / 16;
     if (nb <= 1)
-      MLA_CMB(1, false);
+      MLA_CMB(1, false, 16, 4);
     else if (nb <= 2)
-      MLA_CMB(2, false);
+      MLA_CMB(2, false, 16, 4);
     else if (nb <= 4)
-      MLA_CMB(4, false);
+      MLA_CMB(4, false, 16, 4);
     else
-      MLA_CMB(8, false);
+      MLA_CMB(8, false, 16, 4);
     return hipGetLastError();
   }
 #undef MLA_CMB

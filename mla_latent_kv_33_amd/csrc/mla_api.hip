@@ -158,7 +158,10 @@ int auto_splits(const mla_dims& d, int B, int n_q, int max_kv_len) {
     target = 1024;
   }
   long s = (target + groups - 1) / groups;
-  const long cap = nblk / 4 > 0 ? nblk / 4 : 1;  // >= 4 blocks per split
+  // At least 2 blocks per split for the matrix-core kernel (its copy ring
+  // holds 3 half tiles), 4 for the SIMT kernel.
+  const long minb = decode_mfma_supported(d) ? 2 : 4;
+  const long cap = nblk / minb > 0 ? nblk / minb : 1;
   if (s > cap) s = cap;
   if (s < 1) s = 1;
   return (int)s;

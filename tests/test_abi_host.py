@@ -78,6 +78,9 @@ def test_workspace_sizes():
         64 * ns * 128 * (512 + 2) * 4
     assert B.mla_decode_auto_splits(d, 4, 1, 131073) == 64
     assert B.mla_decode_auto_splits(d, 8, 2048, 10240) == 1
+    # one sequence: as many splits as keep two 64-token blocks each
+    assert B.mla_decode_auto_splits(d, 1, 1, 4097) == 32
+    assert B.mla_decode_auto_splits(d, 1, 1, 100) == 1
     bad = ds_dims(d_r=63)
     assert B.mla_append_workspace_bytes(bad, 64) == 0
 
