@@ -129,6 +129,30 @@ mla_status mla_append_cache(const mla_dims* dims, int32_t T, const void* h,
                             mla_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * mla_append_cache_rmsnorm - mla_append_cache with the latent normalised.
+ *
+ * As mla_append_cache, except that the latent half of the row is passed
+ * through an RMSNorm with weight kv_norm_w before it is stored, while the
+ * RoPE key is not ('MiniMind 学习笔记 10', section 9: kv_norm applies to the
+ * latent only, and the normalised latent is what the cache holds):
+ *   x = W_DKV h,  c_j = kv_norm_w[j] x_j / sqrt(mean_i(x_i^2) + eps)
+ * computed in fp32 and rounded once to the cache dtype.
+ *
+ *   kv_norm_w  [d_c]  activation dtype (device)
+ *   eps        >= 0 (host); a negative or NaN eps is MLA_ERR_SHAPE
+ * Every other argument, the workspace size and the error behaviour are those
+ * of mla_append_cache.  Decode and the query path are unchanged: they read
+ * whatever latent the cache holds.
+ * ---------------------------------------------------------------------- */
+mla_status mla_append_cache_rmsnorm(
+    const mla_dims* dims, int32_t T, const void* h, const int32_t* seq_idx,
+    const int32_t* pos, const void* w_dkv, const void* w_kr,
+    const void* kv_norm_w, float eps, const float* rope_cos,
+    const float* rope_sin, int32_t max_pos, const int32_t* block_table,
+    int32_t max_blocks, void* cache, int32_t num_blocks, void* ws,
+    size_t ws_bytes, mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * mla_absorb_q - query path and absorption of W_UK into the query.
  *
  * c_Q = W_DQ h (kept fp32, not rounded), q_C = W_UQ c_Q, q_R = RoPE_{pos}(W_QR

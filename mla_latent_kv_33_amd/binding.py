@@ -49,6 +49,9 @@ _SIGNATURES = {
     "mla_append_workspace_bytes": (_S, [_DP, _I]),
     "mla_append_cache": (_I, [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I,
                               _P, _I, _P, _S, _P]),
+    "mla_append_cache_rmsnorm": (_I, [_DP, _I, _P, _P, _P, _P, _P, _P,
+                                      ctypes.c_float, _P, _P, _I, _P, _I, _P,
+                                      _I, _P, _S, _P]),
     "mla_absorb_workspace_bytes": (_S, [_DP, _I]),
     "mla_absorb_q": (_I, [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                           _S, _P]),
@@ -166,6 +169,22 @@ def mla_append_cache(dims: MlaDims, h, seq_idx, pos, w_dkv, w_kr, rope_cos,
         _ptr(w_kr), _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
         _ptr(block_table), block_table.shape[1], _ptr(cache), cache.shape[0],
         _ptr(ws), wsb, _stream(stream)))
+
+
+def mla_append_cache_rmsnorm(dims: MlaDims, h, seq_idx, pos, w_dkv, w_kr,
+                             kv_norm_w, eps: float, rope_cos, rope_sin,
+                             block_table, cache, ws=None, stream=None):
+    """mla_append_cache with the latent RMS-normalised (weight kv_norm_w,
+    epsilon eps) before it is cached (see include/mla.h)."""
+    T = h.shape[0]
+    ws, wsb = _workspace(mla_append_workspace_bytes(dims, T) if T else 0,
+                         h.device, ws)
+    _check("mla_append_cache_rmsnorm", lib().mla_append_cache_rmsnorm(
+        ctypes.byref(dims), T, _ptr(h), _ptr(seq_idx), _ptr(pos), _ptr(w_dkv),
+        _ptr(w_kr), _ptr(kv_norm_w), float(eps), _ptr(rope_cos),
+        _ptr(rope_sin), rope_cos.shape[0], _ptr(block_table),
+        block_table.shape[1], _ptr(cache), cache.shape[0], _ptr(ws), wsb,
+        _stream(stream)))
 
 
 def mla_absorb_q(dims: MlaDims, h, pos, w_dq, w_uq, w_qr, w_uk, rope_cos,

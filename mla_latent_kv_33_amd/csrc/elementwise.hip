@@ -128,6 +128,83 @@ hipError_t launch_reduce_parts(const float* src, int nparts, long part_stride,
   return hipGetLastError();
 }
 
+// Latent RMSNorm variant ('MiniMind 学习笔记 10', section 9: the latent
+// half of the down-projection goes through kv_norm before it is cached; the
+// RoPE key does not): one workgroup (4 waves) per token.  Pass 1 sums the
+// squares of the d_c latent values (fp32, the K-split parts summed first),
+// reduced across the workgroup; pass 2 writes
+//   c_j = w_j x_j / sqrt(mean(x^2) + eps)
+// rounded once to the cache dtype, and rotates the RoPE pairs as above.
+template <typename T>
+__global__ __launch_bounds__(256) void append_norm_scatter_kernel(
+    const float* __restrict__ acc, int nparts, long part_stride, int d_c,
+    int d_r, const T* __restrict__ kv_norm_w, float eps,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
+    const float* __restrict__ rcos, const float* __restrict__ rsin,
+    int max_pos, const int32_t* __restrict__ block_table, int max_blocks,
+    int block_size, T* __restrict__ cache) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  const int width = d_c + d_r;
+  const int half = d_r / 2;
+  const long base = (long)t * width;
+  float ss = 0.0f;
+  for (int j = threadIdx.x; j < d_c; j += 256) {
+    const float x = sum_parts(acc, nparts, part_stride, base + j);
+    ss = __builtin_fmaf(x, x, ss);
+  }
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float inv =
+      1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d_c + eps);
+  const int p = pos[t];
+  const int blk = block_table[(long)seq_idx[t] * max_blocks + p / block_size];
+  T* row = cache + ((long)blk * block_size + (p % block_size)) * width;
+  for (int j = threadIdx.x; j < d_c + half; j += 256) {
+    if (j < d_c) {
+      const float x = sum_parts(acc, nparts, part_stride, base + j);
+      DT<T>::store(row, j, DT<T>::load(kv_norm_w, j) * (x * inv));
+    } else {
+      const int jj = j - d_c;
+      const float x1 = sum_parts(acc, nparts, part_stride, base + d_c + jj);
+      const float x2 =
+          sum_parts(acc, nparts, part_stride, base + d_c + jj + half);
+      const bool ok = p >= 0 && p < max_pos;
+      const float c = ok ? rcos[(long)p * half + jj] : NAN;
+      const float s = ok ? rsin[(long)p * half + jj] : NAN;
+      DT<T>::store(row, d_c + jj, x1 * c - x2 * s);
+      DT<T>::store(row, d_c + jj + half, x1 * s + x2 * c);
+    }
+  }
+}
+
+hipError_t launch_append_norm_scatter(const mla_dims& d, int T,
+                                      const float* acc, int nparts,
+                                      long part_stride, const void* kv_norm_w,
+                                      float eps, const int32_t* seq_idx,
+                                      const int32_t* pos,
+                                      const float* rope_cos,
+                                      const float* rope_sin, int max_pos,
+                                      const int32_t* block_table,
+                                      int max_blocks, void* cache,
+                                      hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  if (d.dtype == MLA_BF16)
+    hipLaunchKernelGGL(append_norm_scatter_kernel<uint16_t>, dim3(T),
+                       dim3(256), 0, stream, acc, nparts, part_stride, d.d_c,
+                       d.d_r, (const uint16_t*)kv_norm_w, eps, seq_idx, pos,
+                       rope_cos, rope_sin, max_pos, block_table, max_blocks,
+                       d.block_size, (uint16_t*)cache);
+  else
+    hipLaunchKernelGGL(append_norm_scatter_kernel<float>, dim3(T), dim3(256),
+                       0, stream, acc, nparts, part_stride, d.d_c, d.d_r,
+                       (const float*)kv_norm_w, eps, seq_idx, pos, rope_cos,
+                       rope_sin, max_pos, block_table, max_blocks,
+                       d.block_size, (float*)cache);
+  return hipGetLastError();
+}
+
 hipError_t launch_append_scatter(const mla_dims& d, int T, const float* acc,
                                  int nparts, long part_stride,
                                  const int32_t* seq_idx, const int32_t* pos,

@@ -248,6 +248,39 @@ mla_status mla_append_cache(const mla_dims* dims, int32_t T, const void* h,
   return MLA_OK;
 }
 
+mla_status mla_append_cache_rmsnorm(
+    const mla_dims* dims, int32_t T, const void* h, const int32_t* seq_idx,
+    const int32_t* pos, const void* w_dkv, const void* w_kr,
+    const void* kv_norm_w, float eps, const float* rope_cos,
+    const float* rope_sin, int32_t max_pos, const int32_t* block_table,
+    int32_t max_blocks, void* cache, int32_t num_blocks, void* ws,
+    size_t ws_bytes, mla_stream_t stream) {
+  if (!dims) return MLA_ERR_NULL;
+  if (!dims_ok(dims) || T < 0 || max_pos <= 0 || max_blocks <= 0 ||
+      num_blocks <= 0 || !(eps >= 0.0f))
+    return MLA_ERR_SHAPE;
+  if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  if (T == 0) return MLA_OK;
+  if (!h || !seq_idx || !pos || !w_dkv || !w_kr || !kv_norm_w || !rope_cos ||
+      !rope_sin || !block_table || !cache)
+    return MLA_ERR_NULL;
+  const mla_dims& d = *dims;
+  const size_t need = mla_append_workspace_bytes(dims, T);
+  if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs g = append_gemm(d, T);
+  g.A = h;
+  g.B = w_dkv;
+  g.B2 = w_kr;
+  g.C = (float*)ws;
+  MLA_TRY(launch_gemm(d, g, s));
+  MLA_TRY(launch_append_norm_scatter(d, T, g.C, g.k_split, g.c_ks, kv_norm_w,
+                                     eps, seq_idx, pos, rope_cos, rope_sin,
+                                     max_pos, block_table, max_blocks, cache,
+                                     s));
+  return MLA_OK;
+}
+
 // ------------------------------------------------------------------ absorb
 namespace {
 struct AbsorbWs {

@@ -104,6 +104,19 @@ hipError_t launch_append_scatter(const mla_dims& d, int T, const float* acc,
 // qr rows of ld_qr floats, the [n_h][d_r] block of token t at
 // qr + t * ld_qr -> RoPE -> q_out[t][h][d_c ..] (layer dtype).
 // qr: the sum of nparts fp32 parts spaced part_stride floats apart.
+// The same with the latent half normalised: c_j = w_j x_j / sqrt(mean(x^2)
+// + eps) over the d_c latent values of the row (kv_norm_w: d_c weights in
+// the layer dtype).
+hipError_t launch_append_norm_scatter(const mla_dims& d, int T,
+                                      const float* acc, int nparts,
+                                      long part_stride, const void* kv_norm_w,
+                                      float eps, const int32_t* seq_idx,
+                                      const int32_t* pos,
+                                      const float* rope_cos,
+                                      const float* rope_sin, int max_pos,
+                                      const int32_t* block_table,
+                                      int max_blocks, void* cache,
+                                      hipStream_t stream);
 hipError_t launch_query_rope(const mla_dims& d, int T, const float* qr,
                              int nparts, long part_stride, long ld_qr,
                              const int32_t* pos, const float* rope_cos,

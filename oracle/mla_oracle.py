@@ -32,15 +32,19 @@ Readings where the pages are silent (each listed in the design notes):
 * Score scale 1/sqrt(d_h + d_r) ([MLA] sections "A Attention" and 7; the
   naive path of [MiniMind] section 10 divides by sqrt(qk_head_dim) with
   qk_head_dim = nope + rope, the same number).
-* No normalisation of the latent (the [MiniMind] kv_norm is not on the
-  [MLA] path).
+* No normalisation of the latent on the main path (the [MiniMind] kv_norm
+  is not on the [MLA] path).  The optional ``kv_norm`` of ``kv_latent``
+  follows [MiniMind] section 9 (kv_norm = RMSNorm of the latent only, the
+  RoPE key untouched); the page names RMSNorm without writing it out, so its
+  formula is the usual one: w * x / sqrt(mean(x^2) + eps) over the latent.
 
 Pins (tests/test_oracle_pins.py): absorbed == non-absorbed, value deferral,
 softmax rows sum to one with exact zeros on masked keys, cache width
 d_c + d_r and the pages' printed cache counts, the rank bound of the stacked
 [K_C V_C], the RoPE relative-position identity and R_0 = I, agreement with
 torch's scaled_dot_product_attention on CPU in float64 (MQA form and MHA
-form), latent-basis invariance, a scalar brute-force evaluation of the whole
+form), latent-basis invariance, RMSNorm closed forms (hand-computed values,
+unit RMS with unit weight, scale invariance, k_R untouched), a scalar brute-force evaluation of the whole
 layer on tiny inputs, and closed forms (one key, equal keys).  The RoPE pair
 convention is a reading: the pins hold for either convention, so the pairing
 itself is parity unpinned.
@@ -104,13 +108,25 @@ def apply_rope(x: np.ndarray, pos, base: float) -> np.ndarray:
 # projections ([MLA] sections 3, 6, 7)
 # --------------------------------------------------------------------------
 
-def kv_latent(h, pos, w_dkv, w_kr, base):
+def rms_norm(x, weight, eps):
+    """RMSNorm over the last axis: ``weight * x / sqrt(mean(x^2) + eps)``
+    (the kv_norm of [MiniMind] section 9; formula as read in the header)."""
+    x = np.asarray(x, dtype=F64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return np.asarray(weight, F64) * (x / np.sqrt(ms + float(eps)))
+
+
+def kv_latent(h, pos, w_dkv, w_kr, base, kv_norm=None):
     """What goes into the cache for tokens with hidden states ``h [T, d]`` at
     positions ``pos [T]``: c_KV = W_DKV h ([MLA] section 3) and the shared
-    RoPE key k_R = RoPE(W_KR h) ([MLA] section 6).  Returns
+    RoPE key k_R = RoPE(W_KR h) ([MLA] section 6).  With ``kv_norm =
+    (weight [d_c], eps)`` the latent is RMS-normalised before it is cached
+    and k_R is not ([MiniMind] section 9).  Returns
     ``(c_kv [T, d_c], k_r [T, d_r])``."""
     h = np.asarray(h, dtype=F64)
     c_kv = h @ np.asarray(w_dkv, F64).T
+    if kv_norm is not None:
+        c_kv = rms_norm(c_kv, kv_norm[0], kv_norm[1])
     k_r = apply_rope(h @ np.asarray(w_kr, F64).T, np.asarray(pos), base)
     return c_kv, k_r
 
@@ -257,7 +273,7 @@ def head_values(o_lat, w_uv, d_h):
 # --------------------------------------------------------------------------
 
 def decode_step(w, n_h, base, h_new, ctx_c_kv, ctx_k_r, heads=None,
-                q_rows=None):
+                q_rows=None, kv_norm=None):
     """One step for one sequence, non-absorbed ([MLA] section 7).
 
     The sequence already holds ``ctx`` tokens whose latents are
@@ -265,7 +281,9 @@ def decode_step(w, n_h, base, h_new, ctx_c_kv, ctx_k_r, heads=None,
     the new tokens at positions ctx .. ctx+n_q-1.  Their latents are appended
     (kv_latent), then each new token attends causally over all ctx + n_q
     keys.  ``q_rows`` restricts which of the new tokens are evaluated as
-    queries (all by default); ``heads`` restricts the heads.
+    queries (all by default); ``heads`` restricts the heads.  ``kv_norm``
+    (weight, eps) normalises the new tokens' latents as kv_latent does; the
+    context latents are taken as given.
 
     Returns a dict with c_kv / k_r of the new tokens, q_c, q_r, o, lse and u
     (u only when every head is computed).
@@ -274,7 +292,8 @@ def decode_step(w, n_h, base, h_new, ctx_c_kv, ctx_k_r, heads=None,
     n_new = h_new.shape[0]
     ctx = ctx_c_kv.shape[0]
     pos = ctx + np.arange(n_new)
-    c_new, kr_new = kv_latent(h_new, pos, w["w_dkv"], w["w_kr"], base)
+    c_new, kr_new = kv_latent(h_new, pos, w["w_dkv"], w["w_kr"], base,
+                              kv_norm=kv_norm)
     c_all = np.concatenate([np.asarray(ctx_c_kv, F64), c_new], axis=0)
     kr_all = np.concatenate([np.asarray(ctx_k_r, F64), kr_new], axis=0)
     sel = np.arange(n_new) if q_rows is None else np.asarray(q_rows)

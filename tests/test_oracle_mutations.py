@@ -68,7 +68,7 @@ def _visibility_strict(q_pos, kv_len):
         (np.arange(len(np.atleast_1d(q_pos)))[:, None] == 0)
 
 
-def _kv_latent_unrotated(h, pos, w_dkv, w_kr, base):
+def _kv_latent_unrotated(h, pos, w_dkv, w_kr, base, kv_norm=None):
     h = np.asarray(h, float)
     return h @ np.asarray(w_dkv).T, h @ np.asarray(w_kr).T
 
@@ -107,3 +107,43 @@ def test_mutation_is_caught(name, monkeypatch):
     attr, fn = MUTATIONS[name]
     monkeypatch.setattr(orc, attr, fn)
     assert not _agrees(), name
+
+
+# ---- latent RMSNorm: each planted mistake fails one of its pins ----------
+
+def _norm_mean_not_rms(x, weight, eps):        # divides by the mean square
+    x = np.asarray(x, float)
+    return np.asarray(weight, float) * x / (np.mean(x * x, axis=-1,
+                                                    keepdims=True) + eps)
+
+
+def _norm_sum_not_mean(x, weight, eps):        # sum instead of mean
+    x = np.asarray(x, float)
+    return np.asarray(weight, float) * x / np.sqrt(
+        np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def _norm_weight_reversed(x, weight, eps):     # weight applied back to front
+    x = np.asarray(x, float)
+    return np.asarray(weight, float)[::-1] * x / np.sqrt(
+        np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def _norm_eps_outside(x, weight, eps):         # eps added after the root
+    x = np.asarray(x, float)
+    return np.asarray(weight, float) * x / (np.sqrt(
+        np.mean(x * x, axis=-1, keepdims=True)) + eps)
+
+
+@pytest.mark.parametrize("bad", [_norm_mean_not_rms, _norm_sum_not_mean,
+                                 _norm_weight_reversed, _norm_eps_outside])
+def test_rms_norm_mutation_fails_a_pin(monkeypatch, bad):
+    from tests import test_oracle_pins as pins
+    monkeypatch.setattr(orc, "rms_norm", bad)
+    failed = 0
+    for pin in (pins.test_rms_norm_closed_forms, pins.test_rms_norm_properties):
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed >= 1, f"{bad.__name__} passes every RMSNorm pin"

@@ -443,6 +443,51 @@ def test_head_subset_matches_full():
     assert "u" not in part
 
 
+# ---------------------------------------------------------- latent RMSNorm
+
+def test_rms_norm_closed_forms():
+    """RMSNorm of the latent ([MiniMind] section 9 kv_norm), values worked
+    by hand: x = (3, 4) has mean square 12.5, so with weight (1, 2) and
+    eps = 0 the result is (3, 8) / sqrt(12.5); x = (1, 1) with eps = 1 gives
+    1 / sqrt(2) in both places."""
+    got = orc.rms_norm(np.array([3.0, 4.0]), np.array([1.0, 2.0]), 0.0)
+    np.testing.assert_allclose(got, [3 / math.sqrt(12.5), 8 / math.sqrt(12.5)],
+                               rtol=1e-15)
+    np.testing.assert_allclose(got, [0.8485281374238571, 2.262741699796952],
+                               rtol=1e-15)
+    got = orc.rms_norm(np.array([1.0, 1.0]), np.ones(2), 1.0)
+    np.testing.assert_allclose(got, [1 / math.sqrt(2)] * 2, rtol=1e-15)
+
+
+def test_rms_norm_properties():
+    """Unit weight and eps = 0: every row has root mean square 1, and the
+    result does not change when a row is scaled by a positive factor; the
+    weight multiplies column by column."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((5, 32))
+    y = orc.rms_norm(x, np.ones(32), 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0,
+                               rtol=1e-14)
+    np.testing.assert_allclose(orc.rms_norm(7.5 * x, np.ones(32), 0.0), y,
+                               rtol=1e-13)
+    w = rng.uniform(0.5, 1.5, 32)
+    np.testing.assert_allclose(orc.rms_norm(x, w, 0.0), y * w, rtol=1e-14)
+
+
+def test_kv_norm_touches_only_the_latent():
+    """With kv_norm the cached latent is the RMS-normalised W_DKV h and the
+    RoPE key is exactly the one without it."""
+    w, _, h_new, _, _ = tiny_case(seed=17)
+    pos = np.arange(len(h_new)) + 5
+    g = np.linspace(0.5, 1.5, TINY["d_c"])
+    c0, r0 = orc.kv_latent(h_new, pos, w["w_dkv"], w["w_kr"], BASE)
+    c1, r1 = orc.kv_latent(h_new, pos, w["w_dkv"], w["w_kr"], BASE,
+                           kv_norm=(g, 1e-6))
+    np.testing.assert_array_equal(r1, r0)
+    ms = np.mean(c0 * c0, axis=1, keepdims=True)
+    np.testing.assert_allclose(c1, g * c0 / np.sqrt(ms + 1e-6), rtol=1e-14)
+
+
 # ---------------------------------------------------------- independence
 
 def test_oracle_is_independent_of_product_path():
