@@ -219,6 +219,58 @@ int32_t mla_decode_auto_splits(const mla_dims* dims, int32_t B, int32_t n_q,
                                int32_t max_kv_len);
 
 /* ------------------------------------------------------------------------
+ * MHA-path chunked prefill: explicit per-head keys and values.
+ *
+ * For a chunk of many new tokens per sequence the explicit form costs fewer
+ * operations than the absorbed one ('MiniMind 学习笔记 10', sections 10 and
+ * 12; 'MLA：潜在表示压缩与解耦 RoPE', section 7: the non-absorbed forward).
+ * A prefill step is:
+ *   mla_append_cache (the chunk's rows), mla_query_mha, mla_prefill_mha,
+ *   mla_out_values.
+ *
+ * mla_query_mha: q[t][h] = [q_C (d_h) | RoPE_{pos}(q_R) (d_r)] with c_Q =
+ *   W_DQ h, q_C = W_UQ c_Q, q_R = W_QR c_Q, rounded once to bf16.  Arguments
+ *   as mla_absorb_q (same workspace size, mla_absorb_workspace_bytes), output
+ *   q_out [T][n_h][d_h + d_r] bf16.
+ *
+ * mla_prefill_mha: for sequence b and chunk query i (the chunk's n_q tokens
+ *   are the last n_q of the sequence's kv_lens[b] keys), every head h:
+ *     k_C[t] = W_UK_h c_KV[t], v_C[t] = W_UV_h c_KV[t] for all cached t,
+ *     score_t = (q_C . k_C[t] + q_R . k_R[t]) / sqrt(d_h + d_r),
+ *     o[b][i][h] = sum_t softmax(score)_t v_C[t]   (fp32, d_h values)
+ *   over keys t <= kv_lens[b] - n_q + i (causal != 0) or all keys; lse as in
+ *   mla_decode.  q [B][n_q][n_h][d_h + d_r] bf16 (mla_query_mha), the cache
+ *   and block table as in mla_decode, kv_lens[b] >= n_q, max_kv_len >= every
+ *   kv_lens[b].  ws: mla_prefill_mha_workspace_bytes(dims, B, max_kv_len)
+ *   bytes (the gathered rows and bf16 k_C / v_C of every head: about
+ *   B max_kv_len (d_c + d_r + 4 n_h d_h) bytes).
+ *   Supported: bf16, d_h = 128, d_r = 64; otherwise MLA_ERR_UNSUPPORTED.
+ *
+ * mla_out_values: u = W_O o for o [T][n_h d_h] fp32 (value space, the output
+ *   of mla_prefill_mha), u [T][d] in the activation dtype.  Workspace as
+ *   mla_out (mla_out_workspace_bytes).
+ * ---------------------------------------------------------------------- */
+mla_status mla_query_mha(const mla_dims* dims, int32_t T, const void* h,
+                         const int32_t* pos, const void* w_dq,
+                         const void* w_uq, const void* w_qr,
+                         const float* rope_cos, const float* rope_sin,
+                         int32_t max_pos, void* q_out, void* ws,
+                         size_t ws_bytes, mla_stream_t stream);
+size_t mla_prefill_mha_workspace_bytes(const mla_dims* dims, int32_t B,
+                                       int32_t max_kv_len);
+mla_status mla_prefill_mha(const mla_dims* dims, int32_t B, int32_t n_q,
+                           const void* q, const void* cache,
+                           int32_t num_blocks, const int32_t* block_table,
+                           int32_t max_blocks, const int32_t* kv_lens,
+                           int32_t max_kv_len, int32_t causal,
+                           const void* w_uk, const void* w_uv, float* o_v,
+                           float* lse, void* ws, size_t ws_bytes,
+                           mla_stream_t stream);
+mla_status mla_out_values(const mla_dims* dims, int32_t T, const float* o_v,
+                          const void* w_o, void* u, void* ws, size_t ws_bytes,
+                          mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * mla_out - value up-projection after the weighted sum, then W_O.
  *
  * v_h = W_UV_h o_lat_h (kept fp32), u = W_O [v_0; ...; v_{n_h-1}] rounded

@@ -59,6 +59,12 @@ _SIGNATURES = {
     "mla_decode_auto_splits": (_I, [_DP, _I, _I, _I]),
     "mla_decode": (_I, [_DP, _I, _I, _P, _P, _I, _P, _I, _P, _I, _I, _I, _P,
                         _P, _P, _S, _P]),
+    "mla_query_mha": (_I, [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
+                           _S, _P]),
+    "mla_prefill_mha_workspace_bytes": (_S, [_DP, _I, _I]),
+    "mla_prefill_mha": (_I, [_DP, _I, _I, _P, _P, _I, _P, _I, _P, _I, _I, _P,
+                             _P, _P, _P, _P, _S, _P]),
+    "mla_out_values": (_I, [_DP, _I, _P, _P, _P, _P, _S, _P]),
     "mla_out_workspace_bytes": (_S, [_DP, _I]),
     "mla_out": (_I, [_DP, _I, _P, _P, _P, _P, _P, _S, _P]),
 }
@@ -223,3 +229,46 @@ def mla_out(dims: MlaDims, o_lat, w_uv, w_o, u, ws=None, stream=None):
     _check("mla_out", lib().mla_out(
         ctypes.byref(dims), T, _ptr(o_lat), _ptr(w_uv), _ptr(w_o), _ptr(u),
         _ptr(ws), wsb, _stream(stream)))
+
+
+def mla_query_mha(dims: MlaDims, h, pos, w_dq, w_uq, w_qr, rope_cos, rope_sin,
+                  q_out, ws=None, stream=None):
+    """q_out[t, h] = [q_C | RoPE(q_R)] without absorption (see include/mla.h)."""
+    T = h.shape[0]
+    ws, wsb = _workspace(mla_absorb_workspace_bytes(dims, T) if T else 0,
+                         h.device, ws)
+    _check("mla_query_mha", lib().mla_query_mha(
+        ctypes.byref(dims), T, _ptr(h), _ptr(pos), _ptr(w_dq), _ptr(w_uq),
+        _ptr(w_qr), _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
+        _ptr(q_out), _ptr(ws), wsb, _stream(stream)))
+
+
+def mla_prefill_mha_workspace_bytes(dims: MlaDims, B: int,
+                                    max_kv_len: int) -> int:
+    return lib().mla_prefill_mha_workspace_bytes(ctypes.byref(dims), B,
+                                                 max_kv_len)
+
+
+def mla_prefill_mha(dims: MlaDims, q, cache, block_table, kv_lens,
+                    max_kv_len: int, w_uk, w_uv, o_v, lse=None,
+                    causal: int = 1, ws=None, stream=None):
+    """Explicit-key attention of the chunk q [B, n_q, n_h, d_h + d_r] over
+    the cache (see include/mla.h); writes o_v [B, n_q, n_h, d_h] fp32."""
+    B, n_q = q.shape[0], q.shape[1]
+    ws, wsb = _workspace(mla_prefill_mha_workspace_bytes(dims, B, max_kv_len),
+                         q.device, ws)
+    _check("mla_prefill_mha", lib().mla_prefill_mha(
+        ctypes.byref(dims), B, n_q, _ptr(q), _ptr(cache), cache.shape[0],
+        _ptr(block_table), block_table.shape[1], _ptr(kv_lens), max_kv_len,
+        causal, _ptr(w_uk), _ptr(w_uv), _ptr(o_v), _ptr(lse), _ptr(ws), wsb,
+        _stream(stream)))
+
+
+def mla_out_values(dims: MlaDims, o_v, w_o, u, ws=None, stream=None):
+    """u = W_O o for value-space o [T, n_h * d_h] fp32."""
+    T = o_v.shape[0]
+    ws, wsb = _workspace(mla_out_workspace_bytes(dims, T) if T else 0,
+                         o_v.device, ws)
+    _check("mla_out_values", lib().mla_out_values(
+        ctypes.byref(dims), T, _ptr(o_v), _ptr(w_o), _ptr(u), _ptr(ws), wsb,
+        _stream(stream)))

@@ -1,6 +1,7 @@
 // C ABI of libmla.so: argument checks, workspace layout and the launch
 // sequence of each step.  Declarations and contracts: include/mla.h.
 
+#include <algorithm>
 #include <math.h>
 #include <string.h>
 
@@ -448,6 +449,143 @@ OutWs out_layout(const mla_dims& d, int T, void* base) {
   return w;
 }
 }  // namespace
+
+// ------------------------------------------------------------ MHA prefill
+mla_status mla_query_mha(const mla_dims* dims, int32_t T, const void* h,
+                         const int32_t* pos, const void* w_dq,
+                         const void* w_uq, const void* w_qr,
+                         const float* rope_cos, const float* rope_sin,
+                         int32_t max_pos, void* q_out, void* ws,
+                         size_t ws_bytes, mla_stream_t stream) {
+  if (!dims) return MLA_ERR_NULL;
+  if (!dims_ok(dims) || T < 0 || max_pos <= 0) return MLA_ERR_SHAPE;
+  if (!dims_supported(dims) || !prefill_mha_supported(*dims))
+    return MLA_ERR_UNSUPPORTED;
+  if (T == 0) return MLA_OK;
+  if (!h || !pos || !w_dq || !w_uq || !w_qr || !rope_cos || !rope_sin ||
+      !q_out)
+    return MLA_ERR_NULL;
+  const mla_dims& d = *dims;
+  if (!ws) return MLA_ERR_WORKSPACE;
+  const AbsorbWs w = absorb_layout(d, T, ws);
+  if (ws_bytes < w.bytes) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs g1 = cq_gemm(d, T);
+  g1.A = h;
+  g1.B = w_dq;
+  g1.C = w.cq_parts;
+  MLA_TRY(launch_gemm(d, g1, s));
+  if (g1.k_split > 1)
+    MLA_TRY(launch_reduce_parts(w.cq_parts, g1.k_split, g1.c_ks,
+                                (long)T * d.d_cq, w.cq, s));
+  GemmArgs g2 = qcr_gemm(d, T);
+  g2.A = w.cq;
+  g2.B = w_uq;
+  g2.B2 = w_qr;
+  g2.C = w.qcr_parts;
+  MLA_TRY(launch_gemm(d, g2, s));
+  MLA_TRY(launch_query_mha(d, T, w.qcr_parts, g2.k_split, g2.c_ks, g2.ldc,
+                           pos, rope_cos, rope_sin, max_pos, q_out, s));
+  return MLA_OK;
+}
+
+namespace {
+struct PrefillWs {
+  uint16_t *rows, *kv;
+  size_t bytes;
+};
+// Rows of the gathered latents and of [k_C | v_C]: B kv_cap, at least 128
+// (the up-projection GEMM's bf16 output needs more than 64 rows).
+long prefill_rows(int B, int kv_cap) {
+  return std::max((long)B * kv_cap, 128L);
+}
+PrefillWs prefill_layout(const mla_dims& d, int B, int kv_cap, void* base) {
+  PrefillWs w;
+  char* p = (char*)base;
+  const long R = prefill_rows(B, kv_cap);
+  const size_t rows_b = align_up((size_t)R * (d.d_c + d.d_r) * 2);
+  const size_t kv_b = align_up((size_t)R * 2 * d.n_h * d.d_h * 2);
+  w.rows = (uint16_t*)p;
+  w.kv = (uint16_t*)(p ? p + rows_b : nullptr);
+  w.bytes = rows_b + kv_b;
+  return w;
+}
+}  // namespace
+
+size_t mla_prefill_mha_workspace_bytes(const mla_dims* dims, int32_t B,
+                                       int32_t max_kv_len) {
+  if (!dims_ok(dims) || B <= 0 || max_kv_len <= 0) return 0;
+  return prefill_layout(*dims, B, max_kv_len, nullptr).bytes;
+}
+
+mla_status mla_prefill_mha(const mla_dims* dims, int32_t B, int32_t n_q,
+                           const void* q, const void* cache,
+                           int32_t num_blocks, const int32_t* block_table,
+                           int32_t max_blocks, const int32_t* kv_lens,
+                           int32_t max_kv_len, int32_t causal,
+                           const void* w_uk, const void* w_uv, float* o_v,
+                           float* lse, void* ws, size_t ws_bytes,
+                           mla_stream_t stream) {
+  if (!dims) return MLA_ERR_NULL;
+  if (!dims_ok(dims) || B < 0 || n_q < 0 || num_blocks <= 0 ||
+      max_blocks <= 0 || max_kv_len < n_q || max_kv_len <= 0 ||
+      (long)max_kv_len > (long)max_blocks * dims->block_size)
+    return MLA_ERR_SHAPE;
+  if (!dims_supported(dims) || !prefill_mha_supported(*dims))
+    return MLA_ERR_UNSUPPORTED;
+  if (B == 0 || n_q == 0) return MLA_OK;
+  if (!q || !cache || !block_table || !kv_lens || !w_uk || !w_uv || !o_v)
+    return MLA_ERR_NULL;
+  const mla_dims& d = *dims;
+  if (!ws) return MLA_ERR_WORKSPACE;
+  const PrefillWs w = prefill_layout(d, B, max_kv_len, ws);
+  if (ws_bytes < w.bytes) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  MLA_TRY(launch_gather_rows(d, B, cache, block_table, max_blocks, kv_lens,
+                             max_kv_len, w.rows, s));
+  // [k_C | v_C] of every gathered row, all heads: one GEMM
+  GemmArgs g;
+  g.A = w.rows;
+  g.lda = d.d_c + d.d_r;
+  g.B = w_uk;
+  g.B2 = w_uv;
+  g.nb1 = d.n_h * d.d_h;
+  g.ldb = d.d_c;
+  g.M = (int)prefill_rows(B, max_kv_len);
+  g.N = 2 * d.n_h * d.d_h;
+  g.K = d.d_c;
+  g.ldc = g.N;
+  gemm_plan(d, g);
+  if (g.k_split != 1 || g.ntw != 0) return MLA_ERR_UNSUPPORTED;
+  g.c16 = w.kv;
+  MLA_TRY(launch_gemm(d, g, s));
+  MLA_TRY(launch_prefill_mha(d, B, n_q, q, w.rows, w.kv, kv_lens, max_kv_len,
+                             causal ? 1 : 0, o_v, lse, s));
+  return MLA_OK;
+}
+
+mla_status mla_out_values(const mla_dims* dims, int32_t T, const float* o_v,
+                          const void* w_o, void* u, void* ws, size_t ws_bytes,
+                          mla_stream_t stream) {
+  if (!dims) return MLA_ERR_NULL;
+  if (!dims_ok(dims) || T < 0) return MLA_ERR_SHAPE;
+  if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  if (T == 0) return MLA_OK;
+  if (!o_v || !w_o || !u) return MLA_ERR_NULL;
+  const mla_dims& d = *dims;
+  if (!ws) return MLA_ERR_WORKSPACE;
+  const OutWs w = out_layout(d, T, ws);
+  if (ws_bytes < w.bytes) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  GemmArgs g2 = o_gemm(d, T);
+  g2.A = o_v;
+  g2.B = w_o;
+  g2.C = w.u_parts;
+  MLA_TRY(launch_gemm(d, g2, s));
+  MLA_TRY(launch_convert(d, T, d.d, w.u_parts, d.d, g2.k_split, g2.c_ks, u,
+                         d.d, s));
+  return MLA_OK;
+}
 
 size_t mla_out_workspace_bytes(const mla_dims* dims, int32_t T) {
   if (!dims_ok(dims) || T <= 0) return 0;

@@ -38,6 +38,30 @@ hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
                           const float* m_part, const float* l_part,
                           float* o_lat, float* lse, hipStream_t stream);
 
+// ---- MHA-path prefill (prefill_mha.hip) --------------------------------
+// Shapes the prefill kernel serves: bf16, d_h = 128 (= d_v), d_r = 64.
+bool prefill_mha_supported(const mla_dims& d);
+// rows[b * kv_cap + t] = cache row of token t of sequence b (t < kv_lens[b]).
+hipError_t launch_gather_rows(const mla_dims& d, int B, const void* cache,
+                              const int32_t* block_table, int max_blocks,
+                              const int32_t* kv_lens, int kv_cap, void* rows,
+                              hipStream_t stream);
+// Causal attention of q [B*n_q][n_h][d_h + d_r] over keys [k_C | k_R] and
+// values v_C: kv [B*kv_cap][2 n_h d_h] bf16 (k_C of head h at h d_h, v_C at
+// n_h d_h + h d_h), k_R the last d_r columns of rows; o_v [B*n_q][n_h][d_h]
+// fp32, lse [B*n_q][n_h] (natural log) or null.
+hipError_t launch_prefill_mha(const mla_dims& d, int B, int n_q,
+                              const void* q, const void* rows, const void* kv,
+                              const int32_t* kv_lens, int kv_cap, int causal,
+                              float* o_v, float* lse, hipStream_t stream);
+// q_out[t][h] = [q_C | RoPE(q_R)] (bf16) from the K-split parts of the
+// query up-projection (as launch_absorb_fast reads them).
+hipError_t launch_query_mha(const mla_dims& d, int T, const float* parts,
+                            int nparts, long part_stride, long lda,
+                            const int32_t* pos, const float* rope_cos,
+                            const float* rope_sin, int max_pos, void* q_out,
+                            hipStream_t stream);
+
 // ---- query absorption (absorb.hip) -------------------------------------
 // q_lat[t, h, :] = W_UK_h^T (sum of nparts fp32 parts of q_C[t, h, :]) into
 // the first d_c columns of q_out's rows (bf16), and RoPE(q_R[t, h, :]) into

@@ -119,6 +119,36 @@ def run_step(st: DeviceStep, n_split: Optional[int] = None, stream=None,
     return StepOut(q=q4, o_lat=o_lat, lse=lse, u=u)
 
 
+@dataclasses.dataclass
+class PrefillOut:
+    q: torch.Tensor       # [B, n_q, n_h, d_h + d_r]
+    o_v: torch.Tensor     # [B, n_q, n_h, d_h] fp32
+    lse: torch.Tensor     # [B, n_q, n_h] fp32
+    u: torch.Tensor       # [B * n_q, d]
+
+
+def run_prefill_mha(st: DeviceStep, stream=None,
+                    out: Optional[PrefillOut] = None,
+                    causal: int = 1) -> PrefillOut:
+    """The same step on the explicit-key (MHA) path: append the chunk, its
+    queries without absorption, attention with per-head keys and values
+    up-projected from the cache, output projection."""
+    wl, L = st.wl, st.layer
+    d = wl.dims
+    L.append(st.h_new, st.seq_idx, st.pos, st.table, st.cache, stream=stream)
+    q = L.query_mha(st.h_new, st.pos, q_out=None if out is None else
+                    out.q.view(-1, d.n_h, d.d_h + d.d_r), stream=stream)
+    q4 = q.view(wl.batch, wl.n_q, d.n_h, d.d_h + d.d_r)
+    o_v, lse = L.prefill_mha(q4, st.cache, st.table, st.kv_lens,
+                             st.max_kv_len,
+                             o_v=None if out is None else out.o_v,
+                             lse=None if out is None else out.lse,
+                             causal=causal, stream=stream)
+    u = L.out_values(o_v.view(-1, d.n_h * d.d_h),
+                     u=None if out is None else out.u, stream=stream)
+    return PrefillOut(q=q4, o_v=o_v, lse=lse, u=u)
+
+
 def gather_rows(st: DeviceStep, seq: int, start: int, count: int) -> np.ndarray:
     """Cache rows of positions start .. start+count-1 of a sequence, read back
     to the host as float32 (for checks)."""

@@ -109,3 +109,46 @@ class MlaLayer:
         B.mla_out(self.cdims, o_lat, self.w["w_uv"], self.w["w_o"], u, ws=ws,
                   stream=stream)
         return u
+
+    # ---- MHA-path chunked prefill (explicit keys and values) ---------------
+    def query_mha(self, h, pos, q_out=None, stream=None):
+        d = self.dims
+        T = h.shape[0]
+        if q_out is None:
+            q_out = torch.empty((T, d.n_h, d.d_h + d.d_r),
+                                dtype=torch_dtype(self.dtype),
+                                device=self.device)
+        ws = self.workspace("absorb",
+                            B.mla_absorb_workspace_bytes(self.cdims, T))
+        B.mla_query_mha(self.cdims, h, pos, self.w["w_dq"], self.w["w_uq"],
+                        self.w["w_qr"], self.rope_cos, self.rope_sin, q_out,
+                        ws=ws, stream=stream)
+        return q_out
+
+    def prefill_mha(self, q, cache, block_table, kv_lens, max_kv_len: int,
+                    o_v=None, lse=None, causal: int = 1, stream=None):
+        d = self.dims
+        Bsz, n_q = q.shape[0], q.shape[1]
+        if o_v is None:
+            o_v = torch.empty((Bsz, n_q, d.n_h, d.d_h), dtype=torch.float32,
+                              device=self.device)
+        if lse is None:
+            lse = torch.empty((Bsz, n_q, d.n_h), dtype=torch.float32,
+                              device=self.device)
+        ws = self.workspace("prefill", B.mla_prefill_mha_workspace_bytes(
+            self.cdims, Bsz, max_kv_len))
+        B.mla_prefill_mha(self.cdims, q, cache, block_table, kv_lens,
+                          max_kv_len, self.w["w_uk"], self.w["w_uv"], o_v,
+                          lse=lse, causal=causal, ws=ws, stream=stream)
+        return o_v, lse
+
+    def out_values(self, o_v, u=None, stream=None):
+        d = self.dims
+        T = o_v.shape[0]
+        if u is None:
+            u = torch.empty((T, d.d), dtype=torch_dtype(self.dtype),
+                            device=self.device)
+        ws = self.workspace("out", B.mla_out_workspace_bytes(self.cdims, T))
+        B.mla_out_values(self.cdims, o_v, self.w["w_o"], u, ws=ws,
+                         stream=stream)
+        return u
