@@ -27,6 +27,7 @@ METRIC = ("MLA decode queries/sec + latent-cache GB/s & MFMA util vs peak "
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
 DECODE_KERNEL = "decode_mfma_kernel"
+PREFILL_KERNEL = "prefill_mha_kernel"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "decode_b64_ctx8k_pmc.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "mla_latent_kv_33_amd", "csrc", f)
                   for f in ("decode_mfma.hip", "decode_simt.hip")]
@@ -48,6 +49,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="b64_ctx8k")
+    ap.add_argument("--path", choices=("absorbed", "mha"), default="absorbed",
+                    help="attention form of the step: absorbed queries over "
+                         "the latent cache (mla_absorb_q, mla_decode, "
+                         "mla_out), or explicit per-head keys and values for "
+                         "chunked prefill (mla_query_mha, mla_prefill_mha, "
+                         "mla_out_values)")
     ap.add_argument("--cpu-sample", type=int, default=24,
                     help="sequences of the workload the CPU oracle times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -112,6 +119,21 @@ def cpu_baseline(wl, sample):
                       f"layer step per sequence, fp64 numpy; {total:.1f} s"}
 
 
+def workload_text(wl, mha):
+    d = wl.dims
+    dims = (f"DeepSeek-V2 dims (d {d.d}, n_h {d.n_h}, d_h {d.d_h}, d_c "
+            f"{d.d_c}, d_r {d.d_r}, d_c' {d.d_cq})")
+    ctx = (f"context {wl.ctx[0]}" if len(set(wl.ctx)) == 1 else
+           f"contexts {min(wl.ctx)}..{max(wl.ctx)}")
+    kind = ("MLA chunked-prefill step on the explicit-key (MHA) path"
+            if mha else "MLA decode step" if wl.n_q == 1 else
+            "MLA chunked-prefill step on the absorbed path")
+    return (f"{kind}, B={wl.batch}, {ctx} + {wl.n_q} new token(s) per "
+            f"sequence (causal), {dims}, paged latent cache of 64-token "
+            f"blocks, {'random-permutation' if wl.permuted else 'linear'} "
+            "block table")
+
+
 def stored_traffic(bytes_per_launch_alg):
     """HBM traffic of the decode kernel from the committed counter summary,
     if it was taken on the current kernel source."""
@@ -149,10 +171,13 @@ def main():
     n_split = B.mla_decode_auto_splits(layer.cdims, wl.batch, wl.n_q,
                                        st.max_kv_len) if not wl.n_split \
         else wl.n_split
-    out = flow.run_step(st)   # allocates outputs and workspaces once
+    mha = args.path == "mha"
+    # allocates outputs and workspaces once
+    out = flow.run_prefill_mha(st) if mha else flow.run_step(st)
     torch.cuda.synchronize()
 
-    names = ("append", "absorb", "decode", "out")
+    names = (("append", "query", "prefill", "out") if mha else
+             ("append", "absorb", "decode", "out"))
 
     def new_events(n):
         return [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
@@ -163,16 +188,28 @@ def main():
         the last stage, all of them ("all") or only around decode."""
         rec_all = e is not None and which == "all"
         rec_dec = e is not None
-        q2 = out.q.view(-1, d.n_h, d.d_c + d.d_r)
         if rec_all: e[0].record(stream)
         layer.append(st.h_new, st.seq_idx, st.pos, st.table, st.cache)
         if rec_all: e[1].record(stream)
-        layer.absorb(st.h_new, st.pos, q_out=q2)
+        if mha:
+            layer.query_mha(st.h_new, st.pos,
+                            q_out=out.q.view(-1, d.n_h, d.d_h + d.d_r))
+        else:
+            layer.absorb(st.h_new, st.pos,
+                         q_out=out.q.view(-1, d.n_h, d.d_c + d.d_r))
         if rec_dec: e[2].record(stream)
-        layer.decode(out.q, st.cache, st.table, st.kv_lens, st.max_kv_len,
-                     n_split=n_split, o_lat=out.o_lat, lse=out.lse)
+        if mha:
+            layer.prefill_mha(out.q, st.cache, st.table, st.kv_lens,
+                              st.max_kv_len, o_v=out.o_v, lse=out.lse)
+        else:
+            layer.decode(out.q, st.cache, st.table, st.kv_lens,
+                         st.max_kv_len, n_split=n_split, o_lat=out.o_lat,
+                         lse=out.lse)
         if rec_dec: e[3].record(stream)
-        layer.out(out.o_lat.view(-1, d.n_h, d.d_c), u=out.u)
+        if mha:
+            layer.out_values(out.o_v.view(-1, d.n_h * d.d_h), u=out.u)
+        else:
+            layer.out(out.o_lat.view(-1, d.n_h, d.d_c), u=out.u)
         if rec_all: e[4].record(stream)
 
     for _ in range(args.warmup):
@@ -186,7 +223,8 @@ def main():
         step(ev[i] if i % every == 0 else None, args.timed_events)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # decode stage (decode kernel + split combine) inside the timed steps
+    # attention stage (decode kernel + split combine, or the MHA prefill
+    # call) inside the timed steps
     t_dec_ms = float(np.mean([ev[i][2].elapsed_time(ev[i][3])
                               for i in sampled]))
     if args.timed_events == "all":
@@ -208,14 +246,37 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     queries = wl.batch * wl.n_q
     kv = wl.kv_lens
+    # (query, key) pairs the causal attention visits: query i of a chunk of
+    # n_q sees ctx + i + 1 keys
+    pairs = float(sum(wl.n_q * c + wl.n_q * (wl.n_q + 1) // 2
+                      for c in wl.ctx))
     cache_bytes = float(kv.sum()) * (d.d_c + d.d_r) * 2
-    q_bytes = queries * d.n_h * (d.d_c + d.d_r) * 2
-    olat_bytes = queries * d.n_h * d.d_c * 4
-    alg_bytes = cache_bytes + q_bytes + olat_bytes
-    flops = d.n_h * float(kv.sum()) * (2 * (d.d_c + d.d_r) + 2 * d.d_c)
+    if mha:
+        # gathered rows written and read, [k_C | v_C] written and read once,
+        # queries read, fp32 values written
+        kv_rows = float(wl.batch * st.max_kv_len)
+        kv_el = 2 * d.n_h * d.d_h
+        alg_bytes = (cache_bytes + 2 * kv_rows * (d.d_c + d.d_r) * 2 +
+                     kv_rows * kv_el * 2 * 2 +
+                     queries * d.n_h * (d.d_h + d.d_r) * 2 +
+                     queries * d.n_h * d.d_h * 4)
+        flops = (d.n_h * pairs * (2 * (d.d_h + d.d_r) + 2 * d.d_h) +
+                 2.0 * kv_rows * kv_el * d.d_c)
+    else:
+        q_bytes = queries * d.n_h * (d.d_c + d.d_r) * 2
+        olat_bytes = queries * d.n_h * d.d_c * 4
+        alg_bytes = cache_bytes + q_bytes + olat_bytes
+        flops = d.n_h * pairs * (2 * (d.d_c + d.d_r) + 2 * d.d_c)
     t_dec = t_dec_ms * 1e-3
     achieved = alg_bytes / t_dec / 1e9
-    traffic = stored_traffic(alg_bytes)
+    tflops = flops / t_dec / 1e12
+    # the bound is the roof the stage is closer to
+    mfma_bound = tflops / BF16_PEAK_TFLOPS > achieved / HBM_PEAK_GBPS
+    traffic = None if (mha or wl.name != "b64_ctx8k") else \
+        stored_traffic(alg_bytes)
+    stage_kernel = ("mla_prefill_mha: gather_rows_kernel + gemm_tiled_kernel "
+                    "(k_C, v_C up-projection) + " + PREFILL_KERNEL if mha else
+                    "mla_decode: " + DECODE_KERNEL + " + combine_rows_kernel")
     result = {
         "metric": METRIC,
         "value": queries / (ms_per_step * 1e-3),
@@ -231,26 +292,26 @@ def main():
         "data": "synthetic (seeded N(0,1) hidden states and latent cache "
                 "rows, N(0,1/fan_in) weights)",
         "config": {
-            "workload": "MLA decode step, B=64, context 8192 + 1 query token "
-                        "per sequence, DeepSeek-V2 dims (d 5120, n_h 128, "
-                        "d_h 128, d_c 512, d_r 64, d_c' 1536), paged latent "
-                        "cache of 64-token blocks, random-permutation block "
-                        "table",
+            "workload": workload_text(wl, mha),
             "batch": wl.batch, "context": wl.ctx[0], "kv_len": int(kv[0]),
-            "n_q": wl.n_q, "n_split": int(n_split), "block_size": 64,
+            "n_q": wl.n_q, "n_split": None if mha else int(n_split),
+            "block_size": 64, "path": args.path,
         },
         "roofline": {
-            "bound": "hbm",
-            "kernel": "mla_decode: " + DECODE_KERNEL + " + combine_rows_kernel",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS,
+            "bound": "mfma" if mfma_bound else "hbm",
+            "kernel": stage_kernel,
+            "achieved": tflops if mfma_bound else achieved,
+            "peak": BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBPS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": (tflops / BF16_PEAK_TFLOPS if mfma_bound
+                     else achieved / HBM_PEAK_GBPS),
             "traffic": traffic,
             "alg_bytes_per_launch": alg_bytes,
             "flops_per_launch": flops,
-            "mfma_tflops": flops / t_dec / 1e12,
-            "mfma_frac": flops / t_dec / 1e12 / BF16_PEAK_TFLOPS,
+            "hbm_GBps": achieved,
+            "hbm_frac": achieved / HBM_PEAK_GBPS,
+            "mfma_tflops": tflops,
+            "mfma_frac": tflops / BF16_PEAK_TFLOPS,
             "decode_us": t_dec * 1e6,
         },
         "decode_queries_per_s": queries / t_dec,
@@ -266,6 +327,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+    if mha or wl.name != "b64_ctx8k":
+        result["note"] = ("not the headline configuration: a measurement of "
+                          "another workload or attention path")
     print(json.dumps(result), flush=True)
 
 
