@@ -8,7 +8,7 @@
 // hi = bf16(x), lo = bf16(x - hi), i.e. two MFMAs per fragment; this keeps
 // those intermediates at ~16 significant bits instead of 8.
 //
-// Two kernels:
+// Kernels:
 //   * skinny (M <= 64, NT): decode batches.  The weight stream dominates, so
 //     B fragments are loaded straight from HBM into registers in MFMA
 //     layout; the four waves of a workgroup interleave their 16-wide k-steps
@@ -19,6 +19,8 @@
 //   * tiled (any M, NT or NN): 128x128x32 tiles staged through padded LDS,
 //     2x2 waves of 64x64; NN weights are read with ds_read_b64_tr_b16 so the
 //     MFMA still sees k-contiguous B fragments.
+//   * big (M >= 256, or 128 with fp32 activations; NT, K >= 1024): 256x128
+//     (128x128) tiles in 64-k steps through a three-slot direct-to-LDS ring.
 // fp32 layers use a plain SIMT kernel (small shapes only).
 
 #include "lds_dma.hpp"
@@ -537,6 +539,228 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
   }
 }
 
+// ------------------------------------------------------------------- big
+// Large-M GEMM (prefill chunks): C = A B^T with A [M][K] (bf16, or fp32 as
+// hi + lo bf16 terms), B [N][K] bf16 (NT), K % 64 == 0, one K chunk.
+//
+// Workgroup tile BM x 128 (BM = 256 for bf16 A, 128 for fp32 A, so that the
+// A tile is 32 KiB either way) in 64-k steps, 4 waves as 2 x 2 of
+// (BM / 2) x 64.  Each step's A and B tiles (48 KiB) arrive by direct-to-LDS
+// copies of whole 128/256-byte row runs into a three-slot ring (144 KiB),
+// two steps in flight while the third is computed.  LDS rows hold their
+// 16-byte pieces XOR-swizzled by the row index (bf16 rows of 128 B: piece ^
+// (row / 2) % 8; fp32 rows of 256 B: piece ^ row % 16), so the 16 lanes of
+// one ds_read_b128 phase, 16 consecutive rows at the same piece, hit
+// distinct banks.  The wave computes C^T tiles (A operand = weight rows,
+// B operand = activation rows) so that each lane ends with 4 consecutive
+// output columns of one row: 16-byte fp32 or 8-byte bf16 stores.
+//
+// Tile order: the ids dealt to one XCD (round-robin) form a contiguous run of
+// the grouped order (groups of 8 row tiles, column tiles outer), so the
+// workgroups one XCD runs together share A row bands and B column bands
+// through its L2.
+constexpr int BG_BN = 128;
+constexpr int BG_NSLOT = 3;
+constexpr int BG_A_BYTES = 32 * 1024;
+constexpr int BG_SLOT = BG_A_BYTES + BG_BN * 128;   // 48 KiB
+constexpr int BG_LDS = BG_NSLOT * BG_SLOT;           // 144 KiB
+constexpr int BG_GROUP = 8;
+
+template <bool AF32>
+struct BigCfg {
+  static constexpr int BM = AF32 ? 128 : 256;
+  static constexpr int RB = AF32 ? 256 : 128;   // A bytes per row per 64 k
+  static constexpr int PPR = RB / 16;           // pieces per A row
+  static constexpr int RPC = 1024 / RB;         // A rows per copy
+  static constexpr int MT = BM / 64;            // 32-row tiles per wave
+  static constexpr int A_PER = BG_A_BYTES / 1024 / 4;  // 8 A copies per wave
+  static constexpr int B_PER = BG_BN * 128 / 1024 / 4; // 4 B copies per wave
+  static constexpr int PER = A_PER + B_PER;
+  static_assert(BM * RB == BG_A_BYTES, "A tile size");
+  static_assert(2 * PER <= 63, "vmcnt range");
+};
+
+// Position of piece p of A row r in the LDS row.
+template <bool AF32>
+__device__ __forceinline__ int big_apos(int r, int p) {
+  return AF32 ? p ^ (r & 15) : p ^ ((r >> 1) & 7);
+}
+
+template <bool AF32>
+__global__ __launch_bounds__(256, 1) void gemm_big_kernel(
+    const void* __restrict__ Av, long lda, const uint16_t* __restrict__ B,
+    const uint16_t* __restrict__ B2, int nb1, long ldb,
+    float* __restrict__ C, uint16_t* __restrict__ C16, long ldc, int M,
+    int N, int K, int tiles_m, int tiles_n) {
+  using L = BigCfg<AF32>;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5;
+  const int col = lane & 31;
+  const int wm = wave >> 1, wn = wave & 1;
+  constexpr int esz = AF32 ? 4 : 2;
+
+  // block id -> (tm, tn)
+  const int nwg = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int w = xcd * (nwg >> 3) + min(xcd, nwg & 7) + (blockIdx.x >> 3);
+  const int gsize = BG_GROUP * tiles_n;
+  const int first_m = (w / gsize) * BG_GROUP;
+  const int gm = min(tiles_m - first_m, BG_GROUP);
+  const int wi = w - (w / gsize) * gsize;
+  const int tm = first_m + wi % gm;
+  const int tn = wi / gm;
+  const int m0 = tm * L::BM, n0 = tn * BG_BN;
+
+  // ---- copy offsets (bytes from the per-step scalar bases) ---------------
+  // A copy i = wave A_PER + a covers rows i RPC .. i RPC + RPC - 1; lane l
+  // takes row r = i RPC + l / PPR, LDS position l % PPR, i.e. the piece
+  // that belongs there.  Rows past M repeat row M - 1 (results unused).
+  const char* a_base = (const char*)Av + (size_t)m0 * lda * esz;
+  uint32_t a_off[L::A_PER];
+#pragma unroll
+  for (int a = 0; a < L::A_PER; ++a) {
+    const int r = (wave * L::A_PER + a) * L::RPC + lane / L::PPR;
+    const int piece = big_apos<AF32>(r, lane % L::PPR);
+    a_off[a] = (uint32_t)((size_t)min(r, M - 1 - m0) * lda * esz) +
+               16 * piece;
+  }
+  // B copy j = wave B_PER + b covers rows 8 j .. 8 j + 7 (128 B each).  The
+  // tile lies wholly in B or wholly in B2 (nb1 % 128 == 0 or nb1 >= N).
+  const uint16_t* bt = n0 < nb1 ? B + (size_t)n0 * ldb
+                                : B2 + (size_t)(n0 - nb1) * ldb;
+  uint32_t b_off[L::B_PER];
+#pragma unroll
+  for (int b = 0; b < L::B_PER; ++b) {
+    const int r = 8 * (wave * L::B_PER + b) + (lane >> 3);
+    const int piece = (lane & 7) ^ ((r >> 1) & 7);
+    b_off[b] = (uint32_t)(min(r, N - 1 - n0) * ldb * 2) + 16 * piece;
+  }
+  const uint32_t lds0 = lds_u32(lds);
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    const uint32_t slot = lds0 + (kt % BG_NSLOT) * BG_SLOT;
+    const char* ab = a_base + (size_t)kt * 64 * esz;
+    const char* bb = (const char*)bt + (size_t)kt * 128;
+#pragma unroll
+    for (int a = 0; a < L::A_PER; ++a)
+      dma16(slot + (wave * L::A_PER + a) * 1024, ab, a_off[a]);
+#pragma unroll
+    for (int b = 0; b < L::B_PER; ++b)
+      dma16(slot + BG_A_BYTES + (wave * L::B_PER + b) * 1024, bb, b_off[b]);
+  };
+
+  // ---- fragment reads -----------------------------------------------------
+  // weight fragment (A operand) nt, k-step ks: row wn 64 + 32 nt + col,
+  // piece 2 ks + g; activation fragment (B operand) mt: row
+  // wm BM / 2 + 32 mt + col, bf16 piece 2 ks + g or fp32 pieces 4 ks + 2 g
+  // and 4 ks + 2 g + 1.
+  auto w_read = [&](const lds_char* sl, int nt, int ks) __attribute__((always_inline)) {
+    const int r = wn * 64 + 32 * nt + col;
+    return *(const __attribute__((address_space(3))) bf16x8*)(
+        sl + BG_A_BYTES + r * 128 + 16 * ((2 * ks + g) ^ ((r >> 1) & 7)));
+  };
+  auto a_read = [&](const lds_char* sl, int mt, int piece) __attribute__((always_inline)) {
+    const int r = wm * (L::BM / 2) + 32 * mt + col;
+    return *(const __attribute__((address_space(3))) u32x4*)(
+        sl + r * L::RB + 16 * big_apos<AF32>(r, piece));
+  };
+
+  f32x16 acc[2][L::MT];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < L::MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[nt][mt][r] = 0.0f;
+
+  const int nk = K / 64;
+  issue(0);
+  if (nk > 1) issue(1);
+  for (int kt = 0; kt < nk; ++kt) {
+    // own copies of step kt done (step kt + 1 may stay in flight), then
+    // everybody's; the slot of step kt - 1 is free after the barrier
+    if (kt + 1 < nk) wait_vm<L::PER>();
+    else wait_vm<0>();
+    barrier();
+    if (kt + 2 < nk) issue(kt + 2);
+    const lds_char* sl = (const lds_char*)lds + (kt % BG_NSLOT) * BG_SLOT;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 wf[2], ahi[L::MT], alo[L::MT];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) wf[nt] = w_read(sl, nt, ks);
+#pragma unroll
+      for (int mt = 0; mt < L::MT; ++mt) {
+        if (AF32) {
+          const u32x4 x0 = a_read(sl, mt, 4 * ks + 2 * g);
+          const u32x4 x1 = a_read(sl, mt, 4 * ks + 2 * g + 1);
+          split_hi_lo_hw(__builtin_bit_cast(f32x4, x0),
+                         __builtin_bit_cast(f32x4, x1), ahi[mt], alo[mt]);
+        } else {
+          ahi[mt] = __builtin_bit_cast(bf16x8, a_read(sl, mt, 2 * ks + g));
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < L::MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              wf[nt], ahi[mt], acc[nt][mt], 0, 0, 0);
+          if (AF32)
+            acc[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                wf[nt], alo[mt], acc[nt][mt], 0, 0, 0);
+        }
+    }
+    wait_lgkm0();  // this slot's reads returned before it is refilled
+  }
+
+  // C^T accumulator register r of lane (col, g), tiles (nt, mt): column
+  // n0 + wn 64 + 32 nt + 8 (r / 4) + 4 g + r % 4 of row
+  // m0 + wm BM / 2 + 32 mt + col.  N % 4 == 0, so a group of 4 columns is
+  // wholly inside or outside.
+#pragma unroll
+  for (int mt = 0; mt < L::MT; ++mt) {
+    const int m = m0 + wm * (L::BM / 2) + 32 * mt + col;
+    if (m >= M) continue;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + wn * 64 + 32 * nt + 8 * i + 4 * g;
+        if (n >= N) continue;
+        const f32x4 v = {acc[nt][mt][4 * i], acc[nt][mt][4 * i + 1],
+                         acc[nt][mt][4 * i + 2], acc[nt][mt][4 * i + 3]};
+        if (C16) {
+          const uint32_t lo = pack_bf2(v[0], v[1]), hi = pack_bf2(v[2], v[3]);
+          *(uint2*)(C16 + (size_t)m * ldc + n) = make_uint2(lo, hi);
+        } else {
+          *(f32x4*)(C + (size_t)m * ldc + n) = v;
+        }
+      }
+  }
+}
+
+template <bool AF32>
+hipError_t launch_big(const GemmArgs& g, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(
+        (const void*)gemm_big_kernel<AF32>,
+        hipFuncAttributeMaxDynamicSharedMemorySize, BG_LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tiles_m = (g.M + BigCfg<AF32>::BM - 1) / BigCfg<AF32>::BM;
+  const int tiles_n = (g.N + BG_BN - 1) / BG_BN;
+  hipLaunchKernelGGL(gemm_big_kernel<AF32>, dim3(tiles_m * tiles_n),
+                     dim3(256), BG_LDS, stream, g.A, g.lda,
+                     (const uint16_t*)g.B, (const uint16_t*)g.B2, g.nb1,
+                     g.ldb, g.C, (uint16_t*)g.c16, g.ldc, g.M, g.N, g.K,
+                     tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
 // ----------------------------------------------------------------- tiled
 constexpr int TB_M = 128, TB_N = 128, TB_K = 32;
 constexpr int A_LD = TB_K + 8;     // bf16 elements per LDS row of A / NT B
@@ -751,6 +975,19 @@ void gemm_plan(const mla_dims& d, GemmArgs& g, int max_split) {
   g.ntw = 0;
   g.k_split = 1;
   g.m_split = 1;
+  g.big = 0;
+  // Many rows (prefill chunks): the large-tile kernel, one K chunk.  Its
+  // two-step pipeline fill and the epilogue are paid once per tile, so short
+  // K (the 512-deep up-projection of the latent) stays on the tiled kernel.
+  const int esz = g.a_f32 ? 4 : 2;
+  if (d.dtype == MLA_BF16 && !g.b_nn && g.batch == 1 &&
+      g.M >= (g.a_f32 ? 128 : 256) && g.K >= 1024 && g.K % 64 == 0 &&
+      g.N % 4 == 0 &&
+      g.ldc % 4 == 0 && (g.lda * esz) % 16 == 0 && g.ldb % 8 == 0 &&
+      (g.nb1 >= g.N || g.nb1 % BG_BN == 0)) {
+    g.big = 1;
+    return;
+  }
   if (d.dtype != MLA_BF16 || g.b_nn || g.M > 64 || g.M <= 0 || g.N <= 0 ||
       g.K <= 0)
     return;
@@ -849,6 +1086,10 @@ hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
                        (const float*)g.B2, g.nb1, g.ldb, g.b_bs, g.b_nn, g.C,
                        g.ldc, g.c_bs, g.c_ks, g.M, g.N, g.K, (int)g.K);
     return hipGetLastError();
+  }
+  if (g.big) {
+    if (ks != 1 || g.batch != 1) return hipErrorInvalidValue;
+    return g.a_f32 ? launch_big<true>(g, stream) : launch_big<false>(g, stream);
   }
   const uint16_t* B = (const uint16_t*)g.B;
   const uint16_t* B2 = (const uint16_t*)g.B2;

@@ -104,6 +104,8 @@ struct GemmArgs {
   // LDS-staged kernel: rows in blocks of 32, one workgroup per block (1 or 2)
   int m_split = 1;
   void* c16 = nullptr;  // bf16 output instead of C (tiled kernel, k_split 1)
+  // 1: large-tile kernel for many rows (bf16, NT, batch 1, one K chunk)
+  int big = 0;
 };
 hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
                        hipStream_t stream);
