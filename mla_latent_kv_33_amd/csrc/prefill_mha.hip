@@ -26,8 +26,11 @@
 // maximum needs one exchange with the lane 32 away, and its probabilities,
 // in the token order of the accumulator rows, are directly the B operand of
 // O^T += V^T P^T (A = V^T through transposing LDS reads, the value layout of
-// the decode kernel).  Online softmax in base 2 with the output rescaled by
-// the change of the running maximum.  The 16 query tiles of one (sequence,
+// the decode kernel).  Online softmax in base 2 against a lazily moved
+// reference: O and l are rescaled only when a tile's maximum exceeds the
+// reference by more than 2^8 (a branch the whole wave takes or skips), so
+// most tiles run no vector code on O; masks are applied only on tiles that
+// cross the wave's causal limit.  The 16 query tiles of one (sequence,
 // head) read the same keys; the grid maps them to one XCD so that the keys
 // they stream together are shared through its L2.
 #include "lds_dma.hpp"
@@ -37,7 +40,7 @@
 namespace mla {
 namespace {
 
-constexpr int PF_QT = 128;          // queries per workgroup
+constexpr int PF_QW = 128;          // queries per workgroup (4 waves x 32)
 constexpr int PF_KT = 64;           // keys per tile
 constexpr int PF_DH = 128;          // d_h = d_v
 constexpr int PF_DR = 64;           // d_r
@@ -48,6 +51,7 @@ constexpr int PF_KR_BYTES = PF_KT * PF_DR * 2;   // 8 KiB
 constexpr int PF_V_OFF = PF_KR_OFF + PF_KR_BYTES;
 constexpr int PF_STAGE = PF_V_OFF + PF_KT * PF_DH * 2;  // 40 KiB
 constexpr int PF_LDS = 2 * PF_STAGE;
+constexpr float PF_SLACK = 8.0f;    // log2 headroom of P above the reference
 
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -84,6 +88,11 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
     const int32_t* __restrict__ kv_lens, int kv_cap, int n_q, int n_h,
     int ntq, int causal, float scale_log2, float* __restrict__ o_v,
     float* __restrict__ lse) {
+  // Query groups of 32 per wave.  Two would halve the LDS reads per MFMA
+  // (each key and value fragment serving both), but their queries, scores
+  // and outputs need more registers than a wave has.
+  constexpr int QG = 1;
+  constexpr int QT = PF_QW * QG;  // queries per workgroup
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const lds_char* L = (const lds_char*)lds;
   const int lane = threadIdx.x & 63;
@@ -99,22 +108,29 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
   const int bh = w / ntq, qt = w - bh * ntq;
   const int b = bh / n_h, h = bh - b * n_h;
   const int kvl = min(kv_lens[b], kv_cap);
-  const int i0 = qt * PF_QT;
-  const int iq = i0 + 32 * wave + col;         // this lane's query
-  const int iq_c = min(iq, n_q - 1);
+  const int i0 = qt * QT;
   auto lim_of = [&](int i) { return causal ? kvl - n_q + i : kvl - 1; };
-  const int lim = lim_of(iq_c);
-  const int lim_wave_min = lim_of(min(i0 + 32 * wave, n_q - 1));
-  const int lim_wg_max = lim_of(min(i0 + PF_QT - 1, n_q - 1));
+  // query group u of the wave: queries i0 + 32 (QG wave + u) + 0..31; the
+  // lane owns query col of every group
+  int iq[QG], lim[QG];
+#pragma unroll
+  for (int u = 0; u < QG; ++u) {
+    iq[u] = i0 + 32 * (QG * wave + u) + col;
+    lim[u] = lim_of(min(iq[u], n_q - 1));
+  }
+  const int lim_wave_min = lim_of(min(i0 + 32 * QG * wave, n_q - 1));
+  const int lim_wg_max = lim_of(min(i0 + QT - 1, n_q - 1));
   const int ntiles = (lim_wg_max + PF_KT) / PF_KT;
 
   // queries: lane holds q[iq][16 ks + 8 g .. + 7] for every k-step
-  bf16x8 qreg[PF_KS];
-  {
-    const uint16_t* qp =
-        q + ((size_t)(b * n_q + iq_c) * n_h + h) * (PF_DH + PF_DR) + 8 * g;
+  bf16x8 qreg[QG][PF_KS];
 #pragma unroll
-    for (int ks = 0; ks < PF_KS; ++ks) qreg[ks] = *(const bf16x8*)(qp + 16 * ks);
+  for (int u = 0; u < QG; ++u) {
+    const uint16_t* qp = q + ((size_t)(b * n_q + min(iq[u], n_q - 1)) * n_h +
+                              h) * (PF_DH + PF_DR) + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < PF_KS; ++ks)
+      qreg[u][ks] = *(const bf16x8*)(qp + 16 * ks);
   }
 
   // ---- copies of key tile j into stage j % 2 (10 per wave) --------------
@@ -169,12 +185,17 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
       a_v[e] = vt * 128 + 16 * ((4 * e + vc) ^ swz(vt)) + 8 * (s16 & 1);
   }
 
-  f32x16 o[4];
+  f32x16 o[QG][4];
+  float m_run[QG], l_run[QG];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int u = 0; u < QG; ++u) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[mt][r] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[u][mt][r] = 0.0f;
+    m_run[u] = -INFINITY;
+    l_run[u] = 0.0f;
+  }
 
   issue(0);
   // Queries and tile 0 in (a wait the compiler sees, so that it adds none of
@@ -188,68 +209,93 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
     const lds_char* st = L + (j & 1) * PF_STAGE;
     const int t0 = j * PF_KT;
 
-    // S^T = K Q^T for the tile's two 32-token halves
-    f32x16 s[2];
+    // S^T = K Q^T for the tile's two 32-token halves; each key fragment
+    // serves every query group of the wave
+    f32x16 s[QG][2];
+#pragma unroll
+    for (int u = 0; u < QG; ++u)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[u][tt][r] = 0.0f;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int t = 32 * tt + col;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[tt][r] = 0.0f;
 #pragma unroll
       for (int ks = 0; ks < PF_KS; ++ks) {
         const lds_char* a =
             ks < 8 ? st + t * 256 + 16 * ((2 * ks + g) ^ (t & 15))
                    : st + PF_KR_OFF + t * 128 +
                          16 * ((2 * (ks - 8) + g) ^ ((t >> 1) & 7));
-        s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *(const lds_bf16x8*)a, qreg[ks], s[tt], 0, 0, 0);
+        const bf16x8 kf = *(const lds_bf16x8*)a;
+#pragma unroll
+        for (int u = 0; u < QG; ++u)
+          s[u][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              kf, qreg[u][ks], s[u][tt], 0, 0, 0);
       }
     }
     // Accumulator register r of lane (col, g), half tt: token
-    // t0 + 32 tt + 8 (r / 4) + 4 g + r % 4 of query iq.
-    float mx = -INFINITY;
+    // t0 + 32 tt + 8 (r / 4) + 4 g + r % 4 of query iq[u].
     const bool need_mask = t0 + PF_KT - 1 > lim_wave_min;
+    bf16x8 pb[QG][4];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int u = 0; u < QG; ++u) {
+      // scores stay unscaled; the scale enters the maximum and the
+      // exponent's fused multiply-add
+      if (__builtin_expect(need_mask, 0)) {
+        // token t0 + 32 tt + 8 (r / 4) + 4 g + r % 4 visible iff
+        // 32 tt + 8 (r / 4) + r % 4 <= lim - t0 - 4 g
+        const int rel = lim[u] - t0 - 4 * g;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = s[tt][r] * scale_log2;
-        if (need_mask) {
-          const int tok = t0 + 32 * tt + 8 * (r >> 2) + 4 * g + (r & 3);
-          v = tok <= lim ? v : -INFINITY;
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * tt + 8 * (r >> 2) + (r & 3) > rel)
+              s[u][tt][r] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[u][tt][r]);
+      mx = fmaxf(mx, lane_xor32f(mx, g)) * scale_log2;
+      // Lazy rescaling: the reference m_run moves (and O, l are rescaled)
+      // only when the tile's maximum exceeds it by more than PF_SLACK, so
+      // P <= 2^PF_SLACK.  Both lanes of a query agree (same mx); the branch
+      // is taken by the whole wave or skipped by it.
+      const bool grow = mx > m_run[u] + PF_SLACK;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? mx : m_run[u];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_new);
+        m_run[u] = m_new;
+        l_run[u] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[u][mt][r] *= alpha;
+      }
+      const float nm = -m_run[u];
+      // P (bf16) in k-slot order: k-step kk uses half kk / 2, registers
+      // 8 (kk % 2) .. 8 (kk % 2) + 7.
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        uint32_t pw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(
+              s[u][kk >> 1][8 * (kk & 1) + 2 * e], scale_log2, nm));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(
+              s[u][kk >> 1][8 * (kk & 1) + 2 * e + 1], scale_log2, nm));
+          const bf16x2 pp = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+          l_run[u] = __builtin_amdgcn_fdot2_f32_bf16(
+              pp, __builtin_bit_cast(bf16x2, 0x3F803F80u), l_run[u], false);
+          pw[e] = __builtin_bit_cast(uint32_t, pp);
         }
-        s[tt][r] = v;
-        mx = fmaxf(mx, v);
+        pb[u][kk] =
+            __builtin_bit_cast(bf16x8, (u32x4){pw[0], pw[1], pw[2], pw[3]});
       }
-    mx = fmaxf(mx, lane_xor32f(mx, g));
-    const float m_new = fmaxf(m_run, mx);  // finite: key 0 is always seen
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[mt][r] *= alpha;
-    // P (bf16) in k-slot order: k-step kk uses half kk / 2, registers
-    // 8 (kk % 2) .. 8 (kk % 2) + 7.
-    bf16x8 pb[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      uint32_t pw[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(
-            s[kk >> 1][8 * (kk & 1) + 2 * e] - m_new);
-        const float p1 = __builtin_amdgcn_exp2f(
-            s[kk >> 1][8 * (kk & 1) + 2 * e + 1] - m_new);
-        const bf16x2 pp = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(
-            pp, __builtin_bit_cast(bf16x2, 0x3F803F80u), l_run, false);
-        pw[e] = __builtin_bit_cast(uint32_t, pp);
-      }
-      pb[kk] = __builtin_bit_cast(bf16x8, (u32x4){pw[0], pw[1], pw[2], pw[3]});
     }
-    // O^T += V^T P^T
+    // O^T += V^T P^T; each value fragment serves every query group
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -261,28 +307,33 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
             (lds_s16x4*)(st + ((off ^ 32) + 1024)));
         const bf16x8 vf = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kk], o[mt], 0,
-                                                        0, 0);
+#pragma unroll
+        for (int u = 0; u < QG; ++u)
+          o[u][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              vf, pb[u][kk], o[u][mt], 0, 0, 0);
       }
     wait_lgkm0();  // this stage's reads done before it is refilled
   }
 
   // ---- output: O^T register r of lane (col, g), dv tile mt: value column
-  // 32 mt + 8 (r / 4) + 4 g + r % 4 of query iq.
-  const float l_tot = l_run + lane_xor32f(l_run, g);
-  if (iq < n_q) {
-    const float inv = 1.0f / l_tot;
-    float* dst = o_v + ((size_t)(b * n_q + iq) * n_h + h) * PF_DH + 4 * g;
+  // 32 mt + 8 (r / 4) + 4 g + r % 4 of query iq[u].
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+  for (int u = 0; u < QG; ++u) {
+    const float l_tot = l_run[u] + lane_xor32f(l_run[u], g);
+    if (iq[u] < n_q) {
+      const float inv = 1.0f / l_tot;
+      float* dst = o_v + ((size_t)(b * n_q + iq[u]) * n_h + h) * PF_DH + 4 * g;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *(f32x4*)(dst + 32 * mt + 8 * i) =
-            (f32x4){o[mt][4 * i] * inv, o[mt][4 * i + 1] * inv,
-                    o[mt][4 * i + 2] * inv, o[mt][4 * i + 3] * inv};
-    if (g == 0 && lse)
-      lse[(size_t)(b * n_q + iq) * n_h + h] =
-          (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *(f32x4*)(dst + 32 * mt + 8 * i) =
+              (f32x4){o[u][mt][4 * i] * inv, o[u][mt][4 * i + 1] * inv,
+                      o[u][mt][4 * i + 2] * inv, o[u][mt][4 * i + 3] * inv};
+      if (g == 0 && lse)
+        lse[(size_t)(b * n_q + iq[u]) * n_h + h] =
+            (m_run[u] + __log2f(l_tot)) * 0.69314718055994531f;
+    }
   }
 }
 
@@ -349,6 +400,8 @@ hipError_t launch_prefill_mha(const mla_dims& d, int B, int n_q,
                               const void* q, const void* rows, const void* kv,
                               const int32_t* kv_lens, int kv_cap, int causal,
                               float* o_v, float* lse, hipStream_t stream) {
+  const float scale_log2 =
+      (float)(1.4426950408889634 / __builtin_sqrt((double)(d.d_h + d.d_r)));
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
@@ -357,9 +410,7 @@ hipError_t launch_prefill_mha(const mla_dims& d, int B, int n_q,
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const float scale_log2 =
-      (float)(1.4426950408889634 / __builtin_sqrt((double)(d.d_h + d.d_r)));
-  const int ntq = (n_q + PF_QT - 1) / PF_QT;
+  const int ntq = (n_q + PF_QW - 1) / PF_QW;
   const long nwg = (long)B * d.n_h * ntq;
   hipLaunchKernelGGL(prefill_mha_kernel, dim3((unsigned)nwg), dim3(256),
                      PF_LDS, stream, (const uint16_t*)q,
