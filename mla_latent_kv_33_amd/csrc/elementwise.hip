@@ -120,6 +120,31 @@ inline int grid_for(long n, int threads) {
 
 }  // namespace
 
+// One thread per value: hi to 16 (i / 8) + i % 8 (bf16 units), lo 8 further.
+__global__ void reduce_parts_hl_kernel(const float* __restrict__ src,
+                                       int nparts, long part_stride, long n,
+                                       uint16_t* __restrict__ dst) {
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n;
+       i += (long)gridDim.x * blockDim.x) {
+    const float x = sum_parts(src, nparts, part_stride, i);
+    const uint16_t hi = f2bf(x);
+    const long at = 16 * (i >> 3) + (i & 7);
+    dst[at] = hi;
+    dst[at + 8] = f2bf(x - bf2f(hi));
+  }
+}
+
+hipError_t launch_reduce_parts_hl(const float* src, int nparts,
+                                  long part_stride, long n, int ld, void* dst,
+                                  hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if (ld % 8 != 0 || n % ld != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(reduce_parts_hl_kernel, dim3(grid_for(n, 256)),
+                     dim3(256), 0, stream, src, nparts, part_stride, n,
+                     (uint16_t*)dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_reduce_parts(const float* src, int nparts, long part_stride,
                                long n, float* dst, hipStream_t stream) {
   if (n <= 0) return hipSuccess;

@@ -381,12 +381,15 @@ struct LdsCfg {
   static constexpr int LDS = NBUF * SLOT;
 };
 
-template <int MT, int NTW, bool AF32>
+// HL: A holds pre-split hi|lo pairs (AF32 layout, no split in the kernel);
+// c_hl: C is written as pre-split pairs (one K chunk).
+template <int MT, int NTW, bool AF32, bool HL>
 __global__ __launch_bounds__(256) void gemm_lds_kernel(
     const void* __restrict__ Av, long lda, long a_bs,
     const uint16_t* __restrict__ B, const uint16_t* __restrict__ B2, int nb1,
     long ldb, long b_bs, float* __restrict__ C, long ldc, long c_bs, long c_ks,
-    int M, int N, int K, int k_chunk, int m_split) {
+    int M, int N, int K, int k_chunk, int m_split, int c_hl) {
+  static_assert(!HL || AF32, "pre-split A uses the fp32 layout");
   using L = LdsCfg<MT, NTW, AF32>;
   constexpr int NBUF = L::NBUF;
   extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -499,10 +502,17 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (AF32) {
+          // values 16 ks + 8 g .. + 7: fp32 pieces 4 ks + 2 g and + 1, or
+          // their pre-split hi and lo pieces at the same places
           const u32x4 x0 = a_read(sl, mt, 4 * ks + 2 * g);
           const u32x4 x1 = a_read(sl, mt, 4 * ks + 2 * g + 1);
-          split_hi_lo_hw(__builtin_bit_cast(f32x4, x0),
-                         __builtin_bit_cast(f32x4, x1), ahi[mt], alo[mt]);
+          if (HL) {
+            ahi[mt] = __builtin_bit_cast(bf16x8, x0);
+            alo[mt] = __builtin_bit_cast(bf16x8, x1);
+          } else {
+            split_hi_lo_hw(__builtin_bit_cast(f32x4, x0),
+                           __builtin_bit_cast(f32x4, x1), ahi[mt], alo[mt]);
+          }
         } else {
           ahi[mt] = __builtin_bit_cast(bf16x8, a_read(sl, mt, 2 * ks + g));
         }
@@ -526,6 +536,29 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
   // Accumulator register r of lane (col, g): row 32 mt + 8 (r / 4) + 4 g +
   // r % 4, column 32 (wave NTW + nt) + col.
   float* cz = C + z * c_bs + kz * c_ks;
+  if (c_hl) {
+    // value (m, n) -> hi at 2 m ldc + 16 (n / 8) + n % 8 (bf16 units), lo
+    // 8 further (the batch offset z c_bs is a multiple of 8 values)
+    uint16_t* ch = (uint16_t*)cz;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const int n = n_wg + 32 * (wave * NTW + nt) + col;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (m < M && n < N) {
+            const float x = acc[mt][nt][r];
+            const uint16_t hi = f2bf(x);
+            const long at = 2 * (long)m * ldc + 16 * (n >> 3) + (n & 7);
+            ch[at] = hi;
+            ch[at + 8] = f2bf(x - bf2f(hi));
+          }
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     const int n = n_wg + 32 * (wave * NTW + nt) + col;
@@ -950,22 +983,23 @@ __global__ void gemm_simt_kernel(const float* __restrict__ A, long lda,
   C[z * c_bs + (long)m * ldc + n] = acc;
 }
 
-template <int MT, int NTW, bool AF>
+template <int MT, int NTW, bool AF, bool HL>
 hipError_t launch_lds(const GemmArgs& g, dim3 grid, int k_chunk,
                       hipStream_t stream) {
   constexpr int lds = LdsCfg<MT, NTW, AF>::LDS;
   static bool attr = false;
   if (!attr) {
     const hipError_t e = hipFuncSetAttribute(
-        (const void*)gemm_lds_kernel<MT, NTW, AF>,
+        (const void*)gemm_lds_kernel<MT, NTW, AF, HL>,
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((gemm_lds_kernel<MT, NTW, AF>), grid, dim3(256), lds,
+  hipLaunchKernelGGL((gemm_lds_kernel<MT, NTW, AF, HL>), grid, dim3(256), lds,
                      stream, g.A, g.lda, g.a_bs, (const uint16_t*)g.B,
                      (const uint16_t*)g.B2, g.nb1, g.ldb, g.b_bs, g.C, g.ldc,
-                     g.c_bs, g.c_ks, g.M, g.N, g.K, k_chunk, g.m_split);
+                     g.c_bs, g.c_ks, g.M, g.N, g.K, k_chunk, g.m_split,
+                     g.c_hl);
   return hipGetLastError();
 }
 
@@ -1095,21 +1129,30 @@ hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
   const uint16_t* B2 = (const uint16_t*)g.B2;
   if (g.c16 && (ks != 1 || g.ntw != 0 || (!g.b_nn && g.M <= 64)))
     return hipErrorInvalidValue;  // bf16 output: tiled kernel, one K chunk
+  // pre-split layouts: LDS-staged kernel only; written C needs one K chunk
+  if ((g.a_hl && (g.ntw >= 0 || !g.a_f32)) ||
+      (g.c_hl && (g.ntw >= 0 || ks != 1 || g.c_bs % 8 != 0)))
+    return hipErrorInvalidValue;
   if (g.ntw < 0) {  // LDS-staged kernel, -ntw column tiles per wave
     const int kc = (g.K + ks - 1) / ks;
     k_chunk = (kc + 63) / 64 * 64;
     const int ntw = -g.ntw;
     dim3 grid(ks, (g.N + 128 * ntw - 1) / (128 * ntw), g.batch * g.m_split);
-#define MLA_LK(MT, NTW, AF) \
-  return launch_lds<MT, NTW, AF>(g, grid, (int)k_chunk, stream)
-#define MLA_LK_NTW(MT, AF)                    \
-  if (ntw == 1) MLA_LK(MT, 1, AF);            \
-  else MLA_LK(MT, 2, AF);
+#define MLA_LK(MT, NTW, AF, HL) \
+  return launch_lds<MT, NTW, AF, HL>(g, grid, (int)k_chunk, stream)
+#define MLA_LK_NTW(MT, AF, HL)                \
+  if (ntw == 1) MLA_LK(MT, 1, AF, HL);        \
+  else MLA_LK(MT, 2, AF, HL);
+#define MLA_LK_A(MT)                                           \
+  if (g.a_hl) { MLA_LK_NTW(MT, true, true) }                   \
+  else if (g.a_f32) { MLA_LK_NTW(MT, true, false) }            \
+  else { MLA_LK_NTW(MT, false, false) }
     if (g.M <= 32 || g.m_split > 1) {
-      if (g.a_f32) { MLA_LK_NTW(1, true) } else { MLA_LK_NTW(1, false) }
+      MLA_LK_A(1)
     } else {
-      if (g.a_f32) { MLA_LK_NTW(2, true) } else { MLA_LK_NTW(2, false) }
+      MLA_LK_A(2)
     }
+#undef MLA_LK_A
 #undef MLA_LK_NTW
 #undef MLA_LK
   }

@@ -326,16 +326,26 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
   hipStream_t s = (hipStream_t)stream;
 
   GemmArgs g1 = cq_gemm(d, T);
+  GemmArgs g2 = qcr_gemm(d, T);
+  // c_Q goes to the weight-streaming kernel of the next GEMM pre-split
+  // (hi|lo), written by the reduce of the K parts or by the GEMM itself
+  const bool cq_hl = g2.ntw < 0 && (g1.k_split > 1 || g1.ntw < 0);
   g1.A = h;
   g1.B = w_dq;
   g1.C = w.cq_parts;
+  g1.c_hl = cq_hl && g1.k_split == 1;
   MLA_TRY(launch_gemm(d, g1, s));
-  if (g1.k_split > 1)
-    MLA_TRY(launch_reduce_parts(w.cq_parts, g1.k_split, g1.c_ks,
-                                (long)T * d.d_cq, w.cq, s));
+  if (g1.k_split > 1) {
+    if (cq_hl)
+      MLA_TRY(launch_reduce_parts_hl(w.cq_parts, g1.k_split, g1.c_ks,
+                                     (long)T * d.d_cq, d.d_cq, w.cq, s));
+    else
+      MLA_TRY(launch_reduce_parts(w.cq_parts, g1.k_split, g1.c_ks,
+                                  (long)T * d.d_cq, w.cq, s));
+  }
 
-  GemmArgs g2 = qcr_gemm(d, T);
   g2.A = w.cq;
+  g2.a_hl = cq_hl;
   g2.B = w_uq;
   g2.B2 = w_qr;
   g2.C = w.qcr_parts;
@@ -606,12 +616,17 @@ mla_status mla_out(const mla_dims* dims, int32_t T, const float* o_lat,
   if (ws_bytes < w.bytes) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   GemmArgs g1 = uv_gemm(d, T);
+  GemmArgs g2 = o_gemm(d, T);
+  // v goes to the weight-streaming kernel of W_O pre-split (hi|lo), written
+  // so by the per-head GEMM
+  const bool v_hl = g1.ntw < 0 && g1.k_split == 1 && g2.ntw < 0;
   g1.A = o_lat;
   g1.B = w_uv;
   g1.C = w.v;
+  g1.c_hl = v_hl;
   MLA_TRY(launch_gemm(d, g1, s));
-  GemmArgs g2 = o_gemm(d, T);
   g2.A = w.v;
+  g2.a_hl = v_hl;
   g2.B = w_o;
   g2.C = w.u_parts;
   MLA_TRY(launch_gemm(d, g2, s));

@@ -106,6 +106,13 @@ struct GemmArgs {
   void* c16 = nullptr;  // bf16 output instead of C (tiled kernel, k_split 1)
   // 1: large-tile kernel for many rows (bf16, NT, batch 1, one K chunk)
   int big = 0;
+  // Pre-split fp32 activations ("hi|lo" layout): every 8 consecutive values
+  // of a row are stored as 8 bf16 hi = bf16(x) followed by 8 bf16
+  // lo = bf16(x - hi), 4 bytes per value like fp32.  a_hl: A is in that
+  // layout (with a_f32 set; LDS-staged kernel only); c_hl: C is written in
+  // it (LDS-staged kernel, one K chunk).
+  int a_hl = 0;
+  int c_hl = 0;
 };
 hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
                        hipStream_t stream);
@@ -119,6 +126,11 @@ void gemm_plan(const mla_dims& d, GemmArgs& g, int max_split = 16);
 // dst[i] = sum of the parts at i, for i < n.
 hipError_t launch_reduce_parts(const float* src, int nparts, long part_stride,
                                long n, float* dst, hipStream_t stream);
+// The same sum written in the pre-split hi|lo layout of rows of `ld` values
+// (ld % 8 == 0, n % ld == 0).
+hipError_t launch_reduce_parts_hl(const float* src, int nparts,
+                                  long part_stride, long n, int ld, void* dst,
+                                  hipStream_t stream);
 // acc [T][d_c + d_r] fp32 -> RoPE on the last d_r columns -> cache rows.
 hipError_t launch_append_scatter(const mla_dims& d, int T, const float* acc,
                                  int nparts, long part_stride,
