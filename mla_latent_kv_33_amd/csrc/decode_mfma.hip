@@ -7,7 +7,9 @@
 // over the key range of one split.  In the latent space every head uses the
 // same key (the 576-wide cache row) and the same value (its first 512
 // columns), so one workgroup serves all heads and each cache row crosses
-// HBM once.
+// HBM once.  (Grids too small to fill the chip, e.g. one sequence, split the
+// heads over two workgroups instead; the second read of each row is an L2
+// hit.)
 //
 // Work decomposition (one workgroup = NW waves, NW * 32 heads):
 //   * keys stream in half tiles of 32 tokens (half a 64-token cache block),
