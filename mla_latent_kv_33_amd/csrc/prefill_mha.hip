@@ -19,8 +19,10 @@
 //   query_mha_kernel     q_C (bf16) and RoPE(q_R) rows of the chunk
 //
 // prefill_mha_kernel: workgroup = (sequence, head, 128 queries), 4 waves of
-// 32 queries.  Keys stream in tiles of 64 through a two-stage LDS ring
-// (direct-to-LDS copies: K_C 16 KiB, k_R 8 KiB, V 16 KiB per tile).  The
+// 32 queries.  Keys stream in tiles of 64 by direct-to-LDS copies through
+// two-slot rings, one for keys (K_C 16 KiB + k_R 8 KiB per tile) and one for
+// values (16 KiB), so that the score MFMAs of tile j + 1 run together with
+// the value MFMAs of tile j (80 KiB: two workgroups per CU).  The
 // scores are computed transposed, S^T = K Q^T (A = key rows from LDS, B =
 // the wave's queries held in VGPRs), so each lane owns one query: its row
 // maximum needs one exchange with the lane 32 away, and its probabilities,
@@ -48,9 +50,10 @@ constexpr int PF_KS = (PF_DH + PF_DR) / 16;  // 12 k-steps of the scores
 constexpr int PF_KC_BYTES = PF_KT * PF_DH * 2;   // 16 KiB
 constexpr int PF_KR_OFF = PF_KC_BYTES;
 constexpr int PF_KR_BYTES = PF_KT * PF_DR * 2;   // 8 KiB
-constexpr int PF_V_OFF = PF_KR_OFF + PF_KR_BYTES;
-constexpr int PF_STAGE = PF_V_OFF + PF_KT * PF_DH * 2;  // 40 KiB
-constexpr int PF_LDS = 2 * PF_STAGE;
+constexpr int PF_KSLOT = PF_KR_OFF + PF_KR_BYTES;   // 24 KiB of keys
+constexpr int PF_VSLOT = PF_KT * PF_DH * 2;          // 16 KiB of values
+constexpr int PF_V_BASE = 2 * PF_KSLOT;
+constexpr int PF_LDS = PF_V_BASE + 2 * PF_VSLOT;     // 80 KiB
 constexpr float PF_SLACK = 8.0f;    // log2 headroom of P above the reference
 
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
@@ -88,11 +91,6 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
     const int32_t* __restrict__ kv_lens, int kv_cap, int n_q, int n_h,
     int ntq, int causal, float scale_log2, float* __restrict__ o_v,
     float* __restrict__ lse) {
-  // Query groups of 32 per wave.  Two would halve the LDS reads per MFMA
-  // (each key and value fragment serving both), but their queries, scores
-  // and outputs need more registers than a wave has.
-  constexpr int QG = 1;
-  constexpr int QT = PF_QW * QG;  // queries per workgroup
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const lds_char* L = (const lds_char*)lds;
   const int lane = threadIdx.x & 63;
@@ -108,39 +106,34 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
   const int bh = w / ntq, qt = w - bh * ntq;
   const int b = bh / n_h, h = bh - b * n_h;
   const int kvl = min(kv_lens[b], kv_cap);
-  const int i0 = qt * QT;
+  const int i0 = qt * PF_QW;
   auto lim_of = [&](int i) { return causal ? kvl - n_q + i : kvl - 1; };
-  // query group u of the wave: queries i0 + 32 (QG wave + u) + 0..31; the
-  // lane owns query col of every group
-  int iq[QG], lim[QG];
-#pragma unroll
-  for (int u = 0; u < QG; ++u) {
-    iq[u] = i0 + 32 * (QG * wave + u) + col;
-    lim[u] = lim_of(min(iq[u], n_q - 1));
-  }
-  const int lim_wave_min = lim_of(min(i0 + 32 * QG * wave, n_q - 1));
-  const int lim_wg_max = lim_of(min(i0 + QT - 1, n_q - 1));
+  // the lane owns query iq (wave's queries i0 + 32 wave + 0..31)
+  const int iq = i0 + 32 * wave + col;
+  const int lim = lim_of(min(iq, n_q - 1));
+  const int lim_wave_min = lim_of(min(i0 + 32 * wave, n_q - 1));
+  const int lim_wg_max = lim_of(min(i0 + PF_QW - 1, n_q - 1));
   const int ntiles = (lim_wg_max + PF_KT) / PF_KT;
 
   // queries: lane holds q[iq][16 ks + 8 g .. + 7] for every k-step
-  bf16x8 qreg[QG][PF_KS];
-#pragma unroll
-  for (int u = 0; u < QG; ++u) {
-    const uint16_t* qp = q + ((size_t)(b * n_q + min(iq[u], n_q - 1)) * n_h +
+  bf16x8 qreg[PF_KS];
+  {
+    const uint16_t* qp = q + ((size_t)(b * n_q + min(iq, n_q - 1)) * n_h +
                               h) * (PF_DH + PF_DR) + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < PF_KS; ++ks)
-      qreg[u][ks] = *(const bf16x8*)(qp + 16 * ks);
+      qreg[ks] = *(const bf16x8*)(qp + 16 * ks);
   }
 
-  // ---- copies of key tile j into stage j % 2 (10 per wave) --------------
+  // ---- copies: keys of tile j into key slot j % 2 (6 per wave), values of
+  // tile j into value slot j % 2 (4 per wave) -------------------------------
   const uint32_t l0 = lds_u32(lds);
   const size_t row0 = (size_t)b * kv_cap;
-  auto issue = [&](int j) __attribute__((always_inline)) {
-    const int t0 = j * PF_KT;
-    // rows past the keys repeat the last one (row 0 of an empty sequence)
-    const int last = max(kvl - 1 - t0, 0);
-    const uint32_t st = l0 + (j & 1) * PF_STAGE;
+  // rows past the keys repeat the last one (row 0 of an empty sequence)
+  auto last_of = [&](int j) { return max(kvl - 1 - j * PF_KT, 0); };
+  auto issue_k = [&](int j) __attribute__((always_inline)) {
+    const int t0 = j * PF_KT, last = last_of(j);
+    const uint32_t st = l0 + (j & 1) * PF_KSLOT;
     const char* kvb = (const char*)(kv + (row0 + t0) * ldkv);
     const char* rb = (const char*)(rows + (row0 + t0) * ldr);
 #pragma unroll
@@ -159,6 +152,11 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
       dma16(st + PF_KR_OFF + i * 1024, rb,
             (uint32_t)(min(r, last) * ldr * 2 + (ldr - PF_DR + 8 * ch) * 2));
     }
+  };
+  auto issue_v = [&](int j) __attribute__((always_inline)) {
+    const int t0 = j * PF_KT, last = last_of(j);
+    const uint32_t st = l0 + PF_V_BASE + (j & 1) * PF_VSLOT;
+    const char* kvb = (const char*)(kv + (row0 + t0) * ldkv);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {  // V: group (chunk group cg, tokens tg)
       const int k = 4 * c + wave;
@@ -166,7 +164,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
       const int t8 = lane >> 3;
       const int ch = (lane & 7) ^ swz(t8) ^ (2 * (tg & 1));
       const int r = 8 * tg + t8;
-      dma16(st + PF_V_OFF + 1024 * (8 * cg + tg), kvb,
+      dma16(st + 1024 * (8 * cg + tg), kvb,
             (uint32_t)(min(r, last) * ldkv * 2 +
                        (n_h * PF_DH + h * PF_DH + 8 * (8 * cg + ch)) * 2));
     }
@@ -185,41 +183,15 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
       a_v[e] = vt * 128 + 16 * ((4 * e + vc) ^ swz(vt)) + 8 * (s16 & 1);
   }
 
-  f32x16 o[QG][4];
-  float m_run[QG], l_run[QG];
-#pragma unroll
-  for (int u = 0; u < QG; ++u) {
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[u][mt][r] = 0.0f;
-    m_run[u] = -INFINITY;
-    l_run[u] = 0.0f;
-  }
-
-  issue(0);
-  // Queries and tile 0 in (a wait the compiler sees, so that it adds none of
-  // its own for the queries later, when the next tile's copies are in
-  // flight).
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  for (int j = 0; j < ntiles; ++j) {
-    wait_vm<0>();  // tile j landed (own copies), then everyone's
-    barrier();
-    if (j + 1 < ntiles) issue(j + 1);
-    const lds_char* st = L + (j & 1) * PF_STAGE;
-    const int t0 = j * PF_KT;
-
-    // S^T = K Q^T for the tile's two 32-token halves; each key fragment
-    // serves every query group of the wave
-    f32x16 s[QG][2];
-#pragma unroll
-    for (int u = 0; u < QG; ++u)
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[u][tt][r] = 0.0f;
+  // S^T = K Q^T of tile j (two 32-token halves) from key slot j % 2.
+  // Accumulator register r of lane (col, g), half tt: token
+  // 32 tt + 8 (r / 4) + 4 g + r % 4 of the tile, query iq.
+  auto scores = [&](int j, f32x16 (&s)[2]) __attribute__((always_inline)) {
+    const lds_char* st = L + (j & 1) * PF_KSLOT;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[tt][r] = 0.0f;
       const int t = 32 * tt + col;
 #pragma unroll
       for (int ks = 0; ks < PF_KS; ++ks) {
@@ -227,113 +199,158 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
             ks < 8 ? st + t * 256 + 16 * ((2 * ks + g) ^ (t & 15))
                    : st + PF_KR_OFF + t * 128 +
                          16 * ((2 * (ks - 8) + g) ^ ((t >> 1) & 7));
-        const bf16x8 kf = *(const lds_bf16x8*)a;
-#pragma unroll
-        for (int u = 0; u < QG; ++u)
-          s[u][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              kf, qreg[u][ks], s[u][tt], 0, 0, 0);
+        s[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *(const lds_bf16x8*)a, qreg[ks], s[tt], 0, 0, 0);
       }
     }
-    // Accumulator register r of lane (col, g), half tt: token
-    // t0 + 32 tt + 8 (r / 4) + 4 g + r % 4 of query iq[u].
-    const bool need_mask = t0 + PF_KT - 1 > lim_wave_min;
-    bf16x8 pb[QG][4];
+  };
+  // O^T += V^T P^T of tile j from value slot j % 2
+  f32x16 o[4];
 #pragma unroll
-    for (int u = 0; u < QG; ++u) {
-      // scores stay unscaled; the scale enters the maximum and the
-      // exponent's fused multiply-add
-      if (__builtin_expect(need_mask, 0)) {
-        // token t0 + 32 tt + 8 (r / 4) + 4 g + r % 4 visible iff
-        // 32 tt + 8 (r / 4) + r % 4 <= lim - t0 - 4 g
-        const int rel = lim[u] - t0 - 4 * g;
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * tt + 8 * (r >> 2) + (r & 3) > rel)
-              s[u][tt][r] = -INFINITY;
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[u][tt][r]);
-      mx = fmaxf(mx, lane_xor32f(mx, g)) * scale_log2;
-      // Lazy rescaling: the reference m_run moves (and O, l are rescaled)
-      // only when the tile's maximum exceeds it by more than PF_SLACK, so
-      // P <= 2^PF_SLACK.  Both lanes of a query agree (same mx); the branch
-      // is taken by the whole wave or skipped by it.
-      const bool grow = mx > m_run[u] + PF_SLACK;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = grow ? mx : m_run[u];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[u] - m_new);
-        m_run[u] = m_new;
-        l_run[u] *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[u][mt][r] *= alpha;
-      }
-      const float nm = -m_run[u];
-      // P (bf16) in k-slot order: k-step kk uses half kk / 2, registers
-      // 8 (kk % 2) .. 8 (kk % 2) + 7.
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        uint32_t pw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(
-              s[u][kk >> 1][8 * (kk & 1) + 2 * e], scale_log2, nm));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(
-              s[u][kk >> 1][8 * (kk & 1) + 2 * e + 1], scale_log2, nm));
-          const bf16x2 pp = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
-          l_run[u] = __builtin_amdgcn_fdot2_f32_bf16(
-              pp, __builtin_bit_cast(bf16x2, 0x3F803F80u), l_run[u], false);
-          pw[e] = __builtin_bit_cast(uint32_t, pp);
-        }
-        pb[u][kk] =
-            __builtin_bit_cast(bf16x8, (u32x4){pw[0], pw[1], pw[2], pw[3]});
-      }
-    }
-    // O^T += V^T P^T; each value fragment serves every query group
+    for (int r = 0; r < 16; ++r) o[mt][r] = 0.0f;
+  auto values = [&](int j, const bf16x8 (&pb)[4]) __attribute__((always_inline)) {
+    const lds_char* st = L + PF_V_BASE + (j & 1) * PF_VSLOT;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int off = PF_V_OFF + a_v[mt & 1] + 8192 * (mt >> 1) + 2048 * kk;
+        const int off = a_v[mt & 1] + 8192 * (mt >> 1) + 2048 * kk;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4*)(st + off));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4*)(st + ((off ^ 32) + 1024)));
         const bf16x8 vf = __builtin_bit_cast(
             bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int u = 0; u < QG; ++u)
-          o[u][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              vf, pb[u][kk], o[u][mt], 0, 0, 0);
+        o[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[kk], o[mt], 0,
+                                                        0, 0);
       }
-    wait_lgkm0();  // this stage's reads done before it is refilled
-  }
-
-  // ---- output: O^T register r of lane (col, g), dv tile mt: value column
-  // 32 mt + 8 (r / 4) + 4 g + r % 4 of query iq[u].
+  };
+  // Softmax of tile j against a lazily moved reference m_run: it moves (and
+  // l, O are rescaled by the returned alpha) only when the tile's maximum
+  // exceeds it by more than PF_SLACK, so P <= 2^PF_SLACK.  Both lanes of a
+  // query agree (same mx); the rescale branch is taken by the whole wave or
+  // skipped by it.  Scores stay unscaled; the scale enters the maximum and
+  // the exponent's fused multiply-add.  P (bf16) comes out in k-slot order:
+  // k-step kk uses half kk / 2, registers 8 (kk % 2) .. 8 (kk % 2) + 7.
+  // A tile that does not exist (live false) is masked whole: P = 0 and the
+  // state stays as it is.
+  float m_run = -INFINITY, l_run = 0.0f;
+  auto softmax = [&](int j, bool live, f32x16 (&s)[2], bf16x8 (&pb)[4],
+                     float& alpha) __attribute__((always_inline)) -> bool {
+    const int t0 = j * PF_KT;
+    if (__builtin_expect(t0 + PF_KT - 1 > lim_wave_min || !live, 0)) {
+      // token t0 + 32 tt + 8 (r / 4) + 4 g + r % 4 visible iff
+      // 32 tt + 8 (r / 4) + r % 4 <= lim - t0 - 4 g
+      const int rel = live ? lim - t0 - 4 * g : -1;
 #pragma unroll
-  for (int u = 0; u < QG; ++u) {
-    const float l_tot = l_run[u] + lane_xor32f(l_run[u], g);
-    if (iq[u] < n_q) {
-      const float inv = 1.0f / l_tot;
-      float* dst = o_v + ((size_t)(b * n_q + iq[u]) * n_h + h) * PF_DH + 4 * g;
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * tt + 8 * (r >> 2) + (r & 3) > rel) s[tt][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[tt][r]);
+    mx = fmaxf(mx, lane_xor32f(mx, g)) * scale_log2;
+    const bool grow = mx > m_run + PF_SLACK;
+    const bool any = __builtin_amdgcn_ballot_w64(grow) != 0;
+    // no branch here, so that this code shares a block with the value
+    // MFMAs that follow it in the loop
+    const float m_new = grow ? mx : m_run;
+    alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+    m_run = m_new;
+    l_run *= alpha;
+    const float nm = -m_run;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      uint32_t pw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(
+            s[kk >> 1][8 * (kk & 1) + 2 * e], scale_log2, nm));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(
+            s[kk >> 1][8 * (kk & 1) + 2 * e + 1], scale_log2, nm));
+        const bf16x2 pp = __builtin_convertvector((f32x2){p0, p1}, bf16x2);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(
+            pp, __builtin_bit_cast(bf16x2, 0x3F803F80u), l_run, false);
+        pw[e] = __builtin_bit_cast(uint32_t, pp);
+      }
+      pb[kk] = __builtin_bit_cast(bf16x8, (u32x4){pw[0], pw[1], pw[2], pw[3]});
+    }
+    return any;
+  };
+
+  // ---- pipeline -----------------------------------------------------------
+  // Iteration j: keys of tile j + 1 and values of tile j are in LDS, P of
+  // tile j in registers.  The score MFMAs of tile j + 1 and the value MFMAs
+  // of tile j are independent, so the softmax of tile j + 1 overlaps the
+  // value MFMAs; O is rescaled (rarely) after them.  Copies: keys of tile
+  // j + 2 into the key slot tile j used, values of tile j + 1 into the value
+  // slot tile j - 1 used; both are free after the iteration's barrier.
+  bf16x8 pb[4];
+  issue_k(0);
+  issue_v(0);
+  if (ntiles > 1) issue_k(1);
+  // queries and every copy in (a wait the compiler sees, so that it adds
+  // none of its own for the queries later, when copies are in flight)
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  barrier();
+  {
+    f32x16 s[2];
+    scores(0, s);
+    float a0;
+    softmax(0, true, s, pb, a0);  // O is still zero: no rescale
+  }
+  wait_lgkm0();  // key slot 0 read, before iteration 0 refills it
+  // A moved reference (rare) rescales O before the next value MFMAs: O
+  // then holds the tiles up to the previous one, all against the old
+  // reference.
+  bool rescale = false;
+  float alpha = 1.0f;
+  for (int j = 0; j < ntiles; ++j) {
+    wait_vm<0>();  // own copies of keys j + 1, values j landed
+    barrier();     // everyone's, and every read of the slots refilled next
+    if (rescale) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *(f32x4*)(dst + 32 * mt + 8 * i) =
-              (f32x4){o[u][mt][4 * i] * inv, o[u][mt][4 * i + 1] * inv,
-                      o[u][mt][4 * i + 2] * inv, o[u][mt][4 * i + 3] * inv};
-      if (g == 0 && lse)
-        lse[(size_t)(b * n_q + iq[u]) * n_h + h] =
-            (m_run[u] + __log2f(l_tot)) * 0.69314718055994531f;
+        for (int r = 0; r < 16; ++r) o[mt][r] *= alpha;
     }
+    if (j + 2 < ntiles) issue_k(j + 2);
+    if (j + 1 < ntiles) issue_v(j + 1);
+    // The last iteration's scores read a stale key slot and are masked
+    // whole, so that every iteration runs the same code: the softmax of
+    // tile j + 1 in one block with the value MFMAs of tile j.
+    f32x16 s[2];
+    scores(j + 1, s);
+    bf16x8 pn[4];
+    rescale = softmax(j + 1, j + 1 < ntiles, s, pn, alpha);
+    values(j, pb);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) pb[kk] = pn[kk];
+    wait_lgkm0();  // this iteration's LDS reads done before slots refill
+  }
+
+  // ---- output: O^T register r of lane (col, g), dv tile mt: value column
+  // 32 mt + 8 (r / 4) + 4 g + r % 4 of query iq.
+  const float l_tot = l_run + lane_xor32f(l_run, g);
+  if (iq < n_q) {
+    const float inv = 1.0f / l_tot;
+    float* dst = o_v + ((size_t)(b * n_q + iq) * n_h + h) * PF_DH + 4 * g;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *(f32x4*)(dst + 32 * mt + 8 * i) =
+            (f32x4){o[mt][4 * i] * inv, o[mt][4 * i + 1] * inv,
+                    o[mt][4 * i + 2] * inv, o[mt][4 * i + 3] * inv};
+    if (g == 0 && lse)
+      lse[(size_t)(b * n_q + iq) * n_h + h] =
+          (m_run + __log2f(l_tot)) * 0.69314718055994531f;
   }
 }
 
