@@ -356,7 +356,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
 
 // q_mha[t][h] = [bf16(q_C[t, h]) | bf16(RoPE_pos(q_R[t, h]))] from the
 // K-split parts of the query up-projection (q_C of head h at column h d_h,
-// q_R of head h at n_h d_h + h d_r).
+// q_R of head h at n_h d_h + h d_r).  A thread handles 4 consecutive q_C
+// values, or 4 consecutive RoPE pairs (j, j + d_r / 2): 16-byte loads and
+// 8-byte stores (d_h % 4 == 0, d_r % 8 == 0, lda % 4 == 0).
 __global__ __launch_bounds__(256) void query_mha_kernel(
     const float* __restrict__ parts, int nparts, long part_stride, long lda,
     int n_h, int d_h, int d_r, const int32_t* __restrict__ pos,
@@ -367,27 +369,42 @@ __global__ __launch_bounds__(256) void query_mha_kernel(
   const int p = pos[t];
   const bool ok = p >= 0 && p < max_pos;
   const float* src = parts + (size_t)t * lda;
-  const int per_head = d_h + half;
+  const int per_head = d_h / 4 + half / 4;
+  auto sum4 = [&](long c) {
+    f32x4 x = *(const f32x4*)(src + c);
+    for (int pp = 1; pp < nparts; ++pp) {
+      const f32x4 y = *(const f32x4*)(src + pp * part_stride + c);
+      x[0] += y[0]; x[1] += y[1]; x[2] += y[2]; x[3] += y[3];
+    }
+    return x;
+  };
   for (int i = blockIdx.y * 256 + threadIdx.x; i < n_h * per_head;
        i += gridDim.y * 256) {
     const int hh = i / per_head, j = i - hh * per_head;
     uint16_t* dst = q_out + ((size_t)t * n_h + hh) * (d_h + d_r);
-    if (j < d_h) {
-      float x = 0.0f;
-      for (int pp = 0; pp < nparts; ++pp) x += src[pp * part_stride + hh * d_h + j];
-      dst[j] = f2bf(x);
+    if (j < d_h / 4) {
+      const f32x4 x = sum4((long)hh * d_h + 4 * j);
+      *(uint2*)(dst + 4 * j) =
+          make_uint2(pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3]));
     } else {
-      const int jj = j - d_h;
+      const int jj = 4 * (j - d_h / 4);
       const long c0 = (long)n_h * d_h + hh * d_r + jj;
-      float x1 = 0.0f, x2 = 0.0f;
-      for (int pp = 0; pp < nparts; ++pp) {
-        x1 += src[pp * part_stride + c0];
-        x2 += src[pp * part_stride + c0 + half];
+      const f32x4 x1 = sum4(c0), x2 = sum4(c0 + half);
+      f32x4 c = {NAN, NAN, NAN, NAN}, sn = {NAN, NAN, NAN, NAN};
+      if (ok) {
+        c = *(const f32x4*)(rcos + (long)p * half + jj);
+        sn = *(const f32x4*)(rsin + (long)p * half + jj);
       }
-      const float c = ok ? rcos[(long)p * half + jj] : NAN;
-      const float s = ok ? rsin[(long)p * half + jj] : NAN;
-      dst[d_h + jj] = f2bf(x1 * c - x2 * s);
-      dst[d_h + jj + half] = f2bf(x1 * s + x2 * c);
+      f32x4 y1, y2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y1[e] = x1[e] * c[e] - x2[e] * sn[e];
+        y2[e] = x1[e] * sn[e] + x2[e] * c[e];
+      }
+      *(uint2*)(dst + d_h + jj) =
+          make_uint2(pack_bf2(y1[0], y1[1]), pack_bf2(y1[2], y1[3]));
+      *(uint2*)(dst + d_h + jj + half) =
+          make_uint2(pack_bf2(y2[0], y2[1]), pack_bf2(y2[2], y2[3]));
     }
   }
 }
@@ -443,7 +460,9 @@ hipError_t launch_query_mha(const mla_dims& d, int T, const float* parts,
                             const float* rope_sin, int max_pos, void* q_out,
                             hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  const int items = d.n_h * (d.d_h + d.d_r / 2);
+  if (d.d_h % 4 != 0 || d.d_r % 8 != 0 || lda % 4 != 0 || part_stride % 4)
+    return hipErrorInvalidValue;
+  const int items = d.n_h * (d.d_h / 4 + d.d_r / 8);
   const dim3 grid(T, (items + 255) / 256);
   hipLaunchKernelGGL(query_mha_kernel, grid, dim3(256), 0, stream, parts,
                      nparts, part_stride, lda, d.n_h, d.d_h, d.d_r, pos,
