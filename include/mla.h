@@ -241,9 +241,10 @@ int32_t mla_decode_auto_splits(const mla_dims* dims, int32_t B, int32_t n_q,
  *   over keys t <= kv_lens[b] - n_q + i (causal != 0) or all keys; lse as in
  *   mla_decode.  q [B][n_q][n_h][d_h + d_r] bf16 (mla_query_mha), the cache
  *   and block table as in mla_decode, kv_lens[b] >= n_q, max_kv_len >= every
- *   kv_lens[b].  Device-side values (kv_lens, block ids) are trusted: a
- *   violation yields unspecified outputs, never an access outside the
- *   cache, table or workspace (lengths are clamped to max_kv_len).
+ *   kv_lens[b].  Device-side values are trusted as in mla_decode: block ids
+ *   must name blocks of the pool; a kv_lens[b] outside [n_q, max_kv_len]
+ *   yields unspecified outputs but no access past the table or workspace
+ *   (lengths are clamped to max_kv_len).
  *   ws: mla_prefill_mha_workspace_bytes(dims, B, max_kv_len) bytes (the
  *   gathered rows and bf16 k_C / v_C of every head: about
  *   max(B max_kv_len, 128) (d_c + d_r + 4 n_h d_h) bytes).
