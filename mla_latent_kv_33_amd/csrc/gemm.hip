@@ -8,14 +8,19 @@
 // hi = bf16(x), lo = bf16(x - hi), i.e. two MFMAs per fragment; this keeps
 // those intermediates at ~16 significant bits instead of 8.
 //
-// Kernels:
-//   * skinny (M <= 64, NT): decode batches.  The weight stream dominates, so
-//     B fragments are loaded straight from HBM into registers in MFMA
-//     layout; the four waves of a workgroup interleave their 16-wide k-steps
-//     so that together they read each weight row in 128-byte runs, and sum
-//     their partial tiles through LDS.  Workgroups may further split K; each
-//     K chunk writes its own partial C (summed by the consumer), which keeps
-//     results deterministic.
+// Kernels (gemm_plan picks one):
+//   * lds (M <= 64, NT, K % 64 == 0): decode batches, bound by streaming the
+//     weights once.  Activation rows and 128 or 256 weight rows arrive in
+//     64-k steps by direct-to-LDS copies into a 3-4 slot ring; workgroups
+//     split K, each K chunk writing its own partial C (summed by the
+//     consumer), which keeps results deterministic.  It also reads and
+//     writes fp32 activations pre-split into bf16 hi|lo pairs.
+//   * stream (M <= 64, other K % 16 == 0): weights straight into registers.
+//   * skinny (M <= 64, NT): general fallback.  B fragments are loaded
+//     straight from HBM into registers in MFMA layout; the four waves of a
+//     workgroup interleave their 16-wide k-steps so that together they read
+//     each weight row in 128-byte runs, and sum their partial tiles through
+//     LDS.
 //   * tiled (any M, NT or NN): 128x128x32 tiles staged through padded LDS,
 //     2x2 waves of 64x64; NN weights are read with ds_read_b64_tr_b16 so the
 //     MFMA still sees k-contiguous B fragments.
