@@ -154,3 +154,94 @@ def test_header_cites_pages_and_names_callers():
     assert "MLA：潜在表示压缩与解耦 RoPE" in text
     for fn in ("mla_append_cache", "mla_absorb_q", "mla_decode", "mla_out"):
         assert fn in text
+
+
+def call_rmsnorm(dims, T=4, ws=FAKE, ws_bytes=1 << 30, h=FAKE, eps=1e-6,
+                 norm_w=FAKE, max_pos=16, max_blocks=1, num_blocks=1):
+    return B.lib().mla_append_cache_rmsnorm(
+        ctypes.byref(dims), T, h, FAKE, FAKE, FAKE, FAKE, norm_w, eps, FAKE,
+        FAKE, max_pos, FAKE, max_blocks, FAKE, num_blocks, ws, ws_bytes,
+        None)
+
+
+def test_append_rmsnorm_validation():
+    d = ds_dims()
+    assert call_rmsnorm(ds_dims(d_r=63)) == SHAPE
+    assert call_rmsnorm(d, T=-1) == SHAPE
+    assert call_rmsnorm(d, eps=-1.0) == SHAPE
+    assert call_rmsnorm(d, eps=float("nan")) == SHAPE
+    assert call_rmsnorm(d, max_blocks=0) == SHAPE
+    assert call_rmsnorm(ds_dims(d=5121)) == UNSUP
+    assert call_rmsnorm(d, T=0) == OK          # no-op
+    assert call_rmsnorm(d, norm_w=None) == NULL
+    assert call_rmsnorm(d, ws=None) == WS
+    assert call_rmsnorm(d, ws_bytes=16) == WS
+
+
+def test_prefill_workspace_bytes():
+    d = ds_dims()
+    row, kvw = (512 + 64) * 2, 2 * 128 * 128 * 2
+    big = B.mla_prefill_mha_workspace_bytes(d, 8, 10240)
+    assert big >= 8 * 10240 * (row + kvw)
+    assert big < 8 * 10240 * (row + kvw) + 4096
+    # at least 128 rows (the up-projection GEMM's bf16 output)
+    assert B.mla_prefill_mha_workspace_bytes(d, 1, 37) >= 128 * (row + kvw)
+    assert B.mla_prefill_mha_workspace_bytes(d, 0, 37) == 0
+    assert B.mla_prefill_mha_workspace_bytes(ds_dims(d_r=63), 1, 37) == 0
+
+
+def call_prefill(dims, B_=2, n_q=4, max_kv=100, max_blocks=2, num_blocks=4,
+                 ws=FAKE, ws_bytes=1 << 12, q=FAKE, w_uv=FAKE, causal=1):
+    return B.lib().mla_prefill_mha(
+        ctypes.byref(dims), B_, n_q, q, FAKE, num_blocks, FAKE, max_blocks,
+        FAKE, max_kv, causal, FAKE, w_uv, FAKE, None, ws, ws_bytes, None)
+
+
+def test_prefill_mha_validation():
+    d = ds_dims()
+    lib = B.lib()
+    assert lib.mla_prefill_mha(None, 1, 1, *([None] * 2), 1, None, 1, None,
+                               1, 1, None, None, None, None, None, 0,
+                               None) == NULL
+    assert call_prefill(d, B_=-1) == SHAPE
+    assert call_prefill(d, n_q=-1) == SHAPE
+    assert call_prefill(d, n_q=200, max_kv=100) == SHAPE     # n_q > kv
+    assert call_prefill(d, max_kv=0, n_q=0) == SHAPE
+    assert call_prefill(d, max_blocks=1) == SHAPE            # 100 > 64
+    assert call_prefill(d, num_blocks=0) == SHAPE
+    assert call_prefill(ds_dims(dtype=B.MLA_F32)) == UNSUP   # bf16 only
+    assert call_prefill(ds_dims(d_h=64)) == UNSUP
+    assert call_prefill(d, B_=0) == OK                       # no-op
+    assert call_prefill(d, n_q=0) == OK
+    assert call_prefill(d, q=None) == NULL
+    assert call_prefill(d, w_uv=None) == NULL
+    assert call_prefill(d, ws=None) == WS
+    assert call_prefill(d, ws_bytes=1 << 12) == WS           # far too small
+
+
+def test_query_mha_and_out_values_validation():
+    d = ds_dims()
+    lib = B.lib()
+    args = [FAKE] * 6
+    # (dims, T, h, pos, w_dq, w_uq, w_qr, cos, sin, max_pos, q, ws, bytes, s)
+    assert lib.mla_query_mha(ctypes.byref(d), 4, *args, FAKE, 16, FAKE, None,
+                             0, None) == WS
+    assert lib.mla_query_mha(ctypes.byref(d), 4, *args, FAKE, 16, FAKE, FAKE,
+                             16, None) == WS
+    assert lib.mla_query_mha(ctypes.byref(d), 4, None, *args[1:], FAKE, 16,
+                             FAKE, FAKE, 1 << 30, None) == NULL
+    assert lib.mla_query_mha(ctypes.byref(d), 4, *args, FAKE, 0, FAKE, FAKE,
+                             1 << 30, None) == SHAPE          # max_pos
+    assert lib.mla_query_mha(ctypes.byref(ds_dims(dtype=B.MLA_F32)), 4,
+                             *args, FAKE, 16, FAKE, FAKE, 1 << 30,
+                             None) == UNSUP
+    assert lib.mla_query_mha(ctypes.byref(d), 0, *([None] * 7), 16, None,
+                             None, 0, None) == OK
+    assert lib.mla_out_values(ctypes.byref(d), 4, FAKE, FAKE, FAKE, FAKE, 16,
+                              None) == WS
+    assert lib.mla_out_values(ctypes.byref(d), 4, None, FAKE, FAKE, FAKE,
+                              1 << 30, None) == NULL
+    assert lib.mla_out_values(ctypes.byref(d), -1, FAKE, FAKE, FAKE, FAKE,
+                              1 << 30, None) == SHAPE
+    assert lib.mla_out_values(ctypes.byref(d), 0, None, None, None, None, 0,
+                              None) == OK
