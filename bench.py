@@ -168,9 +168,9 @@ def main():
     layer = flow.make_layer(wl)
     st = flow.prepare(wl, layer)
     stream = torch.cuda.current_stream()
-    n_split = B.mla_decode_auto_splits(layer.cdims, wl.batch, wl.n_q,
-                                       st.max_kv_len) if not wl.n_split \
-        else wl.n_split
+    # 0: the library's automatic splits (balanced per sequence for up to
+    # 256 query rows on the matrix-core path)
+    n_split = wl.n_split
     mha = args.path == "mha"
     # allocates outputs and workspaces once
     out = flow.run_prefill_mha(st) if mha else flow.run_step(st)
@@ -294,7 +294,10 @@ def main():
         "config": {
             "workload": workload_text(wl, mha),
             "batch": wl.batch, "context": wl.ctx[0], "kv_len": int(kv[0]),
-            "n_q": wl.n_q, "n_split": None if mha else int(n_split),
+            "n_q": wl.n_q,
+            "n_split": None if mha else (
+                int(n_split) if n_split > 0 else
+                "balanced" if n_split == B.MLA_SPLIT_BALANCED else "auto"),
             "block_size": 64, "path": args.path,
         },
         "roofline": {

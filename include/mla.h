@@ -196,13 +196,21 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
  *   max_kv_len  host upper bound of kv_lens (sizes the split plan)
  *   causal      must be 1 when n_q > 1 (the only defined rule); ignored for
  *               n_q = 1
- *   n_split     key chunks per (b, query); 0 lets the library choose;
- *               must not exceed ceil(max_kv_len / block_size)
+ *   n_split     key chunks per (b, query); 0 lets the library choose one
+ *               count for every row (mla_decode_auto_splits);
+ *               MLA_SPLIT_BALANCED gives each query row a count
+ *               proportional to its visible keys, planned on the device
+ *               from kv_lens (for batches of uneven lengths: at most 256
+ *               workgroups, the longest chunk as short as that allows;
+ *               used for 2 .. 256 query rows on the bf16 matrix-core path
+ *               with d_c = 512, d_r = 64, block_size = 64, otherwise as
+ *               0); must not exceed ceil(max_kv_len / block_size)
  *   o_lat       [B][n_q][n_h][d_c] fp32 output
  *   lse         [B][n_q][n_h] fp32 output, may be NULL
  *   ws          at least mla_decode_workspace_bytes(dims, B, n_q,
  *               max_kv_len, n_split)
  * ---------------------------------------------------------------------- */
+#define MLA_SPLIT_BALANCED (-1)
 size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t B,
                                   int32_t n_q, int32_t max_kv_len,
                                   int32_t n_split);

@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 
 MLA_F32 = 0
 MLA_BF16 = 1
+# n_split of mla_decode: splits proportional to each query row's keys
+MLA_SPLIT_BALANCED = -1
 
 
 class MlaError(RuntimeError):

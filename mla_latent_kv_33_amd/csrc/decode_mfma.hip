@@ -205,6 +205,92 @@ __device__ __forceinline__ void copy_group(const HC& hc, int wave, int g,
   }
 }
 
+// ---- balanced splits ------------------------------------------------------
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+struct BalWork {
+  int row, split, count, slot0;  // row < 0: no work for this workgroup
+};
+
+// Work item w of the balanced plan (see DecodeBalance): query row r has
+// nb_r visible blocks (at least one), the chunk c is the smallest value >=
+// max(BAL_MIN_CHUNK, ceil(sum nb / slots)) with sum ceil(nb_r / c) <= slots
+// (binary search; c = max nb gives one split per row, rows <= slots), and
+// row r's ceil(nb_r / c) splits take consecutive items.  Every wave
+// computes the same values; lane l holds rows l, l + 64, ...
+__device__ BalWork balanced_work(const int32_t* __restrict__ kv_lens,
+                                 int rows, int n_q, int slots, int w,
+                                 int lane) {
+  constexpr int RPL = BAL_SLOTS / 64;
+  int nb[RPL];
+  int total = 0, nbmax = 0;
+#pragma unroll
+  for (int c = 0; c < RPL; ++c) {
+    const int r = 64 * c + lane;
+    int v = 0;
+    if (r < rows) {
+      const int b = r / n_q, qi = r - b * n_q;
+      v = max((kv_lens[b] - n_q + qi + 1 + BS - 1) / BS, 1);
+    }
+    nb[c] = v;
+    total += v;
+    nbmax = max(nbmax, v);
+  }
+  total = wave_sum_i(total);
+  nbmax = wave_max_i(nbmax);
+  auto items = [&](int ch) {
+    int n = 0;
+#pragma unroll
+    for (int c = 0; c < RPL; ++c) n += (nb[c] + ch - 1) / ch;
+    return wave_sum_i(n);
+  };
+  int lo = max(BAL_MIN_CHUNK, (total + slots - 1) / slots);
+  if (items(lo) > slots) {
+    int hi = max(lo, nbmax);  // items(hi) = rows <= slots
+    while (hi - lo > 1) {     // items(lo) > slots >= items(hi)
+      const int mid = lo + (hi - lo) / 2;
+      if (items(mid) <= slots)
+        hi = mid;
+      else
+        lo = mid;
+    }
+    lo = hi;
+  }
+  const int chunk = lo;
+  int base = 0;
+#pragma unroll
+  for (int c = 0; c < RPL; ++c) {
+    const int n = (nb[c] + chunk - 1) / chunk;  // 0 past the last row
+    const int incl = wave_incl_scan(n, lane);
+    const int tot = __shfl(incl, 63);
+    if (w < base + tot) {
+      const unsigned long long m = __ballot(base + incl > w);
+      const int L = __builtin_ctzll(m);
+      const int cnt = __shfl(n, L), slot0 = base + __shfl(incl, L) - cnt;
+      return {64 * c + L, w - slot0, cnt, slot0};
+    }
+    base += tot;
+  }
+  return {-1, 0, 0, 0};
+}
+
 template <int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(1, 1))) void
@@ -212,7 +298,8 @@ decode_mfma_kernel(
     const uint16_t* __restrict__ q, const char* __restrict__ cache,
     const int32_t* __restrict__ block_table, int max_blocks,
     const int32_t* __restrict__ kv_lens, int n_q, int n_h, int n_split,
-    float scale_log2, float* __restrict__ o_part, float* __restrict__ m_part,
+    int rows, int slots, int2* __restrict__ plan, float scale_log2,
+    float* __restrict__ o_part, float* __restrict__ m_part,
     float* __restrict__ l_part, float* __restrict__ o_final,
     float* __restrict__ lse_final) {
   using C = Cfg<NW>;
@@ -225,10 +312,26 @@ decode_mfma_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 5;     // lane half
   const int col = lane & 31;   // head within a 32-head tile
-  const int bq = blockIdx.x;   // b * n_q + i
-  const int split = blockIdx.y;
   const int hbase = blockIdx.z * C::HEADS;
   const int head = hbase + wave * 32 + col;  // head whose scores this lane owns
+  // (query row, split) of this workgroup; the row's splits fill partial
+  // slots slot0 .. slot0 + n_split - 1
+  int bq, split, slot0;
+  if (plan) {
+    const BalWork bw = balanced_work(kv_lens, rows, n_q, slots, blockIdx.x,
+                                     lane);
+    if (bw.row < 0) return;  // no work left (whole workgroup, no barrier yet)
+    bq = __builtin_amdgcn_readfirstlane(bw.row);
+    split = __builtin_amdgcn_readfirstlane(bw.split);
+    n_split = __builtin_amdgcn_readfirstlane(bw.count);
+    slot0 = __builtin_amdgcn_readfirstlane(bw.slot0);
+    if (split == 0 && blockIdx.z == 0 && threadIdx.x == 0)
+      plan[bq] = make_int2(slot0, n_split);
+  } else {
+    bq = blockIdx.x;   // b * n_q + i
+    split = blockIdx.y;
+    slot0 = bq * n_split;
+  }
   const int b = bq / n_q;
   const int qi = bq - b * n_q;
 
@@ -238,7 +341,7 @@ decode_mfma_kernel(
   // Split j covers blocks [j nblk / n_split, (j + 1) nblk / n_split).
   const int blk0 = (int)((long)split * nblk / n_split);
   const int blk1 = (int)((long)(split + 1) * nblk / n_split);
-  const size_t row_base = ((size_t)bq * n_split + split) * n_h;
+  const size_t row_base = ((size_t)slot0 + split) * n_h;
 
   if (blk0 >= blk1) {  // empty split: no keys, weight zero in the combine
     if (g == 0) {
@@ -640,8 +743,7 @@ decode_mfma_kernel(
     // through the first half-tile buffer: no copy is in flight and every
     // wave is past its last read of it (flag barrier above).
     uint16_t* const o16 = (uint16_t*)o_part;
-    float* const sc_part =
-        (float*)(o16 + (size_t)gridDim.x * n_split * n_h * DC);
+    float* const sc_part = (float*)(o16 + (size_t)slots * n_h * DC);
     float* const mx = (float*)lds;  // [NW][HEADS]
     float inv[NW];
 #pragma unroll
@@ -694,8 +796,9 @@ template <int NW>
 hipError_t launch_nw(const mla_dims& d, int B, int n_q, const void* q,
                      const void* cache, const int32_t* block_table,
                      int max_blocks, const int32_t* kv_lens, int n_split,
-                     float* o_part, float* m_part, float* l_part,
-                     float* o_final, float* lse_final, hipStream_t stream) {
+                     const DecodeBalance& bal, float* o_part, float* m_part,
+                     float* l_part, float* o_final, float* lse_final,
+                     hipStream_t stream) {
   const float scale_log2 =
       (float)(1.4426950408889634 / __builtin_sqrt((double)(d.d_h + d.d_r)));
   constexpr size_t lds = Cfg<NW>::LDS;
@@ -707,11 +810,15 @@ hipError_t launch_nw(const mla_dims& d, int B, int n_q, const void* q,
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  dim3 grid(B * n_q, n_split, d.n_h / (NW * 32));
+  const int rows = B * n_q;
+  const int slots = bal.plan ? BAL_SLOTS : rows * n_split;
+  const dim3 grid(bal.plan ? BAL_SLOTS : rows, bal.plan ? 1 : n_split,
+                  d.n_h / (NW * 32));
   hipLaunchKernelGGL(decode_mfma_kernel<NW>, grid, dim3(NW * 64), lds, stream,
                      (const uint16_t*)q, (const char*)cache, block_table,
-                     max_blocks, kv_lens, n_q, d.n_h, n_split, scale_log2,
-                     o_part, m_part, l_part, o_final, lse_final);
+                     max_blocks, kv_lens, n_q, d.n_h, n_split, rows, slots,
+                     bal.plan, scale_log2, o_part, m_part, l_part, o_final,
+                     lse_final);
   return hipGetLastError();
 }
 
@@ -727,20 +834,21 @@ hipError_t launch_decode_mfma(const mla_dims& d, int B, int n_q,
                               const void* q, const void* cache,
                               const int32_t* block_table, int max_blocks,
                               const int32_t* kv_lens, int n_split,
-                              float* o_part, float* m_part,
-                              float* l_part, float* o_final, float* lse_final,
-                              hipStream_t stream) {
-#define MLA_DECODE_ARGS                                                    \
-  d, B, n_q, q, cache, block_table, max_blocks, kv_lens, n_split, o_part, \
-      m_part, l_part, o_final, lse_final, stream
+                              const DecodeBalance& balance, float* o_part,
+                              float* m_part, float* l_part, float* o_final,
+                              float* lse_final, hipStream_t stream) {
+  if (balance.plan && B * n_q > BAL_SLOTS) return hipErrorInvalidValue;
+#define MLA_DECODE_ARGS                                                     \
+  d, B, n_q, q, cache, block_table, max_blocks, kv_lens, n_split, balance, \
+      o_part, m_part, l_part, o_final, lse_final, stream
   if (d.n_h % 128 == 0) {
     // Small grids (a batch of one or two sequences): two workgroups of 64
     // heads per (query row, split), so that twice the compute units stream
     // the cache and each loads half the queries (B = 1 at 4K context: 32.6
     // -> 27.5 us).  Per-head arithmetic is unchanged, so the results are
     // identical.
-    if ((long)B * n_q * n_split * (d.n_h / 128) <= 128)
-      return launch_nw<2>(MLA_DECODE_ARGS);
+    const long wgs = balance.plan ? balance.est_wgs : (long)B * n_q * n_split;
+    if (wgs * (d.n_h / 128) <= 128) return launch_nw<2>(MLA_DECODE_ARGS);
     return launch_nw<4>(MLA_DECODE_ARGS);
   }
   if (d.n_h == 64) return launch_nw<2>(MLA_DECODE_ARGS);

@@ -151,19 +151,29 @@ __global__ __launch_bounds__(NT) void decode_simt_kernel(
 // the loads in flight.
 template <int NB, bool P16, int TPH, int CS>
 __global__ __launch_bounds__(256) void combine_rows_kernel(
-    int n_h, int d_c, int n_split, const float* __restrict__ o_part,
-    const float* __restrict__ m_part, const float* __restrict__ l_part,
-    float* __restrict__ o_lat, float* __restrict__ lse) {
+    int n_h, int d_c, int n_split, int slots, const int2* __restrict__ plan,
+    const float* __restrict__ o_part, const float* __restrict__ m_part,
+    const float* __restrict__ l_part, float* __restrict__ o_lat,
+    float* __restrict__ lse) {
   constexpr int VW = P16 ? 8 : 4;  // columns per vector
   const int bq = blockIdx.x;
   const int h = blockIdx.y * (256 / TPH) + (threadIdx.x / TPH);
   const int q = threadIdx.x % TPH;
   if (h >= n_h) return;
+  // the row's splits: slots slot0 .. slot0 + n_split - 1 (balanced plan, or
+  // n_split per row)
+  int slot0 = bq * n_split;
+  if (plan) {
+    const int2 pl = plan[bq];
+    slot0 = pl.x;
+    n_split = pl.y;
+    if (n_split == 1) return;  // written final by the decode
+  }
   const int cvn = d_c / VW;
-  const size_t row0 = (size_t)bq * n_split * n_h + h;  // + j n_h
+  const size_t row0 = (size_t)slot0 * n_h + h;  // + j n_h
   const uint16_t* const p16 = (const uint16_t*)o_part;
   const float* const sc_part =
-      (const float*)(p16 + (size_t)gridDim.x * n_split * n_h * d_c);
+      (const float*)(p16 + (size_t)slots * n_h * d_c);
   float M = -INFINITY, L = 0.0f;
   f32x4 acc[NB][VW / 4];
 #pragma unroll
@@ -386,8 +396,11 @@ hipError_t launch_decode_simt(const mla_dims& d, int B, int n_q,
 hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
                           const float* o_part, bool f16_parts,
                           const float* m_part, const float* l_part,
-                          float* o_lat, float* lse, hipStream_t stream) {
+                          float* o_lat, float* lse, hipStream_t stream,
+                          const int2* plan, int slots) {
   if (rows <= 0) return hipSuccess;
+  if (plan && !f16_parts) return hipErrorInvalidValue;
+  if (!plan) slots = rows * n_split;
   // Many rows: 16 threads per head (16 heads per workgroup), 4 splits per
   // chunk.  Few rows: 64 threads per head, 16 splits per chunk, so that a
   // small batch still spreads over a few hundred waves.
@@ -395,8 +408,8 @@ hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
 #define MLA_CMB(NB, P16, TPH, CS)                                             \
   hipLaunchKernelGGL((combine_rows_kernel<NB, P16, TPH, CS>),                  \
                      dim3(rows, (d.n_h + 256 / TPH - 1) / (256 / TPH)),        \
-                     dim3(256), 0, stream, d.n_h, d.d_c, n_split, o_part,     \
-                     m_part, l_part, o_lat, lse)
+                     dim3(256), 0, stream, d.n_h, d.d_c, n_split, slots,      \
+                     plan, o_part, m_part, l_part, o_lat, lse)
   if (f16_parts) {
     if (d.d_c % 8 != 0 || d.d_c > 8 * 16 * 4) return hipErrorInvalidValue;
     if (wide)

@@ -168,11 +168,30 @@ int auto_splits(const mla_dims& d, int B, int n_q, int max_kv_len) {
   return (int)s;
 }
 
+// MLA_SPLIT_BALANCED on the matrix-core path for 2 .. BAL_SLOTS query rows:
+// splits balanced per row by the kernel (DecodeBalance).  Elsewhere it
+// means the automatic uniform count: a single row has nothing to balance
+// (and the plan would put a kv_lens load ahead of its query loads).  The
+// plan costs about 3 us per call on uniform lengths (the same load ahead
+// of the query loads), hence opt-in.
+bool balanced_mode(const mla_dims& d, int B, int n_q, int n_split) {
+  const long rows = (long)B * n_q;
+  return n_split == MLA_SPLIT_BALANCED && decode_mfma_supported(d) &&
+         rows >= 2 && rows <= BAL_SLOTS;
+}
+
 // Effective split count for a requested one (at most one block per split).
 int split_count(const mla_dims& d, int max_kv_len, int want) {
   const int nblk = decode_nblk(d, max_kv_len);
   if (want < 1) want = 1;
   return want > nblk ? nblk : want;
+}
+
+// The uniform split count of a request (0 and MLA_SPLIT_BALANCED: auto).
+int uniform_request(const mla_dims& d, int B, int n_q, int max_kv_len,
+                    int n_split) {
+  return split_count(d, max_kv_len,
+                     n_split > 0 ? n_split : auto_splits(d, B, n_q, max_kv_len));
 }
 
 }  // namespace
@@ -387,11 +406,17 @@ int32_t mla_decode_auto_splits(const mla_dims* dims, int32_t B, int32_t n_q,
 
 size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t B, int32_t n_q,
                                   int32_t max_kv_len, int32_t n_split) {
-  if (!dims_ok(dims) || B <= 0 || n_q <= 0 || max_kv_len <= 0 || n_split < 0)
+  if (!dims_ok(dims) || B <= 0 || n_q <= 0 || max_kv_len <= 0 ||
+      n_split < MLA_SPLIT_BALANCED)
     return 0;
   const mla_dims& d = *dims;
-  const int ns = split_count(
-      d, max_kv_len, n_split ? n_split : auto_splits(d, B, n_q, max_kv_len));
+  if (balanced_mode(d, B, n_q, n_split)) {
+    const size_t rows = (size_t)BAL_SLOTS * d.n_h;
+    return align_up(rows * d.d_c * sizeof(float)) +
+           2 * align_up(rows * sizeof(float)) +
+           align_up((size_t)B * n_q * sizeof(int2));
+  }
+  const int ns = uniform_request(d, B, n_q, max_kv_len, n_split);
   if (ns <= 1) return 0;
   const size_t rows = (size_t)B * n_q * ns * d.n_h;
   return align_up(rows * d.d_c * sizeof(float)) + 2 * align_up(rows * sizeof(float));
@@ -406,7 +431,7 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, int32_t n_q,
                       mla_stream_t stream) {
   if (!dims) return MLA_ERR_NULL;
   if (!dims_ok(dims) || B <= 0 || n_q <= 0 || max_kv_len <= 0 ||
-      num_blocks <= 0 || max_blocks <= 0 || n_split < 0)
+      num_blocks <= 0 || max_blocks <= 0 || n_split < MLA_SPLIT_BALANCED)
     return MLA_ERR_SHAPE;
   if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
   if (!q || !cache || !block_table || !kv_lens || !o_lat) return MLA_ERR_NULL;
@@ -416,31 +441,48 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, int32_t n_q,
   const int nblk = decode_nblk(d, max_kv_len);
   if (nblk > max_blocks) return MLA_ERR_RANGE;
   if (n_split > nblk) return MLA_ERR_RANGE;
-  const int ns = split_count(
-      d, max_kv_len, n_split ? n_split : auto_splits(d, B, n_q, max_kv_len));
   const size_t need = mla_decode_workspace_bytes(dims, B, n_q, max_kv_len, n_split);
   if (need && (!ws || ws_bytes < need)) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
+  const bool mfma = decode_mfma_supported(d);
+  const int rows = B * n_q;
+  if (balanced_mode(d, B, n_q, n_split)) {
+    Carve c(ws);
+    const size_t prow = (size_t)BAL_SLOTS * d.n_h;
+    float* o_part = c.take(prow * d.d_c);
+    float* m_part = c.take(prow);
+    float* l_part = c.take(prow);
+    DecodeBalance bal;
+    bal.plan = (int2*)c.take(2 * (size_t)rows);
+    const long per_row = (nblk + BAL_MIN_CHUNK - 1) / BAL_MIN_CHUNK;
+    bal.est_wgs = (int)std::min((long)BAL_SLOTS, (long)rows * per_row);
+    MLA_TRY(launch_decode_mfma(d, B, n_q, q, cache, block_table, max_blocks,
+                               kv_lens, 1, bal, o_part, m_part, l_part, o_lat,
+                               lse, s));
+    MLA_TRY(launch_combine(d, rows, 1, o_part, true, m_part, l_part, o_lat,
+                           lse, s, bal.plan, BAL_SLOTS));
+    return MLA_OK;
+  }
+  const int ns = uniform_request(d, B, n_q, max_kv_len, n_split);
   float *o_part = nullptr, *m_part = nullptr, *l_part = nullptr;
   if (ns > 1) {
     Carve c(ws);
-    const size_t rows = (size_t)B * n_q * ns * d.n_h;
-    o_part = c.take(rows * d.d_c);
-    m_part = c.take(rows);
-    l_part = c.take(rows);
+    const size_t prow = (size_t)rows * ns * d.n_h;
+    o_part = c.take(prow * d.d_c);
+    m_part = c.take(prow);
+    l_part = c.take(prow);
   }
-  const bool mfma = decode_mfma_supported(d);
   if (mfma)
     MLA_TRY(launch_decode_mfma(d, B, n_q, q, cache, block_table, max_blocks,
-                               kv_lens, ns, o_part, m_part, l_part, o_lat,
-                               lse, s));
+                               kv_lens, ns, DecodeBalance(), o_part, m_part,
+                               l_part, o_lat, lse, s));
   else
     MLA_TRY(launch_decode_simt(d, B, n_q, q, cache, block_table, max_blocks,
                                kv_lens, ns, o_part, m_part, l_part, o_lat,
                                lse, s));
   if (ns > 1)
-    MLA_TRY(launch_combine(d, B * n_q, ns, o_part, mfma, m_part, l_part,
-                           o_lat, lse, s));
+    MLA_TRY(launch_combine(d, rows, ns, o_part, mfma, m_part, l_part, o_lat,
+                           lse, s));
   return MLA_OK;
 }
 

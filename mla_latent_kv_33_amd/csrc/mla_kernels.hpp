@@ -17,13 +17,27 @@ namespace mla {
 // m_part/l_part [B*n_q][n_split][n_h] with m in log2 units.  With n_split == 1 the kernels
 // write o_final [B*n_q][n_h][d_c] and lse_final (natural log) directly.
 bool decode_mfma_supported(const mla_dims& d);
+// Balanced splits (matrix-core kernel, at most BAL_SLOTS query rows): the
+// kernel reads kv_lens and gives query row r n_r = ceil(nb_r / c) splits of
+// its nb_r visible blocks, c the smallest chunk >= BAL_MIN_CHUNK blocks with
+// sum_r n_r <= BAL_SLOTS; the splits of row r take consecutive partial
+// slots from plan[r] = (first slot, n_r) on, written by the row's split 0.
+// A row with one split writes o_final / lse_final directly.
+constexpr int BAL_SLOTS = 256;
+constexpr int BAL_MIN_CHUNK = 2;
+struct DecodeBalance {
+  int2* plan = nullptr;  // [B*n_q]; null: uniform n_split per row
+  int est_wgs = 0;       // upper bound of the workgroups that get work
+};
+// n_split: splits per row (uniform mode); with balance.plan the partial
+// buffers hold BAL_SLOTS slots instead of B*n_q*n_split.
 hipError_t launch_decode_mfma(const mla_dims& d, int B, int n_q,
                               const void* q, const void* cache,
                               const int32_t* block_table, int max_blocks,
                               const int32_t* kv_lens, int n_split,
-                              float* o_part, float* m_part,
-                              float* l_part, float* o_final, float* lse_final,
-                              hipStream_t stream);
+                              const DecodeBalance& balance, float* o_part,
+                              float* m_part, float* l_part, float* o_final,
+                              float* lse_final, hipStream_t stream);
 hipError_t launch_decode_simt(const mla_dims& d, int B, int n_q,
                               const void* q, const void* cache,
                               const int32_t* block_table, int max_blocks,
@@ -32,11 +46,14 @@ hipError_t launch_decode_simt(const mla_dims& d, int B, int n_q,
                               float* l_part, float* o_final, float* lse_final,
                               hipStream_t stream);
 // o_part: fp32 unnormalised partials (decode_simt_kernel), or with
-// f16_parts the scaled fp16 partials of decode_mfma_kernel.
+// f16_parts the scaled fp16 partials of decode_mfma_kernel.  plan (fp16
+// partials only): balanced splits, slots partial slots; rows with one split
+// are already final and skipped.
 hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
                           const float* o_part, bool f16_parts,
                           const float* m_part, const float* l_part,
-                          float* o_lat, float* lse, hipStream_t stream);
+                          float* o_lat, float* lse, hipStream_t stream,
+                          const int2* plan = nullptr, int slots = 0);
 
 // ---- MHA-path prefill (prefill_mha.hip) --------------------------------
 // Shapes the prefill kernel serves: bf16, d_h = 128 (= d_v), d_r = 64.

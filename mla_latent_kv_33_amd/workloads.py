@@ -218,7 +218,9 @@ class Workload:
     n_q: int              # new tokens (queries) per sequence
     seed: int
     permuted: bool        # random-permutation block table
-    n_split: int = 0      # split-KV chunks per sequence (0 = library picks)
+    # split-KV chunks per sequence: 0 = one count chosen by the library,
+    # -1 = balanced per sequence (uneven lengths), else that count
+    n_split: int = 0
     synthetic_context: bool = False   # context given as cache rows
 
     @property
@@ -238,7 +240,7 @@ def workload(name: str) -> Workload:
         return Workload("b1_ctx4k", DEEPSEEK_V2, "bf16", 1, (4096,), 1, 2, False)
     if name == "b64_var":
         return Workload("b64_var", DEEPSEEK_V2, "bf16", 64, _var_ctx(3), 1, 3,
-                        True)
+                        True, n_split=-1)
     if name == "b64_ctx8k":
         return Workload("b64_ctx8k", DEEPSEEK_V2, "bf16", 64, (8192,) * 64, 1,
                         6, True, synthetic_context=True)

@@ -81,6 +81,12 @@ def test_workspace_sizes():
     # one sequence: as many splits as keep two 64-token blocks each
     assert B.mla_decode_auto_splits(d, 1, 1, 4097) == 32
     assert B.mla_decode_auto_splits(d, 1, 1, 100) == 1
+    # balanced splits: partial slots for 256 workgroups plus the row plan
+    bal = B.mla_decode_workspace_bytes(d, 64, 1, 8193, B.MLA_SPLIT_BALANCED)
+    assert bal >= 256 * 128 * (512 + 2) * 4 + 64 * 8
+    # a single row is not balanced: the automatic count's workspace
+    assert B.mla_decode_workspace_bytes(d, 1, 1, 4097, -1) == \
+        B.mla_decode_workspace_bytes(d, 1, 1, 4097, 0)
     bad = ds_dims(d_r=63)
     assert B.mla_append_workspace_bytes(bad, 64) == 0
 
@@ -144,7 +150,12 @@ def test_decode_validation():
     assert call_decode(d, n_q=4, causal=0) == UNSUP
     assert call_decode(d, max_blocks=1) == RANGE             # 100 > 64
     assert call_decode(d, n_split=3) == RANGE                # 2 blocks
-    assert call_decode(d, n_split=-1) == SHAPE
+    assert call_decode(d, n_split=-2) == SHAPE
+    assert call_decode(d, n_split=-1, ws=None) == WS          # balanced
+    # fp32 layers: balanced means the automatic uniform count (4 splits of
+    # 16 blocks here), which needs the workspace as well
+    assert call_decode(ds_dims(dtype=B.MLA_F32), n_split=-1, max_kv=1000,
+                       max_blocks=16, ws=None) == WS
     assert call_decode(d, n_split=2, ws=None) == WS
     assert call_decode(d, n_split=2, ws_bytes=64) == WS
 

@@ -17,13 +17,16 @@ from tests.gpu_common import log
 pytestmark = pytest.mark.gpu
 
 
-def _workload():
+def _workload(n_split):
     # 16 sequences, ragged contexts (partial last blocks), permuted table,
-    # library-chosen splits (several per sequence, so the combine runs).
+    # library-chosen splits (several per sequence, so the combine runs):
+    # one count for all, or balanced per sequence (a plan the decode kernel
+    # writes on every replay).
     base = W.workload("b64_ctx8k")
     return dataclasses.replace(
         base, name="graph_b16", batch=16,
-        ctx=tuple(700 + 131 * i for i in range(16)), seed=11)
+        ctx=tuple(700 + 131 * i for i in range(16)), seed=11,
+        n_split=n_split)
 
 
 def _snapshot(st, out):
@@ -32,9 +35,10 @@ def _snapshot(st, out):
             "cache": st.cache.clone()}
 
 
-def test_step_graph_replays_match_eager():
+@pytest.mark.parametrize("n_split", [0, -1])
+def test_step_graph_replays_match_eager(n_split):
     assert torch.cuda.is_available(), "GPU tests need a GPU"
-    wl = _workload()
+    wl = _workload(n_split)
     layer = flow.make_layer(wl)
     st = flow.prepare(wl, layer)
     out = flow.run_step(st)           # eager: outputs and workspaces

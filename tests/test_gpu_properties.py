@@ -94,7 +94,9 @@ def test_split_count_invariance_and_determinism(dtype):
     """Any split count gives the same result: exactly up to fp32 rounding for
     fp32 layers; for bf16 layers the weights P are rounded to bf16 against
     each split's own reference maximum, so splits agree to that rounding.
-    A fixed split count is bitwise deterministic."""
+    A fixed split count is bitwise deterministic.  n_split = -1 is the
+    balanced plan (on bf16 layers: 1 .. 33 splits per row from the device
+    kv_lens; on fp32 layers the automatic count)."""
     # bf16: each P carries up to 2^-9 relative rounding, so o agrees to
     # ~1e-3 and l (hence lse) to ~2^-9 / sqrt(keys) relative.
     if dtype == "bf16":
@@ -115,7 +117,7 @@ def test_split_count_invariance_and_determinism(dtype):
     q = to_device(0.5 * rng.standard_normal((5, 1, dims.n_h, width)).astype(
         np.float32), dtype)
     base, base_lse = _decode_once(layer, q, cache, table, kv, 4097, 1)
-    for ns in (2, 7, 16, 65):
+    for ns in (2, 7, 16, 65, B.MLA_SPLIT_BALANCED):
         o, lse = _decode_once(layer, q, cache, table, kv, 4097, ns)
         assert_close(f"n_split={ns} vs 1", o.cpu().numpy(),
                      base.cpu().numpy(), "f32", tol=tol)
