@@ -11,7 +11,10 @@
 // heads over two workgroups instead; the second read of each row is an L2
 // hit.)
 //
-// Work decomposition (one workgroup = NW waves, NW * 32 heads):
+// Work decomposition (one workgroup = NW waves, NW * 32 heads, one split of
+// one query row; either n_split splits per row, or a balanced plan that the
+// kernel derives from kv_lens so that long rows get more splits than short
+// ones, see balanced_work):
 //   * keys stream in half tiles of 32 tokens (half a 64-token cache block),
 //     copied HBM -> LDS by direct-to-LDS loads into a ring of four buffers:
 //     while a wave computes on halves j and j+1, halves j+2 and j+3 are in

@@ -11,11 +11,12 @@ namespace mla {
 // ---- split-KV decode ---------------------------------------------------
 // Split j of a (sequence, query) whose visible keys span nblk blocks covers
 // blocks [j nblk / n_split, (j + 1) nblk / n_split).
-// Partials: o_part [B*n_q][n_split][n_h][d_c] (fp32 unnormalised from the
+// Partials: o_part [slot][n_h][d_c], slot = row n_split + split (or the
+// balanced plan's slots, BAL_SLOTS of them) (fp32 unnormalised from the
 // SIMT kernel; from the matrix-core kernel fp16 O / (l s) in the first half
 // of the same buffer, followed by the per-row scales s as fp32),
-// m_part/l_part [B*n_q][n_split][n_h] with m in log2 units.  With n_split == 1 the kernels
-// write o_final [B*n_q][n_h][d_c] and lse_final (natural log) directly.
+// m_part/l_part [slot][n_h] with m in log2 units.  A row with one split
+// writes o_final [B*n_q][n_h][d_c] and lse_final (natural log) directly.
 bool decode_mfma_supported(const mla_dims& d);
 // Balanced splits (matrix-core kernel, at most BAL_SLOTS query rows): the
 // kernel reads kv_lens and gives query row r n_r = ceil(nb_r / c) splits of
