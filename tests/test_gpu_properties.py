@@ -180,6 +180,50 @@ def test_chunk_last_row_equals_decode():
     assert torch.equal(o[:, 0], o_first[:, 0])
 
 
+def test_balanced_causal_chunk():
+    """Balanced splits over the query rows of causal chunks (rows of one
+    sequence see different key counts, two sequences of different lengths):
+    the same result as one split per row, to the bf16 rounding of P against
+    each split's reference, on every row; checked against the oracle's
+    latent attention on sampled rows."""
+    layer, w = ds_layer()
+    rng = np.random.default_rng(12)
+    lens = np.array([3000, 700]) + 90
+    n_q = 90
+    table_np, nb = W.block_table(lens, True, 13)
+    img = np.zeros((nb, 64, 576), np.float32)
+    rows_h = []
+    for b, kvl in enumerate(lens):
+        r = rng.standard_normal((kvl, 576)).astype(np.float32)
+        flow.scatter_rows_host(img, table_np, b, 0, r, 64)
+        rows_h.append(r)
+    cache = to_device(img, "bf16")
+    table = torch.from_numpy(table_np).cuda()
+    kv = torch.from_numpy(lens.astype(np.int32)).cuda()
+    q = to_device(0.5 * rng.standard_normal((2, n_q, 128, 576)).astype(
+        np.float32), "bf16")
+    o1, l1 = _decode_once(layer, q, cache, table, kv, int(lens.max()), 1)
+    ob, lb = _decode_once(layer, q, cache, table, kv, int(lens.max()),
+                          B.MLA_SPLIT_BALANCED)
+    ob2, lb2 = _decode_once(layer, q, cache, table, kv, int(lens.max()),
+                            B.MLA_SPLIT_BALANCED)
+    assert torch.equal(ob, ob2) and torch.equal(lb, lb2)
+    assert_close("balanced vs one split", ob.cpu().numpy(), o1.cpu().numpy(),
+                 "f32", tol=(3e-3, 2e-2))
+    assert_close("balanced lse vs one split", lb.cpu().numpy(),
+                 l1.cpu().numpy(), "f32", tol=(1e-4, 4e-3))
+    qh = q.float().cpu().numpy()
+    for b in (0, 1):
+        rows = W.round_bf16(rows_h[b]).astype(np.float64)
+        sel = [0, 45, n_q - 1]
+        pos = lens[b] - n_q + np.array(sel)
+        o_ref, lse_ref = orc.latent_attention(qh[b, sel], pos, rows, 512, 128)
+        assert_close(f"seq{b} balanced o_lat", ob[b, sel].cpu().numpy(),
+                     o_ref, "bf16")
+        assert_close(f"seq{b} balanced lse", lb[b, sel].cpu().numpy(),
+                     lse_ref, "bf16")
+
+
 def test_single_key_and_zero_tokens():
     """kv_len = 1 (the softmax weight is 1: o_lat is the row itself) and
     T = 0 calls (no-ops)."""
