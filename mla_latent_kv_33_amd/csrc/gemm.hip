@@ -598,24 +598,27 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
 // workgroups one XCD runs together share A row bands and B column bands
 // through its L2.
 constexpr int BG_BN = 128;
-constexpr int BG_NSLOT = 3;
-constexpr int BG_A_BYTES = 32 * 1024;
-constexpr int BG_SLOT = BG_A_BYTES + BG_BN * 128;   // 48 KiB
-constexpr int BG_LDS = BG_NSLOT * BG_SLOT;           // 144 KiB
 constexpr int BG_GROUP = 8;
 
-template <bool AF32>
+// SMALL (bf16 only): 128 x 128 tiles and a two-slot ring, 64 KiB, so that
+// two workgroups share a compute unit and one's ring fill and epilogue
+// overlap the other's k-steps (short K).
+template <bool AF32, bool SMALL = false>
 struct BigCfg {
-  static constexpr int BM = AF32 ? 128 : 256;
+  static_assert(!(AF32 && SMALL), "small tiles are bf16 only");
+  static constexpr int BM = (AF32 || SMALL) ? 128 : 256;
   static constexpr int RB = AF32 ? 256 : 128;   // A bytes per row per 64 k
   static constexpr int PPR = RB / 16;           // pieces per A row
   static constexpr int RPC = 1024 / RB;         // A rows per copy
   static constexpr int MT = BM / 64;            // 32-row tiles per wave
-  static constexpr int A_PER = BG_A_BYTES / 1024 / 4;  // 8 A copies per wave
+  static constexpr int A_BYTES = BM * RB;       // 32 KiB (16 KiB small)
+  static constexpr int SLOT = A_BYTES + BG_BN * 128;
+  static constexpr int NSLOT = SMALL ? 2 : 3;
+  static constexpr int LDS = NSLOT * SLOT;      // 144 KiB (64 KiB small)
+  static constexpr int A_PER = A_BYTES / 1024 / 4;     // A copies per wave
   static constexpr int B_PER = BG_BN * 128 / 1024 / 4; // 4 B copies per wave
   static constexpr int PER = A_PER + B_PER;
-  static_assert(BM * RB == BG_A_BYTES, "A tile size");
-  static_assert(2 * PER <= 63, "vmcnt range");
+  static_assert((NSLOT - 1) * PER <= 63, "vmcnt range");
 };
 
 // Position of piece p of A row r in the LDS row.
@@ -624,13 +627,13 @@ __device__ __forceinline__ int big_apos(int r, int p) {
   return AF32 ? p ^ (r & 15) : p ^ ((r >> 1) & 7);
 }
 
-template <bool AF32>
-__global__ __launch_bounds__(256, 1) void gemm_big_kernel(
+template <bool AF32, bool SMALL>
+__global__ __launch_bounds__(256, SMALL ? 2 : 1) void gemm_big_kernel(
     const void* __restrict__ Av, long lda, const uint16_t* __restrict__ B,
     const uint16_t* __restrict__ B2, int nb1, long ldb,
     float* __restrict__ C, uint16_t* __restrict__ C16, long ldc, int M,
     int N, int K, int tiles_m, int tiles_n) {
-  using L = BigCfg<AF32>;
+  using L = BigCfg<AF32, SMALL>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -677,7 +680,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
   }
   const uint32_t lds0 = lds_u32(lds);
   auto issue = [&](int kt) __attribute__((always_inline)) {
-    const uint32_t slot = lds0 + (kt % BG_NSLOT) * BG_SLOT;
+    const uint32_t slot = lds0 + (kt % L::NSLOT) * L::SLOT;
     const char* ab = a_base + (size_t)kt * 64 * esz;
     const char* bb = (const char*)bt + (size_t)kt * 128;
 #pragma unroll
@@ -685,7 +688,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
       dma16(slot + (wave * L::A_PER + a) * 1024, ab, a_off[a]);
 #pragma unroll
     for (int b = 0; b < L::B_PER; ++b)
-      dma16(slot + BG_A_BYTES + (wave * L::B_PER + b) * 1024, bb, b_off[b]);
+      dma16(slot + L::A_BYTES + (wave * L::B_PER + b) * 1024, bb, b_off[b]);
   };
 
   // ---- fragment reads -----------------------------------------------------
@@ -696,7 +699,7 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
   auto w_read = [&](const lds_char* sl, int nt, int ks) __attribute__((always_inline)) {
     const int r = wn * 64 + 32 * nt + col;
     return *(const __attribute__((address_space(3))) bf16x8*)(
-        sl + BG_A_BYTES + r * 128 + 16 * ((2 * ks + g) ^ ((r >> 1) & 7)));
+        sl + L::A_BYTES + r * 128 + 16 * ((2 * ks + g) ^ ((r >> 1) & 7)));
   };
   auto a_read = [&](const lds_char* sl, int mt, int piece) __attribute__((always_inline)) {
     const int r = wm * (L::BM / 2) + 32 * mt + col;
@@ -713,16 +716,18 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
       for (int r = 0; r < 16; ++r) acc[nt][mt][r] = 0.0f;
 
   const int nk = K / 64;
-  issue(0);
-  if (nk > 1) issue(1);
+#pragma unroll
+  for (int i = 0; i < L::NSLOT - 1; ++i)
+    if (i < nk) issue(i);
   for (int kt = 0; kt < nk; ++kt) {
-    // own copies of step kt done (step kt + 1 may stay in flight), then
-    // everybody's; the slot of step kt - 1 is free after the barrier
-    if (kt + 1 < nk) wait_vm<L::PER>();
+    // own copies of step kt done (with three slots step kt + 1 may stay in
+    // flight), then everybody's; the slot of step kt - 1 is free after the
+    // barrier
+    if (L::NSLOT == 3 && kt + 1 < nk) wait_vm<(L::NSLOT - 2) * L::PER>();
     else wait_vm<0>();
     barrier();
-    if (kt + 2 < nk) issue(kt + 2);
-    const lds_char* sl = (const lds_char*)lds + (kt % BG_NSLOT) * BG_SLOT;
+    if (kt + L::NSLOT - 1 < nk) issue(kt + L::NSLOT - 1);
+    const lds_char* sl = (const lds_char*)lds + (kt % L::NSLOT) * L::SLOT;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       bf16x8 wf[2], ahi[L::MT], alo[L::MT];
@@ -779,20 +784,21 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
   }
 }
 
-template <bool AF32>
+template <bool AF32, bool SMALL>
 hipError_t launch_big(const GemmArgs& g, hipStream_t stream) {
+  using L = BigCfg<AF32, SMALL>;
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
-        (const void*)gemm_big_kernel<AF32>,
-        hipFuncAttributeMaxDynamicSharedMemorySize, BG_LDS);
+        (const void*)gemm_big_kernel<AF32, SMALL>,
+        hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int tiles_m = (g.M + BigCfg<AF32>::BM - 1) / BigCfg<AF32>::BM;
+  const int tiles_m = (g.M + L::BM - 1) / L::BM;
   const int tiles_n = (g.N + BG_BN - 1) / BG_BN;
-  hipLaunchKernelGGL(gemm_big_kernel<AF32>, dim3(tiles_m * tiles_n),
-                     dim3(256), BG_LDS, stream, g.A, g.lda,
+  hipLaunchKernelGGL((gemm_big_kernel<AF32, SMALL>), dim3(tiles_m * tiles_n),
+                     dim3(256), L::LDS, stream, g.A, g.lda,
                      (const uint16_t*)g.B, (const uint16_t*)g.B2, g.nb1,
                      g.ldb, g.C, (uint16_t*)g.c16, g.ldc, g.M, g.N, g.K,
                      tiles_m, tiles_n);
@@ -1016,15 +1022,21 @@ void gemm_plan(const mla_dims& d, GemmArgs& g, int max_split) {
   g.m_split = 1;
   g.big = 0;
   // Many rows (prefill chunks): the large-tile kernel, one K chunk.  Its
-  // two-step pipeline fill and the epilogue are paid once per tile, so short
-  // K (the 512-deep up-projection of the latent) stays on the tiled kernel.
+  // pipeline fill and epilogue are paid once per tile; for short K (the
+  // 512-deep up-projection of the latent) the small-tile variant runs two
+  // workgroups per compute unit so that they hide each other's (big = 2).
   const int esz = g.a_f32 ? 4 : 2;
   if (d.dtype == MLA_BF16 && !g.b_nn && g.batch == 1 &&
-      g.M >= (g.a_f32 ? 128 : 256) && g.K >= 1024 && g.K % 64 == 0 &&
+      g.M >= (g.a_f32 ? 128 : 256) && g.K >= 256 && g.K % 64 == 0 &&
       g.N % 4 == 0 &&
       g.ldc % 4 == 0 && (g.lda * esz) % 16 == 0 && g.ldb % 8 == 0 &&
       (g.nb1 >= g.N || g.nb1 % BG_BN == 0)) {
-    g.big = 1;
+    if (g.K >= 1024)
+      g.big = 1;
+    else if (!g.a_f32)
+      g.big = 2;
+    else
+      return;  // short K with fp32 activations: tiled kernel
     return;
   }
   if (d.dtype != MLA_BF16 || g.b_nn || g.M > 64 || g.M <= 0 || g.N <= 0 ||
@@ -1128,7 +1140,9 @@ hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
   }
   if (g.big) {
     if (ks != 1 || g.batch != 1) return hipErrorInvalidValue;
-    return g.a_f32 ? launch_big<true>(g, stream) : launch_big<false>(g, stream);
+    if (g.a_f32) return launch_big<true, false>(g, stream);
+    return g.big == 2 ? launch_big<false, true>(g, stream)
+                      : launch_big<false, false>(g, stream);
   }
   const uint16_t* B = (const uint16_t*)g.B;
   const uint16_t* B2 = (const uint16_t*)g.B2;
