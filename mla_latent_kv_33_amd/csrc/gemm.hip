@@ -24,8 +24,9 @@
 //   * tiled (any M, NT or NN): 128x128x32 tiles staged through padded LDS,
 //     2x2 waves of 64x64; NN weights are read with ds_read_b64_tr_b16 so the
 //     MFMA still sees k-contiguous B fragments.
-//   * big (M >= 256, or 128 with fp32 activations; NT, K >= 1024): 256x128
-//     (128x128) tiles in 64-k steps through a three-slot direct-to-LDS ring.
+//   * big (M >= 128, or 64 with fp32 activations; NT, K >= 256): 128x128
+//     (64x128) tiles in 64-k steps through a two-slot direct-to-LDS ring,
+//     two workgroups per compute unit.
 // fp32 layers use a plain SIMT kernel (small shapes only).
 
 #include "lds_dma.hpp"
@@ -581,11 +582,13 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
 // Large-M GEMM (prefill chunks): C = A B^T with A [M][K] (bf16, or fp32 as
 // hi + lo bf16 terms), B [N][K] bf16 (NT), K % 64 == 0, one K chunk.
 //
-// Workgroup tile BM x 128 (BM = 256 for bf16 A, 128 for fp32 A, so that the
-// A tile is 32 KiB either way) in 64-k steps, 4 waves as 2 x 2 of
-// (BM / 2) x 64.  Each step's A and B tiles (48 KiB) arrive by direct-to-LDS
-// copies of whole 128/256-byte row runs into a three-slot ring (144 KiB),
-// two steps in flight while the third is computed.  LDS rows hold their
+// Workgroup tile BM x 128 (BM = 128 for bf16 A, 64 for fp32 A, so that the
+// A tile is 16 KiB either way) in 64-k steps, 4 waves as 2 x 2 of
+// (BM / 2) x 64.  Each step's A and B tiles (32 KiB) arrive by direct-to-LDS
+// copies of whole 128/256-byte row runs into a two-slot ring (64 KiB): the
+// next step is in flight while one is computed, and two workgroups per
+// compute unit cover each other's waits, ring fill and epilogue.  LDS rows
+// hold their
 // 16-byte pieces XOR-swizzled by the row index (bf16 rows of 128 B: piece ^
 // (row / 2) % 8; fp32 rows of 256 B: piece ^ row % 16), so the 16 lanes of
 // one ds_read_b128 phase, 16 consecutive rows at the same piece, hit
@@ -600,21 +603,24 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
 constexpr int BG_BN = 128;
 constexpr int BG_GROUP = 8;
 
-// SMALL (bf16 only): 128 x 128 tiles and a two-slot ring, 64 KiB, so that
-// two workgroups share a compute unit and one's ring fill and epilogue
-// overlap the other's k-steps (short K).
-template <bool AF32, bool SMALL = false>
+// Tiles of 128 x 128 (64 x 128 with fp32 activations, so that the
+// activation tile is 16 KiB either way) and a two-slot ring of 32 KiB
+// slots, 64 KiB in all: two workgroups share a compute unit, and one's ring
+// fill and epilogue overlap the other's k-steps.  (Tiles of 256 x 128 with a
+// three-slot ring and one workgroup per compute unit measured 8 - 20 %
+// slower on every shape, and 1.8x slower at K = 512.)
+template <bool AF32>
 struct BigCfg {
-  static_assert(!(AF32 && SMALL), "small tiles are bf16 only");
-  static constexpr int BM = (AF32 || SMALL) ? 128 : 256;
+  static constexpr int BM = AF32 ? 64 : 128;
   static constexpr int RB = AF32 ? 256 : 128;   // A bytes per row per 64 k
   static constexpr int PPR = RB / 16;           // pieces per A row
   static constexpr int RPC = 1024 / RB;         // A rows per copy
   static constexpr int MT = BM / 64;            // 32-row tiles per wave
-  static constexpr int A_BYTES = BM * RB;       // 32 KiB (16 KiB small)
+  static constexpr int A_BYTES = BM * RB;       // 16 KiB
+  static_assert(MT >= 1, "at least one 32-row tile per wave");
   static constexpr int SLOT = A_BYTES + BG_BN * 128;
-  static constexpr int NSLOT = SMALL ? 2 : 3;
-  static constexpr int LDS = NSLOT * SLOT;      // 144 KiB (64 KiB small)
+  static constexpr int NSLOT = 2;
+  static constexpr int LDS = NSLOT * SLOT;      // 64 KiB
   static constexpr int A_PER = A_BYTES / 1024 / 4;     // A copies per wave
   static constexpr int B_PER = BG_BN * 128 / 1024 / 4; // 4 B copies per wave
   static constexpr int PER = A_PER + B_PER;
@@ -627,13 +633,13 @@ __device__ __forceinline__ int big_apos(int r, int p) {
   return AF32 ? p ^ (r & 15) : p ^ ((r >> 1) & 7);
 }
 
-template <bool AF32, bool SMALL>
-__global__ __launch_bounds__(256, SMALL ? 2 : 1) void gemm_big_kernel(
+template <bool AF32>
+__global__ __launch_bounds__(256, 2) void gemm_big_kernel(
     const void* __restrict__ Av, long lda, const uint16_t* __restrict__ B,
     const uint16_t* __restrict__ B2, int nb1, long ldb,
     float* __restrict__ C, uint16_t* __restrict__ C16, long ldc, int M,
     int N, int K, int tiles_m, int tiles_n) {
-  using L = BigCfg<AF32, SMALL>;
+  using L = BigCfg<AF32>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -720,11 +726,9 @@ __global__ __launch_bounds__(256, SMALL ? 2 : 1) void gemm_big_kernel(
   for (int i = 0; i < L::NSLOT - 1; ++i)
     if (i < nk) issue(i);
   for (int kt = 0; kt < nk; ++kt) {
-    // own copies of step kt done (with three slots step kt + 1 may stay in
-    // flight), then everybody's; the slot of step kt - 1 is free after the
-    // barrier
-    if (L::NSLOT == 3 && kt + 1 < nk) wait_vm<(L::NSLOT - 2) * L::PER>();
-    else wait_vm<0>();
+    // own copies of step kt done, then everybody's; the slot of step kt - 1
+    // is free after the barrier
+    wait_vm<0>();
     barrier();
     if (kt + L::NSLOT - 1 < nk) issue(kt + L::NSLOT - 1);
     const lds_char* sl = (const lds_char*)lds + (kt % L::NSLOT) * L::SLOT;
@@ -784,20 +788,20 @@ __global__ __launch_bounds__(256, SMALL ? 2 : 1) void gemm_big_kernel(
   }
 }
 
-template <bool AF32, bool SMALL>
+template <bool AF32>
 hipError_t launch_big(const GemmArgs& g, hipStream_t stream) {
-  using L = BigCfg<AF32, SMALL>;
+  using L = BigCfg<AF32>;
   static bool attr_set = false;
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
-        (const void*)gemm_big_kernel<AF32, SMALL>,
+        (const void*)gemm_big_kernel<AF32>,
         hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int tiles_m = (g.M + L::BM - 1) / L::BM;
   const int tiles_n = (g.N + BG_BN - 1) / BG_BN;
-  hipLaunchKernelGGL((gemm_big_kernel<AF32, SMALL>), dim3(tiles_m * tiles_n),
+  hipLaunchKernelGGL((gemm_big_kernel<AF32>), dim3(tiles_m * tiles_n),
                      dim3(256), L::LDS, stream, g.A, g.lda,
                      (const uint16_t*)g.B, (const uint16_t*)g.B2, g.nb1,
                      g.ldb, g.C, (uint16_t*)g.c16, g.ldc, g.M, g.N, g.K,
@@ -1021,22 +1025,14 @@ void gemm_plan(const mla_dims& d, GemmArgs& g, int max_split) {
   g.k_split = 1;
   g.m_split = 1;
   g.big = 0;
-  // Many rows (prefill chunks): the large-tile kernel, one K chunk.  Its
-  // pipeline fill and epilogue are paid once per tile; for short K (the
-  // 512-deep up-projection of the latent) the small-tile variant runs two
-  // workgroups per compute unit so that they hide each other's (big = 2).
+  // Many rows (prefill chunks): the large-tile kernel, one K chunk.
   const int esz = g.a_f32 ? 4 : 2;
   if (d.dtype == MLA_BF16 && !g.b_nn && g.batch == 1 &&
-      g.M >= (g.a_f32 ? 128 : 256) && g.K >= 256 && g.K % 64 == 0 &&
+      g.M >= (g.a_f32 ? 64 : 128) && g.K >= 256 && g.K % 64 == 0 &&
       g.N % 4 == 0 &&
       g.ldc % 4 == 0 && (g.lda * esz) % 16 == 0 && g.ldb % 8 == 0 &&
       (g.nb1 >= g.N || g.nb1 % BG_BN == 0)) {
-    if (g.K >= 1024)
-      g.big = 1;
-    else if (!g.a_f32)
-      g.big = 2;
-    else
-      return;  // short K with fp32 activations: tiled kernel
+    g.big = 1;
     return;
   }
   if (d.dtype != MLA_BF16 || g.b_nn || g.M > 64 || g.M <= 0 || g.N <= 0 ||
@@ -1140,9 +1136,7 @@ hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
   }
   if (g.big) {
     if (ks != 1 || g.batch != 1) return hipErrorInvalidValue;
-    if (g.a_f32) return launch_big<true, false>(g, stream);
-    return g.big == 2 ? launch_big<false, true>(g, stream)
-                      : launch_big<false, false>(g, stream);
+    return g.a_f32 ? launch_big<true>(g, stream) : launch_big<false>(g, stream);
   }
   const uint16_t* B = (const uint16_t*)g.B;
   const uint16_t* B2 = (const uint16_t*)g.B2;

@@ -122,8 +122,8 @@ struct GemmArgs {
   // LDS-staged kernel: rows in blocks of 32, one workgroup per block (1 or 2)
   int m_split = 1;
   void* c16 = nullptr;  // bf16 output instead of C (tiled kernel, k_split 1)
-  // 1: large-tile kernel for many rows (bf16, NT, batch 1, one K chunk);
-  // 2: its small-tile variant (bf16 activations, short K)
+  // 1: large-tile kernel for many rows (bf16 weights, NT, batch 1, one K
+  // chunk)
   int big = 0;
   // Pre-split fp32 activations ("hi|lo" layout): every 8 consecutive values
   // of a row are stored as 8 bf16 hi = bf16(x) followed by 8 bf16
