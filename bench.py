@@ -274,7 +274,7 @@ def main():
     mfma_bound = tflops / BF16_PEAK_TFLOPS > achieved / HBM_PEAK_GBPS
     traffic = None if (mha or wl.name != "b64_ctx8k") else \
         stored_traffic(alg_bytes)
-    stage_kernel = ("mla_prefill_mha: gather_rows_kernel + gemm_tiled_kernel "
+    stage_kernel = ("mla_prefill_mha: gather_rows_kernel + gemm_big_kernel "
                     "(k_C, v_C up-projection) + " + PREFILL_KERNEL if mha else
                     "mla_decode: " + DECODE_KERNEL + " + combine_rows_kernel")
     result = {
