@@ -24,9 +24,9 @@
 //   * tiled (any M, NT or NN): 128x128x32 tiles staged through padded LDS,
 //     2x2 waves of 64x64; NN weights are read with ds_read_b64_tr_b16 so the
 //     MFMA still sees k-contiguous B fragments.
-//   * big (M >= 128, or 64 with fp32 activations; NT, K >= 256): 128x128
-//     (64x128) tiles in 64-k steps through a two-slot direct-to-LDS ring,
-//     two workgroups per compute unit.
+//   * big (M >= 128; NT, K >= 256): 128x128 tiles (64x128 with fp32
+//     activations) in 64-k steps through a two-slot direct-to-LDS ring, two
+//     workgroups per compute unit, one K chunk per tile.
 // fp32 layers use a plain SIMT kernel (small shapes only).
 
 #include "lds_dma.hpp"
@@ -1025,10 +1025,12 @@ void gemm_plan(const mla_dims& d, GemmArgs& g, int max_split) {
   g.k_split = 1;
   g.m_split = 1;
   g.big = 0;
-  // Many rows (prefill chunks): the large-tile kernel, one K chunk.
+  // Many rows (prefill chunks): the large-tile kernel, one K chunk.  Decode
+  // batches (M <= 64) stay on the K-split weight-streaming kernel below: one
+  // K chunk per tile would leave W_O's 40 column tiles on 40 compute units.
   const int esz = g.a_f32 ? 4 : 2;
   if (d.dtype == MLA_BF16 && !g.b_nn && g.batch == 1 &&
-      g.M >= (g.a_f32 ? 64 : 128) && g.K >= 256 && g.K % 64 == 0 &&
+      g.M >= 128 && g.K >= 256 && g.K % 64 == 0 &&
       g.N % 4 == 0 &&
       g.ldc % 4 == 0 && (g.lda * esz) % 16 == 0 && g.ldb % 8 == 0 &&
       (g.nb1 >= g.N || g.nb1 % BG_BN == 0)) {

@@ -72,6 +72,13 @@ def test_workspace_sizes():
     assert B.mla_append_workspace_bytes(d, 0) == 0
     # one split needs no workspace; several need partial states
     assert B.mla_decode_workspace_bytes(d, 1, 1, 64, 1) == 0
+    # decode batches stream W_O and W_UQ/W_QR with K-split partials (one K
+    # chunk per column tile would leave most compute units idle): the
+    # workspaces hold several fp32 partial copies of u (64 x 5120) and of
+    # q_C/q_R (64 x 24576)
+    assert B.mla_out_workspace_bytes(d, 64) >= \
+        64 * 128 * 512 * 4 + 2 * 64 * 5120 * 4
+    assert B.mla_absorb_workspace_bytes(d, 64) >= 2 * 64 * 24576 * 4
     ns = B.mla_decode_auto_splits(d, 64, 1, 8193)
     assert ns == 4
     assert B.mla_decode_workspace_bytes(d, 64, 1, 8193, 0) >= \
