@@ -183,6 +183,15 @@ def main():
         return [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
                 for _ in range(n)]
 
+    def attention():
+        if mha:
+            layer.prefill_mha(out.q, st.cache, st.table, st.kv_lens,
+                              st.max_kv_len, o_v=out.o_v, lse=out.lse)
+        else:
+            layer.decode(out.q, st.cache, st.table, st.kv_lens,
+                         st.max_kv_len, n_split=n_split, o_lat=out.o_lat,
+                         lse=out.lse)
+
     def step(e=None, which="all"):
         """One pass of the hot path; e[k] recorded before stage k and after
         the last stage, all of them ("all") or only around decode."""
@@ -198,13 +207,7 @@ def main():
             layer.absorb(st.h_new, st.pos,
                          q_out=out.q.view(-1, d.n_h, d.d_c + d.d_r))
         if rec_dec: e[2].record(stream)
-        if mha:
-            layer.prefill_mha(out.q, st.cache, st.table, st.kv_lens,
-                              st.max_kv_len, o_v=out.o_v, lse=out.lse)
-        else:
-            layer.decode(out.q, st.cache, st.table, st.kv_lens,
-                         st.max_kv_len, n_split=n_split, o_lat=out.o_lat,
-                         lse=out.lse)
+        attention()
         if rec_dec: e[3].record(stream)
         if mha:
             layer.out_values(out.o_v.view(-1, d.n_h * d.d_h), u=out.u)
@@ -243,6 +246,30 @@ def main():
     stage_ms = {n: float(np.mean([ev_st[i][k].elapsed_time(ev_st[i][k + 1])
                                   for i in range(n_st)]))
                 for k, n in enumerate(names)}
+    # The attention stage alone, outside the step, medians of 10 calls each:
+    # right after writing a 512 MiB scratch buffer, right after reading one
+    # (either evicts L2 and the 256 MB Infinity Cache, so the cache rows come
+    # from HBM; the write also leaves dirty lines that are written back while
+    # the attention runs), and back to back.
+    scratch = torch.ones(512 << 18, dtype=torch.int32, device="cuda")
+    kinds = ("write", "read", "repeated")
+    ev_fl = {k: [(torch.cuda.Event(enable_timing=True),
+                  torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+             for k in kinds}
+    sink = []
+    for k in kinds:
+        for r in range(10):
+            if k == "write":
+                scratch.fill_(r + 1)
+            elif k == "read":
+                sink.append(scratch.amax())
+            ev_fl[k][r][0].record(stream)
+            attention()
+            ev_fl[k][r][1].record(stream)
+    torch.cuda.synchronize()
+    del scratch, sink
+    att_us = {k: float(np.median([a.elapsed_time(b) for a, b in ev_fl[k]]))
+              * 1e3 for k in kinds}
     ms_per_step = wall * 1e3 / args.steps
     queries = wl.batch * wl.n_q
     kv = wl.kv_lens
@@ -322,6 +349,17 @@ def main():
         "decode_timing": f"HIP events around the mla_decode call in "
                          f"{len(sampled)} of the {args.steps} timed steps "
                          f"(every {every})",
+        "attention_alone_us": {
+            "after_512MiB_write": att_us["write"],
+            "after_512MiB_read": att_us["read"],
+            "repeated": att_us["repeated"],
+            "cache_GBps_after_read_flush":
+                cache_bytes / att_us["read"] / 1e3,
+            "how": "the attention stage called on its own, outside the "
+                   "step: median of 10 calls each right after writing, or "
+                   "after reading, a 512 MiB scratch buffer (L2 and "
+                   "Infinity Cache evicted; the write also leaves dirty "
+                   "lines to write back), and of 10 calls back to back"},
         "stage_us": {k: v * 1e3 for k, v in stage_ms.items()},
         "stage_us_from": ("the timed steps" if args.timed_events == "all"
                           else f"{n_st} untimed steps with an event around "
