@@ -195,6 +195,31 @@ def test_b4_ctx128k_64_splits():
                      ref["o"][:, heads], "bf16")
 
 
+@pytest.mark.parametrize("n_q", [30, 50])
+def test_ds_ragged_chunk_all_queries(n_q):
+    """DeepSeek-V2 dims on the absorbed path with a ragged causal chunk: 3
+    sequences (contexts 0, 150, 333) receive n_q new tokens each, so every
+    projection runs on T = 3 n_q rows with a partial last row tile (T = 90:
+    the tiled kernel throughout; T = 150: the large-tile kernel for W_DKV,
+    W_DQ, W_UQ / W_QR and W_O, the tiled kernel for the per-head absorption
+    and W_UV), and the decode runs n_q causal queries per sequence, the
+    first one over a single key.  Every query, head and appended row against
+    the oracle."""
+    base = W.workload("b8_prefill")
+    wl = dataclasses.replace(base, name=f"ds_ragged_chunk{n_q}", batch=3,
+                             ctx=(0, 150, 333), n_q=n_q, seed=9,
+                             permuted=True)
+    log(f"case DeepSeek-V2 dims, ragged chunk: ctx={wl.ctx} n_q={n_q}")
+    layer, w = layer_for(wl)
+    st = flow.prepare(wl, layer)
+    out = flow.run_step(st)
+    torch.cuda.synchronize()
+    for b in range(wl.batch):
+        ref = oracle_sequence(wl, w, b)
+        check_new_rows(wl, st, ref, b)
+        check_sequence(wl, out, ref, b)
+
+
 def test_b8_chunked_prefill_causal():
     wl = W.workload("b8_prefill")
     log(f"case {wl.name}: B=8 ctx=8192 + chunk 2048 causal bf16")
