@@ -180,16 +180,17 @@ def test_chunk_last_row_equals_decode():
     assert torch.equal(o[:, 0], o_first[:, 0])
 
 
-def test_balanced_causal_chunk():
+@pytest.mark.parametrize("ctx,n_q", [((3000, 700), 90), ((5000, 300), 128)])
+def test_balanced_causal_chunk(ctx, n_q):
     """Balanced splits over the query rows of causal chunks (rows of one
     sequence see different key counts, two sequences of different lengths):
     the same result as one split per row, to the bf16 rounding of P against
     each split's reference, on every row; checked against the oracle's
-    latent attention on sampled rows."""
+    latent attention on sampled rows.  2 x 128 = 256 rows is the plan's
+    maximum, where every row gets exactly one split."""
     layer, w = ds_layer()
     rng = np.random.default_rng(12)
-    lens = np.array([3000, 700]) + 90
-    n_q = 90
+    lens = np.array(ctx) + n_q
     table_np, nb = W.block_table(lens, True, 13)
     img = np.zeros((nb, 64, 576), np.float32)
     rows_h = []
@@ -208,6 +209,10 @@ def test_balanced_causal_chunk():
     ob2, lb2 = _decode_once(layer, q, cache, table, kv, int(lens.max()),
                             B.MLA_SPLIT_BALANCED)
     assert torch.equal(ob, ob2) and torch.equal(lb, lb2)
+    if 2 * n_q == 256:
+        # the plan's 256 slots, one per row: every row is one split, written
+        # directly, with the arithmetic of n_split = 1
+        assert torch.equal(ob, o1) and torch.equal(lb, l1)
     assert_close("balanced vs one split", ob.cpu().numpy(), o1.cpu().numpy(),
                  "f32", tol=(3e-3, 2e-2))
     assert_close("balanced lse vs one split", lb.cpu().numpy(),
