@@ -146,20 +146,28 @@ __global__ __launch_bounds__(NT) void decode_simt_kernel(
 // O_j / (l_j s_j) with s_j the row's scale stored after the fp16 rows
 // (weight w_j l_j s_j), as the matrix-core decode writes them.
 // Shapes: TPH = 16 threads per head and CS = 4 splits per chunk for many
-// query rows; for few rows (a grid of a few dozen workgroups) TPH = 64 and
-// CS = 16 give each head four times the threads and each thread four times
-// the loads in flight.
-template <int NB, bool P16, int TPH, int CS>
+// query rows.  For few rows (a grid of a few dozen workgroups) TPH = 64,
+// CS = 16 and SG = 4 split groups: a head takes the whole workgroup, each
+// group of 64 threads merges its own quarter of the splits (one round of
+// loads for up to 64 splits), and group 0 merges the four partial results
+// through LDS with the same formula.
+template <int NB, bool P16, int TPH, int CS, int SG = 1>
 __global__ __launch_bounds__(256) void combine_rows_kernel(
     int n_h, int d_c, int n_split, int slots, const int2* __restrict__ plan,
     const float* __restrict__ o_part, const float* __restrict__ m_part,
     const float* __restrict__ l_part, float* __restrict__ o_lat,
     float* __restrict__ lse) {
   constexpr int VW = P16 ? 8 : 4;  // columns per vector
+  constexpr int HPW = 256 / (TPH * SG);  // heads per workgroup
+  static_assert(HPW >= 1 && HPW * TPH * SG == 256, "thread split");
   const int bq = blockIdx.x;
-  const int h = blockIdx.y * (256 / TPH) + (threadIdx.x / TPH);
+  const int hl = threadIdx.x / (TPH * SG);
+  const int sg = (threadIdx.x / TPH) % SG;
+  const int h = blockIdx.y * HPW + hl;
   const int q = threadIdx.x % TPH;
-  if (h >= n_h) return;
+  // (with SG > 1 the grid has exactly n_h / HPW columns: no thread leaves
+  // before the barrier below)
+  if (SG == 1 && h >= n_h) return;
   // the row's splits: slots slot0 .. slot0 + n_split - 1 (balanced plan, or
   // n_split per row)
   int slot0 = bq * n_split;
@@ -181,7 +189,11 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
 #pragma unroll
     for (int hh = 0; hh < VW / 4; ++hh)
       acc[b][hh] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j0 = 0; j0 < n_split; j0 += CS) {
+  // this group's splits: [j_lo, j_hi)
+  const int per = (n_split + SG - 1) / SG;
+  const int j_lo = min(sg * per, n_split);
+  const int j_hi = min(j_lo + per, n_split);
+  for (int j0 = j_lo; j0 < j_hi; j0 += CS) {
     float m[CS], l[CS], ps[CS];
     f32x4 v[CS][NB][VW / 4];
     // Every load is issued unconditionally from an in-range address (split
@@ -192,7 +204,7 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
     f32x4 rawf[CS][NB];
 #pragma unroll
     for (int u = 0; u < CS; ++u) {
-      const size_t r = row0 + (size_t)min(j0 + u, n_split - 1) * n_h;
+      const size_t r = row0 + (size_t)min(j0 + u, j_hi - 1) * n_h;
       m[u] = m_part[r];
       l[u] = l_part[r];
       ps[u] = P16 ? sc_part[r] : 1.0f;
@@ -207,7 +219,7 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
     }
 #pragma unroll
     for (int u = 0; u < CS; ++u) {
-      const bool ok = j0 + u < n_split;
+      const bool ok = j0 + u < j_hi;
       m[u] = ok ? m[u] : -INFINITY;
       l[u] = ok ? l[u] : 0.0f;
 #pragma unroll
@@ -254,6 +266,52 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(
             acc[b][hh][e] =
                 live ? __builtin_fmaf(wv, v[u][b][hh][e], acc[b][hh][e])
                      : acc[b][hh][e];
+    }
+    M = mc;
+  }
+  if constexpr (SG > 1) {
+    // groups 1 .. SG-1 hand (M, L, columns) to group 0, which merges them
+    // as one more chunk of splits (a group without splits has M = -inf)
+    __shared__ float sm_ml[HPW][SG][2];
+    __shared__ f32x4 sm_acc[HPW][SG][TPH][NB * VW / 4];
+    if (sg > 0) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int hh = 0; hh < VW / 4; ++hh)
+          sm_acc[hl][sg][q][b * (VW / 4) + hh] = acc[b][hh];
+      if (q == 0) {
+        sm_ml[hl][sg][0] = M;
+        sm_ml[hl][sg][1] = L;
+      }
+    }
+    __syncthreads();
+    if (sg > 0) return;
+    float mc = M;
+#pragma unroll
+    for (int g2 = 1; g2 < SG; ++g2) mc = fmaxf(mc, sm_ml[hl][g2][0]);
+    const float sc = M == -INFINITY ? 0.0f : exp2f(M - mc);
+    L *= sc;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int hh = 0; hh < VW / 4; ++hh) acc[b][hh] *= sc;
+#pragma unroll
+    for (int g2 = 1; g2 < SG; ++g2) {
+      const float mg = sm_ml[hl][g2][0];
+      const bool live = mg != -INFINITY;
+      const float w = live ? exp2f(mg - mc) : 0.0f;
+      L += live ? w * sm_ml[hl][g2][1] : 0.0f;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int hh = 0; hh < VW / 4; ++hh) {
+          const f32x4 a = sm_acc[hl][g2][q][b * (VW / 4) + hh];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[b][hh][e] =
+                live ? __builtin_fmaf(w, a[e], acc[b][hh][e]) : acc[b][hh][e];
+        }
     }
     M = mc;
   }
@@ -402,8 +460,9 @@ hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
   if (plan && !f16_parts) return hipErrorInvalidValue;
   if (!plan) slots = rows * n_split;
   // Many rows: 16 threads per head (16 heads per workgroup), 4 splits per
-  // chunk.  Few rows: 64 threads per head, 16 splits per chunk, so that a
-  // small batch still spreads over a few hundred waves.
+  // chunk.  Few rows: one head per workgroup in four split groups of 64
+  // threads, 16 splits per chunk, so that a small batch still spreads over
+  // hundreds of waves and up to 64 splits take one round of loads.
   const bool wide = (long)rows * ((d.n_h + 15) / 16) < 256;
 #define MLA_CMB(NB, P16, TPH, CS)                                             \
   hipLaunchKernelGGL((combine_rows_kernel<NB, P16, TPH, CS>),                  \
@@ -412,9 +471,14 @@ hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
                      plan, o_part, m_part, l_part, o_lat, lse)
   if (f16_parts) {
     if (d.d_c % 8 != 0 || d.d_c > 8 * 16 * 4) return hipErrorInvalidValue;
-    if (wide)
-      MLA_CMB(1, true, 64, 16);
-    else
+    if (wide) {
+      // one head per workgroup (64 threads x 8 columns cover d_c <= 512),
+      // four split groups
+      hipLaunchKernelGGL((combine_rows_kernel<1, true, 64, 16, 4>),
+                         dim3(rows, d.n_h), dim3(256), 0, stream, d.n_h,
+                         d.d_c, n_split, slots, plan, o_part, m_part, l_part,
+                         o_lat, lse);
+    } else
       MLA_CMB(4, true, 16, 4);
     return hipGetLastError();
   }
