@@ -248,13 +248,12 @@ hipError_t launch_absorb_fast(const mla_dims& d, int T, const float* parts,
                               const void* w_uk, const int32_t* pos,
                               const float* rope_cos, const float* rope_sin,
                               int max_pos, void* q_out, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(
-        (const void*)absorb_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-        AB_W_BYTES + AB_MAX_PARTS * AB_A_BYTES);
+  static std::atomic<unsigned long long> lds_set{0};
+  {
+    const hipError_t e = set_lds_limit_once(
+        (const void*)absorb_kernel, AB_W_BYTES + AB_MAX_PARTS * AB_A_BYTES,
+        lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int row_elems = d.d_c + d.d_r;
   const dim3 grid(d.n_h, d.d_c / AB_N);

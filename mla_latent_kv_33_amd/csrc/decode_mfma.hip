@@ -805,13 +805,11 @@ hipError_t launch_nw(const mla_dims& d, int B, int n_q, const void* q,
   const float scale_log2 =
       (float)(1.4426950408889634 / __builtin_sqrt((double)(d.d_h + d.d_r)));
   constexpr size_t lds = Cfg<NW>::LDS;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        (const void*)decode_mfma_kernel<NW>,
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static std::atomic<unsigned long long> lds_set{0};
+  {
+    const hipError_t e = set_lds_limit_once(
+        (const void*)decode_mfma_kernel<NW>, (int)lds, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int rows = B * n_q;
   const int slots = bal.plan ? BAL_SLOTS : rows * n_split;

@@ -496,13 +496,11 @@ hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
     return hipGetLastError();
   }
 #undef MLA_CMB
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(
-        (const void*)combine_kernel,
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)CMB_LDS_MAX);
+  static std::atomic<unsigned long long> lds_set{0};
+  {
+    const hipError_t e = set_lds_limit_once((const void*)combine_kernel,
+                                            (int)CMB_LDS_MAX, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   // heads per workgroup: their weights must fit the LDS
   const size_t per_head = (size_t)(n_split + 1) * sizeof(float);

@@ -791,13 +791,11 @@ __global__ __launch_bounds__(256, 2) void gemm_big_kernel(
 template <bool AF32>
 hipError_t launch_big(const GemmArgs& g, hipStream_t stream) {
   using L = BigCfg<AF32>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(
-        (const void*)gemm_big_kernel<AF32>,
-        hipFuncAttributeMaxDynamicSharedMemorySize, L::LDS);
+  static std::atomic<unsigned long long> lds_set{0};
+  {
+    const hipError_t e = set_lds_limit_once(
+        (const void*)gemm_big_kernel<AF32>, L::LDS, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int tiles_m = (g.M + L::BM - 1) / L::BM;
   const int tiles_n = (g.N + BG_BN - 1) / BG_BN;
@@ -1002,13 +1000,11 @@ template <int MT, int NTW, bool AF, bool HL>
 hipError_t launch_lds(const GemmArgs& g, dim3 grid, int k_chunk,
                       hipStream_t stream) {
   constexpr int lds = LdsCfg<MT, NTW, AF>::LDS;
-  static bool attr = false;
-  if (!attr) {
-    const hipError_t e = hipFuncSetAttribute(
-        (const void*)gemm_lds_kernel<MT, NTW, AF, HL>,
-        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  static std::atomic<unsigned long long> lds_set{0};
+  {
+    const hipError_t e = set_lds_limit_once(
+        (const void*)gemm_lds_kernel<MT, NTW, AF, HL>, lds, lds_set);
     if (e != hipSuccess) return e;
-    attr = true;
   }
   hipLaunchKernelGGL((gemm_lds_kernel<MT, NTW, AF, HL>), grid, dim3(256), lds,
                      stream, g.A, g.lda, g.a_bs, (const uint16_t*)g.B,

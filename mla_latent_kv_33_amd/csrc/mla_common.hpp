@@ -4,9 +4,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/mla.h"
 
 namespace mla {
+
+// Raises a kernel's dynamic-LDS limit to `bytes` once per device (the
+// setting belongs to the current device).  `done` is that kernel's set of
+// devices already configured; concurrent callers may both set it, which is
+// harmless, and the flag itself is race-free.
+inline hipError_t set_lds_limit_once(const void* kernel, int bytes,
+                                     std::atomic<unsigned long long>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = dev < 64 ? 1ull << dev : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;

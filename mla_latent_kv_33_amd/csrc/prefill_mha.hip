@@ -436,13 +436,11 @@ hipError_t launch_prefill_mha(const mla_dims& d, int B, int n_q,
                               float* o_v, float* lse, hipStream_t stream) {
   const float scale_log2 =
       (float)(1.4426950408889634 / __builtin_sqrt((double)(d.d_h + d.d_r)));
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(
-        (const void*)prefill_mha_kernel,
-        hipFuncAttributeMaxDynamicSharedMemorySize, PF_LDS);
+  static std::atomic<unsigned long long> lds_set{0};
+  {
+    const hipError_t e =
+        set_lds_limit_once((const void*)prefill_mha_kernel, PF_LDS, lds_set);
     if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const int ntq = (n_q + PF_QW - 1) / PF_QW;
   const long nwg = (long)B * d.n_h * ntq;
