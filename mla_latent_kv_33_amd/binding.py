@@ -102,8 +102,12 @@ def _check(fn: str, status: int):
 
 
 def _ptr(t: Optional[torch.Tensor]):
+    """Device pointer of a contiguous GPU tensor (every tensor argument of
+    the library is device memory; a host pointer would reach a kernel)."""
     if t is None:
         return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libmla must be on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensors passed to libmla must be contiguous")
     return ctypes.c_void_p(t.data_ptr())

@@ -8,6 +8,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 from mla_latent_kv_33_amd import binding as B
 from mla_latent_kv_33_amd import workloads as W
@@ -263,3 +264,11 @@ def test_query_mha_and_out_values_validation():
                               1 << 30, None) == SHAPE
     assert lib.mla_out_values(ctypes.byref(d), 0, None, None, None, None, 0,
                               None) == OK
+
+
+def test_binding_rejects_host_and_strided_tensors():
+    # every tensor argument of the library is device memory: a host tensor
+    # must be refused before any call, not handed to a kernel
+    with pytest.raises(ValueError, match="on the GPU"):
+        B._ptr(torch.zeros(8))
+    assert B._ptr(None) is None
