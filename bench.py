@@ -43,9 +43,6 @@ def kernel_source_hash():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # Clocks ramp up over the first few tens of milliseconds of sustained
-    # load (about 60 steps here); the warmup covers that ramp so that the
-    # timed steps see the steady state.
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="b64_ctx8k")
@@ -66,10 +63,20 @@ def parse():
                          "before the next launch, so each one costs a few "
                          "microseconds of idle GPU; the per-stage split is "
                          "taken from separate untimed steps by default.")
-    ap.add_argument("--event-every", type=int, default=8,
+    ap.add_argument("--event-every", type=int, default=2,
                     help="with --timed-events decode: record the pair of "
                          "events around the decode call in every N-th timed "
-                         "step (the decode duration is their average)")
+                         "step (the decode duration is their median)")
+    # The GPU's power management runs the first tens of milliseconds of a
+    # sustained load in a transient (here the decode kernel first runs at
+    # ~155 us, slows to ~190 us over the next ~30 steps, then settles near
+    # ~160 us).  Untimed steps for this long come before the warmup steps,
+    # so that the timed steps see the sustained state whatever W is.
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed steps for at least this long (wall clock) "
+                         "before the warmup steps")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured HBM-read and matrix-core rates")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for "
                          "scaling HBM byte counters)")
@@ -86,6 +93,45 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_each_way": n, "launches": 3}))
+
+
+def measure_peaks(B, torch, stream):
+    """Measured machine rates on this machine, in the power state the step
+    leaves: a plain read of a 1 GiB buffer (4x the Infinity Cache), and a
+    loop of independent bf16 32x32x16 MFMAs (include/mla_peaks.h).  Medians
+    of 10 launches each."""
+    import numpy as np
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    buf.random_(0, 255)
+    wgs_read = 4096
+    sink = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    mf_wgs, mf_iters = 512, 2048
+    mf_sink = torch.empty(B.lib().mla_peak_mfma_sink_bytes(mf_wgs),
+                          dtype=torch.uint8, device="cuda")
+    times = {"read": [], "mfma": []}
+    nbytes = flops = 0
+    for r in range(12):
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        nbytes = B.mla_peak_stream_read(buf, sink, wgs_read)
+        e1.record(stream)
+        flops = B.mla_peak_mfma_loop(mf_wgs, mf_iters, mf_sink)
+        e2.record(stream)
+        torch.cuda.synchronize()
+        if r >= 2:
+            times["read"].append(e0.elapsed_time(e1) * 1e-3)
+            times["mfma"].append(e1.elapsed_time(e2) * 1e-3)
+    t_read = float(np.median(times["read"]))
+    t_mfma = float(np.median(times["mfma"]))
+    del buf, sink, mf_sink
+    return {
+        "hbm_read_GBps": nbytes / t_read / 1e9,
+        "mfma_bf16_TFLOPs": flops / t_mfma / 1e12,
+        "how": "mla_peak_stream_read over a 1 GiB buffer (16-byte loads, "
+               f"{wgs_read} workgroups) and mla_peak_mfma_loop ({mf_wgs} "
+               f"workgroups x 4 waves x {mf_iters} x 8 independent "
+               "32x32x16 bf16 MFMAs); medians of 10 launches after 2, timed "
+               "with HIP events right after the timed steps"}
 
 
 def cpu_baseline(wl, sample):
@@ -215,6 +261,14 @@ def main():
             layer.out(out.o_lat.view(-1, d.n_h, d.d_c), u=out.u)
         if rec_all: e[4].record(stream)
 
+    # settle phase (untimed), then the W warmup steps
+    t_settle = time.perf_counter()
+    settle_steps = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(8):
+            step()
+        settle_steps += 8
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -228,8 +282,9 @@ def main():
     wall = time.perf_counter() - t0
     # attention stage (decode kernel + split combine, or the MHA prefill
     # call) inside the timed steps
-    t_dec_ms = float(np.mean([ev[i][2].elapsed_time(ev[i][3])
-                              for i in sampled]))
+    dec_samples = [ev[i][2].elapsed_time(ev[i][3]) for i in sampled]
+    t_dec_ms = float(np.median(dec_samples))
+    peaks = None if args.no_peaks else measure_peaks(B, torch, stream)
     if args.timed_events == "all":
         ev_st, n_st = ev, args.steps
     else:
@@ -343,12 +398,17 @@ def main():
             "mfma_tflops": tflops,
             "mfma_frac": tflops / BF16_PEAK_TFLOPS,
             "decode_us": t_dec * 1e6,
+            "decode_us_min_max": [min(dec_samples) * 1e3,
+                                  max(dec_samples) * 1e3],
         },
         "decode_queries_per_s": queries / t_dec,
         "latent_cache_GBps": cache_bytes / t_dec / 1e9,
-        "decode_timing": f"HIP events around the mla_decode call in "
-                         f"{len(sampled)} of the {args.steps} timed steps "
-                         f"(every {every})",
+        "decode_timing": f"median of HIP events around the attention "
+                         f"call in {len(sampled)} of the {args.steps} timed "
+                         f"steps (every {every})",
+        "settle": f"{settle_steps} untimed steps ({args.settle_ms:.0f} ms) "
+                  "before the warmup steps: the GPU's power management runs "
+                  "the first tens of ms of sustained load in a transient",
         "attention_alone_us": {
             "after_512MiB_write": att_us["write"],
             "after_512MiB_read": att_us["read"],
@@ -366,6 +426,11 @@ def main():
                                "every stage"),
         "kernel_source_hash": kernel_source_hash(),
     }
+    if peaks is not None:
+        result["peaks_measured"] = peaks
+        rf = result["roofline"]
+        rf["hbm_frac_achievable"] = achieved / peaks["hbm_read_GBps"]
+        rf["mfma_frac_achievable"] = tflops / peaks["mfma_bf16_TFLOPs"]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
     if mha or wl.name != "b64_ctx8k":

@@ -68,8 +68,8 @@ typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
 
 /* Layer dimensions.  Bracketed names are the usual hyper-parameter names
  * ('MiniMind 学习笔记 10', section 8).  Requirements: all positive, d_r even,
- * block_size a power of two; for BF16 also d, d_h, d_c, d_r and d_cq
- * multiples of 8 (else MLA_ERR_UNSUPPORTED).  The matrix-core decode kernel
+ * block_size a power of two; for BF16 also d, d_cq, d_c and n_h * d_h
+ * multiples of 64 and d_h, d_r multiples of 8 (else MLA_ERR_UNSUPPORTED).  The matrix-core decode kernel
  * takes BF16 with d_c = 512, d_r = 64, block_size 64 and n_h = 32, 64 or a
  * multiple of 128; other dims run on the general (SIMT) decode kernel. */
 typedef struct {
@@ -208,7 +208,17 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
  *   o_lat       [B][n_q][n_h][d_c] fp32 output
  *   lse         [B][n_q][n_h] fp32 output, may be NULL
  *   ws          at least mla_decode_workspace_bytes(dims, B, n_q,
- *               max_kv_len, n_split)
+ *               max_kv_len, n_split).  With balanced splits the call
+ *               leaves its plan there for inspection: int32 pairs (first
+ *               partial slot, split count) per query row b * n_q + i, at
+ *               byte offset W - ceil256(8 B n_q), W = the size
+ *               mla_decode_workspace_bytes returns, ceil256 rounding up to
+ *               a multiple of 256.  A row's splits take consecutive slots,
+ *               rows in order; split j of a row with nb visible blocks
+ *               and c splits covers blocks [j nb / c, (j + 1) nb / c).
+ * A query row that sees no key (kv_lens[b] < n_q, outside the contract
+ * above) gets o_lat = 0 and lse = -inf with one split; never a write
+ * through a missing partial buffer.
  * ---------------------------------------------------------------------- */
 #define MLA_SPLIT_BALANCED (-1)
 size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t B,
@@ -225,6 +235,30 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, int32_t n_q,
 /* The split count mla_decode uses for n_split = 0 (host only). */
 int32_t mla_decode_auto_splits(const mla_dims* dims, int32_t B, int32_t n_q,
                                int32_t max_kv_len);
+
+/* Opt-in check of the device-side values the calls above trust, on HOST
+ * copies of them (the caller copies the block table and lengths back, or
+ * checks them before uploading).  Every decode step reads all of a
+ * sequence's cached tokens through its block table ('MLA：潜在表示压缩与
+ * 解耦 RoPE', section 1), so one bad entry sends a kernel outside the pool.
+ *
+ *   block_table  host [B][max_blocks] int32
+ *   kv_lens      host [B] int32
+ *   n_q          queries per sequence of the step (1 for a decode step)
+ *   max_kv_len   the host bound passed to mla_decode (<= 0: not checked)
+ *   bad_seq      host, may be NULL: receives the first offending sequence
+ *                (-1 when none)
+ * For every sequence b: n_q <= kv_lens[b] (and <= max_kv_len when that is
+ * positive), ceil(kv_lens[b] / block_size) <= max_blocks, and the entries
+ * block_table[b][0 .. ceil(kv_lens[b] / block_size) - 1] lie in
+ * [0, num_blocks).  Returns MLA_OK, MLA_ERR_NULL (a required pointer),
+ * MLA_ERR_SHAPE (B, max_blocks, n_q, block_size or num_blocks <= 0) or
+ * MLA_ERR_RANGE (a violation).  Reads only; touches no device. */
+mla_status mla_validate_block_table(const int32_t* block_table, int32_t B,
+                                    int32_t max_blocks, const int32_t* kv_lens,
+                                    int32_t n_q, int32_t block_size,
+                                    int32_t num_blocks, int32_t max_kv_len,
+                                    int32_t* bad_seq);
 
 /* ------------------------------------------------------------------------
  * MHA-path chunked prefill: explicit per-head keys and values.

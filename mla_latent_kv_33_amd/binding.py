@@ -16,7 +16,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmla.so")
+# MLA_LIBRARY names another build of the same library (the host
+# AddressSanitizer build of the ABI tests); the in-tree libmla.so otherwise.
+LIB_PATH = os.environ.get("MLA_LIBRARY") or os.path.join(_HERE, "libmla.so")
 
 MLA_F32 = 0
 MLA_BF16 = 1
@@ -59,6 +61,7 @@ _SIGNATURES = {
                           _S, _P]),
     "mla_decode_workspace_bytes": (_S, [_DP, _I, _I, _I, _I]),
     "mla_decode_auto_splits": (_I, [_DP, _I, _I, _I]),
+    "mla_validate_block_table": (_I, [_P, _I, _I, _P, _I, _I, _I, _I, _P]),
     "mla_decode": (_I, [_DP, _I, _I, _P, _P, _I, _P, _I, _P, _I, _I, _I, _P,
                         _P, _P, _S, _P]),
     "mla_query_mha": (_I, [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
@@ -69,6 +72,11 @@ _SIGNATURES = {
     "mla_out_values": (_I, [_DP, _I, _P, _P, _P, _P, _S, _P]),
     "mla_out_workspace_bytes": (_S, [_DP, _I]),
     "mla_out": (_I, [_DP, _I, _P, _P, _P, _P, _P, _S, _P]),
+    # machine-rate kernels (include/mla_peaks.h), measurement only
+    "mla_peak_stream_read": (_I, [_P, _S, _P, _I, _P]),
+    "mla_peak_mfma_sink_bytes": (_S, [_I]),
+    "mla_peak_mfma_flops": (ctypes.c_double, [_I, _I]),
+    "mla_peak_mfma_loop": (_I, [_I, _I, _P, _P]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -101,16 +109,72 @@ def _check(fn: str, status: int):
         raise MlaError(fn, status, lib().mla_status_string(status).decode())
 
 
-def _ptr(t: Optional[torch.Tensor]):
-    """Device pointer of a contiguous GPU tensor (every tensor argument of
-    the library is device memory; a host pointer would reach a kernel)."""
+def _layer_dtype(dims: MlaDims) -> torch.dtype:
+    return torch.bfloat16 if dims.dtype == MLA_BF16 else torch.float32
+
+
+def _spec(t: Optional[torch.Tensor], name: str = "tensor", dtype=None,
+          shape=None, numel: Optional[int] = None,
+          ndim: Optional[int] = None) -> None:
+    """Element type, rank, shape (None entries are free) and element count
+    of a tensor argument, as include/mla.h states them."""
+    if t is None:
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got "
+                         f"{tuple(t.shape)}")
+    if shape is not None:
+        if t.dim() != len(shape) or any(
+                e is not None and e != a for e, a in zip(shape, t.shape)):
+            want = tuple("*" if e is None else e for e in shape)
+            raise ValueError(f"{name} must have shape {want}, got "
+                             f"{tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got "
+                         f"{t.numel()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: Optional[torch.Tensor], name: str = "tensor", **spec):
+    """Device pointer of a contiguous GPU tensor on the current device.
+
+    Every tensor argument of the library is device memory read or written
+    with the element type and extent that include/mla.h states; a host
+    pointer, another device's memory, a wrong element type (an int64 index
+    tensor read as int32) or a short buffer would reach a kernel.
+    """
     if t is None:
         return None
+    _spec(t, name, **spec)
     if not t.is_cuda:
-        raise ValueError("tensors passed to libmla must be on the GPU")
-    if not t.is_contiguous():
-        raise ValueError("tensors passed to libmla must be contiguous")
+        raise ValueError(f"{name} must be on the GPU (libmla takes device "
+                         "memory)")
+    cur = torch.cuda.current_device()
+    if t.device.index != cur:
+        raise ValueError(f"{name} is on cuda:{t.device.index}; the current "
+                         f"device is cuda:{cur}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _ptrs(*args):
+    """Pointers of (tensor, name, spec) triples: every element type and
+    shape is checked before any device check, so a malformed argument is
+    named even when another one sits on the wrong device."""
+    for t, name, spec in args:
+        _spec(t, name, **spec)
+    return [_ptr(t, name) for t, name, _ in args]
+
+
+def _a(t, name, dtype=None, shape=None, **kw):
+    """One argument triple for _ptrs."""
+    return (t, name, dict(dtype=dtype, shape=shape, **kw))
+
+
+_I32 = torch.int32
+_F32 = torch.float32
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -165,8 +229,72 @@ def mla_decode_auto_splits(dims: MlaDims, B: int, n_q: int,
                                         max_kv_len)
 
 
+def mla_validate_block_table(block_table, kv_lens, n_q: int,
+                             block_size: int, num_blocks: int,
+                             max_kv_len: int = 0) -> int:
+    """Host check of a block table and lengths (numpy or CPU tensors);
+    raises MlaError (status MLA_ERR_RANGE) naming the first bad sequence."""
+    table = np.ascontiguousarray(np.asarray(block_table), dtype=np.int32)
+    lens = np.ascontiguousarray(np.asarray(kv_lens), dtype=np.int32)
+    if table.ndim != 2 or lens.ndim != 1 or table.shape[0] < lens.shape[0]:
+        raise ValueError("block_table must be [B, max_blocks] and kv_lens [B]")
+    bad = ctypes.c_int32(-1)
+    st = lib().mla_validate_block_table(
+        table.ctypes.data_as(_P), lens.shape[0], table.shape[1],
+        lens.ctypes.data_as(_P), n_q, block_size, num_blocks, max_kv_len,
+        ctypes.byref(bad))
+    if st != 0:
+        raise MlaError("mla_validate_block_table", st,
+                       f"{mla_status_string(st)}; sequence {bad.value}")
+    return 0
+
+
 def mla_out_workspace_bytes(dims: MlaDims, T: int) -> int:
     return lib().mla_out_workspace_bytes(ctypes.byref(dims), T)
+
+
+def _append_args(dims, h, seq_idx, pos, w_dkv, w_kr, rope_cos, rope_sin,
+                 block_table, cache):
+    """Argument triples of the append (include/mla.h layouts)."""
+    lt = _layer_dtype(dims)
+    T = h.shape[0]
+    return [_a(h, "h", lt, (T, dims.d)),
+            _a(seq_idx, "seq_idx", _I32, (T,)),
+            _a(pos, "pos", _I32, (T,)),
+            _a(w_dkv, "w_dkv", lt, (dims.d_c, dims.d)),
+            _a(w_kr, "w_kr", lt, (dims.d_r, dims.d)),
+            _a(rope_cos, "rope_cos", _F32, (None, dims.d_r // 2)),
+            _a(rope_sin, "rope_sin", _F32, tuple(rope_cos.shape)),
+            _a(block_table, "block_table", _I32, ndim=2),
+            _a(cache, "cache", lt,
+               (None, dims.block_size, dims.d_c + dims.d_r))]
+
+
+def _query_args(dims, h, pos, w_dq, w_uq, w_qr, rope_cos, rope_sin):
+    """Argument triples of the query path (include/mla.h layouts)."""
+    lt = _layer_dtype(dims)
+    T = h.shape[0]
+    return [_a(h, "h", lt, (T, dims.d)),
+            _a(pos, "pos", _I32, (T,)),
+            _a(w_dq, "w_dq", lt, (dims.d_cq, dims.d)),
+            _a(w_uq, "w_uq", lt, (dims.n_h * dims.d_h, dims.d_cq)),
+            _a(w_qr, "w_qr", lt, (dims.n_h * dims.d_r, dims.d_cq)),
+            _a(rope_cos, "rope_cos", _F32, (None, dims.d_r // 2)),
+            _a(rope_sin, "rope_sin", _F32, tuple(rope_cos.shape))]
+
+
+def _attention_args(dims, q, cache, block_table, kv_lens, qwidth):
+    """Argument triples of q, cache, block_table and kv_lens."""
+    lt = _layer_dtype(dims)
+    B, n_q = q.shape[0], q.shape[1]
+    if block_table.dim() == 2 and block_table.shape[0] < B:
+        raise ValueError(f"block_table has {block_table.shape[0]} rows for "
+                         f"{B} sequences")
+    return [_a(q, "q", lt, (B, n_q, dims.n_h, qwidth)),
+            _a(cache, "cache", lt,
+               (None, dims.block_size, dims.d_c + dims.d_r)),
+            _a(block_table, "block_table", _I32, ndim=2),
+            _a(kv_lens, "kv_lens", _I32, (B,))]
 
 
 def mla_append_cache(dims: MlaDims, h, seq_idx, pos, w_dkv, w_kr, rope_cos,
@@ -174,13 +302,14 @@ def mla_append_cache(dims: MlaDims, h, seq_idx, pos, w_dkv, w_kr, rope_cos,
     """c_KV = W_DKV h and k_R = RoPE(W_KR h) for T = h.shape[0] tokens,
     written into the paged cache (see include/mla.h)."""
     T = h.shape[0]
+    p = _ptrs(*_append_args(dims, h, seq_idx, pos, w_dkv, w_kr, rope_cos,
+                            rope_sin, block_table, cache))
     ws, wsb = _workspace(mla_append_workspace_bytes(dims, T) if T else 0,
                          h.device, ws)
     _check("mla_append_cache", lib().mla_append_cache(
-        ctypes.byref(dims), T, _ptr(h), _ptr(seq_idx), _ptr(pos), _ptr(w_dkv),
-        _ptr(w_kr), _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
-        _ptr(block_table), block_table.shape[1], _ptr(cache), cache.shape[0],
-        _ptr(ws), wsb, _stream(stream)))
+        ctypes.byref(dims), T, *p[:7], rope_cos.shape[0], p[7],
+        block_table.shape[1], p[8], cache.shape[0], _ptr(ws, "ws"), wsb,
+        _stream(stream)))
 
 
 def mla_append_cache_rmsnorm(dims: MlaDims, h, seq_idx, pos, w_dkv, w_kr,
@@ -189,26 +318,32 @@ def mla_append_cache_rmsnorm(dims: MlaDims, h, seq_idx, pos, w_dkv, w_kr,
     """mla_append_cache with the latent RMS-normalised (weight kv_norm_w,
     epsilon eps) before it is cached (see include/mla.h)."""
     T = h.shape[0]
+    p = _ptrs(*_append_args(dims, h, seq_idx, pos, w_dkv, w_kr, rope_cos,
+                            rope_sin, block_table, cache),
+              _a(kv_norm_w, "kv_norm_w", _layer_dtype(dims), (dims.d_c,)))
     ws, wsb = _workspace(mla_append_workspace_bytes(dims, T) if T else 0,
                          h.device, ws)
     _check("mla_append_cache_rmsnorm", lib().mla_append_cache_rmsnorm(
-        ctypes.byref(dims), T, _ptr(h), _ptr(seq_idx), _ptr(pos), _ptr(w_dkv),
-        _ptr(w_kr), _ptr(kv_norm_w), float(eps), _ptr(rope_cos),
-        _ptr(rope_sin), rope_cos.shape[0], _ptr(block_table),
-        block_table.shape[1], _ptr(cache), cache.shape[0], _ptr(ws), wsb,
-        _stream(stream)))
+        ctypes.byref(dims), T, *p[:5], p[9], float(eps), p[5], p[6],
+        rope_cos.shape[0], p[7], block_table.shape[1], p[8], cache.shape[0],
+        _ptr(ws, "ws"), wsb, _stream(stream)))
 
 
 def mla_absorb_q(dims: MlaDims, h, pos, w_dq, w_uq, w_qr, w_uk, rope_cos,
                  rope_sin, q_out, ws=None, stream=None):
     """q_out[t, h] = [W_UK_h^T q_C | RoPE(W_QR c_Q)_h] (see include/mla.h)."""
     T = h.shape[0]
+    lt = _layer_dtype(dims)
+    p = _ptrs(*_query_args(dims, h, pos, w_dq, w_uq, w_qr, rope_cos,
+                           rope_sin),
+              _a(w_uk, "w_uk", lt, (dims.n_h * dims.d_h, dims.d_c)),
+              _a(q_out, "q_out", lt,
+                 numel=T * dims.n_h * (dims.d_c + dims.d_r)))
     ws, wsb = _workspace(mla_absorb_workspace_bytes(dims, T) if T else 0,
                          h.device, ws)
     _check("mla_absorb_q", lib().mla_absorb_q(
-        ctypes.byref(dims), T, _ptr(h), _ptr(pos), _ptr(w_dq), _ptr(w_uq),
-        _ptr(w_qr), _ptr(w_uk), _ptr(rope_cos), _ptr(rope_sin),
-        rope_cos.shape[0], _ptr(q_out), _ptr(ws), wsb, _stream(stream)))
+        ctypes.byref(dims), T, *p[:5], p[7], p[5], p[6], rope_cos.shape[0],
+        p[8], _ptr(ws, "ws"), wsb, _stream(stream)))
 
 
 def mla_decode(dims: MlaDims, q, cache, block_table, kv_lens, max_kv_len: int,
@@ -217,36 +352,47 @@ def mla_decode(dims: MlaDims, q, cache, block_table, kv_lens, max_kv_len: int,
     """Latent attention of q [B, n_q, n_h, d_c + d_r] over the cache
     (see include/mla.h); writes o_lat [B, n_q, n_h, d_c] fp32 and lse."""
     B, n_q = q.shape[0], q.shape[1]
+    p = _ptrs(*_attention_args(dims, q, cache, block_table, kv_lens,
+                               dims.d_c + dims.d_r),
+              _a(o_lat, "o_lat", _F32,
+                 numel=B * n_q * dims.n_h * dims.d_c),
+              _a(lse, "lse", _F32, numel=B * n_q * dims.n_h))
     ws, wsb = _workspace(
         mla_decode_workspace_bytes(dims, B, n_q, max_kv_len, n_split),
         q.device, ws)
     _check("mla_decode", lib().mla_decode(
-        ctypes.byref(dims), B, n_q, _ptr(q), _ptr(cache), cache.shape[0],
-        _ptr(block_table), block_table.shape[1], _ptr(kv_lens), max_kv_len,
-        causal, n_split, _ptr(o_lat), _ptr(lse), _ptr(ws), wsb,
-        _stream(stream)))
+        ctypes.byref(dims), B, n_q, p[0], p[1], cache.shape[0], p[2],
+        block_table.shape[1], p[3], max_kv_len, causal, n_split, p[4], p[5],
+        _ptr(ws, "ws"), wsb, _stream(stream)))
 
 
 def mla_out(dims: MlaDims, o_lat, w_uv, w_o, u, ws=None, stream=None):
     """u = W_O [W_UV_h o_lat_h]_h for T = o_lat.shape[0] rows."""
     T = o_lat.shape[0]
+    lt = _layer_dtype(dims)
+    p = _ptrs(_a(o_lat, "o_lat", _F32, numel=T * dims.n_h * dims.d_c),
+              _a(w_uv, "w_uv", lt, (dims.n_h * dims.d_h, dims.d_c)),
+              _a(w_o, "w_o", lt, (dims.d, dims.n_h * dims.d_h)),
+              _a(u, "u", lt, numel=T * dims.d))
     ws, wsb = _workspace(mla_out_workspace_bytes(dims, T) if T else 0,
                          o_lat.device, ws)
     _check("mla_out", lib().mla_out(
-        ctypes.byref(dims), T, _ptr(o_lat), _ptr(w_uv), _ptr(w_o), _ptr(u),
-        _ptr(ws), wsb, _stream(stream)))
+        ctypes.byref(dims), T, *p, _ptr(ws, "ws"), wsb, _stream(stream)))
 
 
 def mla_query_mha(dims: MlaDims, h, pos, w_dq, w_uq, w_qr, rope_cos, rope_sin,
                   q_out, ws=None, stream=None):
     """q_out[t, h] = [q_C | RoPE(q_R)] without absorption (see include/mla.h)."""
     T = h.shape[0]
+    p = _ptrs(*_query_args(dims, h, pos, w_dq, w_uq, w_qr, rope_cos,
+                           rope_sin),
+              _a(q_out, "q_out", _layer_dtype(dims),
+                 numel=T * dims.n_h * (dims.d_h + dims.d_r)))
     ws, wsb = _workspace(mla_absorb_workspace_bytes(dims, T) if T else 0,
                          h.device, ws)
     _check("mla_query_mha", lib().mla_query_mha(
-        ctypes.byref(dims), T, _ptr(h), _ptr(pos), _ptr(w_dq), _ptr(w_uq),
-        _ptr(w_qr), _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
-        _ptr(q_out), _ptr(ws), wsb, _stream(stream)))
+        ctypes.byref(dims), T, *p[:7], rope_cos.shape[0], p[7],
+        _ptr(ws, "ws"), wsb, _stream(stream)))
 
 
 def mla_prefill_mha_workspace_bytes(dims: MlaDims, B: int,
@@ -261,20 +407,49 @@ def mla_prefill_mha(dims: MlaDims, q, cache, block_table, kv_lens,
     """Explicit-key attention of the chunk q [B, n_q, n_h, d_h + d_r] over
     the cache (see include/mla.h); writes o_v [B, n_q, n_h, d_h] fp32."""
     B, n_q = q.shape[0], q.shape[1]
+    lt = _layer_dtype(dims)
+    p = _ptrs(*_attention_args(dims, q, cache, block_table, kv_lens,
+                               dims.d_h + dims.d_r),
+              _a(w_uk, "w_uk", lt, (dims.n_h * dims.d_h, dims.d_c)),
+              _a(w_uv, "w_uv", lt, (dims.n_h * dims.d_h, dims.d_c)),
+              _a(o_v, "o_v", _F32, numel=B * n_q * dims.n_h * dims.d_h),
+              _a(lse, "lse", _F32, numel=B * n_q * dims.n_h))
     ws, wsb = _workspace(mla_prefill_mha_workspace_bytes(dims, B, max_kv_len),
                          q.device, ws)
     _check("mla_prefill_mha", lib().mla_prefill_mha(
-        ctypes.byref(dims), B, n_q, _ptr(q), _ptr(cache), cache.shape[0],
-        _ptr(block_table), block_table.shape[1], _ptr(kv_lens), max_kv_len,
-        causal, _ptr(w_uk), _ptr(w_uv), _ptr(o_v), _ptr(lse), _ptr(ws), wsb,
-        _stream(stream)))
+        ctypes.byref(dims), B, n_q, p[0], p[1], cache.shape[0], p[2],
+        block_table.shape[1], p[3], max_kv_len, causal, *p[4:],
+        _ptr(ws, "ws"), wsb, _stream(stream)))
 
 
 def mla_out_values(dims: MlaDims, o_v, w_o, u, ws=None, stream=None):
     """u = W_O o for value-space o [T, n_h * d_h] fp32."""
     T = o_v.shape[0]
+    lt = _layer_dtype(dims)
+    p = _ptrs(_a(o_v, "o_v", _F32, numel=T * dims.n_h * dims.d_h),
+              _a(w_o, "w_o", lt, (dims.d, dims.n_h * dims.d_h)),
+              _a(u, "u", lt, numel=T * dims.d))
     ws, wsb = _workspace(mla_out_workspace_bytes(dims, T) if T else 0,
                          o_v.device, ws)
     _check("mla_out_values", lib().mla_out_values(
-        ctypes.byref(dims), T, _ptr(o_v), _ptr(w_o), _ptr(u), _ptr(ws), wsb,
+        ctypes.byref(dims), T, *p, _ptr(ws, "ws"), wsb, _stream(stream)))
+
+
+def mla_peak_stream_read(buf, sink, workgroups: int, stream=None):
+    """One read of the whole device buffer `buf` (include/mla_peaks.h)."""
+    nbytes = buf.numel() * buf.element_size()
+    _check("mla_peak_stream_read", lib().mla_peak_stream_read(
+        _ptr(buf, "buf"), nbytes, _ptr(sink, "sink"), workgroups,
         _stream(stream)))
+    return nbytes
+
+
+def mla_peak_mfma_loop(workgroups: int, iters: int, sink, stream=None):
+    """One launch of the matrix-core loop; returns its flop count."""
+    _spec(sink, "sink", numel=None)
+    if sink.numel() * sink.element_size() < \
+            lib().mla_peak_mfma_sink_bytes(workgroups):
+        raise ValueError("sink is smaller than mla_peak_mfma_sink_bytes")
+    _check("mla_peak_mfma_loop", lib().mla_peak_mfma_loop(
+        workgroups, iters, _ptr(sink, "sink"), _stream(stream)))
+    return lib().mla_peak_mfma_flops(workgroups, iters)

@@ -346,8 +346,15 @@ decode_mfma_kernel(
   const int blk1 = (int)((long)(split + 1) * nblk / n_split);
   const size_t row_base = ((size_t)slot0 + split) * n_h;
 
-  if (blk0 >= blk1) {  // empty split: no keys, weight zero in the combine
-    if (g == 0) {
+  if (blk0 >= blk1) {
+    // No visible key (an empty split, or kv_len < n_q): weight zero in the
+    // combine.  With one split there are no partials; the row's output is
+    // written as zeros with lse = -inf instead.
+    if (n_split == 1) {
+      float* dst = o_final + ((size_t)bq * n_h + head) * DC;
+      for (int c = 4 * g; c < DC; c += 8) *(f32x4*)(dst + c) = (f32x4){0, 0, 0, 0};
+      if (g == 0 && lse_final) lse_final[(size_t)bq * n_h + head] = -INFINITY;
+    } else if (g == 0) {
       m_part[row_base + head] = -INFINITY;
       l_part[row_base + head] = 0.0f;
     }

@@ -58,7 +58,14 @@ __global__ __launch_bounds__(NT) void decode_simt_kernel(
   const int tok1 = min(visible, (int)((long)(split + 1) * nblk / n_split) * bs);
   const size_t row_id = ((size_t)bq * n_split + split) * n_h + h;
   if (tok0 >= tok1) {
-    if (tid == 0) {
+    // No visible key (an empty split, or kv_len < n_q): weight zero in the
+    // combine.  With one split there are no partials; the row's output is
+    // written as zeros with lse = -inf instead.
+    if (n_split == 1) {
+      float* dst = o_final + ((size_t)bq * n_h + h) * d_c;
+      for (int j = tid; j < d_c; j += NT) dst[j] = 0.0f;
+      if (tid == 0 && lse_final) lse_final[(size_t)bq * n_h + h] = -INFINITY;
+    } else if (tid == 0) {
       m_part[row_id] = -INFINITY;
       l_part[row_id] = 0.0f;
     }

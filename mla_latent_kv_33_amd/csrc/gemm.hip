@@ -15,13 +15,8 @@
 //     split K, each K chunk writing its own partial C (summed by the
 //     consumer), which keeps results deterministic.  It also reads and
 //     writes fp32 activations pre-split into bf16 hi|lo pairs.
-//   * stream (M <= 64, other K % 16 == 0): weights straight into registers.
-//   * skinny (M <= 64, NT): general fallback.  B fragments are loaded
-//     straight from HBM into registers in MFMA layout; the four waves of a
-//     workgroup interleave their 16-wide k-steps so that together they read
-//     each weight row in 128-byte runs, and sum their partial tiles through
-//     LDS.
-//   * tiled (any M, NT or NN): 128x128x32 tiles staged through padded LDS,
+//   * tiled (any M, NT or NN; the fallback for shapes the others do not
+//     take): 128x128x32 tiles staged through padded LDS,
 //     2x2 waves of 64x64; NN weights are read with ds_read_b64_tr_b16 so the
 //     MFMA still sees k-contiguous B fragments.
 //   * big (M >= 128; NT, K >= 256): 128x128 tiles (64x128 with fp32
@@ -76,280 +71,6 @@ __device__ __forceinline__ const uint16_t* brow(const uint16_t* B,
                                                 const uint16_t* B2, int nb1,
                                                 long ldb, int n) {
   return n < nb1 ? B + (long)n * ldb : B2 + (long)(n - nb1) * ldb;
-}
-
-// ---------------------------------------------------------------- skinny
-constexpr int SK_WAVES = 4;
-constexpr int SK_UNROLL = 4;
-
-template <int MT, bool AF32>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(
-    const void* __restrict__ Av, long lda, long a_bs,
-    const uint16_t* __restrict__ B, const uint16_t* __restrict__ B2, int nb1,
-    long ldb, long b_bs, float* __restrict__ C, long ldc, long c_bs, long c_ks,
-    int M, int N, int K, int k_chunk) {
-  __shared__ float red[SK_WAVES - 1][MT][16][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int g = lane >> 5;
-  const int col = lane & 31;
-  const int n0 = blockIdx.x * 32;
-  const int kz = blockIdx.y;
-  const int z = blockIdx.z;
-  const int kbeg = kz * k_chunk;
-  const int kend = min(K, kbeg + k_chunk);
-
-  const int n = n0 + col;
-  const bool n_ok = n < N;
-  const uint16_t* bz = B + z * b_bs;
-  const uint16_t* b2z = B2 ? B2 + z * b_bs : nullptr;
-  const uint16_t* brow_p = n_ok ? brow(bz, b2z, nb1, ldb, n) : bz;
-
-  f32x16 acc[MT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
-
-  // wave w takes k-steps kbeg + 16 (w + 4 j)
-  for (int k0 = kbeg + 16 * wave; k0 < kend; k0 += 16 * SK_WAVES * SK_UNROLL) {
-    bf16x8 bf[SK_UNROLL];
-#pragma unroll
-    for (int u = 0; u < SK_UNROLL; ++u) {
-      const int k = k0 + 16 * SK_WAVES * u + 8 * g;
-      bf[u] = load8_bf16(brow_p, k, kend, n_ok && k0 + 16 * SK_WAVES * u < kend);
-    }
-#pragma unroll
-    for (int u = 0; u < SK_UNROLL; ++u) {
-      const int k = k0 + 16 * SK_WAVES * u + 8 * g;
-      if (k0 + 16 * SK_WAVES * u >= kend) break;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = 32 * mt + col;
-        const bool m_ok = m < M;
-        if (AF32) {
-          const float* ar = (const float*)Av + z * a_bs + (long)m * lda;
-          float x[8];
-          load8_f32(ar, k, kend, m_ok, x);
-          bf16x8 hi, lo;
-          split_hi_lo(x, hi, lo);
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, bf[u], acc[mt],
-                                                            0, 0, 0);
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, bf[u], acc[mt],
-                                                            0, 0, 0);
-        } else {
-          const uint16_t* ar = (const uint16_t*)Av + z * a_bs + (long)m * lda;
-          const bf16x8 a = load8_bf16(ar, k, kend, m_ok);
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bf[u], acc[mt],
-                                                            0, 0, 0);
-        }
-      }
-    }
-  }
-
-  if (wave > 0) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) red[wave - 1][mt][r][lane] = acc[mt][r];
-  }
-  __syncthreads();
-  if (wave == 0) {
-    float* cz = C + z * c_bs + kz * c_ks;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = acc[mt][r];
-#pragma unroll
-        for (int w = 0; w < SK_WAVES - 1; ++w) v += red[w][mt][r][lane];
-        const int m = 32 * mt + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (m < M && n_ok) cz[(long)m * ldc + n] = v;
-      }
-  }
-}
-
-// ---------------------------------------------------------------- stream
-// Weight-streaming kernel for M <= 64 (decode batches), NT, K % 16 == 0.
-// Workgroup = 4 waves over 32 NTW output columns; wave w takes a contiguous
-// quarter of the workgroup's K chunk, so its consecutive k-steps read each
-// weight row in 128-byte runs, and every activation fragment it loads feeds
-// NTW column tiles.  Weight fragments are loaded straight from HBM into
-// registers PFB k-steps ahead (a ring of PFB x NTW fragments), activation
-// fragments PFA k-steps ahead.  The four partial tiles are summed through LDS
-// one column tile at a time; each K chunk writes its own partial C.  Rows
-// past M or N read a valid row and are dropped at the store.
-
-// Prefetch depth in k-steps, the same for weights and activations: loads
-// retire in order, so the shallower ring would set the depth of both.
-// About 144 VGPRs of ring: per step NTW weight fragments (4 VGPRs each) and
-// MT activation fragments (8 VGPRs fp32, 4 bf16).
-template <int MT, int NTW, bool AF32>
-struct StreamCfg {
-  static constexpr int PER_STEP = 4 * NTW + MT * (AF32 ? 8 : 4);
-  static constexpr int PF0 = 144 / PER_STEP;
-  static constexpr int PF = PF0 < 2 ? 2 : PF0 > 16 ? 16 : PF0;
-};
-
-template <int MT, int NTW, bool AF32>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(
-    const void* __restrict__ Av, long lda, long a_bs,
-    const uint16_t* __restrict__ B, const uint16_t* __restrict__ B2, int nb1,
-    long ldb, long b_bs, float* __restrict__ C, long ldc, long c_bs, long c_ks,
-    int M, int N, int K, int k_chunk) {
-  constexpr int PFB = StreamCfg<MT, NTW, AF32>::PF;
-  constexpr int PFA = PFB;
-  constexpr int R = PFB;
-  __shared__ float red[4][MT][16][64];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 5;
-  const int col = lane & 31;
-  // K chunk fastest in the launch order: workgroups are dealt to the XCDs
-  // round-robin, so with a power-of-two split each XCD works on the same
-  // chunk(s) and keeps their activation slice in its own L2.
-  const int kz = blockIdx.x;
-  const int n_base = blockIdx.y * 32 * NTW;
-  const int z = blockIdx.z;
-  const int kbeg = kz * k_chunk;
-  const int kend = min(K, kbeg + k_chunk);
-  const int steps = max(0, (kend - kbeg) / 16);
-  const int per = (steps + 3) / 4;
-  const int s0 = min(steps, wave * per);
-  const int nsteps = min(steps, s0 + per) - s0;
-  const int kw = kbeg + 16 * s0 + 8 * g;  // this lane's first k
-
-  const uint16_t* brow_p[NTW];
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    const int n = min(n_base + 32 * nt + col, N - 1);
-    brow_p[nt] = (n < nb1 ? B + z * b_bs + (long)n * ldb
-                          : B2 + z * b_bs + (long)(n - nb1) * ldb) + kw;
-  }
-  const char* arow_p[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = min(32 * mt + col, M - 1);
-    arow_p[mt] = AF32 ? (const char*)((const float*)Av + z * a_bs +
-                                      (long)m * lda + kw)
-                      : (const char*)((const uint16_t*)Av + z * a_bs +
-                                      (long)m * lda + kw);
-  }
-
-  struct AFrag {
-    f32x4 x0, x1;   // fp32 activations (AF32)
-    bf16x8 h;       // bf16 activations
-  };
-  auto load_b = [&](int j, bf16x8 (&dst)[NTW]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt)
-      dst[nt] = *(const bf16x8*)(brow_p[nt] + 16 * j);
-  };
-  auto load_a = [&](int j, AFrag (&dst)[MT]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (AF32) {
-        const float* p = (const float*)arow_p[mt] + 16 * j;
-        dst[mt].x0 = *(const f32x4*)p;
-        dst[mt].x1 = *(const f32x4*)(p + 4);
-      } else {
-        dst[mt].h = *(const bf16x8*)((const uint16_t*)arow_p[mt] + 16 * j);
-      }
-    }
-  };
-
-  f32x16 acc[MT][NTW];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.0f;
-
-  bf16x8 bq[PFB][NTW];
-  AFrag aq[PFA][MT];
-  // One k-step: consume ring slot u % PFB (weights) and u % PFA
-  // (activations), refill them with steps j + PFB and j + PFA (only those
-  // below nsteps when `guard`).
-  auto step = [&](int u, int j, bool guard) __attribute__((always_inline)) {
-    bf16x8 ahi[MT], alo[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (AF32)
-        split_hi_lo_hw(aq[u % PFA][mt].x0, aq[u % PFA][mt].x1, ahi[mt],
-                       alo[mt]);
-      else
-        ahi[mt] = aq[u % PFA][mt].h;
-    }
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            ahi[mt], bq[u % PFB][nt], acc[mt][nt], 0, 0, 0);
-        if (AF32)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              alo[mt], bq[u % PFB][nt], acc[mt][nt], 0, 0, 0);
-      }
-    if (!guard || j + PFA < nsteps) load_a(j + PFA, aq[u % PFA]);
-    if (!guard || j + PFB < nsteps) load_b(j + PFB, bq[u % PFB]);
-    // Keep each step's loads in that step: the scheduler would otherwise
-    // sink the prefetches next to their uses and wait for them at once.
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // Prologue in the loop's own issue order (step i issues A(i + PFA), then
-  // B(i + PFB)).  When the steady-state loop runs, its prologue is
-  // unconditional and is its only entry, so the loads outstanding at the
-  // loop entry line up with those at its back edge and the waits stay
-  // exact; the steady-state body has no branches.  The last < R + PFB steps
-  // run in an unrolled, guarded tail.
-  int jb = 0;
-  if (nsteps >= R + PFB) {
-#pragma unroll
-    for (int i = -PFB; i < 0; ++i) {
-      if (i + PFA >= 0) load_a(i + PFA, aq[i + PFA]);
-      load_b(i + PFB, bq[i + PFB]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    for (; jb + R + PFB <= nsteps; jb += R) {
-#pragma unroll
-      for (int u = 0; u < R; ++u) step(u, jb + u, false);
-    }
-  } else {
-#pragma unroll
-    for (int i = -PFB; i < 0; ++i) {
-      if (i + PFA >= 0 && i + PFA < nsteps) load_a(i + PFA, aq[i + PFA]);
-      if (i + PFB < nsteps) load_b(i + PFB, bq[i + PFB]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < R + PFB; ++u)
-    if (jb + u < nsteps) step(u, jb + u, true);
-
-  // Sum the four waves' tiles, one column tile at a time.  Accumulator
-  // register r of lane (col, g) is row 32 mt + 8 (r / 4) + 4 g + r % 4,
-  // column 32 nt + col.
-  float* cz = C + z * c_bs + kz * c_ks;
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) red[wave][mt][r][lane] = acc[mt][nt][r];
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < MT * 4; ++i) {
-      const int idx = threadIdx.x + 256 * i;
-      const int mt = idx >> 10, r = (idx >> 6) & 15, l = idx & 63;
-      const float v = red[0][mt][r][l] + red[1][mt][r][l] + red[2][mt][r][l] +
-                      red[3][mt][r][l];
-      const int m = 32 * mt + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-      const int n = n_base + 32 * nt + (l & 31);
-      if (m < M && n < N) cz[(long)m * ldc + n] = v;
-    }
-    __syncthreads();
-  }
 }
 
 // ------------------------------------------------------------------ ldsk
@@ -1075,48 +796,7 @@ void gemm_plan(const mla_dims& d, GemmArgs& g, int max_split) {
     g.m_split = (g.M > 32 && 2 * wgs <= 256) ? 2 : 1;
     return;
   }
-  if (g.K % 16) {
-    // Older skinny kernel: aim for >= ~1024 workgroups, >= 512 of K each.
-    const long tiles = (long)((g.N + 31) / 32) * g.batch;
-    int ks = 1;
-    while (tiles * ks < 1024 && (long)g.K / (ks * 2) >= 512 &&
-           ks * 2 <= max_split)
-      ks *= 2;
-    g.k_split = ks;
-    return;
-  }
-  // Streaming kernel: pick column tiles per wave and the K split that
-  // minimise the bytes moved (weights once, padded to whole column tiles;
-  // activations per column slice,
-  // mostly from L2; partial tiles written and read back) divided by the
-  // fraction of the 256 compute units the grid keeps busy.
-  const double a_el = g.a_f32 ? 4.0 : 2.0;
-  double best = 1e300;
-  for (int ntw = 4; ntw >= 1; --ntw) {
-    const long slices = (long)((g.N + 32 * ntw - 1) / (32 * ntw)) * g.batch;
-    // weight rows streamed, counting the padding of the last column tile
-    const double wbytes = 2.0 * slices * 32.0 * ntw * (double)g.K;
-    for (int s = 1; s <= max_split; ++s) {
-      const int kc = (g.K + s - 1) / s;
-      const int kc16 = (kc + 63) / 64 * 64;
-      if (s > 1 && kc16 < 256) break;   // at least 4 k-steps per wave
-      const int se = (g.K + kc16 - 1) / kc16;
-      if (se != s) continue;
-      const long wgs = slices * se;
-      const long rounds = (wgs + 255) / 256;
-      const double eff = (double)wgs / (rounds * 256.0);
-      const double parts = se > 1 ? 2.0 * se * g.M * (double)g.N * 4.0 *
-                                        g.batch
-                                  : 0.0;
-      const double abytes = 0.25 * slices * g.M * (double)g.K * a_el;
-      const double cost = (wbytes + parts + abytes) / eff;
-      if (cost < best * 0.999) {
-        best = cost;
-        g.ntw = ntw;
-        g.k_split = se;
-      }
-    }
-  }
+  // Other decode-batch shapes take the tiled kernel.
 }
 
 hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
@@ -1166,46 +846,6 @@ hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
 #undef MLA_LK_A
 #undef MLA_LK_NTW
 #undef MLA_LK
-  }
-  if (g.ntw > 0) {
-    const int kc = (g.K + ks - 1) / ks;
-    k_chunk = (kc + 63) / 64 * 64;
-    dim3 grid(ks, (g.N + 32 * g.ntw - 1) / (32 * g.ntw), g.batch);
-#define MLA_ST(MT, NTW, AF)                                                   \
-  hipLaunchKernelGGL((gemm_stream_kernel<MT, NTW, AF>), grid, dim3(256), 0,   \
-                     stream, g.A, g.lda, g.a_bs, B, B2, g.nb1, g.ldb, g.b_bs, \
-                     g.C, g.ldc, g.c_bs, g.c_ks, g.M, g.N, g.K, (int)k_chunk)
-#define MLA_ST_NTW(MT, AF)                          \
-  switch (g.ntw) {                                  \
-    case 1: MLA_ST(MT, 1, AF); break;               \
-    case 2: MLA_ST(MT, 2, AF); break;               \
-    case 3: MLA_ST(MT, 3, AF); break;               \
-    case 4: MLA_ST(MT, 4, AF); break;               \
-    default: MLA_ST(MT, 5, AF); break;              \
-  }
-    if (g.M <= 32) {
-      if (g.a_f32) { MLA_ST_NTW(1, true) } else { MLA_ST_NTW(1, false) }
-    } else {
-      if (g.a_f32) { MLA_ST_NTW(2, true) } else { MLA_ST_NTW(2, false) }
-    }
-#undef MLA_ST_NTW
-#undef MLA_ST
-    return hipGetLastError();
-  }
-  if (!g.b_nn && g.M <= 64) {
-    k_chunk = (k_chunk + 63) / 64 * 64;
-    dim3 grid((g.N + 31) / 32, ks, g.batch);
-#define MLA_SK(MT, AF)                                                       \
-  hipLaunchKernelGGL((gemm_skinny_kernel<MT, AF>), grid, dim3(256), 0,       \
-                     stream, g.A, g.lda, g.a_bs, B, B2, g.nb1, g.ldb, g.b_bs, \
-                     g.C, g.ldc, g.c_bs, g.c_ks, g.M, g.N, g.K, (int)k_chunk)
-    if (g.M <= 32) {
-      if (g.a_f32) MLA_SK(1, true); else MLA_SK(1, false);
-    } else {
-      if (g.a_f32) MLA_SK(2, true); else MLA_SK(2, false);
-    }
-#undef MLA_SK
-    return hipGetLastError();
   }
   k_chunk = (k_chunk + TB_K - 1) / TB_K * TB_K;
   const int tiles_n = (g.N + TB_N - 1) / TB_N;

@@ -39,11 +39,15 @@ bool dims_ok(const mla_dims* d) {
   return true;
 }
 
-// The bf16 kernels move 8 elements (16 bytes) at a time along every row.
+// The bf16 kernels move 8 elements (16 bytes) at a time along every row,
+// and the decode-batch projections stream their weights in 64-deep k steps:
+// every contraction length of a projection (d, d_cq, d_c, n_h d_h) is a
+// multiple of 64.
 bool dims_supported(const mla_dims* d) {
   if (d->dtype != MLA_BF16) return true;
-  return d->d % 8 == 0 && d->d_h % 8 == 0 && d->d_c % 8 == 0 &&
-         d->d_r % 8 == 0 && d->d_cq % 8 == 0;
+  return d->d % 64 == 0 && d->d_cq % 64 == 0 && d->d_c % 64 == 0 &&
+         ((long)d->n_h * d->d_h) % 64 == 0 && d->d_h % 8 == 0 &&
+         d->d_r % 8 == 0;
 }
 
 mla_status dev(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_DEVICE; }
@@ -483,6 +487,32 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, int32_t n_q,
   if (ns > 1)
     MLA_TRY(launch_combine(d, rows, ns, o_part, mfma, m_part, l_part, o_lat,
                            lse, s));
+  return MLA_OK;
+}
+
+mla_status mla_validate_block_table(const int32_t* block_table, int32_t B,
+                                    int32_t max_blocks, const int32_t* kv_lens,
+                                    int32_t n_q, int32_t block_size,
+                                    int32_t num_blocks, int32_t max_kv_len,
+                                    int32_t* bad_seq) {
+  if (bad_seq) *bad_seq = -1;
+  if (!block_table || !kv_lens) return MLA_ERR_NULL;
+  if (B <= 0 || max_blocks <= 0 || n_q <= 0 || block_size <= 0 ||
+      num_blocks <= 0)
+    return MLA_ERR_SHAPE;
+  for (int32_t b = 0; b < B; ++b) {
+    const long kv = kv_lens[b];
+    bool ok = kv >= n_q && (max_kv_len <= 0 || kv <= max_kv_len);
+    const long need = (kv + block_size - 1) / block_size;
+    ok = ok && need <= max_blocks;
+    const int32_t* row = block_table + (size_t)b * max_blocks;
+    for (long k = 0; ok && k < need; ++k)
+      ok = row[k] >= 0 && row[k] < num_blocks;
+    if (!ok) {
+      if (bad_seq) *bad_seq = b;
+      return MLA_ERR_RANGE;
+    }
+  }
   return MLA_OK;
 }
 

@@ -116,8 +116,7 @@ struct GemmArgs {
   long ldc = 0, c_bs = 0, c_ks = 0;
   int M = 0, N = 0, K = 0, batch = 1;
   int k_split = 1;
-  // > 0: register-streaming kernel with ntw 32-column tiles per wave;
-  // < 0: LDS-staged kernel with -ntw tiles per wave; 0: skinny / tiled.
+  // < 0: LDS-staged kernel with -ntw tiles per wave; 0: tiled (or big).
   int ntw = 0;
   // LDS-staged kernel: rows in blocks of 32, one workgroup per block (1 or 2)
   int m_split = 1;

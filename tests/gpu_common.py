@@ -70,3 +70,47 @@ def oracle_sequence(wl: W.Workload, weights, b: int, q_rows=None, heads=None):
     log(f"  oracle seq {b} (ctx {wl.ctx[b]}, queries "
         f"{'all' if q_rows is None else len(q_rows)}): {time.time() - t0:.1f}s")
     return ref
+
+
+def oracle_latent(wl: W.Workload, weights, b: int, q_rows=None):
+    """Oracle o_lat / lse of sequence b in the absorbed form only: the
+    query path and absorption of the new tokens (rows `q_rows`), then
+    attention over the latent rows.  The absorbed form equals the
+    non-absorbed attention (pinned on the CPU), and it costs one pass over
+    the rows per head, so it checks every sequence of a large batch."""
+    d = wl.dims
+    c_kv, k_r = context_latents(wl, weights, b)
+    h_new = W.hidden_states(d, wl.dtype, wl.seed, b, wl.ctx[b], wl.n_q)
+    pos = wl.ctx[b] + np.arange(wl.n_q)
+    c_new, kr_new = orc.kv_latent(h_new, pos, weights["w_dkv"],
+                                  weights["w_kr"], W.ROPE_BASE)
+    rows = np.concatenate([np.concatenate([c_kv, c_new]),
+                           np.concatenate([k_r, kr_new])], axis=1)
+    sel = np.arange(wl.n_q) if q_rows is None else np.asarray(q_rows)
+    q_c, q_r = orc.query(h_new[sel], pos[sel], weights["w_dq"],
+                         weights["w_uq"], weights["w_qr"], d.n_h, W.ROPE_BASE)
+    q = orc.absorb_query(q_c, q_r, weights["w_uk"])
+    return orc.latent_attention(q, pos[sel], rows, d.d_c, d.d_h)
+
+
+def check_all_sequences_latent(wl: W.Workload, weights, out, q_rows=None):
+    """o_lat and lse of every sequence (rows `q_rows` of each) against
+    oracle_latent; logs the worst errors."""
+    rows = np.arange(wl.n_q) if q_rows is None else np.asarray(q_rows)
+    o_all = out.o_lat[:, rows].cpu().numpy()
+    l_all = out.lse[:, rows].cpu().numpy()
+    t0 = time.time()
+    worst = [0.0, 0.0, 0.0, 0.0]
+    bar_rel, bar_abs = TOL[wl.dtype]
+    for b in range(wl.batch):
+        o_ref, l_ref = oracle_latent(wl, weights, b, q_rows=rows)
+        for k, (name, got, ref) in enumerate((("o_lat", o_all[b], o_ref),
+                                              ("lse", l_all[b], l_ref))):
+            rel, mx = errors(got, ref)
+            worst[2 * k] = max(worst[2 * k], rel)
+            worst[2 * k + 1] = max(worst[2 * k + 1], mx)
+            if rel > bar_rel or mx > bar_abs or not np.all(np.isfinite(got)):
+                assert_close(f"seq{b} {name} (latent)", got, ref, wl.dtype)
+    log(f"  all {wl.batch} sequences ({len(rows)} query rows each): worst "
+        f"o_lat rel {worst[0]:.3e} max {worst[1]:.3e}, lse rel "
+        f"{worst[2]:.3e} max {worst[3]:.3e} ({time.time() - t0:.1f}s)")

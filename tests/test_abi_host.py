@@ -14,15 +14,21 @@ from mla_latent_kv_33_amd import binding as B
 from mla_latent_kv_33_amd import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mla.h")
+HEADERS = [os.path.join(ROOT, "include", f)
+           for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 OK, NULL, SHAPE, UNSUP, WS, RANGE = 0, 1, 2, 3, 4, 5
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every case fails first
 
 
 def declared_functions():
-    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+    """Every function declared in include/*.h."""
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -115,6 +121,13 @@ def test_append_validation():
     assert call_append(ds_dims(block_size=48)) == SHAPE
     assert call_append(ds_dims(dtype=7)) == SHAPE
     assert call_append(ds_dims(d=5121)) == UNSUP
+    # bf16 projections stream weights in 64-deep k steps: every contraction
+    # length must be a multiple of 64 (1552 and 1544 are multiples of 16 / 8)
+    assert call_append(ds_dims(d_cq=1552)) == UNSUP
+    assert call_append(ds_dims(d_cq=1544)) == UNSUP
+    assert call_append(ds_dims(d=5120 + 32)) == UNSUP
+    assert call_append(ds_dims(d_c=512 + 32)) == UNSUP
+    assert call_append(ds_dims(n_h=127, d_h=8)) == UNSUP
     assert call_append(d, T=-1) == SHAPE
     assert call_append(d, T=0) == OK          # no-op
     assert call_append(d, h=None) == NULL
@@ -169,7 +182,7 @@ def test_decode_validation():
 
 
 def test_header_cites_pages_and_names_callers():
-    text = open(HEADER).read()
+    text = open(os.path.join(ROOT, "include", "mla.h")).read()
     assert "MLA：潜在表示压缩与解耦 RoPE" in text
     for fn in ("mla_append_cache", "mla_absorb_q", "mla_decode", "mla_out"):
         assert fn in text
@@ -272,3 +285,135 @@ def test_binding_rejects_host_and_strided_tensors():
     with pytest.raises(ValueError, match="on the GPU"):
         B._ptr(torch.zeros(8))
     assert B._ptr(None) is None
+
+
+def test_binding_checks_dtype_shape_before_any_call():
+    # An int64 index tensor (torch's default integer type) would be read as
+    # int32 by the kernels, a bf16 o_lat would take out-of-bounds fp32
+    # writes, a short q a read past its end: each is refused in the binding
+    # (element type and shape are checked before the device, so these run on
+    # CPU tensors).
+    dims = B.make_dims(W.DEEPSEEK_V2, "bf16")
+    d = W.DEEPSEEK_V2
+    bf, i32, f32 = torch.bfloat16, torch.int32, torch.float32
+    Bsz, n_q, nb = 2, 1, 4
+    q = torch.zeros(Bsz, n_q, d.n_h, d.d_c + d.d_r, dtype=bf)
+    cache = torch.zeros(nb, 64, d.d_c + d.d_r, dtype=bf)
+    table = torch.zeros(Bsz, 2, dtype=i32)
+    lens = torch.ones(Bsz, dtype=i32)
+    o_lat = torch.zeros(Bsz, n_q, d.n_h, d.d_c, dtype=f32)
+
+    def dec(**kw):
+        a = dict(q=q, cache=cache, block_table=table, kv_lens=lens,
+                 o_lat=o_lat)
+        a.update(kw)
+        B.mla_decode(dims, a["q"], a["cache"], a["block_table"],
+                     a["kv_lens"], 100, a["o_lat"])
+
+    with pytest.raises(TypeError, match="kv_lens must be torch.int32"):
+        dec(kv_lens=lens.to(torch.int64))
+    with pytest.raises(TypeError, match="block_table must be torch.int32"):
+        dec(block_table=table.to(torch.int64))
+    with pytest.raises(TypeError, match="o_lat must be torch.float32"):
+        dec(o_lat=o_lat.to(bf))
+    with pytest.raises(TypeError, match="q must be torch.bfloat16"):
+        dec(q=q.float())
+    with pytest.raises(ValueError, match="q must have shape"):
+        dec(q=q[..., :512].contiguous())
+    with pytest.raises(ValueError, match="cache must have shape"):
+        dec(cache=cache.view(nb * 64, -1))
+    with pytest.raises(ValueError, match="kv_lens must have shape"):
+        dec(kv_lens=torch.ones(Bsz + 1, dtype=i32))
+    with pytest.raises(ValueError, match="o_lat must hold"):
+        dec(o_lat=o_lat[:1].contiguous())
+    with pytest.raises(ValueError, match="block_table has 1 rows"):
+        dec(block_table=table[:1].contiguous())
+    # a well-formed call on host tensors gets as far as the device check
+    with pytest.raises(ValueError, match="on the GPU"):
+        dec()
+
+    T = 3
+    h = torch.zeros(T, d.d, dtype=bf)
+    pos = torch.zeros(T, dtype=i32)
+    cos = torch.zeros(16, d.d_r // 2, dtype=f32)
+    w = {k: torch.zeros(tuple(s), dtype=bf) for k, s in (
+        ("w_dkv", (d.d_c, d.d)), ("w_kr", (d.d_r, d.d)),
+        ("w_dq", (d.d_cq, d.d)), ("w_uq", (d.n_h * d.d_h, d.d_cq)),
+        ("w_qr", (d.n_h * d.d_r, d.d_cq)), ("w_uk", (d.n_h * d.d_h, d.d_c)),
+        ("w_uv", (d.n_h * d.d_h, d.d_c)), ("w_o", (d.d, d.n_h * d.d_h)))}
+    with pytest.raises(TypeError, match="pos must be torch.int32"):
+        B.mla_append_cache(dims, h, pos, pos.long(), w["w_dkv"], w["w_kr"],
+                           cos, cos, table, cache)
+    with pytest.raises(TypeError, match="rope_cos must be torch.float32"):
+        B.mla_append_cache(dims, h, pos, pos, w["w_dkv"], w["w_kr"],
+                           cos.double(), cos, table, cache)
+    with pytest.raises(ValueError, match="w_kr must have shape"):
+        B.mla_append_cache(dims, h, pos, pos, w["w_dkv"], w["w_dkv"], cos,
+                           cos, table, cache)
+    q_out = torch.zeros(T, d.n_h, d.d_c + d.d_r, dtype=bf)
+    with pytest.raises(ValueError, match="w_uq must have shape"):
+        B.mla_absorb_q(dims, h, pos, w["w_dq"], w["w_uk"], w["w_qr"],
+                       w["w_uk"], cos, cos, q_out)
+    with pytest.raises(ValueError, match="q_out must hold"):
+        B.mla_absorb_q(dims, h, pos, w["w_dq"], w["w_uq"], w["w_qr"],
+                       w["w_uk"], cos, cos, q_out[:2].contiguous())
+    ol = torch.zeros(T, d.n_h, d.d_c, dtype=f32)
+    with pytest.raises(TypeError, match="u must be torch.bfloat16"):
+        B.mla_out(dims, ol, w["w_uv"], w["w_o"],
+                  torch.zeros(T, d.d, dtype=f32))
+    with pytest.raises(ValueError, match="w_o must have shape"):
+        B.mla_out(dims, ol, w["w_uv"], w["w_uv"],
+                  torch.zeros(T, d.d, dtype=bf))
+
+
+def test_peak_kernels_validate_arguments():
+    lib = B.lib()
+    assert lib.mla_peak_stream_read(None, 1 << 20, FAKE, 8, None) == NULL
+    assert lib.mla_peak_stream_read(FAKE, 1000, FAKE, 8, None) == SHAPE
+    assert lib.mla_peak_stream_read(FAKE, 1 << 20, FAKE, 0, None) == SHAPE
+    assert lib.mla_peak_mfma_loop(8, 10, None, None) == NULL
+    assert lib.mla_peak_mfma_loop(0, 10, FAKE, None) == SHAPE
+    assert lib.mla_peak_mfma_loop(8, 0, FAKE, None) == SHAPE
+    assert lib.mla_peak_mfma_sink_bytes(8) == 8 * 256 * 4
+    assert lib.mla_peak_mfma_sink_bytes(0) == 0
+    # 4 waves x 8 MFMAs of 32x32x16 (2 flops per multiply-add) per iteration
+    assert lib.mla_peak_mfma_flops(3, 5) == 3 * 4 * 5 * 8 * 2 * 32 * 32 * 16
+
+
+def test_validate_block_table():
+    """The opt-in host check of device-trusted values: ids outside the pool,
+    lengths past the table's capacity or below n_q, and the max_kv_len
+    bound are reported with the first offending sequence; unused entries
+    (-1 past a sequence's blocks) are ignored."""
+    table, nb = W.block_table(np.array([130, 64, 1]), True, 5)
+    lens = np.array([130, 64, 1], np.int32)
+    assert B.mla_validate_block_table(table, lens, 1, 64, nb) == 0
+    assert B.mla_validate_block_table(table, lens, 1, 64, nb, 130) == 0
+
+    def bad(tab, ln, n_q=1, num=nb, max_kv=0):
+        with pytest.raises(B.MlaError) as ei:
+            B.mla_validate_block_table(tab, ln, n_q, 64, num, max_kv)
+        assert ei.value.status == RANGE
+        return int(str(ei.value).rsplit("sequence ", 1)[1].rstrip(")"))
+
+    t2 = table.copy()
+    t2[1, 0] = nb                          # id past the pool
+    assert bad(t2, lens) == 1
+    t2 = table.copy()
+    t2[2, 0] = -1                          # a used entry left unset
+    assert bad(t2, lens) == 2
+    assert bad(table, np.array([130, 64, 65], np.int32)) == 2  # 2 blocks
+    assert bad(table, np.array([130, 0, 1], np.int32)) == 1    # < n_q
+    assert bad(table, lens, n_q=2) == 2                          # 1 < 2
+    assert bad(table, lens, max_kv=129) == 0                     # > bound
+    assert bad(table, lens, num=nb - 1) in (0, 1, 2)
+    lib = B.lib()
+    assert lib.mla_validate_block_table(None, 1, 1, None, 1, 64, 1, 0,
+                                        None) == NULL
+    buf = np.zeros(4, np.int32)
+    p = buf.ctypes.data_as(ctypes.c_void_p)
+    for args in ((0, 1, 1, 64, 1), (1, 0, 1, 64, 1), (1, 1, 0, 64, 1),
+                 (1, 1, 1, 0, 1), (1, 1, 1, 64, 0)):
+        Bn, mb, nq, bs, num = args
+        assert lib.mla_validate_block_table(p, Bn, mb, p, nq, bs, num, 0,
+                                            None) == SHAPE

@@ -14,8 +14,8 @@ import torch
 from mla_latent_kv_33_amd import flow
 from mla_latent_kv_33_amd import workloads as W
 from oracle import mla_oracle as orc
-from tests.gpu_common import assert_close, context_latents, log, \
-    oracle_sequence
+from tests.gpu_common import assert_close, check_all_sequences_latent, \
+    context_latents, log, oracle_sequence
 
 pytestmark = pytest.mark.gpu
 
@@ -161,6 +161,7 @@ def test_b64_var():
         ref = oracle_sequence(wl, w, b)
         check_new_rows(wl, st, ref, b)
         check_sequence(wl, out, ref, b)
+    check_all_sequences_latent(wl, w, out)
 
 
 def test_b64_ctx8k_headline():
@@ -174,6 +175,7 @@ def test_b64_ctx8k_headline():
         ref = oracle_sequence(wl, w, b)
         check_new_rows(wl, st, ref, b)
         check_sequence(wl, out, ref, b)
+    check_all_sequences_latent(wl, w, out)
 
 
 def test_b4_ctx128k_64_splits():
@@ -193,6 +195,7 @@ def test_b4_ctx128k_64_splits():
                               wl.dims.d_h)
         assert_close(f"seq{b} o heads {heads}", o_h[:, heads],
                      ref["o"][:, heads], "bf16")
+    check_all_sequences_latent(wl, w, out)
 
 
 @pytest.mark.parametrize("n_q", [30, 50])
@@ -231,6 +234,9 @@ def test_b8_chunked_prefill_causal():
     for b in (0, 5):
         ref = oracle_sequence(wl, w, b, q_rows=rows)
         check_sequence(wl, out, ref, b, q_rows=rows)
+    # every 64th query row (and the last) of every sequence, absorbed form
+    check_all_sequences_latent(wl, w, out,
+                               q_rows=list(range(0, wl.n_q, 64)) + [2047])
     # every appended row of one sequence
     c_kv, k_r = orc.kv_latent(st.h_new_np[2 * wl.n_q:3 * wl.n_q],
                               wl.ctx[2] + np.arange(wl.n_q), w["w_dkv"],

@@ -307,3 +307,100 @@ def test_score_jump_restart(n_split):
     ref_o, ref_lse = orc.latent_attention(q[0], [kvl - 1], rows, 512, 128)
     assert_close("o_lat after restart", o[0].cpu().numpy(), ref_o, "bf16")
     assert_close("lse after restart", lse[0].cpu().numpy(), ref_lse, "bf16")
+
+
+def _host_chunk(nb, slots=256, min_chunk=2):
+    """The balanced plan's chunk from its definition: the smallest c >=
+    max(min_chunk, ceil(sum nb / slots)) with sum ceil(nb_r / c) <= slots."""
+    nb = np.asarray(nb)
+    c = max(min_chunk, -(-int(nb.sum()) // slots))
+    while int(np.sum(-(-nb // c))) > slots:
+        c += 1
+    return c
+
+
+@pytest.mark.parametrize("case", range(5))
+def test_balanced_plan_readback(case):
+    """The balanced plan the decode writes (read back from its workspace)
+    for seeded random batches: each row's splits take consecutive slots in
+    row order, at most 256 slots in all, every row's count is ceil(nb / c)
+    for the minimal chunk c, so its splits cover its visible blocks exactly
+    once with none empty; and the decode equals one split per row."""
+    layer, _ = ds_layer()
+    rng = np.random.default_rng(100 + case)
+    Bsz = int(rng.choice([2, 7, 64, 100, 256]))
+    n_q = 1
+    hi = int(rng.choice([300, 5000, 20000]))
+    lens = rng.integers(1, hi + 1, size=Bsz)
+    lens[rng.integers(0, Bsz)] = 1          # a one-key row
+    lens[rng.integers(0, Bsz)] = hi         # the longest row
+    log(f"case {case}: B={Bsz} lens in [1, {hi}]")
+    table_np, nb_total = W.block_table(lens, True, 200 + case)
+    cache = torch.randn((nb_total, 64, 576), device="cuda").to(torch.bfloat16)
+    table = torch.from_numpy(table_np).cuda()
+    kv = torch.from_numpy(lens.astype(np.int32)).cuda()
+    q = (0.5 * torch.randn((Bsz, n_q, 128, 576), device="cuda")).to(
+        torch.bfloat16)
+    max_kv = int(lens.max())
+    nbytes = B.mla_decode_workspace_bytes(layer.cdims, Bsz, n_q, max_kv,
+                                          B.MLA_SPLIT_BALANCED)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    o = torch.empty((Bsz, n_q, 128, 512), device="cuda")
+    lse = torch.empty((Bsz, n_q, 128), device="cuda")
+    B.mla_decode(layer.cdims, q, cache, table, kv, max_kv, o, lse,
+                 n_split=B.MLA_SPLIT_BALANCED, ws=ws)
+    torch.cuda.synchronize()
+    rows = Bsz * n_q
+    off = nbytes - (-(-8 * rows // 256) * 256)
+    plan = ws[off:off + 8 * rows].cpu().numpy().view(np.int32).reshape(rows, 2)
+    slot0, count = plan[:, 0], plan[:, 1]
+    nb = np.maximum(-(-lens // 64), 1)
+    c = _host_chunk(nb)
+    np.testing.assert_array_equal(count, -(-nb // c))
+    np.testing.assert_array_equal(slot0, np.concatenate([[0],
+                                                         np.cumsum(count)[:-1]]))
+    assert int(count.sum()) <= 256
+    # minimality: one block less per chunk would not fit (or is below the
+    # lower bound)
+    lo = max(2, -(-int(nb.sum()) // 256))
+    assert c == lo or int(np.sum(-(-nb // (c - 1)))) > 256
+    # split j of a row covers [j nb / cnt, (j + 1) nb / cnt): contiguous,
+    # disjoint, none empty, union = all the row's blocks
+    for n, k in zip(nb, count):
+        edges = [(j * int(n)) // int(k) for j in range(int(k) + 1)]
+        assert edges[0] == 0 and edges[-1] == n
+        assert all(b > a for a, b in zip(edges, edges[1:]))
+    o1, l1 = _decode_once(layer, q, cache, table, kv, max_kv, 1)
+    assert_close("balanced vs one split", o.cpu().numpy(), o1.cpu().numpy(),
+                 "f32", tol=(3e-3, 2e-2))
+    assert_close("balanced lse vs one split", lse.cpu().numpy(),
+                 l1.cpu().numpy(), "f32", tol=(1e-4, 4e-3))
+
+
+@pytest.mark.parametrize("dims_name", ["ds", "tiny"])
+def test_row_without_visible_key(dims_name):
+    """A row outside the contract (kv_lens[b] < n_q, no visible key) with one
+    split gets o_lat = 0 and lse = -inf; the other rows are unaffected."""
+    if dims_name == "ds":
+        layer, _ = ds_layer()
+        d, dt, tdt = DS, "bf16", torch.bfloat16
+    else:
+        d, dt, tdt = W.TINY, "f32", torch.float32
+        layer = MlaLayer(d, dt, W.make_weights(d, dt, 1), 256)
+    row = d.d_c + d.d_r
+    rng = np.random.default_rng(31)
+    cache = torch.from_numpy(rng.standard_normal((2, 64, row)).astype(
+        np.float32)).to(tdt).cuda()
+    table = torch.tensor([[0], [1]], dtype=torch.int32, device="cuda")
+    kv = torch.tensor([5, 0], dtype=torch.int32, device="cuda")
+    q = torch.from_numpy(rng.standard_normal((2, 1, d.n_h, row)).astype(
+        np.float32)).to(tdt).cuda()
+    o, lse = _decode_once(layer, q, cache, table, kv, 64, 1)
+    assert torch.all(o[1] == 0)
+    assert torch.all(torch.isneginf(lse[1]))
+    assert torch.all(torch.isfinite(o[0])) and torch.all(torch.isfinite(lse[0]))
+    rows = cache[0, :5].float().cpu().numpy().astype(np.float64)
+    o_ref, l_ref = orc.latent_attention(
+        q[0].float().cpu().numpy().astype(np.float64), [4], rows, d.d_c,
+        d.d_h)
+    assert_close("valid row", o[0].cpu().numpy(), o_ref, dt)
