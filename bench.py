@@ -103,7 +103,7 @@ def measure_peaks(B, torch, stream):
     import numpy as np
     buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     buf.random_(0, 255)
-    wgs_read = 4096
+    wgs_read = 512
     sink = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
     mf_wgs, mf_iters = 512, 2048
     mf_sink = torch.empty(B.lib().mla_peak_mfma_sink_bytes(mf_wgs),
@@ -128,7 +128,8 @@ def measure_peaks(B, torch, stream):
         "hbm_read_GBps": nbytes / t_read / 1e9,
         "mfma_bf16_TFLOPs": flops / t_mfma / 1e12,
         "how": "mla_peak_stream_read over a 1 GiB buffer (16-byte loads, "
-               f"{wgs_read} workgroups) and mla_peak_mfma_loop ({mf_wgs} "
+               f"{wgs_read} workgroups, a contiguous 2 MiB chunk each) and "
+               f"mla_peak_mfma_loop ({mf_wgs} "
                f"workgroups x 4 waves x {mf_iters} x 8 independent "
                "32x32x16 bf16 MFMAs); medians of 10 launches after 2, timed "
                "with HIP events right after the timed steps"}

@@ -22,14 +22,14 @@
 extern "C" {
 #endif
 
-/* Reads `bytes` (a multiple of 16) of `buf` once, 16 bytes per lane per
- * load, with `workgroups` workgroups of 256 threads walking the buffer in a
- * grid-stride order.  `sink` (device, >= 4 * workgroups bytes) receives at
+/* Reads `bytes` of `buf` once, 16 bytes per lane per load: `workgroups`
+ * workgroups of 256 threads each stream their own contiguous chunk of
+ * bytes / workgroups.  `sink` (device, >= 4 * workgroups bytes) receives at
  * most one word per workgroup (to keep the loads live); its contents are
  * meaningless.  Rate = bytes / elapsed time.  Use a buffer well above the
  * 256 MB Infinity Cache so that the reads come from HBM.
- * MLA_ERR_NULL, MLA_ERR_SHAPE (bytes not a positive multiple of 16,
- * workgroups <= 0), MLA_ERR_DEVICE. */
+ * MLA_ERR_NULL, MLA_ERR_SHAPE (bytes not a positive multiple of
+ * 16 * workgroups, workgroups <= 0), MLA_ERR_DEVICE. */
 mla_status mla_peak_stream_read(const void* buf, size_t bytes, void* sink,
                                 int32_t workgroups, mla_stream_t stream);
 

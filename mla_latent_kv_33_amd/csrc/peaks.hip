@@ -4,10 +4,10 @@
 // compute nothing of the layer; the decode measurement divides by these
 // rates next to the datasheet peaks.
 //
-// stream_read_kernel: every lane reads 16-byte vectors of a buffer larger
-// than the 256 MB Infinity Cache, eight loads in flight per lane, in a
-// grid-stride order so that each wave reads 1 KiB contiguous per load, and
-// folds them into one word so the loads cannot be removed.
+// stream_read_kernel: every workgroup reads its own contiguous chunk of a
+// buffer larger than the 256 MB Infinity Cache in 16-byte vectors, eight
+// loads in flight per lane, and folds them into one word so that the loads
+// cannot be removed.
 //
 // mfma_loop_kernel: every wave issues independent v_mfma_f32_32x32x16_bf16
 // on register operands (eight accumulators, so no MFMA waits for another),
@@ -24,21 +24,24 @@ namespace {
 constexpr int SR_THREADS = 256;
 constexpr int SR_UNROLL = 8;
 
+// Workgroup w reads its own contiguous chunk of the buffer (the access
+// pattern of a kernel that streams whole cache blocks per workgroup); each
+// wave reads 1 KiB per load, SR_UNROLL loads in flight per lane.
 __global__ __launch_bounds__(SR_THREADS) void stream_read_kernel(
-    const u32x4* __restrict__ buf, size_t n_vec, uint32_t* __restrict__ sink) {
-  const size_t stride = (size_t)gridDim.x * SR_THREADS;
-  size_t i = (size_t)blockIdx.x * SR_THREADS + threadIdx.x;
+    const u32x4* __restrict__ buf, size_t per_wg, uint32_t* __restrict__ sink) {
+  const u32x4* p = buf + (size_t)blockIdx.x * per_wg;
   uint32_t acc = 0;
-  for (; i + (SR_UNROLL - 1) * stride < n_vec; i += SR_UNROLL * stride) {
+  size_t i = threadIdx.x;
+  for (; i + (SR_UNROLL - 1) * SR_THREADS < per_wg; i += SR_UNROLL * SR_THREADS) {
     u32x4 v[SR_UNROLL];
 #pragma unroll
     for (int u = 0; u < SR_UNROLL; ++u)
-      v[u] = __builtin_nontemporal_load(buf + i + u * stride);
+      v[u] = __builtin_nontemporal_load(p + i + u * SR_THREADS);
 #pragma unroll
     for (int u = 0; u < SR_UNROLL; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
-  for (; i < n_vec; i += stride) {
-    const u32x4 v = buf[i];
+  for (; i < per_wg; i += SR_THREADS) {
+    const u32x4 v = p[i];
     acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }
   // one word per workgroup, written only when the fold is a value no
@@ -106,10 +109,13 @@ extern "C" {
 mla_status mla_peak_stream_read(const void* buf, size_t bytes, void* sink,
                                 int32_t workgroups, mla_stream_t stream) {
   if (!buf || !sink) return MLA_ERR_NULL;
-  if (bytes < 16 || bytes % 16 || workgroups <= 0) return MLA_ERR_SHAPE;
+  if (bytes < 16 || bytes % 16 || workgroups <= 0 ||
+      (bytes / 16) % (size_t)workgroups)
+    return MLA_ERR_SHAPE;
   hipLaunchKernelGGL(mla::stream_read_kernel, dim3(workgroups),
                      dim3(mla::SR_THREADS), 0, (hipStream_t)stream,
-                     (const mla::u32x4*)buf, bytes / 16, (uint32_t*)sink);
+                     (const mla::u32x4*)buf, bytes / 16 / workgroups,
+                     (uint32_t*)sink);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_DEVICE;
 }
 

@@ -371,6 +371,7 @@ def test_peak_kernels_validate_arguments():
     assert lib.mla_peak_stream_read(None, 1 << 20, FAKE, 8, None) == NULL
     assert lib.mla_peak_stream_read(FAKE, 1000, FAKE, 8, None) == SHAPE
     assert lib.mla_peak_stream_read(FAKE, 1 << 20, FAKE, 0, None) == SHAPE
+    assert lib.mla_peak_stream_read(FAKE, 16 * 7, FAKE, 2, None) == SHAPE
     assert lib.mla_peak_mfma_loop(8, 10, None, None) == NULL
     assert lib.mla_peak_mfma_loop(0, 10, FAKE, None) == SHAPE
     assert lib.mla_peak_mfma_loop(8, 0, FAKE, None) == SHAPE
