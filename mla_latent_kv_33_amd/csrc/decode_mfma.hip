@@ -70,6 +70,11 @@ constexpr int KSTEPS = ROW / 16;      // 36 k-steps of the score MFMA
 constexpr int MT_LAT = DC / 32;       // 16 latent tiles of the value MFMA
 constexpr float REF_SLACK = 64.0f;    // log2 headroom above m_ref
 constexpr int SDEPTH = 3;             // score fragments in flight
+// Epilogue staging of the fp16 partial rows: one padded row per head (the
+// 16-byte pad moves consecutive heads to other banks), after the per-head
+// maxima at the start of LDS.
+constexpr int EPI_OFF = 2048;
+constexpr int EPI_STRIDE = DC * 2 + 16;
 
 template <int NW>
 struct Cfg {
@@ -84,6 +89,9 @@ struct Cfg {
   static_assert(PER_HALF <= 63, "outstanding copies must fit vmcnt");
   static_assert(MTW % 2 == 0, "latent tiles per wave must be even");
   static_assert(LDS <= 160 * 1024, "LDS budget");
+  static_assert(EPI_OFF >= NW * HEADS * 4 &&
+                    EPI_OFF + HEADS * EPI_STRIDE <= P_OFF,
+                "epilogue staging lies between the maxima and the P buffers");
 };
 
 // Value of lane l ^ 32.  permlane32_swap(x, x) returns {[x_lo, x_lo],
@@ -125,6 +133,8 @@ __device__ __forceinline__ void mfma_v_drain(f32x16& d) {
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 
 // Copy half `hf` (tokens 32 hf .. 32 hf + 31) of a cache block into an LDS
@@ -380,14 +390,11 @@ decode_mfma_kernel(
     CopyAll<0, PER>::run(hc, wave);
   };
 
-  // Query slice: lane holds Q[head][16ks + 8g .. +7] for every k-step.
+  // Query slice: lane holds Q[head][16ks + 8g .. +7] for every k-step
+  // (loaded in the first pass's prologue, behind the copies of half 0).
   bf16x8 qreg[KSTEPS];
-  {
-    const bf16x8* qp =
-        (const bf16x8*)(q + ((size_t)bq * n_h + head) * ROW) + g;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = qp[2 * ks];
-  }
+  const bf16x8* const qp =
+      (const bf16x8*)(q + ((size_t)bq * n_h + head) * ROW) + g;
 
   f32x16 o[MTW][NW];
   float m_ref = -INFINITY;  // per owned head, log2 units
@@ -638,24 +645,29 @@ decode_mfma_kernel(
   // there regardless.
   bool first_pass = true;
   for (int pass = 0;; ++pass) {
+    // Prologue: the copies of half 0 and (first pass) the query loads go
+    // out first, and the scores and P of half 0 start as soon as both
+    // landed, while halves 1 and 2 are in flight.  The query loads are
+    // retired by a wait the compiler sees (a builtin, not asm), issued
+    // before the copies of halves 1 and 2: the compiler's own waits for the
+    // query registers then never stand for those copies, and inside the
+    // loop vmcnt tracks the copies only.
+    issue(0);
+    if (first_pass) {
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = qp[2 * ks];
+      first_pass = false;
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if (n_half > 1) issue(1);
+    if (n_half > 2) issue(2);
 #pragma unroll
     for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
       for (int nt = 0; nt < NW; ++nt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[mt][nt][r] = 0.0f;
-    // Prologue: halves 0 and 1 landed, half 2 in flight; P of half 0.
-    issue(0);
-    if (n_half > 1) issue(1);
-    if (first_pass) {
-      // Also retires the query loads, so that inside the loop vmcnt only
-      // tracks the copies.
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      first_pass = false;
-    }
-    wait_vm<0>();
-    if (n_half > 2) issue(2);
-    barrier();
+    barrier();  // half 0 visible to every wave
     {
       Half h;
       h.s = s_phase(0, [](int) __attribute__((always_inline)) {});
@@ -665,6 +677,12 @@ decode_mfma_kernel(
       for (int st = 0; st < 25; ++st) softmax_step(h, st);
       store_p(0, h);
     }
+    // Half 1 landed before the first step's barrier; half 2 may stay in
+    // flight.
+    if (n_half > 2)
+      wait_vm<PER>();
+    else
+      wait_vm<0>();
     wait_lgkm0();
 
     // Step j: entry state (after the barrier) is P of half j and the
@@ -751,7 +769,11 @@ decode_mfma_kernel(
     // and every value keeps 11 significant bits.  The rows' scales follow
     // the fp16 rows in the same buffer.  Per-head maxima cross the waves
     // through the first half-tile buffer: no copy is in flight and every
-    // wave is past its last read of it (flag barrier above).
+    // wave is past its last read of it (flag barrier above).  The rows
+    // themselves are assembled in LDS (the ring is free) and stored whole:
+    // stored straight from the accumulator layout, every instruction would
+    // write 32 scattered 16-byte pieces, and the stores then took most of
+    // the epilogue.
     uint16_t* const o16 = (uint16_t*)o_part;
     float* const sc_part = (float*)(o16 + (size_t)slots * n_h * DC);
     float* const mx = (float*)lds;  // [NW][HEADS]
@@ -778,8 +800,9 @@ decode_mfma_kernel(
                         ? min(max(__builtin_amdgcn_frexp_expf(hm) - 15, -100), 120)
                         : 0;
       const float mul = inv[nt] * __builtin_amdgcn_ldexpf(1.0f, -e);
-      uint16_t* dst = o16 + (row_base + hbase + 32 * nt + col) * DC +
-                      32 * MTW * wave;
+      // this lane's 4-column pieces into LDS row 32 nt + col
+      lds_char* row = L + EPI_OFF + (32 * nt + col) * EPI_STRIDE +
+                      2 * 32 * MTW * wave;
 #pragma unroll
       for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
@@ -788,12 +811,30 @@ decode_mfma_kernel(
               ((f32x4){o[mt][nt][4 * i], o[mt][nt][4 * i + 1],
                        o[mt][nt][4 * i + 2], o[mt][nt][4 * i + 3]}) * mul,
               f16x4);
-          *(uint2*)(dst + 32 * mt + 8 * i + 4 * g) =
-              __builtin_bit_cast(uint2, h);
+          *(lds_u32x2*)(row + 2 * (32 * mt + 8 * i + 4 * g)) =
+              __builtin_bit_cast(u32x2, h);
         }
       if (g == 0 && wave == 0)
         sc_part[row_base + hbase + 32 * nt + col] =
             __builtin_amdgcn_ldexpf(1.0f, e);
+    }
+    wait_lgkm0();
+    barrier();
+    // Wave w stores rows 32 w .. 32 w + 31, one whole 1 KiB row per
+    // instruction (16 bytes per lane), eight rows in flight.
+    {
+      uint16_t* const dst0 = o16 + (row_base + hbase + 32 * wave) * DC;
+      const lds_char* const src0 = L + EPI_OFF + 32 * wave * EPI_STRIDE;
+#pragma unroll
+      for (int r0 = 0; r0 < 32; r0 += 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          v[r] = *(const lds_u32x4*)(src0 + (r0 + r) * EPI_STRIDE + 16 * lane);
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          *(u32x4*)(dst0 + (size_t)(r0 + r) * DC + 8 * lane) = v[r];
+      }
     }
     if (g == 0) {
       m_part[row_base + head] = m_ref;
