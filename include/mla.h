@@ -287,9 +287,12 @@ mla_status mla_validate_block_table(const int32_t* block_table, int32_t B,
  *   must name blocks of the pool; a kv_lens[b] outside [n_q, max_kv_len]
  *   yields unspecified outputs but no access past the table or workspace
  *   (lengths are clamped to max_kv_len).
- *   ws: mla_prefill_mha_workspace_bytes(dims, B, max_kv_len) bytes (the
- *   gathered rows and bf16 k_C / v_C of every head: about
- *   max(B max_kv_len, 128) (d_c + d_r + 4 n_h d_h) bytes).
+ *   ws: mla_prefill_mha_workspace_bytes(dims, B, max_kv_len) bytes: the
+ *   gathered rows, max(B max_kv_len, 128) (d_c + d_r) 2 bytes, and the bf16
+ *   k_C / v_C of one group of heads at a time, the group being the largest
+ *   divisor of n_h whose k_C / v_C fit 768 MiB (at least one head): for 8
+ *   sequences of 10240 keys at DeepSeek-V2 dims, 16 heads and 765 MB in
+ *   all.  The groups run one after another in the call.
  *   Errors: MLA_ERR_SHAPE for max_kv_len < n_q or max_kv_len > max_blocks
  *   block_size, MLA_ERR_WORKSPACE for a short workspace, MLA_ERR_UNSUPPORTED
  *   unless bf16 with d_h = 128 and d_r = 64.

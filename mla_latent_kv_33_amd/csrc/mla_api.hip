@@ -574,6 +574,7 @@ mla_status mla_query_mha(const mla_dims* dims, int32_t T, const void* h,
 namespace {
 struct PrefillWs {
   uint16_t *rows, *kv;
+  int group;  // heads whose k_C / v_C are materialised at a time
   size_t bytes;
 };
 // Rows of the gathered latents and of [k_C | v_C]: B kv_cap, at least 128
@@ -581,12 +582,26 @@ struct PrefillWs {
 long prefill_rows(int B, int kv_cap) {
   return std::max((long)B * kv_cap, 128L);
 }
+// The explicit keys and values are materialised for one group of heads at
+// a time: the largest divisor of n_h whose [k_C | v_C] rows fit
+// PREFILL_KV_BUDGET bytes (at least one head).  The heads are independent,
+// so the groups run one after another with no merge.
+constexpr size_t PREFILL_KV_BUDGET = 768ull << 20;
+int prefill_group(const mla_dims& d, long R) {
+  const size_t per_head = (size_t)R * 2 * d.d_h * 2;
+  int best = 1;
+  for (int gsz = 1; gsz <= d.n_h; ++gsz)
+    if (d.n_h % gsz == 0 && (size_t)gsz * per_head <= PREFILL_KV_BUDGET)
+      best = gsz;
+  return best;
+}
 PrefillWs prefill_layout(const mla_dims& d, int B, int kv_cap, void* base) {
   PrefillWs w;
   char* p = (char*)base;
   const long R = prefill_rows(B, kv_cap);
+  w.group = prefill_group(d, R);
   const size_t rows_b = align_up((size_t)R * (d.d_c + d.d_r) * 2);
-  const size_t kv_b = align_up((size_t)R * 2 * d.n_h * d.d_h * 2);
+  const size_t kv_b = align_up((size_t)R * 2 * w.group * d.d_h * 2);
   w.rows = (uint16_t*)p;
   w.kv = (uint16_t*)(p ? p + rows_b : nullptr);
   w.bytes = rows_b + kv_b;
@@ -625,24 +640,28 @@ mla_status mla_prefill_mha(const mla_dims* dims, int32_t B, int32_t n_q,
   hipStream_t s = (hipStream_t)stream;
   MLA_TRY(launch_gather_rows(d, B, cache, block_table, max_blocks, kv_lens,
                              max_kv_len, w.rows, s));
-  // [k_C | v_C] of every gathered row, all heads: one GEMM
-  GemmArgs g;
-  g.A = w.rows;
-  g.lda = d.d_c + d.d_r;
-  g.B = w_uk;
-  g.B2 = w_uv;
-  g.nb1 = d.n_h * d.d_h;
-  g.ldb = d.d_c;
-  g.M = (int)prefill_rows(B, max_kv_len);
-  g.N = 2 * d.n_h * d.d_h;
-  g.K = d.d_c;
-  g.ldc = g.N;
-  gemm_plan(d, g);
-  if (g.k_split != 1 || g.ntw != 0) return MLA_ERR_UNSUPPORTED;
-  g.c16 = w.kv;
-  MLA_TRY(launch_gemm(d, g, s));
-  MLA_TRY(launch_prefill_mha(d, B, n_q, q, w.rows, w.kv, kv_lens, max_kv_len,
-                             causal ? 1 : 0, o_v, lse, s));
+  // Per group of heads: [k_C | v_C] of every gathered row (one GEMM), then
+  // the attention of those heads.
+  for (int h0 = 0; h0 < d.n_h; h0 += w.group) {
+    GemmArgs g;
+    g.A = w.rows;
+    g.lda = d.d_c + d.d_r;
+    g.B = (const uint16_t*)w_uk + (size_t)h0 * d.d_h * d.d_c;
+    g.B2 = (const uint16_t*)w_uv + (size_t)h0 * d.d_h * d.d_c;
+    g.nb1 = w.group * d.d_h;
+    g.ldb = d.d_c;
+    g.M = (int)prefill_rows(B, max_kv_len);
+    g.N = 2 * w.group * d.d_h;
+    g.K = d.d_c;
+    g.ldc = g.N;
+    gemm_plan(d, g);
+    if (g.k_split != 1 || g.ntw != 0) return MLA_ERR_UNSUPPORTED;
+    g.c16 = w.kv;
+    MLA_TRY(launch_gemm(d, g, s));
+    MLA_TRY(launch_prefill_mha(d, B, n_q, q, w.rows, w.kv, h0, w.group,
+                               kv_lens, max_kv_len, causal ? 1 : 0, o_v, lse,
+                               s));
+  }
   return MLA_OK;
 }
 

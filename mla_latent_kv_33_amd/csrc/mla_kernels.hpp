@@ -70,8 +70,9 @@ hipError_t launch_gather_rows(const mla_dims& d, int B, const void* cache,
 // fp32, lse [B*n_q][n_h] (natural log) or null.
 hipError_t launch_prefill_mha(const mla_dims& d, int B, int n_q,
                               const void* q, const void* rows, const void* kv,
-                              const int32_t* kv_lens, int kv_cap, int causal,
-                              float* o_v, float* lse, hipStream_t stream);
+                              int h0, int gh, const int32_t* kv_lens,
+                              int kv_cap, int causal, float* o_v, float* lse,
+                              hipStream_t stream);
 // q_out[t][h] = [q_C | RoPE(q_R)] (bf16) from the K-split parts of the
 // query up-projection (as launch_absorb_fast reads them).
 hipError_t launch_query_mha(const mla_dims& d, int T, const float* parts,

@@ -89,8 +89,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ rows,
     int ldr, const uint16_t* __restrict__ kv, int ldkv,
     const int32_t* __restrict__ kv_lens, int kv_cap, int n_q, int n_h,
-    int ntq, int causal, float scale_log2, float* __restrict__ o_v,
-    float* __restrict__ lse) {
+    int h0, int gh, int ntq, int causal, float scale_log2,
+    float* __restrict__ o_v, float* __restrict__ lse) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const lds_char* L = (const lds_char*)lds;
   const int lane = threadIdx.x & 63;
@@ -103,8 +103,9 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
   const int nwg = gridDim.x;
   const int xcd = blockIdx.x & 7;
   const int w = xcd * (nwg >> 3) + min(xcd, nwg & 7) + (blockIdx.x >> 3);
+  // heads h0 .. h0 + gh - 1 of n_h; kv holds [k_C | v_C] of those heads
   const int bh = w / ntq, qt = w - bh * ntq;
-  const int b = bh / n_h, h = bh - b * n_h;
+  const int b = bh / gh, hl = bh - b * gh, h = h0 + hl;
   const int kvl = min(kv_lens[b], kv_cap);
   const int i0 = qt * PF_QW;
   auto lim_of = [&](int i) { return causal ? kvl - n_q + i : kvl - 1; };
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
       const int r = 4 * i + (lane >> 4);
       const int ch = (lane & 15) ^ (r & 15);
       dma16(st + i * 1024, kvb,
-            (uint32_t)(min(r, last) * ldkv * 2 + (h * PF_DH + 8 * ch) * 2));
+            (uint32_t)(min(r, last) * ldkv * 2 + (hl * PF_DH + 8 * ch) * 2));
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {  // k_R: rows 8 i .. 8 i + 7
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(256, 2) void prefill_mha_kernel(
       const int r = 8 * tg + t8;
       dma16(st + 1024 * (8 * cg + tg), kvb,
             (uint32_t)(min(r, last) * ldkv * 2 +
-                       (n_h * PF_DH + h * PF_DH + 8 * (8 * cg + ch)) * 2));
+                       (gh * PF_DH + hl * PF_DH + 8 * (8 * cg + ch)) * 2));
     }
   };
 
@@ -432,8 +433,9 @@ hipError_t launch_gather_rows(const mla_dims& d, int B, const void* cache,
 
 hipError_t launch_prefill_mha(const mla_dims& d, int B, int n_q,
                               const void* q, const void* rows, const void* kv,
-                              const int32_t* kv_lens, int kv_cap, int causal,
-                              float* o_v, float* lse, hipStream_t stream) {
+                              int h0, int gh, const int32_t* kv_lens,
+                              int kv_cap, int causal, float* o_v, float* lse,
+                              hipStream_t stream) {
   const float scale_log2 =
       (float)(1.4426950408889634 / __builtin_sqrt((double)(d.d_h + d.d_r)));
   static std::atomic<unsigned long long> lds_set{0};
@@ -443,12 +445,12 @@ hipError_t launch_prefill_mha(const mla_dims& d, int B, int n_q,
     if (e != hipSuccess) return e;
   }
   const int ntq = (n_q + PF_QW - 1) / PF_QW;
-  const long nwg = (long)B * d.n_h * ntq;
+  const long nwg = (long)B * gh * ntq;
   hipLaunchKernelGGL(prefill_mha_kernel, dim3((unsigned)nwg), dim3(256),
                      PF_LDS, stream, (const uint16_t*)q,
                      (const uint16_t*)rows, d.d_c + d.d_r,
-                     (const uint16_t*)kv, 2 * d.n_h * d.d_h, kv_lens, kv_cap,
-                     n_q, d.n_h, ntq, causal, scale_log2, o_v, lse);
+                     (const uint16_t*)kv, 2 * gh * d.d_h, kv_lens, kv_cap,
+                     n_q, d.n_h, h0, gh, ntq, causal, scale_log2, o_v, lse);
   return hipGetLastError();
 }
 

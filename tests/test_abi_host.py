@@ -211,13 +211,33 @@ def test_append_rmsnorm_validation():
 
 
 def test_prefill_workspace_bytes():
+    """Gathered rows plus bf16 [k_C | v_C] of one group of heads: the
+    largest divisor of n_h whose k_C / v_C fit 768 MiB."""
     d = ds_dims()
-    row, kvw = (512 + 64) * 2, 2 * 128 * 128 * 2
+    row, kv_head = (512 + 64) * 2, 2 * 128 * 2
+    budget = 768 << 20
+
+    def expect(R):
+        g = max(x for x in range(1, 129)
+                if 128 % x == 0 and (x * R * kv_head <= budget or x == 1))
+        return g, R * row + g * R * kv_head
+
+    g, want = expect(8 * 10240)
+    assert g == 16                        # 16 of 128 heads at a time
     big = B.mla_prefill_mha_workspace_bytes(d, 8, 10240)
-    assert big >= 8 * 10240 * (row + kvw)
-    assert big < 8 * 10240 * (row + kvw) + 4096
+    assert want <= big < want + 4096
+    assert big < 1 << 30                  # the chunked-prefill shape < 1 GB
+    g, want = expect(4 * 131073)          # long contexts: 2 heads at a time
+    assert g == 2
+    got = B.mla_prefill_mha_workspace_bytes(d, 4, 131073)
+    assert want <= got < want + 4096
+    g, want = expect(3 * 533)             # short: every head at once
+    assert g == 128
+    got = B.mla_prefill_mha_workspace_bytes(d, 3, 533)
+    assert want <= got < want + 4096
     # at least 128 rows (the up-projection GEMM's bf16 output)
-    assert B.mla_prefill_mha_workspace_bytes(d, 1, 37) >= 128 * (row + kvw)
+    assert B.mla_prefill_mha_workspace_bytes(d, 1, 37) >= 128 * (
+        row + 128 * kv_head)
     assert B.mla_prefill_mha_workspace_bytes(d, 0, 37) == 0
     assert B.mla_prefill_mha_workspace_bytes(ds_dims(d_r=63), 1, 37) == 0
 

@@ -4,7 +4,9 @@ oracle's non-absorbed attention ('MLA：潜在表示压缩与解耦 RoPE', secti
 The chunk's queries q = [q_C | RoPE(q_R)], the value-space attention output
 o (fp32), its log-sum-exp and u = W_O o are compared with the oracle on every
 query and head of small ragged cases (several 128-query tiles, partial 64-key
-tiles, an empty context, a single query, the non-causal form) and on sampled
+tiles, an empty context, a single query, the non-causal form, a context
+long enough that the explicit keys and values are built for two groups of
+heads in turn) and on sampled
 queries of the 8 x (8192 + 2048) chunked-prefill step.  Bars as for the
 decode path: rel-Frobenius 5e-3 and max-abs 2e-2 (bf16 inputs)."""
 import dataclasses
@@ -26,6 +28,9 @@ CASES = {
     "b1_short": ((0,), 37, 1),
     "b2_single": ((64, 500), 1, 1),
     "b2_noncausal": ((10, 300), 70, 0),
+    # 2 x 7016 gathered rows: k_C / v_C of 64 heads fit the workspace
+    # budget, so the call runs two head groups one after the other
+    "b2_head_groups": ((7000, 6500), 16, 1),
 }
 
 
