@@ -232,6 +232,29 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, int32_t n_q,
                       float* lse, void* ws, size_t ws_bytes,
                       mla_stream_t stream);
 
+/* mla_decode without a workspace argument, for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments, results and errors are those of
+ * mla_decode; the partial results live in a file-scope device array of
+ * MLA_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends (its device address is taken once per device, at the
+ * first call on it).  Requests whose mla_decode_workspace_bytes exceed
+ * that size return MLA_ERR_WORKSPACE (the largest: 32768 partial rows
+ * (query rows x splits x heads) at d_c = 512, e.g. 64 sequences x 4 splits
+ * x 128 heads, or the balanced plan's 256 slots x 128 heads).  The call
+ * allocates nothing and clears nothing: every value it reads back from the
+ * array it wrote first.  All calls on one GPU share the array, so calls
+ * that overlap on one GPU (different streams, or host threads) race: the
+ * caller serialises them. */
+#define MLA_NOALLOC_SCRATCH_BYTES (65u * 1024u * 1024u)
+mla_status mla_decode_noalloc(const mla_dims* dims, int32_t B, int32_t n_q,
+                              const void* q, const void* cache,
+                              int32_t num_blocks, const int32_t* block_table,
+                              int32_t max_blocks, const int32_t* kv_lens,
+                              int32_t max_kv_len, int32_t causal,
+                              int32_t n_split, float* o_lat, float* lse,
+                              mla_stream_t stream);
+
 /* The split count mla_decode uses for n_split = 0 (host only). */
 int32_t mla_decode_auto_splits(const mla_dims* dims, int32_t B, int32_t n_q,
                                int32_t max_kv_len);

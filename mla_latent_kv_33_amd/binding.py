@@ -61,6 +61,8 @@ _SIGNATURES = {
                           _S, _P]),
     "mla_decode_workspace_bytes": (_S, [_DP, _I, _I, _I, _I]),
     "mla_decode_auto_splits": (_I, [_DP, _I, _I, _I]),
+    "mla_decode_noalloc": (_I, [_DP, _I, _I, _P, _P, _I, _P, _I, _P, _I, _I,
+                                _I, _P, _P, _P]),
     "mla_validate_block_table": (_I, [_P, _I, _I, _P, _I, _I, _I, _I, _P]),
     "mla_decode": (_I, [_DP, _I, _I, _P, _P, _I, _P, _I, _P, _I, _I, _I, _P,
                         _P, _P, _S, _P]),
@@ -364,6 +366,23 @@ def mla_decode(dims: MlaDims, q, cache, block_table, kv_lens, max_kv_len: int,
         ctypes.byref(dims), B, n_q, p[0], p[1], cache.shape[0], p[2],
         block_table.shape[1], p[3], max_kv_len, causal, n_split, p[4], p[5],
         _ptr(ws, "ws"), wsb, _stream(stream)))
+
+
+def mla_decode_noalloc(dims: MlaDims, q, cache, block_table, kv_lens,
+                       max_kv_len: int, o_lat, lse=None, causal: int = 1,
+                       n_split: int = 0, stream=None):
+    """mla_decode with the library's static scratch array instead of a
+    workspace (see include/mla.h); allocates nothing."""
+    B, n_q = q.shape[0], q.shape[1]
+    p = _ptrs(*_attention_args(dims, q, cache, block_table, kv_lens,
+                               dims.d_c + dims.d_r),
+              _a(o_lat, "o_lat", _F32,
+                 numel=B * n_q * dims.n_h * dims.d_c),
+              _a(lse, "lse", _F32, numel=B * n_q * dims.n_h))
+    _check("mla_decode_noalloc", lib().mla_decode_noalloc(
+        ctypes.byref(dims), B, n_q, p[0], p[1], cache.shape[0], p[2],
+        block_table.shape[1], p[3], max_kv_len, causal, n_split, p[4], p[5],
+        _stream(stream)))
 
 
 def mla_out(dims: MlaDims, o_lat, w_uv, w_o, u, ws=None, stream=None):

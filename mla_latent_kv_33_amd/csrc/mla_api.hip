@@ -3,6 +3,7 @@
 
 #include <algorithm>
 #include <math.h>
+#include <mutex>
 #include <string.h>
 
 #include "mla_common.hpp"
@@ -514,6 +515,62 @@ mla_status mla_validate_block_table(const int32_t* block_table, int32_t B,
     }
   }
   return MLA_OK;
+}
+
+// ------------------------------------------------- decode, no allocation
+// The workspace of mla_decode_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  In host code its name is only a
+// stand-in; the device address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address reaches
+// kernels.
+static __device__ __align__(256) unsigned char scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of this device's `scratch`, or null on failure.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES)
+    return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess)
+      return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+}  // namespace
+
+mla_status mla_decode_noalloc(const mla_dims* dims, int32_t B, int32_t n_q,
+                              const void* q, const void* cache,
+                              int32_t num_blocks, const int32_t* block_table,
+                              int32_t max_blocks, const int32_t* kv_lens,
+                              int32_t max_kv_len, int32_t causal,
+                              int32_t n_split, float* o_lat, float* lse,
+                              mla_stream_t stream) {
+  if (!dims) return MLA_ERR_NULL;
+  if (!dims_ok(dims) || B <= 0 || n_q <= 0 || max_kv_len <= 0 ||
+      num_blocks <= 0 || max_blocks <= 0 || n_split < MLA_SPLIT_BALANCED)
+    return MLA_ERR_SHAPE;
+  const size_t need =
+      mla_decode_workspace_bytes(dims, B, n_q, max_kv_len, n_split);
+  if (need > MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need) {
+    ws = scratch_address();
+    if (!ws) return MLA_ERR_DEVICE;
+  }
+  // Every partial, maximum, sum and plan entry the decode reads is written
+  // by the same call first, so nothing in `scratch` needs clearing.
+  return mla_decode(dims, B, n_q, q, cache, num_blocks, block_table,
+                    max_blocks, kv_lens, max_kv_len, causal, n_split, o_lat,
+                    lse, ws, need ? (size_t)MLA_NOALLOC_SCRATCH_BYTES : 0,
+                    stream);
 }
 
 // --------------------------------------------------------------------- out
