@@ -106,6 +106,10 @@ struct LdsCfg {
   static_assert(NBUF >= 2, "LDS ring");
   static_assert((NBUF - 2) * D_PER <= 63, "vmcnt range");
   static constexpr int LDS = NBUF * SLOT;
+  // A row swizzle (see the copy offsets)
+  static __device__ __forceinline__ int sw(int r) {
+    return PPR == 16 ? (r & 15) : ((r >> 1) & 7);
+  }
 };
 
 // HL: A holds pre-split hi|lo pairs (AF32 layout, no split in the kernel);
@@ -140,8 +144,11 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
 
   // ---- per-lane copy offsets (bytes from the per-super-step scalar base)
   // A: copy i (= wave A_PER + a) covers rows i RPI .. i RPI + RPI - 1; lane l
-  // takes row r = i RPI + l / PPR and piece (l % PPR) ^ (r % 8) of it, so
-  // that LDS position p of row r holds piece p ^ (r % 8).
+  // takes row r = i RPI + l / PPR and piece (l % PPR) ^ sw(r) of it, so that
+  // LDS position p of row r holds piece p ^ sw(r).  A 256-byte fp32 row
+  // spans all 16 bank groups of 16 bytes: sw = r % 16.  Two 128-byte bf16
+  // rows share a bank row (r % 2 picks the half): sw = (r / 2) % 8.  Either
+  // way the 16 rows a ds_read_b128 cycle serves hit 16 distinct groups.
   const char* a_base = (const char*)Av + (size_t)z * a_bs * esz +
                        (size_t)m0 * lda * esz + (size_t)kbeg * esz;
   uint32_t a_off[L::A_PER];
@@ -150,10 +157,13 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
     const int r = (wave * L::A_PER + a) * L::RPI + lane / L::PPR;
     const int pos = lane % L::PPR;
     a_off[a] = (uint32_t)((size_t)min(r, M - 1) * lda * esz) +
-               16 * (pos ^ (r & 7));
+               16 * (pos ^ L::sw(r));
   }
-  // B: column tile t = wave NTW + nt (32 rows), copies q = 0..3 of 8 rows;
-  // lane l takes row 8 q + l / 8 and chunk (l % 8) ^ swz(l / 8).
+  // B: column tile t = wave NTW + nt (32 rows), copies q = 0..3 of 8 rows
+  // (1 KiB groups); lane l takes row 8 q + l / 8 and chunk
+  // (l % 8) ^ swz(l / 8) ^ 2 (q % 2): the group parity term moves odd groups
+  // onto the other half of each 256-byte bank row, so that rows t and t + 8
+  // of a tile (1 KiB apart, the same banks otherwise) do not collide.
   const char* b_base[NTW];
   uint32_t b_off[NTW][4];
 #pragma unroll
@@ -166,7 +176,7 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
     for (int q = 0; q < 4; ++q) {
       const int rr = min(row0 + 8 * q + (lane >> 3), N - 1) - row0;
       b_off[nt][q] = (uint32_t)(rr * ldb * 2) +
-                     16 * ((lane & 7) ^ swz(lane >> 3));
+                     16 * ((lane & 7) ^ swz(lane >> 3) ^ (2 * (q & 1)));
     }
   }
   const uint32_t lds0 = lds_u32(lds);
@@ -192,14 +202,14 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
   auto a_read = [&](const lds_char* sl, int mt, int piece) __attribute__((always_inline)) {
     const int m = 32 * mt + ar;
     return *(const __attribute__((address_space(3))) u32x4*)(
-        sl + m * L::RB + 16 * (piece ^ (m & 7)));
+        sl + m * L::RB + 16 * (piece ^ L::sw(m)));
   };
   const int b_row_off = (col >> 3) * 1024 + (col & 7) * 128;
   auto b_read = [&](const lds_char* sl, int nt, int ks) __attribute__((always_inline)) {
     const int c = 2 * ks + g;
     return *(const __attribute__((address_space(3))) bf16x8*)(
         sl + L::B_OFF + (wave * NTW + nt) * 4096 + b_row_off +
-        16 * (c ^ swz(col & 7)));
+        16 * (c ^ swz(col & 7) ^ (2 * ((col >> 3) & 1))));
   };
 
   f32x16 acc[MT][NTW];
