@@ -75,6 +75,16 @@ def parse():
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed steps for at least this long (wall clock) "
                          "before the warmup steps")
+    ap.add_argument("--streams", type=int, choices=(1, 2), default=1,
+                    help="2: the append runs on a second stream, concurrent "
+                         "with the query path (both read only h; the decode "
+                         "waits for both); 1: the four calls on one stream")
+    ap.add_argument("--query", choices=("absorbed", "merged"),
+                    default="absorbed",
+                    help="absorbed path only: the query projection as "
+                         "mla_absorb_q (W_UQ, then W_UK_h^T per head) or "
+                         "mla_absorb_q_merged (one projection onto the "
+                         "pre-merged W_UK_h^T W_UQ_h, built once)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured HBM-read and matrix-core rates")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -239,20 +249,58 @@ def main():
                          st.max_kv_len, n_split=n_split, o_lat=out.o_lat,
                          lse=out.lse)
 
-    def step(e=None, which="all"):
-        """One pass of the hot path; e[k] recorded before stage k and after
-        the last stage, all of them ("all") or only around decode."""
-        rec_all = e is not None and which == "all"
-        rec_dec = e is not None
-        if rec_all: e[0].record(stream)
-        layer.append(st.h_new, st.seq_idx, st.pos, st.table, st.cache)
-        if rec_all: e[1].record(stream)
-        if mha:
+    # The append and the query path both read only h: with two streams the
+    # append runs on a side stream (default priority), forked from and
+    # joined to the main stream by events, so its small kernels fill the
+    # gaps of the query path's chain.
+    side = torch.cuda.Stream() if args.streams == 2 else None
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+
+    merged = merged_ws = None
+    if args.query == "merged" and not mha:
+        import ctypes
+        merged = torch.empty((d.n_h, d.d_c, d.d_cq), dtype=torch.bfloat16,
+                             device="cuda")
+        B.mla_merge_uq_uk(layer.cdims, layer.w["w_uq"], layer.w["w_uk"],
+                          merged)
+        merged_ws = torch.empty(
+            B.lib().mla_absorb_merged_workspace_bytes(
+                ctypes.byref(layer.cdims), st.h_new.shape[0]),
+            dtype=torch.uint8, device="cuda")
+
+    def query_path():
+        if merged is not None:
+            B.mla_absorb_q_merged(layer.cdims, st.h_new, st.pos,
+                                  layer.w["w_dq"], merged, layer.w["w_qr"],
+                                  layer.rope_cos, layer.rope_sin,
+                                  out.q.view(-1, d.n_h, d.d_c + d.d_r),
+                                  ws=merged_ws)
+        elif mha:
             layer.query_mha(st.h_new, st.pos,
                             q_out=out.q.view(-1, d.n_h, d.d_h + d.d_r))
         else:
             layer.absorb(st.h_new, st.pos,
                          q_out=out.q.view(-1, d.n_h, d.d_c + d.d_r))
+
+    def step(e=None, which="all"):
+        """One pass of the hot path; e[k] recorded before stage k and after
+        the last stage, all of them ("all", one stream) or only around
+        decode."""
+        rec_all = e is not None and which == "all"
+        rec_dec = e is not None
+        if side is not None and not rec_all:
+            fork.record(stream)
+            side.wait_event(fork)
+            layer.append(st.h_new, st.seq_idx, st.pos, st.table, st.cache,
+                         stream=side)
+            join.record(side)
+            query_path()
+            stream.wait_event(join)
+        else:
+            if rec_all: e[0].record(stream)
+            layer.append(st.h_new, st.seq_idx, st.pos, st.table, st.cache)
+            if rec_all: e[1].record(stream)
+            query_path()
         if rec_dec: e[2].record(stream)
         attention()
         if rec_dec: e[3].record(stream)
@@ -424,7 +472,10 @@ def main():
         "stage_us": {k: v * 1e3 for k, v in stage_ms.items()},
         "stage_us_from": ("the timed steps" if args.timed_events == "all"
                           else f"{n_st} untimed steps with an event around "
-                               "every stage"),
+                               "every stage (one stream)"),
+        "streams": ("append on a second stream, concurrent with the query "
+                    "path" if side is not None else "one stream"),
+        "query": args.query,
         "kernel_source_hash": kernel_source_hash(),
     }
     if peaks is not None:
@@ -434,9 +485,9 @@ def main():
         rf["mfma_frac_achievable"] = tflops / peaks["mfma_bf16_TFLOPs"]
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
-    if mha or wl.name != "b64_ctx8k":
+    if mha or wl.name != "b64_ctx8k" or merged is not None:
         result["note"] = ("not the headline configuration: a measurement of "
-                          "another workload or attention path")
+                          "another workload, attention path or query form")
     print(json.dumps(result), flush=True)
 
 

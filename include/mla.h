@@ -176,6 +176,36 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
                         size_t ws_bytes, mla_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Pre-merged query absorption (a variant the pages allow: W_UQ^T W_UK can
+ * be merged ahead of time, 'MLA：潜在表示压缩与解耦 RoPE', section 4; the
+ * RoPE part cannot, section 5).
+ *
+ * mla_merge_uq_uk (once per layer): w_merged [n_h][d_c][d_cq] with
+ *   w_merged[h] = W_UK_h^T W_UQ_h (fp32 sums of d_h products, rounded once
+ *   to the weight dtype).  w_uq, w_uk as in mla_absorb_q; w_merged is
+ *   caller-allocated (n_h d_c d_cq elements).
+ * mla_absorb_q_merged: the output of mla_absorb_q, computed as
+ *   q_lat_h = w_merged[h] c_Q (c_Q = W_DQ h in fp32) and q_R = RoPE(W_QR
+ *   c_Q); one projection onto [w_merged; W_QR] replaces W_UQ and the
+ *   per-head absorption.  It streams n_h d_c d_cq merged weights instead of
+ *   n_h d_h (d_cq + d_c) (3x at DeepSeek-V2 dims), so the unmerged
+ *   mla_absorb_q is the faster form at every batch size measured; this
+ *   entry point exists to measure that.  Arguments as mla_absorb_q, with
+ *   w_merged in place of w_uq and w_uk; ws at least
+ *   mla_absorb_merged_workspace_bytes(dims, T).
+ * ---------------------------------------------------------------------- */
+mla_status mla_merge_uq_uk(const mla_dims* dims, const void* w_uq,
+                           const void* w_uk, void* w_merged,
+                           mla_stream_t stream);
+size_t mla_absorb_merged_workspace_bytes(const mla_dims* dims, int32_t T);
+mla_status mla_absorb_q_merged(const mla_dims* dims, int32_t T, const void* h,
+                               const int32_t* pos, const void* w_dq,
+                               const void* w_merged, const void* w_qr,
+                               const float* rope_cos, const float* rope_sin,
+                               int32_t max_pos, void* q_out, void* ws,
+                               size_t ws_bytes, mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * mla_decode - attention of absorbed queries over the latent cache.
  *
  * Sequence b has kv_lens[b] cached rows (positions 0 .. kv_lens[b]-1) and

@@ -59,6 +59,10 @@ _SIGNATURES = {
     "mla_absorb_workspace_bytes": (_S, [_DP, _I]),
     "mla_absorb_q": (_I, [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                           _S, _P]),
+    "mla_merge_uq_uk": (_I, [_DP, _P, _P, _P, _P]),
+    "mla_absorb_merged_workspace_bytes": (_S, [_DP, _I]),
+    "mla_absorb_q_merged": (_I, [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P,
+                                 _P, _S, _P]),
     "mla_decode_workspace_bytes": (_S, [_DP, _I, _I, _I, _I]),
     "mla_decode_auto_splits": (_I, [_DP, _I, _I, _I]),
     "mla_decode_noalloc": (_I, [_DP, _I, _I, _P, _P, _I, _P, _I, _P, _I, _I,
@@ -93,6 +97,11 @@ def lib() -> ctypes.CDLL:
                 "python -m mla_latent_kv_33_amd.build")
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
+            # a build without one of the functions (an older library named by
+            # MLA_LIBRARY) fails at that function's first call; the in-tree
+            # build exports all of them (host test)
+            if not hasattr(handle, name):
+                continue
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args
@@ -346,6 +355,34 @@ def mla_absorb_q(dims: MlaDims, h, pos, w_dq, w_uq, w_qr, w_uk, rope_cos,
     _check("mla_absorb_q", lib().mla_absorb_q(
         ctypes.byref(dims), T, *p[:5], p[7], p[5], p[6], rope_cos.shape[0],
         p[8], _ptr(ws, "ws"), wsb, _stream(stream)))
+
+
+def mla_merge_uq_uk(dims: MlaDims, w_uq, w_uk, w_merged, stream=None):
+    """w_merged [n_h, d_c, d_cq] = W_UK_h^T W_UQ_h per head."""
+    lt = _layer_dtype(dims)
+    p = _ptrs(_a(w_uq, "w_uq", lt, (dims.n_h * dims.d_h, dims.d_cq)),
+              _a(w_uk, "w_uk", lt, (dims.n_h * dims.d_h, dims.d_c)),
+              _a(w_merged, "w_merged", lt, (dims.n_h, dims.d_c, dims.d_cq)))
+    _check("mla_merge_uq_uk", lib().mla_merge_uq_uk(
+        ctypes.byref(dims), *p, _stream(stream)))
+
+
+def mla_absorb_q_merged(dims: MlaDims, h, pos, w_dq, w_merged, w_qr,
+                        rope_cos, rope_sin, q_out, ws=None, stream=None):
+    """The output of mla_absorb_q through the pre-merged W_UK_h^T W_UQ_h."""
+    T = h.shape[0]
+    lt = _layer_dtype(dims)
+    a = _query_args(dims, h, pos, w_dq, w_qr.new_empty((0,)), w_qr, rope_cos,
+                    rope_sin)
+    a[3] = _a(w_merged, "w_merged", lt, (dims.n_h, dims.d_c, dims.d_cq))
+    p = _ptrs(*a, _a(q_out, "q_out", lt,
+                     numel=T * dims.n_h * (dims.d_c + dims.d_r)))
+    ws, wsb = _workspace(
+        lib().mla_absorb_merged_workspace_bytes(ctypes.byref(dims), T)
+        if T else 0, h.device, ws)
+    _check("mla_absorb_q_merged", lib().mla_absorb_q_merged(
+        ctypes.byref(dims), T, *p[:7], rope_cos.shape[0], p[7],
+        _ptr(ws, "ws"), wsb, _stream(stream)))
 
 
 def mla_decode(dims: MlaDims, q, cache, block_table, kv_lens, max_kv_len: int,

@@ -12,7 +12,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla.so")
 SOURCES = ["mla_api.hip", "gemm.hip", "elementwise.hip", "decode_simt.hip",
-           "decode_mfma.hip", "absorb.hip", "prefill_mha.hip", "peaks.hip"]
+           "decode_mfma.hip", "absorb.hip", "prefill_mha.hip", "peaks.hip",
+           "gemv.hip", "merged.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Wno-inline-asm",

@@ -101,15 +101,20 @@ __global__ void query_rope_kernel(const float* __restrict__ qr, int nparts,
 }
 
 template <typename T>
+// Source row r sits at (r / grp) * lds_grp + (r % grp) * lds: groups of grp
+// rows, lds apart inside a group and lds_grp between groups.
 __global__ void convert_kernel(const float* __restrict__ src, long lds,
-                               int nparts, long part_stride, int rows,
-                               int cols, T* __restrict__ dst, long ldd) {
+                               int grp, long lds_grp, int nparts,
+                               long part_stride, int rows, int cols,
+                               T* __restrict__ dst, long ldd) {
   const long n = (long)rows * cols;
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n;
        i += (long)gridDim.x * blockDim.x) {
     const long r = i / cols, c = i - r * cols;
+    const long g = r / grp;
     DT<T>::store(dst, r * ldd + c,
-                 sum_parts(src, nparts, part_stride, r * lds + c));
+                 sum_parts(src, nparts, part_stride,
+                           g * lds_grp + (r - g * grp) * lds + c));
   }
 }
 
@@ -275,17 +280,21 @@ hipError_t launch_query_rope(const mla_dims& d, int T, const float* qr,
 hipError_t launch_convert(const mla_dims& d, int rows, int cols,
                           const float* src, long lds, int nparts,
                           long part_stride, void* dst, long ldd,
-                          hipStream_t stream) {
+                          hipStream_t stream, int grp, long lds_grp) {
   const long n = (long)rows * cols;
   if (n <= 0) return hipSuccess;
+  if (grp <= 0) {
+    grp = rows;
+    lds_grp = 0;
+  }
   if (d.dtype == MLA_BF16)
     hipLaunchKernelGGL(convert_kernel<uint16_t>, dim3(grid_for(n, 256)),
-                       dim3(256), 0, stream, src, lds, nparts, part_stride,
-                       rows, cols, (uint16_t*)dst, ldd);
+                       dim3(256), 0, stream, src, lds, grp, lds_grp, nparts,
+                       part_stride, rows, cols, (uint16_t*)dst, ldd);
   else
     hipLaunchKernelGGL(convert_kernel<float>, dim3(grid_for(n, 256)),
-                       dim3(256), 0, stream, src, lds, nparts, part_stride,
-                       rows, cols, (float*)dst, ldd);
+                       dim3(256), 0, stream, src, lds, grp, lds_grp, nparts,
+                       part_stride, rows, cols, (float*)dst, ldd);
   return hipGetLastError();
 }
 

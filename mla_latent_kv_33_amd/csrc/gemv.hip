@@ -1,0 +1,439 @@
+// Projections of a decode step with at most GV_MAXT (4) new tokens, as
+// matrix-vector products ('MLA：潜在表示压缩与解耦 RoPE', sections 3, 4, 6
+// and 7: c_KV = W_DKV h, k_R = RoPE(W_KR h), c_Q = W_DQ h, q_C = W_UQ c_Q,
+// q_R = RoPE(W_QR c_Q), q_lat_h = W_UK_h^T q_C_h, v_h = W_UV_h o_lat_h,
+// u = W_O v).
+//
+// With one to four tokens every projection only streams its weights once;
+// the matrix cores would compute 32-row tiles for one real row, and a K
+// split would need a second pass to sum its parts.  Here one wave owns R
+// whole weight rows: its 64 lanes read each row in 1 KiB runs (16 bytes
+// per lane per load, GV_U loads in flight per row), multiply them by the
+// activations in fp32 (the activations, bf16 or fp32, are read through the
+// L1 cache, shared by the waves of a compute unit), and reduce across the
+// lanes.  No partial results leave the wave, so each projection is one
+// kernel whose epilogue writes the final form: cache rows with the RoPE key
+// rotated, c_Q / q_C / v in fp32 for the next projection, the rotated q_R
+// into the query row, u in bf16.
+//
+// The absorption q_lat_h = W_UK_h^T q_C_h reads W_UK_h [d_h][d_c] by rows:
+// one workgroup per head, each of its 8 waves accumulates 16 rows (lanes
+// own 8 latent columns each) and the waves' sums meet in LDS.
+
+#include "mla_common.hpp"
+#include "mla_kernels.hpp"
+
+namespace mla {
+namespace {
+
+// 16-byte weight loads in flight per row and lane: a whole row of the
+// 5120-wide projections (10 loads, 2 rows per wave), a quarter of W_O's
+// 16384-wide rows (8 loads, 4 rows per wave); enough bytes in flight for
+// the chip's memory latency even when the projection is small.
+constexpr int GV_U_WIDE = 8;
+constexpr int GV_U_D = 10;
+
+// 8 consecutive activations of token row x (bf16 or fp32) as fp32.
+template <bool XF32>
+__device__ __forceinline__ void load_x8(const void* x, long i, float* v) {
+  if (XF32) {
+    const f32x4 a = *(const f32x4*)((const float*)x + i);
+    const f32x4 b = *(const f32x4*)((const float*)x + i + 4);
+    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+    v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  } else {
+    const u32x4 u = *(const u32x4*)((const uint16_t*)x + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __uint_as_float(u[e] << 16);
+      v[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+    }
+  }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// acc[t][r] = sum_k W[row r][k] x[t][k] over this lane's 16-byte pieces
+// p = lane, lane + 64, ..., then summed over the wave (every lane holds the
+// totals).  K % 8 == 0.
+template <int T, int R, bool XF32, int GV_U = 4>
+__device__ __forceinline__ void gemv_rows(const uint16_t* const (&w)[R],
+                                          const void* x, long ldx, int K,
+                                          int lane, float (&acc)[T][R]) {
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[t][r] = 0.0f;
+  const int np = K / 8;
+  for (int p0 = lane; p0 < np; p0 += 64 * GV_U) {
+    u32x4 wv[GV_U][R];
+#pragma unroll
+    for (int u = 0; u < GV_U; ++u) {
+      const int p = p0 + 64 * u;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        wv[u][r] = p < np ? *(const u32x4*)(w[r] + 8 * p) : (u32x4){0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < GV_U; ++u) {
+      const int p = p0 + 64 * u;
+      if (p >= np) break;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        float xv[8];
+        if (XF32)
+          load_x8<true>((const char*)x + (size_t)t * ldx * 4, 8L * p, xv);
+        else
+          load_x8<false>((const char*)x + (size_t)t * ldx * 2, 8L * p, xv);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[t][r] = __builtin_fmaf(__uint_as_float(wv[u][r][e] << 16),
+                                       xv[2 * e], acc[t][r]);
+            acc[t][r] = __builtin_fmaf(
+                __uint_as_float(wv[u][r][e] & 0xFFFF0000u), xv[2 * e + 1],
+                acc[t][r]);
+          }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[t][r] = wave_sum(acc[t][r]);
+}
+
+// RoPE of the pair (x1, x2) = (x_j, x_{j + d_r/2}) at position p: NaN for a
+// position outside the table (the documented behaviour of every path).
+__device__ __forceinline__ void rope_pair(float x1, float x2, int p, int j,
+                                          int half, int max_pos,
+                                          const float* __restrict__ rcos,
+                                          const float* __restrict__ rsin,
+                                          float& y1, float& y2) {
+  const bool ok = p >= 0 && p < max_pos;
+  const float c = ok ? rcos[(long)p * half + j] : NAN;
+  const float s = ok ? rsin[(long)p * half + j] : NAN;
+  y1 = x1 * c - x2 * s;
+  y2 = x1 * s + x2 * c;
+}
+
+// ---- append: c_KV rows (pairs of rows) and k_R pairs (j, j + d_r/2) ----
+// task < d_c / 2: rows 2 task, 2 task + 1 of W_DKV; then k_R task
+// jt = task - d_c / 2: rows j = 2 jt, 2 jt + 1 and j + d_r/2 of W_KR.
+template <int T>
+__global__ __launch_bounds__(64) void gemv_append_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_dkv,
+    const uint16_t* __restrict__ w_kr, int d, int d_c, int d_r,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
+    const float* __restrict__ rcos, const float* __restrict__ rsin,
+    int max_pos, const int32_t* __restrict__ block_table, int max_blocks,
+    int block_size, uint16_t* __restrict__ cache) {
+  const int lane = threadIdx.x;
+  const int task = blockIdx.x;
+  const int width = d_c + d_r, half = d_r / 2;
+  const bool is_kv = task < d_c / 2;
+  int cols[4];
+  float acc[T][4];
+  if (is_kv) {  // (wave-uniform branch)
+    cols[0] = 2 * task; cols[1] = 2 * task + 1;
+    const uint16_t* w[2] = {w_dkv + (size_t)cols[0] * d,
+                            w_dkv + (size_t)cols[1] * d};
+    float a2[T][2];
+    gemv_rows<T, 2, false, GV_U_D>(w, h, d, d, lane, a2);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      acc[t][0] = a2[t][0];
+      acc[t][1] = a2[t][1];
+      acc[t][2] = acc[t][3] = 0.0f;
+    }
+  } else {
+    const int j = 2 * (task - d_c / 2);
+    cols[0] = j; cols[1] = j + 1; cols[2] = j + half; cols[3] = j + 1 + half;
+    const uint16_t* w[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w[r] = w_kr + (size_t)cols[r] * d;
+    gemv_rows<T, 4, false, GV_U_D / 2>(w, h, d, d, lane, acc);
+  }
+  if (lane >= T) return;
+  // lane t writes token t's values (after the sums every lane holds all)
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    if (t != lane) continue;
+    const int p = pos[t];
+    const int blk =
+        block_table[(long)seq_idx[t] * max_blocks + p / block_size];
+    uint16_t* row = cache + ((long)blk * block_size + (p % block_size)) * width;
+    if (is_kv) {
+      row[cols[0]] = f2bf(acc[t][0]);
+      row[cols[1]] = f2bf(acc[t][1]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        float y1, y2;
+        rope_pair(acc[t][k], acc[t][k + 2], p, cols[k], half, max_pos, rcos,
+                  rsin, y1, y2);
+        row[d_c + cols[k]] = f2bf(y1);
+        row[d_c + cols[k] + half] = f2bf(y2);
+      }
+    }
+  }
+}
+
+// ---- plain rows: y[t][n] = W[n] . x[t] for rows n of one or two parts ----
+// Rows R task .. R task + R - 1 (< N); xsel: per-head activations (W_UV: x
+// of row n is x + (n / d_h) xhead; d_h % R == 0); out fp32 (ldy) or bf16.
+template <int T, bool XF32, bool OUT_BF16, int R, int U>
+__global__ __launch_bounds__(64) void gemv_plain_kernel(
+    const uint16_t* __restrict__ W, int N, int K, const void* __restrict__ x,
+    long ldx, int d_h_sel, long xhead, void* __restrict__ y, long ldy) {
+  const int lane = threadIdx.x;
+  const int n0 = R * blockIdx.x;
+  const uint16_t* w[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) w[r] = W + (size_t)min(n0 + r, N - 1) * K;
+  const void* xs = x;
+  if (d_h_sel > 0)
+    xs = (const char*)x + (size_t)(n0 / d_h_sel) * xhead * (XF32 ? 4 : 2);
+  float acc[T][R];
+  gemv_rows<T, R, XF32, U>(w, xs, ldx, K, lane, acc);
+  // lane R t + r writes (t, row r)
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (lane == R * t + r && n0 + r < N) {
+        if (OUT_BF16)
+          ((uint16_t*)y)[(size_t)t * ldy + n0 + r] = f2bf(acc[t][r]);
+        else
+          ((float*)y)[(size_t)t * ldy + n0 + r] = acc[t][r];
+      }
+}
+
+// ---- query up-projection: q_C rows (fp32 out) and q_R pairs (rotated,
+// bf16 into the query row) ----------------------------------------------
+// task < n_h d_h / 4: rows 4 task .. + 3 of W_UQ -> qc[t][n]; then task
+// jt = task - n_h d_h / 4 of the RoPE part: head hh = jt / (d_r / 4), rows
+// j, j + 1, j + d_r/2, j + 1 + d_r/2 of W_QR_hh (j = 2 (jt % (d_r / 4))).
+template <int T>
+__global__ __launch_bounds__(64) void gemv_uq_kernel(
+    const float* __restrict__ cq, int d_cq, const uint16_t* __restrict__ w_uq,
+    const uint16_t* __restrict__ w_qr, int n_h, int d_h, int d_c, int d_r,
+    float* __restrict__ qc, const int32_t* __restrict__ pos,
+    const float* __restrict__ rcos, const float* __restrict__ rsin,
+    int max_pos, uint16_t* __restrict__ q_out) {
+  const int lane = threadIdx.x;
+  const int task = blockIdx.x;
+  const int nqc = n_h * d_h, half = d_r / 2;
+  const bool is_c = task < nqc / 4;
+  const uint16_t* w[4];
+  int hh = 0, j = 0;
+  if (is_c) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) w[r] = w_uq + (size_t)(4 * task + r) * d_cq;
+  } else {
+    const int jt = task - nqc / 4;
+    hh = jt / (d_r / 4);
+    j = 2 * (jt % (d_r / 4));
+    const uint16_t* wh = w_qr + (size_t)hh * d_r * d_cq;
+    w[0] = wh + (size_t)j * d_cq;
+    w[1] = wh + (size_t)(j + 1) * d_cq;
+    w[2] = wh + (size_t)(j + half) * d_cq;
+    w[3] = wh + (size_t)(j + 1 + half) * d_cq;
+  }
+  float acc[T][4];
+  gemv_rows<T, 4, true>(w, cq, d_cq, d_cq, lane, acc);
+  if (is_c) {
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (lane == 4 * t + r) qc[(size_t)t * nqc + 4 * task + r] = acc[t][r];
+  } else {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if (lane != t) continue;
+      uint16_t* dst =
+          q_out + ((size_t)t * n_h + hh) * (d_c + d_r) + d_c;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        float y1, y2;
+        rope_pair(acc[t][k], acc[t][k + 2], pos[t], j + k, half, max_pos,
+                  rcos, rsin, y1, y2);
+        dst[j + k] = f2bf(y1);
+        dst[j + k + half] = f2bf(y2);
+      }
+    }
+  }
+}
+
+// ---- absorption: q_lat_h = W_UK_h^T q_C_h -------------------------------
+// Workgroup = head hh, 8 waves; wave w accumulates rows i = w, w + 8, ...
+// of W_UK_h (d_h rows of d_c), lane l owning latent columns
+// 8 l + 512 c (c = 0 .. d_c / 512 - 1); the waves' sums are added in LDS and
+// written as bf16 into the first d_c columns of each token's query row.
+constexpr int AB_WAVES = 8;
+template <int T>
+__global__ __launch_bounds__(64 * AB_WAVES) void gemv_absorb_kernel(
+    const float* __restrict__ qc, const uint16_t* __restrict__ w_uk,
+    int n_h, int d_h, int d_c, int d_r, uint16_t* __restrict__ q_out) {
+  extern __shared__ float red[];  // [AB_WAVES][T][d_c]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int hh = blockIdx.x;
+  const int nch = d_c / 512;  // 512-column chunks (d_c % 512 == 0)
+  const uint16_t* wh = w_uk + (size_t)hh * d_h * d_c;
+  const float* qh = qc + (size_t)hh * d_h;
+  for (int c = 0; c < nch; ++c) {
+    float acc[T][8];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[t][e] = 0.0f;
+    const int col = 512 * c + 8 * lane;
+    // all of the wave's rows in flight at once (16 for d_h = 128)
+    constexpr int AU = 16;
+    for (int i0 = wave; i0 < d_h; i0 += AB_WAVES * AU) {
+      u32x4 wv[AU];
+#pragma unroll
+      for (int u = 0; u < AU; ++u) {
+        const int i = i0 + AB_WAVES * u;
+        wv[u] = i < d_h ? *(const u32x4*)(wh + (size_t)i * d_c + col)
+                        : (u32x4){0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < AU; ++u) {
+        const int i = i0 + AB_WAVES * u;
+        if (i >= d_h) break;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const float s = qh[(size_t)t * n_h * d_h + i];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[t][2 * e] = __builtin_fmaf(
+                __uint_as_float(wv[u][e] << 16), s, acc[t][2 * e]);
+            acc[t][2 * e + 1] = __builtin_fmaf(
+                __uint_as_float(wv[u][e] & 0xFFFF0000u), s,
+                acc[t][2 * e + 1]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        red[((size_t)wave * T + t) * 512 + 8 * lane + e] = acc[t][e];
+    __syncthreads();
+    for (int k = threadIdx.x; k < T * 512; k += 64 * AB_WAVES) {
+      const int t = k / 512, cc = k % 512;
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < AB_WAVES; ++w) s += red[((size_t)w * T + t) * 512 + cc];
+      q_out[((size_t)t * n_h + hh) * (d_c + d_r) + 512 * c + cc] = f2bf(s);
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+bool gemv_supported(const mla_dims& d, int T) {
+  return d.dtype == MLA_BF16 && T >= 1 && T <= GV_MAXT && d.d % 8 == 0 &&
+         d.d_cq % 8 == 0 && d.d_c % 512 == 0 && d.d_c % 4 == 0 &&
+         d.d_r % 4 == 0 && d.d_h % 4 == 0 && (d.n_h * d.d_h) % 8 == 0;
+}
+
+#define MLA_GV_T(T, CALL) \
+  switch (T) {            \
+    case 1: CALL(1); break; \
+    case 2: CALL(2); break; \
+    case 3: CALL(3); break; \
+    default: CALL(4); break; \
+  }
+
+hipError_t launch_gemv_append(const mla_dims& d, int T, const void* h,
+                              const void* w_dkv, const void* w_kr,
+                              const int32_t* seq_idx, const int32_t* pos,
+                              const float* rope_cos, const float* rope_sin,
+                              int max_pos, const int32_t* block_table,
+                              int max_blocks, void* cache,
+                              hipStream_t stream) {
+  const int tasks = d.d_c / 2 + d.d_r / 4;
+#define MLA_APP(TT)                                                          \
+  hipLaunchKernelGGL(gemv_append_kernel<TT>, dim3(tasks), dim3(64), 0,       \
+                     stream, (const uint16_t*)h, (const uint16_t*)w_dkv,      \
+                     (const uint16_t*)w_kr, d.d, d.d_c, d.d_r, seq_idx, pos, \
+                     rope_cos, rope_sin, max_pos, block_table, max_blocks,   \
+                     d.block_size, (uint16_t*)cache)
+  MLA_GV_T(T, MLA_APP)
+#undef MLA_APP
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_query(const mla_dims& d, int T, const void* h,
+                             const void* w_dq, const void* w_uq,
+                             const void* w_qr, const void* w_uk,
+                             const int32_t* pos, const float* rope_cos,
+                             const float* rope_sin, int max_pos, float* cq,
+                             float* qc, void* q_out, hipStream_t stream) {
+  // c_Q = W_DQ h (fp32)
+  const int t1 = (d.d_cq + 1) / 2;
+#define MLA_DQ(TT)                                                           \
+  hipLaunchKernelGGL((gemv_plain_kernel<TT, false, false, 2, GV_U_D>),       \
+                     dim3(t1),                                               \
+                     dim3(64), 0, stream, (const uint16_t*)w_dq, d.d_cq, d.d, \
+                     h, (long)d.d, 0, 0L, (void*)cq, (long)d.d_cq)
+  MLA_GV_T(T, MLA_DQ)
+#undef MLA_DQ
+  // q_C (fp32) and RoPE(q_R) into the query rows
+  const int t2 = d.n_h * d.d_h / 4 + d.n_h * (d.d_r / 4);
+#define MLA_UQ(TT)                                                           \
+  hipLaunchKernelGGL(gemv_uq_kernel<TT>, dim3(t2), dim3(64), 0, stream, cq,   \
+                     d.d_cq, (const uint16_t*)w_uq, (const uint16_t*)w_qr,    \
+                     d.n_h, d.d_h, d.d_c, d.d_r, qc, pos,                     \
+                     rope_cos, rope_sin, max_pos, (uint16_t*)q_out)
+  MLA_GV_T(T, MLA_UQ)
+#undef MLA_UQ
+  // q_lat_h = W_UK_h^T q_C_h
+#define MLA_AB(TT)                                                          \
+  hipLaunchKernelGGL(gemv_absorb_kernel<TT>, dim3(d.n_h),                   \
+                     dim3(64 * AB_WAVES), AB_WAVES * TT * 512 * 4, stream, qc, \
+                     (const uint16_t*)w_uk, d.n_h, d.d_h, d.d_c, d.d_r,      \
+                     (uint16_t*)q_out)
+  MLA_GV_T(T, MLA_AB)
+#undef MLA_AB
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_out(const mla_dims& d, int T, const float* o_lat,
+                           const void* w_uv, const void* w_o, float* v,
+                           void* u, hipStream_t stream) {
+  const int nv = d.n_h * d.d_h;
+  // v_h = W_UV_h o_lat_h (fp32): rows of head h read x = o_lat[t][h]
+#define MLA_UV(TT)                                                           \
+  hipLaunchKernelGGL((gemv_plain_kernel<TT, true, false, 4, 1>),            \
+                     dim3(nv / 4),                                           \
+                     dim3(64), 0, stream, (const uint16_t*)w_uv, nv, d.d_c,   \
+                     (const void*)o_lat, (long)d.n_h * d.d_c, d.d_h,          \
+                     (long)d.d_c, (void*)v, (long)nv)
+  MLA_GV_T(T, MLA_UV)
+#undef MLA_UV
+  // u = W_O v (bf16)
+#define MLA_O(TT)                                                            \
+  hipLaunchKernelGGL((gemv_plain_kernel<TT, true, true, 4, GV_U_WIDE>),      \
+                     dim3((d.d + 3) / 4),                                    \
+                     dim3(64), 0, stream, (const uint16_t*)w_o, d.d, nv,      \
+                     (const void*)v, (long)nv, 0, 0L, u, (long)d.d)
+  MLA_GV_T(T, MLA_O)
+#undef MLA_O
+  return hipGetLastError();
+}
+
+#undef MLA_GV_T
+
+}  // namespace mla

@@ -261,6 +261,10 @@ mla_status mla_append_cache(const mla_dims* dims, int32_t T, const void* h,
   const size_t need = mla_append_workspace_bytes(dims, T);
   if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
+  if (gemv_supported(d, T))
+    return dev(launch_gemv_append(d, T, h, w_dkv, w_kr, seq_idx, pos,
+                                  rope_cos, rope_sin, max_pos, block_table,
+                                  max_blocks, cache, s));
   GemmArgs g = append_gemm(d, T);
   g.A = h;
   g.B = w_dkv;
@@ -293,6 +297,10 @@ mla_status mla_append_cache_rmsnorm(
   const size_t need = mla_append_workspace_bytes(dims, T);
   if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
+  if (gemv_supported(d, T))
+    return dev(launch_gemv_append(d, T, h, w_dkv, w_kr, seq_idx, pos,
+                                  rope_cos, rope_sin, max_pos, block_table,
+                                  max_blocks, cache, s));
   GemmArgs g = append_gemm(d, T);
   g.A = h;
   g.B = w_dkv;
@@ -348,6 +356,15 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
   const AbsorbWs w = absorb_layout(d, T, ws);
   if (ws_bytes < w.bytes) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
+  if (gemv_supported(d, T)) {
+    // c_Q and q_C in fp32 at the start of the workspace (the layout above
+    // holds at least T (d_cq + n_h (d_h + d_r)) floats)
+    float* cq = (float*)ws;
+    float* qc = cq + (size_t)T * d.d_cq;
+    return dev(launch_gemv_query(d, T, h, w_dq, w_uq, w_qr, w_uk, pos,
+                                 rope_cos, rope_sin, max_pos, cq, qc, q_out,
+                                 s));
+  }
 
   GemmArgs g1 = cq_gemm(d, T);
   GemmArgs g2 = qcr_gemm(d, T);
@@ -399,6 +416,99 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
   else
     g3.C = (float*)q_out;
   MLA_TRY(launch_gemm(d, g3, s));
+  return MLA_OK;
+}
+
+// ------------------------------------------------- pre-merged absorption
+namespace {
+GemmArgs merged_gemm(const mla_dims& d, int T) {
+  GemmArgs g;
+  g.a_f32 = 1;
+  g.lda = d.d_cq;
+  g.nb1 = d.n_h * d.d_c;
+  g.ldb = d.d_cq;
+  g.ldc = (long)d.n_h * (d.d_c + d.d_r);
+  g.c_ks = (long)T * g.ldc;
+  g.M = T;
+  g.N = d.n_h * (d.d_c + d.d_r);
+  g.K = d.d_cq;
+  gemm_plan(d, g);
+  return g;
+}
+struct MergedWs {
+  float *cq_parts, *cq, *parts;
+  size_t bytes;
+};
+MergedWs merged_layout(const mla_dims& d, int T, void* base) {
+  Carve c(base);
+  MergedWs w;
+  const GemmArgs g1 = cq_gemm(d, T), g2 = merged_gemm(d, T);
+  w.cq_parts = c.take(parts_floats(g1));
+  w.cq = g1.k_split > 1 ? c.take((size_t)T * d.d_cq) : w.cq_parts;
+  w.parts = c.take(parts_floats(g2));
+  w.bytes = c.used;
+  return w;
+}
+}  // namespace
+
+mla_status mla_merge_uq_uk(const mla_dims* dims, const void* w_uq,
+                           const void* w_uk, void* w_merged,
+                           mla_stream_t stream) {
+  if (!dims) return MLA_ERR_NULL;
+  if (!dims_ok(dims)) return MLA_ERR_SHAPE;
+  if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  if (!w_uq || !w_uk || !w_merged) return MLA_ERR_NULL;
+  return dev(launch_merge_uq_uk(*dims, w_uq, w_uk, w_merged,
+                                (hipStream_t)stream));
+}
+
+size_t mla_absorb_merged_workspace_bytes(const mla_dims* dims, int32_t T) {
+  if (!dims_ok(dims) || T <= 0) return 0;
+  return merged_layout(*dims, T, nullptr).bytes;
+}
+
+mla_status mla_absorb_q_merged(const mla_dims* dims, int32_t T, const void* h,
+                               const int32_t* pos, const void* w_dq,
+                               const void* w_merged, const void* w_qr,
+                               const float* rope_cos, const float* rope_sin,
+                               int32_t max_pos, void* q_out, void* ws,
+                               size_t ws_bytes, mla_stream_t stream) {
+  if (!dims) return MLA_ERR_NULL;
+  if (!dims_ok(dims) || T < 0 || max_pos <= 0) return MLA_ERR_SHAPE;
+  if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  if (T == 0) return MLA_OK;
+  if (!h || !pos || !w_dq || !w_merged || !w_qr || !rope_cos || !rope_sin ||
+      !q_out)
+    return MLA_ERR_NULL;
+  const mla_dims& d = *dims;
+  if (!ws) return MLA_ERR_WORKSPACE;
+  const MergedWs w = merged_layout(d, T, ws);
+  if (ws_bytes < w.bytes) return MLA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  // c_Q = W_DQ h (fp32)
+  GemmArgs g1 = cq_gemm(d, T);
+  g1.A = h;
+  g1.B = w_dq;
+  g1.C = w.cq_parts;
+  MLA_TRY(launch_gemm(d, g1, s));
+  if (g1.k_split > 1)
+    MLA_TRY(launch_reduce_parts(w.cq_parts, g1.k_split, g1.c_ks,
+                                (long)T * d.d_cq, w.cq, s));
+  // [q_lat of every head | q_R before RoPE] = c_Q [M_0; ...; W_QR]^T
+  GemmArgs g2 = merged_gemm(d, T);
+  g2.A = w.cq;
+  g2.B = w_merged;
+  g2.B2 = w_qr;
+  g2.C = w.parts;
+  MLA_TRY(launch_gemm(d, g2, s));
+  // q_lat rows (t, h) of d_c values into the first d_c columns of the query
+  // rows (source: token t's GEMM row, head h's d_c columns), then RoPE(q_R)
+  // into the last d_r
+  MLA_TRY(launch_convert(d, T * d.n_h, d.d_c, w.parts, d.d_c, g2.k_split,
+                         g2.c_ks, q_out, d.d_c + d.d_r, s, d.n_h, g2.ldc));
+  MLA_TRY(launch_query_rope(d, T, w.parts + (long)d.n_h * d.d_c, g2.k_split,
+                            g2.c_ks, g2.ldc, pos, rope_cos, rope_sin, max_pos,
+                            q_out, s));
   return MLA_OK;
 }
 
@@ -763,6 +873,8 @@ mla_status mla_out(const mla_dims* dims, int32_t T, const float* o_lat,
   const OutWs w = out_layout(d, T, ws);
   if (ws_bytes < w.bytes) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
+  if (gemv_supported(d, T))  // v in fp32 (the layout holds T n_h d_h floats)
+    return dev(launch_gemv_out(d, T, o_lat, w_uv, w_o, (float*)ws, u, s));
   GemmArgs g1 = uv_gemm(d, T);
   GemmArgs g2 = o_gemm(d, T);
   // v goes to the weight-streaming kernel of W_O pre-split (hi|lo), written

@@ -56,6 +56,37 @@ hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
                           float* o_lat, float* lse, hipStream_t stream,
                           const int2* plan = nullptr, int slots = 0);
 
+// ---- projections of decode steps with at most GV_MAXT tokens (gemv.hip) --
+// One wave per group of weight rows, full contraction, no partial results.
+constexpr int GV_MAXT = 4;
+bool gemv_supported(const mla_dims& d, int T);
+// c_KV and RoPE(k_R) of T tokens straight into their cache rows.
+hipError_t launch_gemv_append(const mla_dims& d, int T, const void* h,
+                              const void* w_dkv, const void* w_kr,
+                              const int32_t* seq_idx, const int32_t* pos,
+                              const float* rope_cos, const float* rope_sin,
+                              int max_pos, const int32_t* block_table,
+                              int max_blocks, void* cache,
+                              hipStream_t stream);
+// c_Q -> cq [T][d_cq] fp32, q_C -> qc [T][n_h d_h] fp32, then q_out[t][h] =
+// [W_UK_h^T q_C_h | RoPE(q_R)_h] in bf16.
+hipError_t launch_gemv_query(const mla_dims& d, int T, const void* h,
+                             const void* w_dq, const void* w_uq,
+                             const void* w_qr, const void* w_uk,
+                             const int32_t* pos, const float* rope_cos,
+                             const float* rope_sin, int max_pos, float* cq,
+                             float* qc, void* q_out, hipStream_t stream);
+// v [T][n_h d_h] fp32 = W_UV_h o_lat_h, then u [T][d] bf16 = W_O v.
+hipError_t launch_gemv_out(const mla_dims& d, int T, const float* o_lat,
+                           const void* w_uv, const void* w_o, float* v,
+                           void* u, hipStream_t stream);
+
+// ---- pre-merged absorption (merged.hip) ---------------------------------
+// out [n_h][d_c][d_cq] = W_UK_h^T W_UQ_h per head, in the weight dtype.
+hipError_t launch_merge_uq_uk(const mla_dims& d, const void* w_uq,
+                              const void* w_uk, void* out,
+                              hipStream_t stream);
+
 // ---- MHA-path prefill (prefill_mha.hip) --------------------------------
 // Shapes the prefill kernel serves: bf16, d_h = 128 (= d_v), d_r = 64.
 bool prefill_mha_supported(const mla_dims& d);
@@ -181,9 +212,11 @@ hipError_t launch_query_rope(const mla_dims& d, int T, const float* qr,
                              hipStream_t stream);
 // src fp32 [rows][cols] (row stride lds, parts) -> dst layer dtype (row
 // stride ldd).
+// grp > 0: source rows in groups of grp, lds apart within a group and
+// lds_grp from one group to the next (grp <= 0: one group)
 hipError_t launch_convert(const mla_dims& d, int rows, int cols,
                           const float* src, long lds, int nparts,
                           long part_stride, void* dst, long ldd,
-                          hipStream_t stream);
+                          hipStream_t stream, int grp = 0, long lds_grp = 0);
 
 }  // namespace mla

@@ -438,3 +438,30 @@ def test_validate_block_table():
         Bn, mb, nq, bs, num = args
         assert lib.mla_validate_block_table(p, Bn, mb, p, nq, bs, num, 0,
                                             None) == SHAPE
+
+
+def test_premerged_absorption_validation():
+    lib = B.lib()
+    d = ds_dims()
+    assert lib.mla_merge_uq_uk(None, FAKE, FAKE, FAKE, None) == NULL
+    assert lib.mla_merge_uq_uk(ctypes.byref(d), FAKE, None, FAKE, None) == NULL
+    assert lib.mla_merge_uq_uk(ctypes.byref(ds_dims(d_r=63)), FAKE, FAKE,
+                               FAKE, None) == SHAPE
+    assert lib.mla_merge_uq_uk(ctypes.byref(ds_dims(d_cq=1552)), FAKE, FAKE,
+                               FAKE, None) == UNSUP
+    need = lib.mla_absorb_merged_workspace_bytes(ctypes.byref(d), 64)
+    # c_Q plus the merged projection's outputs: at least T (d_cq + n_h
+    # (d_c + d_r)) floats
+    assert need >= 64 * (1536 + 128 * 576) * 4
+    assert lib.mla_absorb_merged_workspace_bytes(ctypes.byref(d), 0) == 0
+
+    def call(T=4, ws=FAKE, ws_bytes=1 << 30, h=FAKE, max_pos=16):
+        return lib.mla_absorb_q_merged(ctypes.byref(d), T, h, FAKE, FAKE,
+                                       FAKE, FAKE, FAKE, FAKE, max_pos, FAKE,
+                                       ws, ws_bytes, None)
+    assert call(T=-1) == SHAPE
+    assert call(T=0) == OK
+    assert call(h=None) == NULL
+    assert call(ws=None) == WS
+    assert call(ws_bytes=16) == WS
+    assert call(max_pos=0) == SHAPE

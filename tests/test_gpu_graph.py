@@ -17,7 +17,11 @@ from tests.gpu_common import log
 pytestmark = pytest.mark.gpu
 
 
-def _workload(n_split):
+def _workload(name, n_split):
+    if name == "b1_ctx4k":
+        # the single-sequence step (1 x 4096 context + 1 token): 32 splits
+        # of 64 heads each, the combine for few query rows
+        return dataclasses.replace(W.workload("b1_ctx4k"), n_split=n_split)
     # 16 sequences, ragged contexts (partial last blocks), permuted table,
     # library-chosen splits (several per sequence, so the combine runs):
     # one count for all, or balanced per sequence (a plan the decode kernel
@@ -35,10 +39,13 @@ def _snapshot(st, out):
             "cache": st.cache.clone()}
 
 
-@pytest.mark.parametrize("n_split", [0, -1])
-def test_step_graph_replays_match_eager(n_split):
+@pytest.mark.parametrize("name,n_split", [("graph_b16", 0),
+                                          ("graph_b16", -1),
+                                          ("b1_ctx4k", 0)])
+def test_step_graph_replays_match_eager(name, n_split):
     assert torch.cuda.is_available(), "GPU tests need a GPU"
-    wl = _workload(n_split)
+    wl = _workload(name, n_split)
+    log(f"case {name} n_split={n_split}")
     layer = flow.make_layer(wl)
     st = flow.prepare(wl, layer)
     out = flow.run_step(st)           # eager: outputs and workspaces

@@ -148,6 +148,31 @@ def test_b1_ctx4k():
     check_sequence(wl, out, ref, 0)
 
 
+@pytest.mark.parametrize("ctx,n_q", [((300, 1000), 1),
+                                     ((64, 129, 2000), 1),
+                                     ((1, 50, 700, 1500), 1),
+                                     ((900,), 4)])
+def test_ds_few_tokens(ctx, n_q):
+    """DeepSeek-V2 dims with 2 to 4 new tokens per step (several sequences
+    of one token, or one sequence with a causal 4-token chunk): every
+    projection takes the matrix-vector path of at most four tokens.  Every
+    sequence, query, head and appended row against the oracle."""
+    base = W.workload("b1_ctx4k")
+    wl = dataclasses.replace(base, name=f"ds_few{len(ctx)}x{n_q}",
+                             batch=len(ctx), ctx=ctx, n_q=n_q, seed=13,
+                             permuted=True)
+    log(f"case DeepSeek-V2 dims, {len(ctx) * n_q} tokens: ctx={ctx} "
+        f"n_q={n_q}")
+    layer, w = layer_for(wl)
+    st = flow.prepare(wl, layer)
+    out = flow.run_step(st)
+    torch.cuda.synchronize()
+    for b in range(wl.batch):
+        ref = oracle_sequence(wl, w, b)
+        check_new_rows(wl, st, ref, b)
+        check_sequence(wl, out, ref, b)
+
+
 def test_b64_var():
     wl = W.workload("b64_var")
     log(f"case {wl.name}: B=64 ctx U[1024,8192] permuted table bf16")
@@ -244,3 +269,40 @@ def test_b8_chunked_prefill_causal():
     got = flow.gather_rows(st, 2, wl.ctx[2], wl.n_q)
     assert_close("seq2 chunk rows", got, np.concatenate([c_kv, k_r], 1),
                  "bf16")
+
+
+@pytest.mark.parametrize("T", [1, 64, 150])
+def test_premerged_absorption(T):
+    """The pre-merged query path (M_h = W_UK_h^T W_UQ_h built once, then
+    q_lat_h = M_h c_Q) against the oracle's absorbed query on T tokens (a
+    single token, a decode batch, a prefill-size chunk), and against the
+    unmerged mla_absorb_q."""
+    from mla_latent_kv_33_amd import binding as B
+    # context 4096 so that the RoPE tables cover the positions below
+    wl = dataclasses.replace(W.workload("b1_ctx4k"), batch=1, ctx=(4096,),
+                             n_q=T, seed=21)
+    d = wl.dims
+    layer, w = layer_for(wl)
+    merged = torch.empty((d.n_h, d.d_c, d.d_cq), dtype=torch.bfloat16,
+                         device="cuda")
+    B.mla_merge_uq_uk(layer.cdims, layer.w["w_uq"], layer.w["w_uk"], merged)
+    h_np = W.hidden_states(d, wl.dtype, wl.seed, 0, 0, T)
+    pos_np = np.arange(T) * 37 % 4000
+    h = torch.from_numpy(h_np.astype(np.float32)).to(torch.bfloat16).cuda()
+    pos = torch.from_numpy(pos_np.astype(np.int32)).cuda()
+    q_m = torch.empty((T, d.n_h, d.d_c + d.d_r), dtype=torch.bfloat16,
+                      device="cuda")
+    B.mla_absorb_q_merged(layer.cdims, h, pos, layer.w["w_dq"], merged,
+                          layer.w["w_qr"], layer.rope_cos, layer.rope_sin,
+                          q_m)
+    q_u = layer.absorb(h, pos)
+    torch.cuda.synchronize()
+    q_c, q_r = orc.query(h_np, pos_np, w["w_dq"], w["w_uq"], w["w_qr"],
+                         d.n_h, W.ROPE_BASE)
+    ref = orc.absorb_query(q_c, q_r, w["w_uk"])
+    assert_close(f"T={T} merged q", q_m.float().cpu().numpy(), ref, "bf16")
+    assert_close(f"T={T} unmerged q", q_u.float().cpu().numpy(), ref, "bf16")
+    # the RoPE columns come from the same W_QR projection in both forms
+    assert_close(f"T={T} merged vs unmerged q_R",
+                 q_m[..., d.d_c:].float().cpu().numpy(),
+                 q_u[..., d.d_c:].float().cpu().numpy(), "bf16")
