@@ -26,29 +26,29 @@
 namespace mla {
 namespace {
 
-// 16-byte weight loads in flight per row and lane: a whole row of the
-// 5120-wide projections (10 loads, 2 rows per wave), a quarter of W_O's
-// 16384-wide rows (8 loads, 4 rows per wave); enough bytes in flight for
-// the chip's memory latency even when the projection is small.
-constexpr int GV_U_WIDE = 8;
-constexpr int GV_U_D = 10;
+// 16-byte weight loads per row and lane in one register set (two sets in
+// flight): half a row of the 5120-wide projections (5 loads, 2 rows per
+// wave, 20 loads in flight), an eighth of W_O's 16384-wide rows (4 loads,
+// 4 rows per wave, 32 in flight); enough bytes in flight for the chip's
+// memory latency even when the projection is small.
+constexpr int GV_U_WIDE = 4;
+constexpr int GV_U_D = 5;
 
-// 8 consecutive activations of token row x (bf16 or fp32) as fp32.
-template <bool XF32>
-__device__ __forceinline__ void load_x8(const void* x, long i, float* v) {
-  if (XF32) {
-    const f32x4 a = *(const f32x4*)((const float*)x + i);
-    const f32x4 b = *(const f32x4*)((const float*)x + i + 4);
-    v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
-    v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
-  } else {
-    const u32x4 u = *(const u32x4*)((const uint16_t*)x + i);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[2 * e] = __uint_as_float(u[e] << 16);
-      v[2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
-    }
-  }
+// Activation forms a row routine reads (per token row, along k):
+//   XB16: bf16 values;
+//   XHL:  fp32 values stored pre-split as bf16 pairs, hi = bf16(x) and
+//         lo = bf16(x - hi): for every 8 consecutive values (one 16-byte
+//         weight piece) 16 bytes of hi then 16 bytes of lo;
+//   XF32: fp32 values.
+// bf16 activations meet the weights in v_dot2c_f32_bf16 (two products per
+// instruction, fp32 accumulate), the pre-split ones in two of them (hi and
+// lo), fp32 ones in fp32 fused multiply-adds.
+enum { XB16 = 0, XHL = 1, XF32 = 2 };
+
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                         __builtin_bit_cast(bf16x2, x), acc,
+                                         false);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -57,10 +57,69 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Activations of token row t at weight piece p (8 values along k), in the
+// registers the multiply reads: 4 words (XB16) or 8 (XHL: hi then lo; XF32).
+template <int XM>
+struct XPiece {
+  u32x4 a, b;
+};
+template <int T, int XM>
+__device__ __forceinline__ void load_x(const void* x, long ldx, int p,
+                                       XPiece<XM> (&xv)[T]) {
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    if (XM == XB16) {
+      xv[t].a = *(const u32x4*)((const uint16_t*)x + t * ldx + 8L * p);
+    } else if (XM == XHL) {
+      // token row t of the pre-split layout: 2 ldx bf16 values
+      const u32x4* xp =
+          (const u32x4*)((const uint16_t*)x + 2 * t * ldx + 16L * p);
+      xv[t].a = xp[0];
+      xv[t].b = xp[1];
+    } else {
+      const u32x4* xp = (const u32x4*)((const float*)x + t * ldx + 8L * p);
+      xv[t].a = xp[0];
+      xv[t].b = xp[1];
+    }
+  }
+}
+
+// Weight piece (16 bytes, 8 values along k) of every row times the token
+// rows' activations at the same k, accumulated into acc[t][r].
+template <int T, int R, int XM>
+__device__ __forceinline__ void mul_piece(const u32x4 (&wv)[R],
+                                          const XPiece<XM> (&xv)[T],
+                                          float (&acc)[T][R]) {
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (XM == XB16) {
+          acc[t][r] = dot2(wv[r][e], xv[t].a[e], acc[t][r]);
+        } else if (XM == XHL) {
+          acc[t][r] = dot2(wv[r][e], xv[t].a[e], acc[t][r]);
+          acc[t][r] = dot2(wv[r][e], xv[t].b[e], acc[t][r]);
+        } else {
+          const float x0 = __uint_as_float(e < 2 ? xv[t].a[2 * e] : xv[t].b[2 * e - 4]);
+          const float x1 = __uint_as_float(e < 2 ? xv[t].a[2 * e + 1] : xv[t].b[2 * e - 3]);
+          acc[t][r] = __builtin_fmaf(__uint_as_float(wv[r][e] << 16), x0,
+                                     acc[t][r]);
+          acc[t][r] = __builtin_fmaf(__uint_as_float(wv[r][e] & 0xFFFF0000u),
+                                     x1, acc[t][r]);
+        }
+      }
+}
+
 // acc[t][r] = sum_k W[row r][k] x[t][k] over this lane's 16-byte pieces
 // p = lane, lane + 64, ..., then summed over the wave (every lane holds the
-// totals).  K % 8 == 0.
-template <int T, int R, bool XF32, int GV_U = 4>
+// totals).  K % 512 == 0 (whole 64-lane piece groups).  Whole sets of U
+// groups run in two register sets: a set's activations are loaded, then the
+// next set's weights are issued, then the set is multiplied, so that the
+// wait for the activations leaves the next weights in flight.  A remainder
+// of fewer than U groups follows one group at a time.
+template <int T, int R, int XM, int U>
 __device__ __forceinline__ void gemv_rows(const uint16_t* const (&w)[R],
                                           const void* x, long ldx, int K,
                                           int lane, float (&acc)[T][R]) {
@@ -68,44 +127,72 @@ __device__ __forceinline__ void gemv_rows(const uint16_t* const (&w)[R],
   for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[t][r] = 0.0f;
-  const int np = K / 8;
-  for (int p0 = lane; p0 < np; p0 += 64 * GV_U) {
-    u32x4 wv[GV_U][R];
+  const int np = K / 8;  // pieces per row, a multiple of 64
+  constexpr int STEP = 64 * U;
+  const int nsets = np / STEP;
+  auto load_w = [&](u32x4 (&wv)[U][R], int q0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < GV_U; ++u) {
-      const int p = p0 + 64 * u;
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int r = 0; r < R; ++r)
-        wv[u][r] = p < np ? *(const u32x4*)(w[r] + 8 * p) : (u32x4){0, 0, 0, 0};
+        wv[u][r] = *(const u32x4*)(w[r] + 8 * (q0 + 64 * u + lane));
+  };
+  auto load_xs = [&](XPiece<XM> (&xv)[U][T], int q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_x<T, XM>(x, ldx, q0 + 64 * u + lane, xv[u]);
+  };
+  auto mul = [&](const u32x4 (&wv)[U][R], const XPiece<XM> (&xv)[U][T])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) mul_piece<T, R, XM>(wv[u], xv[u], acc);
+  };
+  if (nsets > 0) {
+    // No load in the loop body is conditional: a wait after a conditional
+    // load would have to assume it absent and drain the queue.
+    u32x4 wa[U][R], wb[U][R];
+    XPiece<XM> xs[U][T];
+    load_w(wa, 0);
+    int s = 0;
+    for (; s + 2 < nsets; s += 2) {
+      load_xs(xs, s * STEP);
+      load_w(wb, (s + 1) * STEP);
+      mul(wa, xs);
+      load_xs(xs, (s + 1) * STEP);
+      load_w(wa, (s + 2) * STEP);
+      mul(wb, xs);
     }
-#pragma unroll
-    for (int u = 0; u < GV_U; ++u) {
-      const int p = p0 + 64 * u;
-      if (p >= np) break;
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        float xv[8];
-        if (XF32)
-          load_x8<true>((const char*)x + (size_t)t * ldx * 4, 8L * p, xv);
-        else
-          load_x8<false>((const char*)x + (size_t)t * ldx * 2, 8L * p, xv);
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc[t][r] = __builtin_fmaf(__uint_as_float(wv[u][r][e] << 16),
-                                       xv[2 * e], acc[t][r]);
-            acc[t][r] = __builtin_fmaf(
-                __uint_as_float(wv[u][r][e] & 0xFFFF0000u), xv[2 * e + 1],
-                acc[t][r]);
-          }
-      }
+    load_xs(xs, s * STEP);
+    if (s + 1 < nsets) {
+      load_w(wb, (s + 1) * STEP);
+      mul(wa, xs);
+      load_xs(xs, (s + 1) * STEP);
+      mul(wb, xs);
+    } else {
+      mul(wa, xs);
     }
+  }
+  for (int q0 = nsets * STEP; q0 < np; q0 += 64) {
+    u32x4 wv[R];
+    XPiece<XM> xv[T];
+#pragma unroll
+    for (int r = 0; r < R; ++r) wv[r] = *(const u32x4*)(w[r] + 8 * (q0 + lane));
+    load_x<T, XM>(x, ldx, q0 + lane, xv);
+    mul_piece<T, R, XM>(wv, xv, acc);
   }
 #pragma unroll
   for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[t][r] = wave_sum(acc[t][r]);
+}
+
+// Writes value y of (token t, column n) in the pre-split layout of a row of
+// ld values: hi at 16 (n / 8) + n % 8 (bf16 units), lo 8 further.
+__device__ __forceinline__ void store_hl(uint16_t* y, long ld, int t, long n,
+                                         float v) {
+  const uint16_t hi = f2bf(v);
+  uint16_t* row = y + 2 * t * ld + 16 * (n >> 3) + (n & 7);
+  row[0] = hi;
+  row[8] = f2bf(v - bf2f(hi));
 }
 
 // RoPE of the pair (x1, x2) = (x_j, x_{j + d_r/2}) at position p: NaN for a
@@ -124,7 +211,7 @@ __device__ __forceinline__ void rope_pair(float x1, float x2, int p, int j,
 
 // ---- append: c_KV rows (pairs of rows) and k_R pairs (j, j + d_r/2) ----
 // task < d_c / 2: rows 2 task, 2 task + 1 of W_DKV; then k_R task
-// jt = task - d_c / 2: rows j = 2 jt, 2 jt + 1 and j + d_r/2 of W_KR.
+// j = task - d_c / 2: rows j and j + d_r/2 of W_KR (one RoPE pair).
 template <int T>
 __global__ __launch_bounds__(64) void gemv_append_kernel(
     const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_dkv,
@@ -137,28 +224,12 @@ __global__ __launch_bounds__(64) void gemv_append_kernel(
   const int task = blockIdx.x;
   const int width = d_c + d_r, half = d_r / 2;
   const bool is_kv = task < d_c / 2;
-  int cols[4];
-  float acc[T][4];
-  if (is_kv) {  // (wave-uniform branch)
-    cols[0] = 2 * task; cols[1] = 2 * task + 1;
-    const uint16_t* w[2] = {w_dkv + (size_t)cols[0] * d,
-                            w_dkv + (size_t)cols[1] * d};
-    float a2[T][2];
-    gemv_rows<T, 2, false, GV_U_D>(w, h, d, d, lane, a2);
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      acc[t][0] = a2[t][0];
-      acc[t][1] = a2[t][1];
-      acc[t][2] = acc[t][3] = 0.0f;
-    }
-  } else {
-    const int j = 2 * (task - d_c / 2);
-    cols[0] = j; cols[1] = j + 1; cols[2] = j + half; cols[3] = j + 1 + half;
-    const uint16_t* w[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) w[r] = w_kr + (size_t)cols[r] * d;
-    gemv_rows<T, 4, false, GV_U_D / 2>(w, h, d, d, lane, acc);
-  }
+  const int c0 = is_kv ? 2 * task : task - d_c / 2;
+  const int c1 = is_kv ? c0 + 1 : c0 + half;
+  const uint16_t* wm = is_kv ? w_dkv : w_kr;
+  const uint16_t* w[2] = {wm + (size_t)c0 * d, wm + (size_t)c1 * d};
+  float acc[T][2];
+  gemv_rows<T, 2, XB16, GV_U_D>(w, h, d, d, lane, acc);
   if (lane >= T) return;
   // lane t writes token t's values (after the sums every lane holds all)
 #pragma unroll
@@ -169,25 +240,25 @@ __global__ __launch_bounds__(64) void gemv_append_kernel(
         block_table[(long)seq_idx[t] * max_blocks + p / block_size];
     uint16_t* row = cache + ((long)blk * block_size + (p % block_size)) * width;
     if (is_kv) {
-      row[cols[0]] = f2bf(acc[t][0]);
-      row[cols[1]] = f2bf(acc[t][1]);
+      row[c0] = f2bf(acc[t][0]);
+      row[c1] = f2bf(acc[t][1]);
     } else {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        float y1, y2;
-        rope_pair(acc[t][k], acc[t][k + 2], p, cols[k], half, max_pos, rcos,
-                  rsin, y1, y2);
-        row[d_c + cols[k]] = f2bf(y1);
-        row[d_c + cols[k] + half] = f2bf(y2);
-      }
+      float y1, y2;
+      rope_pair(acc[t][0], acc[t][1], p, c0, half, max_pos, rcos, rsin, y1,
+                y2);
+      row[d_c + c0] = f2bf(y1);
+      row[d_c + c1] = f2bf(y2);
     }
   }
 }
 
-// ---- plain rows: y[t][n] = W[n] . x[t] for rows n of one or two parts ----
-// Rows R task .. R task + R - 1 (< N); xsel: per-head activations (W_UV: x
-// of row n is x + (n / d_h) xhead; d_h % R == 0); out fp32 (ldy) or bf16.
-template <int T, bool XF32, bool OUT_BF16, int R, int U>
+// ---- plain rows: y[t][n] = W[n] . x[t] ----------------------------------
+// Rows R task .. R task + R - 1 (< N); d_h_sel > 0: per-head activations
+// (W_UV: x of row n is x + (n / d_h_sel) xhead values; d_h_sel % R == 0).
+// Output: fp32, bf16, or the pre-split hi|lo pairs the next projection
+// reads (ldy values per token row).
+enum { YF32 = 0, YB16 = 1, YHL = 2 };
+template <int T, int XM, int YM, int R, int U>
 __global__ __launch_bounds__(64) void gemv_plain_kernel(
     const uint16_t* __restrict__ W, int N, int K, const void* __restrict__ x,
     long ldx, int d_h_sel, long xhead, void* __restrict__ y, long ldy) {
@@ -198,30 +269,34 @@ __global__ __launch_bounds__(64) void gemv_plain_kernel(
   for (int r = 0; r < R; ++r) w[r] = W + (size_t)min(n0 + r, N - 1) * K;
   const void* xs = x;
   if (d_h_sel > 0)
-    xs = (const char*)x + (size_t)(n0 / d_h_sel) * xhead * (XF32 ? 4 : 2);
+    xs = (const char*)x +
+         (size_t)(n0 / d_h_sel) * xhead * (XM == XF32 ? 4 : 2);
   float acc[T][R];
-  gemv_rows<T, R, XF32, U>(w, xs, ldx, K, lane, acc);
+  gemv_rows<T, R, XM, U>(w, xs, ldx, K, lane, acc);
   // lane R t + r writes (t, row r)
 #pragma unroll
   for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (lane == R * t + r && n0 + r < N) {
-        if (OUT_BF16)
+        if (YM == YB16)
           ((uint16_t*)y)[(size_t)t * ldy + n0 + r] = f2bf(acc[t][r]);
+        else if (YM == YHL)
+          store_hl((uint16_t*)y, ldy, t, n0 + r, acc[t][r]);
         else
           ((float*)y)[(size_t)t * ldy + n0 + r] = acc[t][r];
       }
 }
 
 // ---- query up-projection: q_C rows (fp32 out) and q_R pairs (rotated,
-// bf16 into the query row) ----------------------------------------------
+// bf16 into the query row), from c_Q in pre-split pairs ------------------
 // task < n_h d_h / 4: rows 4 task .. + 3 of W_UQ -> qc[t][n]; then task
 // jt = task - n_h d_h / 4 of the RoPE part: head hh = jt / (d_r / 4), rows
 // j, j + 1, j + d_r/2, j + 1 + d_r/2 of W_QR_hh (j = 2 (jt % (d_r / 4))).
 template <int T>
 __global__ __launch_bounds__(64) void gemv_uq_kernel(
-    const float* __restrict__ cq, int d_cq, const uint16_t* __restrict__ w_uq,
+    const uint16_t* __restrict__ cq, int d_cq,
+    const uint16_t* __restrict__ w_uq,
     const uint16_t* __restrict__ w_qr, int n_h, int d_h, int d_c, int d_r,
     float* __restrict__ qc, const int32_t* __restrict__ pos,
     const float* __restrict__ rcos, const float* __restrict__ rsin,
@@ -246,7 +321,7 @@ __global__ __launch_bounds__(64) void gemv_uq_kernel(
     w[3] = wh + (size_t)(j + 1 + half) * d_cq;
   }
   float acc[T][4];
-  gemv_rows<T, 4, true>(w, cq, d_cq, d_cq, lane, acc);
+  gemv_rows<T, 4, XHL, 3>(w, cq, d_cq, d_cq, lane, acc);
   if (is_c) {
 #pragma unroll
     for (int t = 0; t < T; ++t)
@@ -343,9 +418,10 @@ __global__ __launch_bounds__(64 * AB_WAVES) void gemv_absorb_kernel(
 }  // namespace
 
 bool gemv_supported(const mla_dims& d, int T) {
-  return d.dtype == MLA_BF16 && T >= 1 && T <= GV_MAXT && d.d % 8 == 0 &&
-         d.d_cq % 8 == 0 && d.d_c % 512 == 0 && d.d_c % 4 == 0 &&
-         d.d_r % 4 == 0 && d.d_h % 4 == 0 && (d.n_h * d.d_h) % 8 == 0;
+  // every contraction length a multiple of 512 (whole 64-lane piece sets)
+  return d.dtype == MLA_BF16 && T >= 1 && T <= GV_MAXT && d.d % 512 == 0 &&
+         d.d_cq % 512 == 0 && d.d_c % 512 == 0 && d.d_r % 4 == 0 &&
+         d.d_h % 4 == 0 && (d.n_h * d.d_h) % 512 == 0;
 }
 
 #define MLA_GV_T(T, CALL) \
@@ -363,7 +439,7 @@ hipError_t launch_gemv_append(const mla_dims& d, int T, const void* h,
                               int max_pos, const int32_t* block_table,
                               int max_blocks, void* cache,
                               hipStream_t stream) {
-  const int tasks = d.d_c / 2 + d.d_r / 4;
+  const int tasks = d.d_c / 2 + d.d_r / 2;
 #define MLA_APP(TT)                                                          \
   hipLaunchKernelGGL(gemv_append_kernel<TT>, dim3(tasks), dim3(64), 0,       \
                      stream, (const uint16_t*)h, (const uint16_t*)w_dkv,      \
@@ -381,10 +457,10 @@ hipError_t launch_gemv_query(const mla_dims& d, int T, const void* h,
                              const int32_t* pos, const float* rope_cos,
                              const float* rope_sin, int max_pos, float* cq,
                              float* qc, void* q_out, hipStream_t stream) {
-  // c_Q = W_DQ h (fp32)
+  // c_Q = W_DQ h, pre-split into hi|lo pairs for the next projection
   const int t1 = (d.d_cq + 1) / 2;
 #define MLA_DQ(TT)                                                           \
-  hipLaunchKernelGGL((gemv_plain_kernel<TT, false, false, 2, GV_U_D>),       \
+  hipLaunchKernelGGL((gemv_plain_kernel<TT, XB16, YHL, 2, GV_U_D>),          \
                      dim3(t1),                                               \
                      dim3(64), 0, stream, (const uint16_t*)w_dq, d.d_cq, d.d, \
                      h, (long)d.d, 0, 0L, (void*)cq, (long)d.d_cq)
@@ -393,7 +469,8 @@ hipError_t launch_gemv_query(const mla_dims& d, int T, const void* h,
   // q_C (fp32) and RoPE(q_R) into the query rows
   const int t2 = d.n_h * d.d_h / 4 + d.n_h * (d.d_r / 4);
 #define MLA_UQ(TT)                                                           \
-  hipLaunchKernelGGL(gemv_uq_kernel<TT>, dim3(t2), dim3(64), 0, stream, cq,   \
+  hipLaunchKernelGGL(gemv_uq_kernel<TT>, dim3(t2), dim3(64), 0, stream,      \
+                     (const uint16_t*)cq,                                    \
                      d.d_cq, (const uint16_t*)w_uq, (const uint16_t*)w_qr,    \
                      d.n_h, d.d_h, d.d_c, d.d_r, qc, pos,                     \
                      rope_cos, rope_sin, max_pos, (uint16_t*)q_out)
@@ -414,9 +491,10 @@ hipError_t launch_gemv_out(const mla_dims& d, int T, const float* o_lat,
                            const void* w_uv, const void* w_o, float* v,
                            void* u, hipStream_t stream) {
   const int nv = d.n_h * d.d_h;
-  // v_h = W_UV_h o_lat_h (fp32): rows of head h read x = o_lat[t][h]
+  // v_h = W_UV_h o_lat_h, pre-split into hi|lo pairs: rows of head h read
+  // x = o_lat[t][h]
 #define MLA_UV(TT)                                                           \
-  hipLaunchKernelGGL((gemv_plain_kernel<TT, true, false, 4, 1>),            \
+  hipLaunchKernelGGL((gemv_plain_kernel<TT, XF32, YHL, 4, 1>),              \
                      dim3(nv / 4),                                           \
                      dim3(64), 0, stream, (const uint16_t*)w_uv, nv, d.d_c,   \
                      (const void*)o_lat, (long)d.n_h * d.d_c, d.d_h,          \
@@ -425,7 +503,7 @@ hipError_t launch_gemv_out(const mla_dims& d, int T, const float* o_lat,
 #undef MLA_UV
   // u = W_O v (bf16)
 #define MLA_O(TT)                                                            \
-  hipLaunchKernelGGL((gemv_plain_kernel<TT, true, true, 4, GV_U_WIDE>),      \
+  hipLaunchKernelGGL((gemv_plain_kernel<TT, XHL, YB16, 4, GV_U_WIDE>),      \
                      dim3((d.d + 3) / 4),                                    \
                      dim3(64), 0, stream, (const uint16_t*)w_o, d.d, nv,      \
                      (const void*)v, (long)nv, 0, 0L, u, (long)d.d)
