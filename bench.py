@@ -85,6 +85,12 @@ def parse():
                          "mla_absorb_q (W_UQ, then W_UK_h^T per head) or "
                          "mla_absorb_q_merged (one projection onto the "
                          "pre-merged W_UK_h^T W_UQ_h, built once)")
+    ap.add_argument("--graph", action="store_true",
+                    help="timed steps replay HIP graphs (captured once after "
+                         "the warmup: append + query, attention, output) "
+                         "instead of launching each kernel from the host; "
+                         "for small batches, where the host's launch calls "
+                         "take longer than the GPU work")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured HBM-read and matrix-core rates")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -321,12 +327,49 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    graphs = None
+    if args.graph:
+        if args.streams != 1 or args.timed_events != "decode":
+            sys.exit("--graph needs one stream and --timed-events decode")
+
+        def out_stage():
+            if mha:
+                layer.out_values(out.o_v.view(-1, d.n_h * d.d_h), u=out.u)
+            else:
+                layer.out(out.o_lat.view(-1, d.n_h, d.d_c), u=out.u)
+
+        def pre_stage():
+            layer.append(st.h_new, st.seq_idx, st.pos, st.table, st.cache)
+            query_path()
+
+        # every call is capture-safe (no allocation, memset or
+        # synchronisation inside); three graphs so that the timed steps can
+        # still bracket the attention stage with events
+        graphs = []
+        for fn in (pre_stage, attention, out_stage):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            for g in graphs:
+                g.replay()
+        torch.cuda.synchronize()
     ev = new_events(args.steps)
     every = 1 if args.timed_events == "all" else max(1, args.event_every)
     sampled = [i for i in range(args.steps) if i % every == 0]
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(ev[i] if i % every == 0 else None, args.timed_events)
+    if graphs is not None:
+        for i in range(args.steps):
+            graphs[0].replay()
+            if i % every == 0: ev[i][2].record(stream)
+            graphs[1].replay()
+            if i % every == 0: ev[i][3].record(stream)
+            graphs[2].replay()
+    else:
+        for i in range(args.steps):
+            step(ev[i] if i % every == 0 else None, args.timed_events)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # attention stage (decode kernel + split combine, or the MHA prefill
@@ -476,6 +519,9 @@ def main():
         "streams": ("append on a second stream, concurrent with the query "
                     "path" if side is not None else "one stream"),
         "query": args.query,
+        "launch": ("timed steps replay three HIP graphs (append + query, "
+                   "attention, output) captured after the warmup"
+                   if graphs is not None else "eager launches from the host"),
         "kernel_source_hash": kernel_source_hash(),
     }
     if peaks is not None:
