@@ -417,9 +417,10 @@ __global__ __launch_bounds__(64 * AB_WAVES) void gemv_absorb_kernel(
 
 }  // namespace
 
-bool gemv_supported(const mla_dims& d, int T) {
+bool gemv_supported(const mla_dims& d, int T, int t_max) {
   // every contraction length a multiple of 512 (whole 64-lane piece sets)
-  return d.dtype == MLA_BF16 && T >= 1 && T <= GV_MAXT && d.d % 512 == 0 &&
+  return d.dtype == MLA_BF16 && T >= 1 && T <= t_max && T <= GV_MAXT &&
+         d.d % 512 == 0 &&
          d.d_cq % 512 == 0 && d.d_c % 512 == 0 && d.d_r % 4 == 0 &&
          d.d_h % 4 == 0 && (d.n_h * d.d_h) % 512 == 0;
 }

@@ -297,10 +297,9 @@ mla_status mla_append_cache_rmsnorm(
   const size_t need = mla_append_workspace_bytes(dims, T);
   if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  if (gemv_supported(d, T))
-    return dev(launch_gemv_append(d, T, h, w_dkv, w_kr, seq_idx, pos,
-                                  rope_cos, rope_sin, max_pos, block_table,
-                                  max_blocks, cache, s));
+  // The norm needs each whole c_KV row, which the matrix-vector append (two
+  // rows per wave) never holds: every T takes the GEMM and the normalising
+  // scatter.
   GemmArgs g = append_gemm(d, T);
   g.A = h;
   g.B = w_dkv;
@@ -356,9 +355,10 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
   const AbsorbWs w = absorb_layout(d, T, ws);
   if (ws_bytes < w.bytes) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  if (gemv_supported(d, T)) {
-    // c_Q and q_C in fp32 at the start of the workspace (the layout above
-    // holds at least T (d_cq + n_h (d_h + d_r)) floats)
+  if (gemv_supported(d, T, GV_QO_MAXT)) {
+    // c_Q (bf16 hi|lo pairs, 4 bytes per value) and q_C (fp32) at the start
+    // of the workspace (the layout above holds at least
+    // T (d_cq + n_h (d_h + d_r)) floats)
     float* cq = (float*)ws;
     float* qc = cq + (size_t)T * d.d_cq;
     return dev(launch_gemv_query(d, T, h, w_dq, w_uq, w_qr, w_uk, pos,
@@ -873,7 +873,8 @@ mla_status mla_out(const mla_dims* dims, int32_t T, const float* o_lat,
   const OutWs w = out_layout(d, T, ws);
   if (ws_bytes < w.bytes) return MLA_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
-  if (gemv_supported(d, T))  // v in fp32 (the layout holds T n_h d_h floats)
+  // v as bf16 hi|lo pairs (the layout holds T n_h d_h floats)
+  if (gemv_supported(d, T, GV_QO_MAXT))
     return dev(launch_gemv_out(d, T, o_lat, w_uv, w_o, (float*)ws, u, s));
   GemmArgs g1 = uv_gemm(d, T);
   GemmArgs g2 = o_gemm(d, T);

@@ -58,8 +58,12 @@ hipError_t launch_combine(const mla_dims& d, int rows, int n_split,
 
 // ---- projections of decode steps with at most GV_MAXT tokens (gemv.hip) --
 // One wave per group of weight rows, full contraction, no partial results.
+// The append takes this path up to GV_MAXT tokens; the query and output
+// projections, whose per-token arithmetic is larger, up to GV_QO_MAXT (at 3
+// and 4 tokens the weight-streaming GEMMs measured faster).
 constexpr int GV_MAXT = 4;
-bool gemv_supported(const mla_dims& d, int T);
+constexpr int GV_QO_MAXT = 2;
+bool gemv_supported(const mla_dims& d, int T, int t_max = GV_MAXT);
 // c_KV and RoPE(k_R) of T tokens straight into their cache rows.
 hipError_t launch_gemv_append(const mla_dims& d, int T, const void* h,
                               const void* w_dkv, const void* w_kr,
@@ -68,15 +72,17 @@ hipError_t launch_gemv_append(const mla_dims& d, int T, const void* h,
                               int max_pos, const int32_t* block_table,
                               int max_blocks, void* cache,
                               hipStream_t stream);
-// c_Q -> cq [T][d_cq] fp32, q_C -> qc [T][n_h d_h] fp32, then q_out[t][h] =
-// [W_UK_h^T q_C_h | RoPE(q_R)_h] in bf16.
+// c_Q -> cq [T][d_cq] as bf16 hi|lo pairs (4 bytes per value), q_C -> qc
+// [T][n_h d_h] fp32, then q_out[t][h] = [W_UK_h^T q_C_h | RoPE(q_R)_h] in
+// bf16.
 hipError_t launch_gemv_query(const mla_dims& d, int T, const void* h,
                              const void* w_dq, const void* w_uq,
                              const void* w_qr, const void* w_uk,
                              const int32_t* pos, const float* rope_cos,
                              const float* rope_sin, int max_pos, float* cq,
                              float* qc, void* q_out, hipStream_t stream);
-// v [T][n_h d_h] fp32 = W_UV_h o_lat_h, then u [T][d] bf16 = W_O v.
+// v [T][n_h d_h] = W_UV_h o_lat_h as bf16 hi|lo pairs (4 bytes per value),
+// then u [T][d] bf16 = W_O v.
 hipError_t launch_gemv_out(const mla_dims& d, int T, const float* o_lat,
                            const void* w_uv, const void* w_o, float* v,
                            void* u, hipStream_t stream);

@@ -36,8 +36,11 @@ def _append_norm(layer, h, seq, pos, table, cache, g_dev):
                                layer.rope_sin, table, cache, ws=ws)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_append_rmsnorm_rows(dtype):
+@pytest.mark.parametrize("dtype,chunk", [("bf16", 0), ("f32", 0),
+                                         ("bf16", 3)])
+def test_append_rmsnorm_rows(dtype, chunk):
+    """chunk > 0: the rows are appended in calls of `chunk` tokens (the
+    token counts a decode step appends)."""
     dims = W.DEEPSEEK_V2 if dtype == "bf16" else W.TINY
     w = W.make_weights(dims, dtype, 31)
     layer = MlaLayer(dims, dtype, w, 4096)
@@ -53,10 +56,13 @@ def test_append_rmsnorm_rows(dtype):
     seq = np.repeat(np.arange(len(lens)), lens).astype(np.int32)
     pos = np.concatenate([np.arange(n) for n in lens]).astype(np.int32)
     perm = np.random.default_rng(35).permutation(T)
-    _append_norm(layer, to_device(h[perm], dtype),
-                 torch.from_numpy(seq[perm]).cuda(),
-                 torch.from_numpy(pos[perm]).cuda(), table, cache,
-                 to_device(g, dtype))
+    step = chunk if chunk else T
+    for i in range(0, T, step):
+        sel = perm[i:i + step]
+        _append_norm(layer, to_device(h[sel], dtype),
+                     torch.from_numpy(seq[sel]).cuda(),
+                     torch.from_numpy(pos[sel]).cuda(), table, cache,
+                     to_device(g, dtype))
     torch.cuda.synchronize()
     host = cache.float().cpu().numpy()
     c_ref, r_ref = orc.kv_latent(h, pos, w["w_dkv"], w["w_kr"], W.ROPE_BASE,
@@ -72,7 +78,7 @@ def test_append_rmsnorm_rows(dtype):
     for s_, p in zip(seq, pos):
         owned[table_np[s_, p // 64], p % 64] = True
     assert np.isnan(host[~owned]).all()
-    log(f"  {T} rows ({dtype})")
+    log(f"  {T} rows ({dtype}, calls of {step} tokens)")
 
 
 def test_decode_step_over_normalised_cache():
@@ -91,9 +97,12 @@ def test_decode_step_over_normalised_cache():
     h_all = W.hidden_states(dims, "bf16", 44, 0, 0, ctx + 1)
     pos = np.arange(ctx + 1, dtype=np.int32)
     seq = np.zeros(ctx + 1, np.int32)
-    _append_norm(layer, to_device(h_all, "bf16"), torch.from_numpy(seq).cuda(),
-                 torch.from_numpy(pos).cuda(), table, cache,
-                 to_device(g, "bf16"))
+    # the context in one call, the new token in a call of its own
+    for lo, hi in ((0, ctx), (ctx, ctx + 1)):
+        _append_norm(layer, to_device(h_all[lo:hi], "bf16"),
+                     torch.from_numpy(seq[lo:hi]).cuda(),
+                     torch.from_numpy(pos[lo:hi]).cuda(), table, cache,
+                     to_device(g, "bf16"))
     h_new = h_all[ctx:]
     q = layer.absorb(to_device(h_new, "bf16"),
                      torch.from_numpy(pos[ctx:]).cuda())

@@ -154,8 +154,9 @@ def test_b1_ctx4k():
                                      ((900,), 4)])
 def test_ds_few_tokens(ctx, n_q):
     """DeepSeek-V2 dims with 2 to 4 new tokens per step (several sequences
-    of one token, or one sequence with a causal 4-token chunk): every
-    projection takes the matrix-vector path of at most four tokens.  Every
+    of one token, or one sequence with a causal 4-token chunk): the append
+    takes the matrix-vector path at every count, the query and output
+    projections at 2 tokens (the weight-streaming GEMMs at 3 and 4).  Every
     sequence, query, head and appended row against the oracle."""
     base = W.workload("b1_ctx4k")
     wl = dataclasses.replace(base, name=f"ds_few{len(ctx)}x{n_q}",
