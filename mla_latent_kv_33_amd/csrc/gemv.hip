@@ -26,13 +26,16 @@
 namespace mla {
 namespace {
 
-// 16-byte weight loads per row and lane in one register set (two sets in
-// flight): half a row of the 5120-wide projections (5 loads, 2 rows per
-// wave, 20 loads in flight), an eighth of W_O's 16384-wide rows (4 loads,
-// 4 rows per wave, 32 in flight); enough bytes in flight for the chip's
-// memory latency even when the projection is small.
-constexpr int GV_U_WIDE = 4;
-constexpr int GV_U_D = 5;
+// 16-byte weight loads per row and lane in one register set: a whole row of
+// the 5120-wide projections (10 loads, 2 rows per wave, one set), a
+// sixteenth of W_O's 16384-wide rows (2 loads, 4 rows per wave, two sets of
+// 8 in flight), a third of the 1536-wide W_UQ / W_QR rows (1 load, 4 rows
+// per wave, two sets of 4 in flight).  Measured at one token against 5, 4
+// and 3 loads: 1.4 us less over the three projections; these kernels are
+// bound by the HBM stream, not by the depth.
+constexpr int GV_U_WIDE = 2;
+constexpr int GV_U_D = 10;
+constexpr int GV_U_UQ = 1;
 
 // Activation forms a row routine reads (per token row, along k):
 //   XB16: bf16 values;
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(64) void gemv_uq_kernel(
     w[3] = wh + (size_t)(j + 1 + half) * d_cq;
   }
   float acc[T][4];
-  gemv_rows<T, 4, XHL, 3>(w, cq, d_cq, d_cq, lane, acc);
+  gemv_rows<T, 4, XHL, GV_U_UQ>(w, cq, d_cq, d_cq, lane, acc);
   if (is_c) {
 #pragma unroll
     for (int t = 0; t < T; ++t)
