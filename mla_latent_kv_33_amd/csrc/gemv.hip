@@ -8,13 +8,15 @@
 // the matrix cores would compute 32-row tiles for one real row, and a K
 // split would need a second pass to sum its parts.  Here one wave owns R
 // whole weight rows: its 64 lanes read each row in 1 KiB runs (16 bytes
-// per lane per load, GV_U loads in flight per row), multiply them by the
-// activations in fp32 (the activations, bf16 or fp32, are read through the
-// L1 cache, shared by the waves of a compute unit), and reduce across the
-// lanes.  No partial results leave the wave, so each projection is one
-// kernel whose epilogue writes the final form: cache rows with the RoPE key
-// rotated, c_Q / q_C / v in fp32 for the next projection, the rotated q_R
-// into the query row, u in bf16.
+// per lane per load, two register sets of loads in flight), multiply them
+// by the activations with fp32 accumulation (the activations are read
+// through the L1 cache, shared by the waves of a compute unit), and reduce
+// across the lanes.  No partial results leave the wave, so each projection
+// is one kernel whose epilogue writes the final form: cache rows with the
+// RoPE key rotated, c_Q and v as bf16 hi|lo pairs and q_C in fp32 for the
+// next projection, the rotated q_R into the query row, u in bf16.  The
+// append serves up to four tokens; the query and output projections, whose
+// products grow with the token count, serve up to two (GV_QO_MAXT).
 //
 // The absorption q_lat_h = W_UK_h^T q_C_h reads W_UK_h [d_h][d_c] by rows:
 // one workgroup per head, each of its 8 waves accumulates 16 rows (lanes

@@ -272,27 +272,28 @@ def test_b8_chunked_prefill_causal():
                  "bf16")
 
 
-@pytest.mark.parametrize("T", [1, 64, 150])
-def test_premerged_absorption(T):
+@pytest.mark.parametrize("name,T", [("b1_ctx4k", 1), ("b1_ctx4k", 64),
+                                    ("b1_ctx4k", 150), ("tiny", 5)])
+def test_premerged_absorption(name, T):
     """The pre-merged query path (M_h = W_UK_h^T W_UQ_h built once, then
     q_lat_h = M_h c_Q) against the oracle's absorbed query on T tokens (a
-    single token, a decode batch, a prefill-size chunk), and against the
-    unmerged mla_absorb_q."""
+    single token, a decode batch, a prefill-size chunk; bf16 DeepSeek-V2
+    dims, and the fp32 tiny dims), and against the unmerged mla_absorb_q."""
     from mla_latent_kv_33_amd import binding as B
-    # context 4096 so that the RoPE tables cover the positions below
-    wl = dataclasses.replace(W.workload("b1_ctx4k"), batch=1, ctx=(4096,),
+    # a context long enough for the RoPE tables to cover the positions below
+    ctx = 4096 if name == "b1_ctx4k" else 64
+    wl = dataclasses.replace(W.workload(name), batch=1, ctx=(ctx,),
                              n_q=T, seed=21)
     d = wl.dims
     layer, w = layer_for(wl)
-    merged = torch.empty((d.n_h, d.d_c, d.d_cq), dtype=torch.bfloat16,
-                         device="cuda")
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    merged = torch.empty((d.n_h, d.d_c, d.d_cq), dtype=tdt, device="cuda")
     B.mla_merge_uq_uk(layer.cdims, layer.w["w_uq"], layer.w["w_uk"], merged)
     h_np = W.hidden_states(d, wl.dtype, wl.seed, 0, 0, T)
-    pos_np = np.arange(T) * 37 % 4000
-    h = torch.from_numpy(h_np.astype(np.float32)).to(torch.bfloat16).cuda()
+    pos_np = np.arange(T) * 37 % (ctx - 1)
+    h = torch.from_numpy(h_np.astype(np.float32)).to(tdt).cuda()
     pos = torch.from_numpy(pos_np.astype(np.int32)).cuda()
-    q_m = torch.empty((T, d.n_h, d.d_c + d.d_r), dtype=torch.bfloat16,
-                      device="cuda")
+    q_m = torch.empty((T, d.n_h, d.d_c + d.d_r), dtype=tdt, device="cuda")
     B.mla_absorb_q_merged(layer.cdims, h, pos, layer.w["w_dq"], merged,
                           layer.w["w_qr"], layer.rope_cos, layer.rope_sin,
                           q_m)
@@ -301,9 +302,9 @@ def test_premerged_absorption(T):
     q_c, q_r = orc.query(h_np, pos_np, w["w_dq"], w["w_uq"], w["w_qr"],
                          d.n_h, W.ROPE_BASE)
     ref = orc.absorb_query(q_c, q_r, w["w_uk"])
-    assert_close(f"T={T} merged q", q_m.float().cpu().numpy(), ref, "bf16")
-    assert_close(f"T={T} unmerged q", q_u.float().cpu().numpy(), ref, "bf16")
+    assert_close(f"T={T} merged q", q_m.float().cpu().numpy(), ref, wl.dtype)
+    assert_close(f"T={T} unmerged q", q_u.float().cpu().numpy(), ref, wl.dtype)
     # the RoPE columns come from the same W_QR projection in both forms
     assert_close(f"T={T} merged vs unmerged q_R",
                  q_m[..., d.d_c:].float().cpu().numpy(),
-                 q_u[..., d.d_c:].float().cpu().numpy(), "bf16")
+                 q_u[..., d.d_c:].float().cpu().numpy(), wl.dtype)
