@@ -437,6 +437,13 @@ bool gemv_supported(const mla_dims& d, int T, int t_max) {
     case 3: CALL(3); break; \
     default: CALL(4); break; \
   }
+// the query and output projections take this path up to GV_QO_MAXT tokens
+static_assert(GV_QO_MAXT == 2, "token-count dispatch below");
+#define MLA_GV_T2(T, CALL) \
+  switch (T) {             \
+    case 1: CALL(1); break;  \
+    default: CALL(2); break; \
+  }
 
 hipError_t launch_gemv_append(const mla_dims& d, int T, const void* h,
                               const void* w_dkv, const void* w_kr,
@@ -445,6 +452,7 @@ hipError_t launch_gemv_append(const mla_dims& d, int T, const void* h,
                               int max_pos, const int32_t* block_table,
                               int max_blocks, void* cache,
                               hipStream_t stream) {
+  if (T < 1 || T > GV_MAXT) return hipErrorInvalidValue;
   const int tasks = d.d_c / 2 + d.d_r / 2;
 #define MLA_APP(TT)                                                          \
   hipLaunchKernelGGL(gemv_append_kernel<TT>, dim3(tasks), dim3(64), 0,       \
@@ -463,6 +471,7 @@ hipError_t launch_gemv_query(const mla_dims& d, int T, const void* h,
                              const int32_t* pos, const float* rope_cos,
                              const float* rope_sin, int max_pos, float* cq,
                              float* qc, void* q_out, hipStream_t stream) {
+  if (T < 1 || T > GV_QO_MAXT) return hipErrorInvalidValue;
   // c_Q = W_DQ h, pre-split into hi|lo pairs for the next projection
   const int t1 = (d.d_cq + 1) / 2;
 #define MLA_DQ(TT)                                                           \
@@ -470,7 +479,7 @@ hipError_t launch_gemv_query(const mla_dims& d, int T, const void* h,
                      dim3(t1),                                               \
                      dim3(64), 0, stream, (const uint16_t*)w_dq, d.d_cq, d.d, \
                      h, (long)d.d, 0, 0L, (void*)cq, (long)d.d_cq)
-  MLA_GV_T(T, MLA_DQ)
+  MLA_GV_T2(T, MLA_DQ)
 #undef MLA_DQ
   // q_C (fp32) and RoPE(q_R) into the query rows
   const int t2 = d.n_h * d.d_h / 4 + d.n_h * (d.d_r / 4);
@@ -480,7 +489,7 @@ hipError_t launch_gemv_query(const mla_dims& d, int T, const void* h,
                      d.d_cq, (const uint16_t*)w_uq, (const uint16_t*)w_qr,    \
                      d.n_h, d.d_h, d.d_c, d.d_r, qc, pos,                     \
                      rope_cos, rope_sin, max_pos, (uint16_t*)q_out)
-  MLA_GV_T(T, MLA_UQ)
+  MLA_GV_T2(T, MLA_UQ)
 #undef MLA_UQ
   // q_lat_h = W_UK_h^T q_C_h
 #define MLA_AB(TT)                                                          \
@@ -488,7 +497,7 @@ hipError_t launch_gemv_query(const mla_dims& d, int T, const void* h,
                      dim3(64 * AB_WAVES), AB_WAVES * TT * 512 * 4, stream, qc, \
                      (const uint16_t*)w_uk, d.n_h, d.d_h, d.d_c, d.d_r,      \
                      (uint16_t*)q_out)
-  MLA_GV_T(T, MLA_AB)
+  MLA_GV_T2(T, MLA_AB)
 #undef MLA_AB
   return hipGetLastError();
 }
@@ -496,6 +505,7 @@ hipError_t launch_gemv_query(const mla_dims& d, int T, const void* h,
 hipError_t launch_gemv_out(const mla_dims& d, int T, const float* o_lat,
                            const void* w_uv, const void* w_o, float* v,
                            void* u, hipStream_t stream) {
+  if (T < 1 || T > GV_QO_MAXT) return hipErrorInvalidValue;
   const int nv = d.n_h * d.d_h;
   // v_h = W_UV_h o_lat_h, pre-split into hi|lo pairs: rows of head h read
   // x = o_lat[t][h]
@@ -505,7 +515,7 @@ hipError_t launch_gemv_out(const mla_dims& d, int T, const float* o_lat,
                      dim3(64), 0, stream, (const uint16_t*)w_uv, nv, d.d_c,   \
                      (const void*)o_lat, (long)d.n_h * d.d_c, d.d_h,          \
                      (long)d.d_c, (void*)v, (long)nv)
-  MLA_GV_T(T, MLA_UV)
+  MLA_GV_T2(T, MLA_UV)
 #undef MLA_UV
   // u = W_O v (bf16)
 #define MLA_O(TT)                                                            \
@@ -513,11 +523,12 @@ hipError_t launch_gemv_out(const mla_dims& d, int T, const float* o_lat,
                      dim3((d.d + 3) / 4),                                    \
                      dim3(64), 0, stream, (const uint16_t*)w_o, d.d, nv,      \
                      (const void*)v, (long)nv, 0, 0L, u, (long)d.d)
-  MLA_GV_T(T, MLA_O)
+  MLA_GV_T2(T, MLA_O)
 #undef MLA_O
   return hipGetLastError();
 }
 
 #undef MLA_GV_T
+#undef MLA_GV_T2
 
 }  // namespace mla
