@@ -274,8 +274,8 @@ __global__ __launch_bounds__(64) void gemv_plain_kernel(
   for (int r = 0; r < R; ++r) w[r] = W + (size_t)min(n0 + r, N - 1) * K;
   const void* xs = x;
   if (d_h_sel > 0)
-    xs = (const char*)x +
-         (size_t)(n0 / d_h_sel) * xhead * (XM == XF32 ? 4 : 2);
+    xs = (const char*)x +  // 2 bytes per bf16 value, 4 per fp32 or hi|lo pair
+         (size_t)(n0 / d_h_sel) * xhead * (XM == XB16 ? 2 : 4);
   float acc[T][R];
   gemv_rows<T, R, XM, U>(w, xs, ldx, K, lane, acc);
   // lane R t + r writes (t, row r)
