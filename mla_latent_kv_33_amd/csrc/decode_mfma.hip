@@ -348,6 +348,17 @@ decode_mfma_kernel(
   const int b = bq / n_q;
   const int qi = bq - b * n_q;
 
+  // Query slice: lane holds Q[head][16ks + 8g .. +7] for every k-step.  Its
+  // address needs neither kv_lens nor the block table, so the loads go out
+  // first and travel while those two dependent scalar loads return.
+  bf16x8 qreg[KSTEPS];
+  {
+    const bf16x8* const qp =
+        (const bf16x8*)(q + ((size_t)bq * n_h + head) * ROW) + g;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = qp[2 * ks];
+  }
+
   const int kv = kv_lens[b];
   const int visible = kv - n_q + qi + 1;  // keys 0 .. P
   const int nblk = (visible + BS - 1) / BS;
@@ -368,6 +379,7 @@ decode_mfma_kernel(
       m_part[row_base + head] = -INFINITY;
       l_part[row_base + head] = 0.0f;
     }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the query loads
     return;
   }
   const int tok0 = blk0 * BS;
@@ -389,12 +401,6 @@ decode_mfma_kernel(
     const HalfCopy<NW> hc = half_copy(j, block_of(j));
     CopyAll<0, PER>::run(hc, wave);
   };
-
-  // Query slice: lane holds Q[head][16ks + 8g .. +7] for every k-step
-  // (loaded in the first pass's prologue, behind the copies of half 0).
-  bf16x8 qreg[KSTEPS];
-  const bf16x8* const qp =
-      (const bf16x8*)(q + ((size_t)bq * n_h + head) * ROW) + g;
 
   f32x16 o[MTW][NW];
   float m_ref = -INFINITY;  // per owned head, log2 units
@@ -643,21 +649,17 @@ decode_mfma_kernel(
   // rises, and after the first pass every half tile's maximum is at most
   // m_ref + REF_SLACK, so the second pass cannot overflow; the loop stops
   // there regardless.
-  bool first_pass = true;
+  // The copies of half 0 of the first pass go out right behind the query
+  // loads, before the pass loop (whose header reloads spilled values).
+  issue(0);
   for (int pass = 0;; ++pass) {
-    // Prologue: the copies of half 0 and (first pass) the query loads go
-    // out first, and the scores and P of half 0 start as soon as both
-    // landed, while halves 1 and 2 are in flight.  The query loads are
-    // retired by a wait the compiler sees (a builtin, not asm), issued
-    // before the copies of halves 1 and 2: the compiler's own waits for the
-    // query registers then never stand for those copies, and inside the
-    // loop vmcnt tracks the copies only.
-    issue(0);
-    if (first_pass) {
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) qreg[ks] = qp[2 * ks];
-      first_pass = false;
-    }
+    // Prologue: the scores and P of half 0 start as soon as its copies and
+    // the query slice landed, while halves 1 and 2 are in flight.  The query
+    // loads are retired by a wait the compiler sees (a builtin, not asm),
+    // issued before the copies of halves 1 and 2: the compiler's own waits
+    // for the query registers then never stand for those copies, and inside
+    // the loop vmcnt tracks the copies only.
+    if (pass > 0) issue(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     if (n_half > 1) issue(1);
     if (n_half > 2) issue(2);

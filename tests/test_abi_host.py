@@ -92,9 +92,12 @@ def test_workspace_sizes():
         64 * ns * 128 * (512 + 2) * 4
     assert B.mla_decode_auto_splits(d, 4, 1, 131073) == 64
     assert B.mla_decode_auto_splits(d, 8, 2048, 10240) == 1
-    # one sequence: as many splits as keep two 64-token blocks each
-    assert B.mla_decode_auto_splits(d, 1, 1, 4097) == 32
-    assert B.mla_decode_auto_splits(d, 1, 1, 100) == 1
+    # one sequence: down to one 64-token block per split, a count of 8 or
+    # more rounded down to a multiple of 8
+    assert B.mla_decode_auto_splits(d, 1, 1, 4097) == 64
+    assert B.mla_decode_auto_splits(d, 1, 1, 8193) == 128
+    assert B.mla_decode_auto_splits(d, 1, 1, 100) == 2
+    assert B.mla_decode_auto_splits(d, 2, 1, 4097) == 64
     # balanced splits: partial slots for 256 workgroups plus the row plan
     bal = B.mla_decode_workspace_bytes(d, 64, 1, 8193, B.MLA_SPLIT_BALANCED)
     assert bal >= 256 * 128 * (512 + 2) * 4 + 64 * 8
