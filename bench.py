@@ -85,6 +85,13 @@ def parse():
                          "mla_absorb_q (W_UQ, then W_UK_h^T per head) or "
                          "mla_absorb_q_merged (one projection onto the "
                          "pre-merged W_UK_h^T W_UQ_h, built once)")
+    ap.add_argument("--project", choices=("stacked", "separate"),
+                    default="stacked",
+                    help="absorbed path, --query absorbed: the append and "
+                         "the query projection as one mla_append_absorb_q "
+                         "call (the down-projections W_DQ, W_DKV, W_KR of h "
+                         "stacked into one weight stream) or as "
+                         "mla_append_cache followed by mla_absorb_q")
     ap.add_argument("--graph", action="store_true",
                     help="timed steps replay HIP graphs (captured once after "
                          "the warmup: append + query, attention, output) "
@@ -239,6 +246,9 @@ def main():
     out = flow.run_prefill_mha(st) if mha else flow.run_step(st)
     torch.cuda.synchronize()
 
+    # one call for the append and the query path (stacked projections)
+    stacked = (not mha and args.query == "absorbed" and
+               args.project == "stacked" and args.streams == 1)
     names = (("append", "query", "prefill", "out") if mha else
              ("append", "absorb", "decode", "out"))
 
@@ -302,6 +312,14 @@ def main():
             join.record(side)
             query_path()
             stream.wait_event(join)
+        elif stacked:
+            # e[0] and e[1] together: the append stage is part of the call
+            if rec_all:
+                e[0].record(stream)
+                e[1].record(stream)
+            layer.append_absorb(st.h_new, st.seq_idx, st.pos, st.table,
+                                st.cache,
+                                q_out=out.q.view(-1, d.n_h, d.d_c + d.d_r))
         else:
             if rec_all: e[0].record(stream)
             layer.append(st.h_new, st.seq_idx, st.pos, st.table, st.cache)
@@ -339,6 +357,11 @@ def main():
                 layer.out(out.o_lat.view(-1, d.n_h, d.d_c), u=out.u)
 
         def pre_stage():
+            if stacked:
+                layer.append_absorb(
+                    st.h_new, st.seq_idx, st.pos, st.table, st.cache,
+                    q_out=out.q.view(-1, d.n_h, d.d_c + d.d_r))
+                return
             layer.append(st.h_new, st.seq_idx, st.pos, st.table, st.cache)
             query_path()
 
@@ -393,6 +416,9 @@ def main():
     stage_ms = {n: float(np.mean([ev_st[i][k].elapsed_time(ev_st[i][k + 1])
                                   for i in range(n_st)]))
                 for k, n in enumerate(names)}
+    if stacked:
+        stage_ms = {"append+absorb": stage_ms["append"] + stage_ms["absorb"],
+                    "decode": stage_ms["decode"], "out": stage_ms["out"]}
     # The attention stage alone, outside the step, medians of 10 calls each:
     # right after writing a 512 MiB scratch buffer, right after reading one
     # (either evicts L2 and the 256 MB Infinity Cache, so the cache rows come
@@ -519,6 +545,9 @@ def main():
         "streams": ("append on a second stream, concurrent with the query "
                     "path" if side is not None else "one stream"),
         "query": args.query,
+        "projections": ("one mla_append_absorb_q call (W_DQ, W_DKV, W_KR "
+                        "stacked)" if stacked else
+                        "mla_append_cache, then the query call"),
         "launch": ("timed steps replay three HIP graphs (append + query, "
                    "attention, output) captured after the warmup"
                    if graphs is not None else "eager launches from the host"),

@@ -176,6 +176,38 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
                         size_t ws_bytes, mla_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * mla_append_absorb_q - mla_append_cache and mla_absorb_q on the same tokens
+ * in one call.
+ *
+ * Both calls start from the new tokens' hidden states: the cached latent
+ * c_KV = W_DKV h and the RoPE key RoPE(W_KR h) on one side, the query latent
+ * c_Q = W_DQ h on the other ('MLA：潜在表示压缩与解耦 RoPE', section 3, joint
+ * compression of keys/values and of queries; section 6, the decoupled RoPE
+ * key).  For decode batches (bf16 layers, token counts past the
+ * matrix-vector path, up to 64) the three weights are streamed as one
+ * stacked projection [W_DQ; W_DKV; W_KR] h, and one epilogue launch sums its
+ * K parts into both the cache rows and c_Q; the query path then continues as
+ * in mla_absorb_q.  Other shapes run the two calls' own paths in sequence.
+ * The cache rows and q_out equal those of mla_append_cache followed by
+ * mla_absorb_q up to the order of the fp32 sums of each projection.
+ *
+ * Arguments: those of mla_append_cache and mla_absorb_q, with h, pos, the
+ * RoPE tables and max_pos shared; ws at least
+ * mla_append_absorb_workspace_bytes(dims, T) (at least either call's own
+ * size).  Every argument is checked before anything is enqueued; the error
+ * codes are those of the two calls.
+ * ---------------------------------------------------------------------- */
+size_t mla_append_absorb_workspace_bytes(const mla_dims* dims, int32_t T);
+mla_status mla_append_absorb_q(
+    const mla_dims* dims, int32_t T, const void* h, const int32_t* seq_idx,
+    const int32_t* pos, const void* w_dkv, const void* w_kr, const void* w_dq,
+    const void* w_uq, const void* w_qr, const void* w_uk,
+    const float* rope_cos, const float* rope_sin, int32_t max_pos,
+    const int32_t* block_table, int32_t max_blocks, void* cache,
+    int32_t num_blocks, void* q_out, void* ws, size_t ws_bytes,
+    mla_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Pre-merged query absorption (a variant the pages allow: W_UQ^T W_UK can
  * be merged ahead of time, 'MLA：潜在表示压缩与解耦 RoPE', section 4; the
  * RoPE part cannot, section 5).

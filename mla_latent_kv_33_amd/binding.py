@@ -59,6 +59,9 @@ _SIGNATURES = {
     "mla_absorb_workspace_bytes": (_S, [_DP, _I]),
     "mla_absorb_q": (_I, [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P,
                           _S, _P]),
+    "mla_append_absorb_workspace_bytes": (_S, [_DP, _I]),
+    "mla_append_absorb_q": (_I, [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _P, _P, _I, _P, _I, _P, _I, _P, _P, _S, _P]),
     "mla_merge_uq_uk": (_I, [_DP, _P, _P, _P, _P]),
     "mla_absorb_merged_workspace_bytes": (_S, [_DP, _I]),
     "mla_absorb_q_merged": (_I, [_DP, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P,
@@ -228,6 +231,10 @@ def mla_absorb_workspace_bytes(dims: MlaDims, T: int) -> int:
     return lib().mla_absorb_workspace_bytes(ctypes.byref(dims), T)
 
 
+def mla_append_absorb_workspace_bytes(dims: MlaDims, T: int) -> int:
+    return lib().mla_append_absorb_workspace_bytes(ctypes.byref(dims), T)
+
+
 def mla_decode_workspace_bytes(dims: MlaDims, B: int, n_q: int,
                                max_kv_len: int, n_split: int) -> int:
     return lib().mla_decode_workspace_bytes(ctypes.byref(dims), B, n_q,
@@ -355,6 +362,30 @@ def mla_absorb_q(dims: MlaDims, h, pos, w_dq, w_uq, w_qr, w_uk, rope_cos,
     _check("mla_absorb_q", lib().mla_absorb_q(
         ctypes.byref(dims), T, *p[:5], p[7], p[5], p[6], rope_cos.shape[0],
         p[8], _ptr(ws, "ws"), wsb, _stream(stream)))
+
+
+def mla_append_absorb_q(dims: MlaDims, h, seq_idx, pos, w_dkv, w_kr, w_dq,
+                        w_uq, w_qr, w_uk, rope_cos, rope_sin, block_table,
+                        cache, q_out, ws=None, stream=None):
+    """mla_append_cache and mla_absorb_q on the same tokens in one call (see
+    include/mla.h)."""
+    T = h.shape[0]
+    lt = _layer_dtype(dims)
+    p = _ptrs(*_append_args(dims, h, seq_idx, pos, w_dkv, w_kr, rope_cos,
+                            rope_sin, block_table, cache),
+              _a(w_dq, "w_dq", lt, (dims.d_cq, dims.d)),
+              _a(w_uq, "w_uq", lt, (dims.n_h * dims.d_h, dims.d_cq)),
+              _a(w_qr, "w_qr", lt, (dims.n_h * dims.d_r, dims.d_cq)),
+              _a(w_uk, "w_uk", lt, (dims.n_h * dims.d_h, dims.d_c)),
+              _a(q_out, "q_out", lt,
+                 numel=T * dims.n_h * (dims.d_c + dims.d_r)))
+    ws, wsb = _workspace(mla_append_absorb_workspace_bytes(dims, T) if T
+                         else 0, h.device, ws)
+    # p: h seq_idx pos w_dkv w_kr cos sin table cache w_dq w_uq w_qr w_uk q
+    _check("mla_append_absorb_q", lib().mla_append_absorb_q(
+        ctypes.byref(dims), T, *p[:5], p[9], p[10], p[11], p[12], p[5], p[6],
+        rope_cos.shape[0], p[7], block_table.shape[1], p[8], cache.shape[0],
+        p[13], _ptr(ws, "ws"), wsb, _stream(stream)))
 
 
 def mla_merge_uq_uk(dims: MlaDims, w_uq, w_uk, w_merged, stream=None):

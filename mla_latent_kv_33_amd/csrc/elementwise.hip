@@ -38,26 +38,24 @@ __global__ void reduce_parts_kernel(const float* __restrict__ src, int nparts,
     dst[i] = sum_parts(src, nparts, part_stride, i);
 }
 
-// Workgroup (token, slice of 256 items): items j < d_c are copied columns,
-// the rest rotate the d_r RoPE columns in pairs; the row goes to its paged
-// cache slot.
+// Token t's cache row from acc (row t at t * ld_acc, d_c + d_r columns):
+// items j < d_c are copied columns, the rest rotate the d_r RoPE columns in
+// pairs; this thread takes items j0, j0 + jstep, ...
 template <typename T>
-__global__ void append_scatter_kernel(
-    const float* __restrict__ acc, int nparts, long part_stride, int d_c,
-    int d_r, const int32_t* __restrict__ seq_idx,
-    const int32_t* __restrict__ pos, const float* __restrict__ rcos,
-    const float* __restrict__ rsin, int max_pos,
-    const int32_t* __restrict__ block_table, int max_blocks, int block_size,
-    T* __restrict__ cache) {
-  const int t = blockIdx.x;
+__device__ __forceinline__ void scatter_row(
+    const float* __restrict__ acc, int nparts, long part_stride, long ld_acc,
+    int t, int j0, int jstep, int d_c, int d_r,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
+    const float* __restrict__ rcos, const float* __restrict__ rsin,
+    int max_pos, const int32_t* __restrict__ block_table, int max_blocks,
+    int block_size, T* __restrict__ cache) {
   const int width = d_c + d_r;
   const int half = d_r / 2;
   const int p = pos[t];
   const int blk = block_table[(long)seq_idx[t] * max_blocks + p / block_size];
   T* row = cache + ((long)blk * block_size + (p % block_size)) * width;
-  const long base = (long)t * width;
-  for (int j = blockIdx.y * blockDim.x + threadIdx.x; j < d_c + half;
-       j += gridDim.y * blockDim.x) {
+  const long base = (long)t * ld_acc;
+  for (int j = j0; j < d_c + half; j += jstep) {
     if (j < d_c) {
       DT<T>::store(row, j, sum_parts(acc, nparts, part_stride, base + j));
     } else {
@@ -72,6 +70,21 @@ __global__ void append_scatter_kernel(
       DT<T>::store(row, d_c + jj + half, x1 * s + x2 * c);
     }
   }
+}
+
+// Workgroup (token, slice of 256 items) of the rows acc [T][d_c + d_r].
+template <typename T>
+__global__ void append_scatter_kernel(
+    const float* __restrict__ acc, int nparts, long part_stride, int d_c,
+    int d_r, const int32_t* __restrict__ seq_idx,
+    const int32_t* __restrict__ pos, const float* __restrict__ rcos,
+    const float* __restrict__ rsin, int max_pos,
+    const int32_t* __restrict__ block_table, int max_blocks, int block_size,
+    T* __restrict__ cache) {
+  scatter_row<T>(acc, nparts, part_stride, d_c + d_r, blockIdx.x,
+                 blockIdx.y * blockDim.x + threadIdx.x, gridDim.y * blockDim.x,
+                 d_c, d_r, seq_idx, pos, rcos, rsin, max_pos, block_table,
+                 max_blocks, block_size, cache);
 }
 
 template <typename T>
@@ -125,18 +138,60 @@ inline int grid_for(long n, int threads) {
 
 }  // namespace
 
-// One thread per value: hi to 16 (i / 8) + i % 8 (bf16 units), lo 8 further.
+// Value i of rows of `cols` values (cols % 8 == 0), summed from rows ld_src
+// apart: hi to 16 (i / 8) + i % 8 (bf16 units), lo 8 further.
+__device__ __forceinline__ void reduce_hl_item(const float* __restrict__ src,
+                                               int nparts, long part_stride,
+                                               long ld_src, int cols, long i,
+                                               uint16_t* __restrict__ dst) {
+  const long r = i / cols;
+  const float x = sum_parts(src, nparts, part_stride, i + r * (ld_src - cols));
+  const uint16_t hi = f2bf(x);
+  const long at = 16 * (i >> 3) + (i & 7);
+  dst[at] = hi;
+  dst[at + 8] = f2bf(x - bf2f(hi));
+}
+
+// One thread per value.
 __global__ void reduce_parts_hl_kernel(const float* __restrict__ src,
                                        int nparts, long part_stride, long n,
-                                       uint16_t* __restrict__ dst) {
+                                       int cols, uint16_t* __restrict__ dst) {
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n;
-       i += (long)gridDim.x * blockDim.x) {
-    const float x = sum_parts(src, nparts, part_stride, i);
-    const uint16_t hi = f2bf(x);
-    const long at = 16 * (i >> 3) + (i & 7);
-    dst[at] = hi;
-    dst[at + 8] = f2bf(x - bf2f(hi));
+       i += (long)gridDim.x * blockDim.x)
+    reduce_hl_item(src, nparts, part_stride, cols, cols, i, dst);
+}
+
+// The epilogue of the stacked down-projection [W_DQ; W_DKV; W_KR] h of a
+// decode batch, one launch for both consumers of its K parts (rows of
+// ld_acc = d_cq + d_c + d_r floats): workgroups below nq_blocks write c_Q
+// (the first d_cq columns) in the pre-split hi|lo layout, the next
+// T * nsl workgroups the cache rows (the other columns, RoPE on k_R), nsl
+// slices of 256 items per token, one item per thread (every item is a sum
+// over the K parts, a chain of dependent loads: one per thread keeps the
+// chains short).
+template <typename T>
+__global__ __launch_bounds__(256) void project_epilogue_kernel(
+    const float* __restrict__ acc, int nparts, long part_stride, int d_cq,
+    int ntok, int nq_blocks, int nsl, uint16_t* __restrict__ cq, int d_c,
+    int d_r,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
+    const float* __restrict__ rcos, const float* __restrict__ rsin,
+    int max_pos, const int32_t* __restrict__ block_table, int max_blocks,
+    int block_size, T* __restrict__ cache) {
+  const long ld_acc = (long)d_cq + d_c + d_r;
+  if ((int)blockIdx.x < nq_blocks) {
+    const long n = (long)ntok * d_cq;
+    for (long i = blockIdx.x * 256L + threadIdx.x; i < n;
+         i += (long)nq_blocks * 256)
+      reduce_hl_item(acc, nparts, part_stride, ld_acc, d_cq, i, cq);
+    return;
   }
+  const int w = (int)blockIdx.x - nq_blocks;
+  const int t = w / nsl;
+  scatter_row<T>(acc + d_cq, nparts, part_stride, ld_acc, t,
+                 (w - t * nsl) * 256 + threadIdx.x, nsl * 256, d_c, d_r,
+                 seq_idx, pos, rcos, rsin, max_pos, block_table, max_blocks,
+                 block_size, cache);
 }
 
 hipError_t launch_reduce_parts_hl(const float* src, int nparts,
@@ -145,8 +200,28 @@ hipError_t launch_reduce_parts_hl(const float* src, int nparts,
   if (n <= 0) return hipSuccess;
   if (ld % 8 != 0 || n % ld != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(reduce_parts_hl_kernel, dim3(grid_for(n, 256)),
-                     dim3(256), 0, stream, src, nparts, part_stride, n,
+                     dim3(256), 0, stream, src, nparts, part_stride, n, ld,
                      (uint16_t*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_project_epilogue(const mla_dims& d, int T, const float* acc,
+                                   int nparts, long part_stride, void* cq,
+                                   const int32_t* seq_idx, const int32_t* pos,
+                                   const float* rope_cos,
+                                   const float* rope_sin, int max_pos,
+                                   const int32_t* block_table, int max_blocks,
+                                   void* cache, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  // bf16 layers (the pre-split c_Q feeds the weight-streaming kernel)
+  if (d.dtype != MLA_BF16 || d.d_cq % 8 != 0) return hipErrorInvalidValue;
+  const int nq = grid_for((long)T * d.d_cq, 256);
+  const int nsl = (d.d_c + d.d_r / 2 + 255) / 256;
+  hipLaunchKernelGGL(project_epilogue_kernel<uint16_t>, dim3(nq + T * nsl),
+                     dim3(256), 0, stream, acc, nparts, part_stride, d.d_cq,
+                     T, nq, nsl, (uint16_t*)cq, d.d_c, d.d_r, seq_idx, pos,
+                     rope_cos, rope_sin, max_pos, block_table, max_blocks,
+                     d.block_size, (uint16_t*)cache);
   return hipGetLastError();
 }
 

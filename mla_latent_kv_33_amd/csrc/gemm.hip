@@ -74,8 +74,9 @@ __device__ __forceinline__ const uint16_t* brow(const uint16_t* B,
 }
 
 // ------------------------------------------------------------------ ldsk
-// LDS-staged weight-streaming kernel for M <= 64, NT, K % 64 == 0 (and the
-// B / B2 boundary at a multiple of 32 rows).  Workgroup = 4 waves over
+// LDS-staged weight-streaming kernel for M <= 64, NT, K % 64 == 0, with a
+// weight of up to three parts stacked by rows (rows < nb1 from B, < nb2
+// from B2, the rest from B3; both boundaries multiples of 32 rows).  Workgroup = 4 waves over
 // 128 NTW output columns and 32 MT rows (row block gridDim.z / batch of a
 // row split: a small grid can run each half of the rows in its own
 // workgroup, the pair sharing the weights through L2),
@@ -118,6 +119,7 @@ template <int MT, int NTW, bool AF32, bool HL>
 __global__ __launch_bounds__(256) void gemm_lds_kernel(
     const void* __restrict__ Av, long lda, long a_bs,
     const uint16_t* __restrict__ B, const uint16_t* __restrict__ B2, int nb1,
+    const uint16_t* __restrict__ B3, int nb2,
     long ldb, long b_bs, float* __restrict__ C, long ldc, long c_bs, long c_ks,
     int M, int N, int K, int k_chunk, int m_split, int c_hl) {
   static_assert(!HL || AF32, "pre-split A uses the fp32 layout");
@@ -169,8 +171,10 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
     const int row0 = min(n_wg + 32 * (wave * NTW + nt), N - 1);
-    const uint16_t* bb = row0 < nb1 ? B + z * b_bs + (long)row0 * ldb
-                                    : B2 + z * b_bs + (long)(row0 - nb1) * ldb;
+    const uint16_t* bb =
+        row0 < nb1   ? B + z * b_bs + (long)row0 * ldb
+        : row0 < nb2 ? B2 + z * b_bs + (long)(row0 - nb1) * ldb
+                     : B3 + z * b_bs + (long)(row0 - nb2) * ldb;
     b_base[nt] = (const char*)(bb + kbeg);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -748,9 +752,9 @@ hipError_t launch_lds(const GemmArgs& g, dim3 grid, int k_chunk,
   }
   hipLaunchKernelGGL((gemm_lds_kernel<MT, NTW, AF, HL>), grid, dim3(256), lds,
                      stream, g.A, g.lda, g.a_bs, (const uint16_t*)g.B,
-                     (const uint16_t*)g.B2, g.nb1, g.ldb, g.b_bs, g.C, g.ldc,
-                     g.c_bs, g.c_ks, g.M, g.N, g.K, k_chunk, g.m_split,
-                     g.c_hl);
+                     (const uint16_t*)g.B2, g.nb1, (const uint16_t*)g.B3,
+                     g.nb2, g.ldb, g.b_bs, g.C, g.ldc, g.c_bs, g.c_ks, g.M,
+                     g.N, g.K, k_chunk, g.m_split, g.c_hl);
   return hipGetLastError();
 }
 
@@ -769,14 +773,15 @@ void gemm_plan(const mla_dims& d, GemmArgs& g, int max_split) {
       g.M >= 128 && g.K >= 256 && g.K % 64 == 0 &&
       g.N % 4 == 0 &&
       g.ldc % 4 == 0 && (g.lda * esz) % 16 == 0 && g.ldb % 8 == 0 &&
-      (g.nb1 >= g.N || g.nb1 % BG_BN == 0)) {
+      (g.nb1 >= g.N || g.nb1 % BG_BN == 0) && g.nb2 >= g.N) {
     g.big = 1;
     return;
   }
   if (d.dtype != MLA_BF16 || g.b_nn || g.M > 64 || g.M <= 0 || g.N <= 0 ||
       g.K <= 0)
     return;
-  if (g.K % 64 == 0 && (g.nb1 >= g.N || g.nb1 % 32 == 0)) {
+  if (g.K % 64 == 0 && (g.nb1 >= g.N || g.nb1 % 32 == 0) &&
+      (g.nb2 >= g.N || g.nb2 % 32 == 0)) {
     // LDS-staged kernel: 128 or 256 columns per workgroup and a K split
     // (64-multiple chunks) with at most one workgroup per compute unit.
     // Cost = weights (padded to whole column slices) + half the activation
@@ -831,6 +836,8 @@ hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
                        g.ldc, g.c_bs, g.c_ks, g.M, g.N, g.K, (int)g.K);
     return hipGetLastError();
   }
+  // a third weight part: LDS-staged kernel only
+  if (g.nb2 < g.N && (g.big || g.ntw >= 0)) return hipErrorInvalidValue;
   if (g.big) {
     if (ks != 1 || g.batch != 1) return hipErrorInvalidValue;
     return g.a_f32 ? launch_big<true>(g, stream) : launch_big<false>(g, stream);

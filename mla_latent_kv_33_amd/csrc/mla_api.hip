@@ -341,6 +341,52 @@ AbsorbWs absorb_layout(const mla_dims& d, int T, void* base) {
 }
 }  // namespace
 
+namespace {
+// The query path from c_Q on (fp32, or pre-split hi|lo when cq_hl): q_C and
+// q_R = W_UQ c_Q, W_QR c_Q, then RoPE(q_R) and q_lat_h = W_UK_h^T q_C_h into
+// the query rows.
+mla_status query_from_cq(const mla_dims& d, int T, const float* cq,
+                         bool cq_hl, float* qcr_parts, float* qcr,
+                         const int32_t* pos, const void* w_uq,
+                         const void* w_qr, const void* w_uk,
+                         const float* rope_cos, const float* rope_sin,
+                         int max_pos, void* q_out, hipStream_t s) {
+  GemmArgs g2 = qcr_gemm(d, T);
+  g2.A = cq;
+  g2.a_hl = cq_hl;
+  g2.B = w_uq;
+  g2.B2 = w_qr;
+  g2.C = qcr_parts;
+  MLA_TRY(launch_gemm(d, g2, s));
+  // Decode batches: one kernel reads the K-split parts of q_C / q_R and
+  // writes both halves of every query row.
+  if (absorb_fast_supported(d, T, g2.k_split))
+    return dev(launch_absorb_fast(d, T, qcr_parts, g2.k_split, g2.c_ks,
+                                  g2.ldc, w_uk, pos, rope_cos, rope_sin,
+                                  max_pos, q_out, s));
+  if (g2.k_split > 1)
+    MLA_TRY(launch_reduce_parts(qcr_parts, g2.k_split, g2.c_ks,
+                                (long)T * g2.N, qcr, s));
+
+  MLA_TRY(launch_query_rope(d, T, qcr + (long)d.n_h * d.d_h, 1, 0, g2.ldc,
+                            pos, rope_cos, rope_sin, max_pos, q_out, s));
+
+  // q_lat_h = W_UK_h^T q_C_h straight into the first d_c columns of each
+  // head's q row (rounded to bf16 by the GEMM for bf16 layers).
+  GemmArgs g3 = absorb_gemm(d, T);
+  g3.A = qcr;
+  g3.B = w_uk;
+  g3.ldc = (long)d.n_h * (d.d_c + d.d_r);
+  g3.c_bs = d.d_c + d.d_r;
+  if (d.dtype == MLA_BF16)
+    g3.c16 = q_out;
+  else
+    g3.C = (float*)q_out;
+  MLA_TRY(launch_gemm(d, g3, s));
+  return MLA_OK;
+}
+}  // namespace
+
 size_t mla_absorb_workspace_bytes(const mla_dims* dims, int32_t T) {
   if (!dims_ok(dims) || T <= 0) return 0;
   return absorb_layout(*dims, T, nullptr).bytes;
@@ -376,7 +422,7 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
   }
 
   GemmArgs g1 = cq_gemm(d, T);
-  GemmArgs g2 = qcr_gemm(d, T);
+  const GemmArgs g2 = qcr_gemm(d, T);
   // c_Q goes to the weight-streaming kernel of the next GEMM pre-split
   // (hi|lo), written by the reduce of the K parts or by the GEMM itself
   const bool cq_hl = g2.ntw < 0 && (g1.k_split > 1 || g1.ntw < 0);
@@ -393,39 +439,113 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
       MLA_TRY(launch_reduce_parts(w.cq_parts, g1.k_split, g1.c_ks,
                                   (long)T * d.d_cq, w.cq, s));
   }
+  return query_from_cq(d, T, w.cq, cq_hl, w.qcr_parts, w.qcr, pos, w_uq,
+                       w_qr, w_uk, rope_cos, rope_sin, max_pos, q_out, s);
+}
 
-  g2.A = w.cq;
-  g2.a_hl = cq_hl;
-  g2.B = w_uq;
-  g2.B2 = w_qr;
-  g2.C = w.qcr_parts;
-  MLA_TRY(launch_gemm(d, g2, s));
-  // Decode batches: one kernel reads the K-split parts of q_C / q_R and
-  // writes both halves of every query row.
-  if (absorb_fast_supported(d, T, g2.k_split))
-    return dev(launch_absorb_fast(d, T, w.qcr_parts, g2.k_split, g2.c_ks,
-                                  g2.ldc, w_uk, pos, rope_cos, rope_sin,
-                                  max_pos, q_out, s));
-  if (g2.k_split > 1)
-    MLA_TRY(launch_reduce_parts(w.qcr_parts, g2.k_split, g2.c_ks,
-                                (long)T * g2.N, w.qcr, s));
 
-  MLA_TRY(launch_query_rope(d, T, w.qcr + (long)d.n_h * d.d_h, 1, 0, g2.ldc,
-                            pos, rope_cos, rope_sin, max_pos, q_out, s));
+// ---------------------------------------- append and query in one call
+namespace {
+// [W_DQ; W_DKV; W_KR] h: the three down-projections of the new tokens
+// stacked as one weight of d_cq + d_c + d_r rows.
+GemmArgs down_gemm(const mla_dims& d, int T) {
+  GemmArgs g;
+  g.lda = d.d;
+  g.ldb = d.d;
+  g.nb1 = d.d_cq;
+  g.nb2 = d.d_cq + d.d_c;
+  g.ldc = d.d_cq + d.d_c + d.d_r;
+  g.c_ks = (long)T * g.ldc;
+  g.M = T;
+  g.N = (int)g.ldc;
+  g.K = d.d;
+  gemm_plan(d, g);
+  return g;
+}
+// The stacked form serves bf16 decode batches past the matrix-vector token
+// counts: one weight-streaming projection with K parts (summed by the
+// shared epilogue), feeding a W_UQ / W_QR projection that takes c_Q
+// pre-split.
+bool stacked_down(const mla_dims& d, int T) {
+  if (d.dtype != MLA_BF16 || gemv_supported(d, T) ||
+      gemv_supported(d, T, GV_QO_MAXT))
+    return false;
+  const GemmArgs g = down_gemm(d, T), g2 = qcr_gemm(d, T);
+  return g.ntw < 0 && g.k_split > 1 && g2.ntw < 0 && d.d_cq % 8 == 0;
+}
+struct StackedWs {
+  float *parts, *cq, *qcr_parts, *qcr;
+  size_t bytes;
+};
+StackedWs stacked_layout(const mla_dims& d, int T, void* base) {
+  Carve c(base);
+  StackedWs w;
+  const GemmArgs g = down_gemm(d, T), g2 = qcr_gemm(d, T);
+  w.parts = c.take(parts_floats(g));
+  w.cq = c.take((size_t)T * d.d_cq);  // hi|lo pairs, 4 bytes per value
+  w.qcr_parts = c.take(parts_floats(g2));
+  w.qcr = g2.k_split > 1 ? c.take((size_t)T * g2.N) : w.qcr_parts;
+  w.bytes = c.used;
+  return w;
+}
+}  // namespace
 
-  // q_lat_h = W_UK_h^T q_C_h straight into the first d_c columns of each
-  // head's q row (rounded to bf16 by the GEMM for bf16 layers).
-  GemmArgs g3 = absorb_gemm(d, T);
-  g3.A = w.qcr;
-  g3.B = w_uk;
-  g3.ldc = (long)d.n_h * (d.d_c + d.d_r);
-  g3.c_bs = d.d_c + d.d_r;
-  if (d.dtype == MLA_BF16)
-    g3.c16 = q_out;
-  else
-    g3.C = (float*)q_out;
-  MLA_TRY(launch_gemm(d, g3, s));
-  return MLA_OK;
+size_t mla_append_absorb_workspace_bytes(const mla_dims* dims, int32_t T) {
+  if (!dims_ok(dims) || T <= 0) return 0;
+  size_t n = mla_append_workspace_bytes(dims, T);
+  const size_t a = mla_absorb_workspace_bytes(dims, T);
+  if (a > n) n = a;
+  if (dims_supported(dims) && stacked_down(*dims, T)) {
+    const size_t f = stacked_layout(*dims, T, nullptr).bytes;
+    if (f > n) n = f;
+  }
+  return n;
+}
+
+mla_status mla_append_absorb_q(
+    const mla_dims* dims, int32_t T, const void* h, const int32_t* seq_idx,
+    const int32_t* pos, const void* w_dkv, const void* w_kr, const void* w_dq,
+    const void* w_uq, const void* w_qr, const void* w_uk,
+    const float* rope_cos, const float* rope_sin, int32_t max_pos,
+    const int32_t* block_table, int32_t max_blocks, void* cache,
+    int32_t num_blocks, void* q_out, void* ws, size_t ws_bytes,
+    mla_stream_t stream) {
+  if (!dims) return MLA_ERR_NULL;
+  if (!dims_ok(dims) || T < 0 || max_pos <= 0 || max_blocks <= 0 ||
+      num_blocks <= 0)
+    return MLA_ERR_SHAPE;
+  if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  if (T == 0) return MLA_OK;
+  if (!h || !seq_idx || !pos || !w_dkv || !w_kr || !w_dq || !w_uq || !w_qr ||
+      !w_uk || !rope_cos || !rope_sin || !block_table || !cache || !q_out)
+    return MLA_ERR_NULL;
+  if (!ws || ws_bytes < mla_append_absorb_workspace_bytes(dims, T))
+    return MLA_ERR_WORKSPACE;
+  const mla_dims& d = *dims;
+  if (!stacked_down(d, T)) {
+    // the two calls' own paths, one after the other on the stream (the
+    // workspace is free again once the append's kernels have run)
+    const mla_status st = mla_append_cache(
+        dims, T, h, seq_idx, pos, w_dkv, w_kr, rope_cos, rope_sin, max_pos,
+        block_table, max_blocks, cache, num_blocks, ws, ws_bytes, stream);
+    if (st != MLA_OK) return st;
+    return mla_absorb_q(dims, T, h, pos, w_dq, w_uq, w_qr, w_uk, rope_cos,
+                        rope_sin, max_pos, q_out, ws, ws_bytes, stream);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const StackedWs w = stacked_layout(d, T, ws);
+  GemmArgs g = down_gemm(d, T);
+  g.A = h;
+  g.B = w_dq;
+  g.B2 = w_dkv;
+  g.B3 = w_kr;
+  g.C = w.parts;
+  MLA_TRY(launch_gemm(d, g, s));
+  MLA_TRY(launch_project_epilogue(d, T, w.parts, g.k_split, g.c_ks, w.cq,
+                                  seq_idx, pos, rope_cos, rope_sin, max_pos,
+                                  block_table, max_blocks, cache, s));
+  return query_from_cq(d, T, w.cq, true, w.qcr_parts, w.qcr, pos, w_uq, w_qr,
+                       w_uk, rope_cos, rope_sin, max_pos, q_out, s);
 }
 
 // ------------------------------------------------- pre-merged absorption

@@ -148,6 +148,9 @@ struct GemmArgs {
   const void* B = nullptr;
   const void* B2 = nullptr;
   int nb1 = 1 << 30;
+  // rows >= nb2 from B3 (LDS-staged kernel only)
+  const void* B3 = nullptr;
+  int nb2 = 1 << 30;
   int b_nn = 0;  // B stored [K][N]
   long ldb = 0, b_bs = 0;
   float* C = nullptr;
@@ -187,6 +190,16 @@ hipError_t launch_reduce_parts(const float* src, int nparts, long part_stride,
 hipError_t launch_reduce_parts_hl(const float* src, int nparts,
                                   long part_stride, long n, int ld, void* dst,
                                   hipStream_t stream);
+// The stacked down-projection's K parts, rows [c_Q | c_KV | k_R] of
+// d_cq + d_c + d_r floats: c_Q to `cq` in the pre-split hi|lo layout, and
+// each token's cache row (RoPE on k_R), in one launch.
+hipError_t launch_project_epilogue(const mla_dims& d, int T, const float* acc,
+                                   int nparts, long part_stride, void* cq,
+                                   const int32_t* seq_idx, const int32_t* pos,
+                                   const float* rope_cos,
+                                   const float* rope_sin, int max_pos,
+                                   const int32_t* block_table, int max_blocks,
+                                   void* cache, hipStream_t stream);
 // acc [T][d_c + d_r] fp32 -> RoPE on the last d_r columns -> cache rows.
 hipError_t launch_append_scatter(const mla_dims& d, int T, const float* acc,
                                  int nparts, long part_stride,

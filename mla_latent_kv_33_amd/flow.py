@@ -100,15 +100,22 @@ class StepOut:
 
 
 def run_step(st: DeviceStep, n_split: Optional[int] = None, stream=None,
-             out: Optional[StepOut] = None) -> StepOut:
+             out: Optional[StepOut] = None, stacked: bool = True) -> StepOut:
     """One pass of the hot path: append the new tokens, absorb their
-    queries, decode over the cache, project the output."""
+    queries, decode over the cache, project the output.  stacked: the
+    append and the query path as one mla_append_absorb_q call (else
+    mla_append_cache, then mla_absorb_q)."""
     wl, L = st.wl, st.layer
     d = wl.dims
     ns = wl.n_split if n_split is None else n_split
-    L.append(st.h_new, st.seq_idx, st.pos, st.table, st.cache, stream=stream)
-    q = L.absorb(st.h_new, st.pos, q_out=None if out is None else
-                 out.q.view(-1, d.n_h, d.d_c + d.d_r), stream=stream)
+    q_out = None if out is None else out.q.view(-1, d.n_h, d.d_c + d.d_r)
+    if stacked:
+        q = L.append_absorb(st.h_new, st.seq_idx, st.pos, st.table, st.cache,
+                            q_out=q_out, stream=stream)
+    else:
+        L.append(st.h_new, st.seq_idx, st.pos, st.table, st.cache,
+                 stream=stream)
+        q = L.absorb(st.h_new, st.pos, q_out=q_out, stream=stream)
     q4 = q.view(wl.batch, wl.n_q, d.n_h, d.d_c + d.d_r)
     o_lat, lse = L.decode(q4, st.cache, st.table, st.kv_lens, st.max_kv_len,
                           n_split=ns,

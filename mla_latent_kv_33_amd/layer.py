@@ -82,6 +82,26 @@ class MlaLayer:
                        self.rope_sin, q_out, ws=ws, stream=stream)
         return q_out
 
+    def append_absorb(self, h, seq_idx, pos, block_table, cache, q_out=None,
+                      stream=None):
+        """append and absorb of the same tokens as one library call."""
+        d = self.dims
+        T = h.shape[0]
+        if q_out is None:
+            q_out = torch.empty((T, d.n_h, d.d_c + d.d_r),
+                                dtype=torch_dtype(self.dtype),
+                                device=self.device)
+        ws = self.workspace("append_absorb",
+                            B.mla_append_absorb_workspace_bytes(self.cdims,
+                                                                T)) \
+            if T else None
+        B.mla_append_absorb_q(self.cdims, h, seq_idx, pos, self.w["w_dkv"],
+                              self.w["w_kr"], self.w["w_dq"], self.w["w_uq"],
+                              self.w["w_qr"], self.w["w_uk"], self.rope_cos,
+                              self.rope_sin, block_table, cache, q_out, ws=ws,
+                              stream=stream)
+        return q_out
+
     def decode(self, q, cache, block_table, kv_lens, max_kv_len: int,
                n_split: int = 0, o_lat=None, lse=None, stream=None):
         d = self.dims

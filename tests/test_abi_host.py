@@ -468,3 +468,42 @@ def test_premerged_absorption_validation():
     assert call(ws=None) == WS
     assert call(ws_bytes=16) == WS
     assert call(max_pos=0) == SHAPE
+
+
+def test_append_absorb_validation():
+    """mla_append_absorb_q checks every argument of both calls before it
+    enqueues anything, and sizes its workspace for either path."""
+    lib = B.lib()
+    d = ds_dims()
+    for T in (1, 3, 8, 64, 200):
+        need = B.mla_append_absorb_workspace_bytes(d, T)
+        assert need >= B.mla_append_workspace_bytes(d, T)
+        assert need >= B.mla_absorb_workspace_bytes(d, T)
+    # the stacked decode-batch form: K parts of T x (d_cq + d_c + d_r)
+    # floats plus c_Q, beyond what the query path alone needs
+    assert B.mla_append_absorb_workspace_bytes(d, 64) >= \
+        64 * (1536 + 512 + 64) * 4 * 2
+    assert B.mla_append_absorb_workspace_bytes(d, 0) == 0
+
+    def call(dims=d, T=4, ws=FAKE, ws_bytes=1 << 30, h=FAKE, q=FAKE,
+             max_pos=16, max_blocks=1, num_blocks=1, w_uk=FAKE):
+        return lib.mla_append_absorb_q(
+            ctypes.byref(dims), T, h, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+            FAKE, w_uk, FAKE, FAKE, max_pos, FAKE, max_blocks, FAKE,
+            num_blocks, q, ws, ws_bytes, None)
+    assert lib.mla_append_absorb_q(None, 1, *([None] * 11), 16, None, 1,
+                                   None, 1, None, None, 0, None) == NULL
+    assert call(dims=ds_dims(d_r=63)) == SHAPE
+    assert call(dims=ds_dims(d_cq=1552)) == UNSUP
+    assert call(T=-1) == SHAPE
+    assert call(T=0) == OK
+    assert call(h=None) == NULL
+    assert call(q=None) == NULL
+    assert call(w_uk=None) == NULL
+    assert call(max_pos=0) == SHAPE
+    assert call(max_blocks=0) == SHAPE
+    assert call(num_blocks=0) == SHAPE
+    for T in (4, 64):
+        assert call(T=T, ws=None) == WS
+        assert call(T=T, ws_bytes=B.mla_append_absorb_workspace_bytes(
+            d, T) - 1) == WS

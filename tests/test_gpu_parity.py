@@ -174,6 +174,59 @@ def test_ds_few_tokens(ctx, n_q):
         check_sequence(wl, out, ref, b)
 
 
+def assert_reordered(name, a, b):
+    """a and b computed from the same products summed in another fp32
+    order, then rounded to bf16: every element within one bf16 step of the
+    larger magnitude, plus 2^-10 of the array's RMS (values that cancel to
+    near zero carry the sums' absolute error, not a relative one), and
+    rel-Frobenius <= 1e-3."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    rms = float(np.sqrt(np.mean(b * b)))
+    bound = np.exp2(-7.0) * np.maximum(np.abs(a), np.abs(b)) + rms / 1024
+    excess = np.abs(a - b) - bound
+    at = np.unravel_index(int(np.argmax(excess)), a.shape)
+    worst = float(excess[at])
+    rel = float(np.linalg.norm(a - b) / np.linalg.norm(b))
+    assert worst <= 0.0 and rel <= 1e-3, \
+        (f"{name}: excess over bound {worst:.3g} at {at} ({a[at]:.6g} vs "
+         f"{b[at]:.6g}, rms {rms:.3g}), rel-Frobenius {rel:.3g}")
+
+
+@pytest.mark.parametrize("batch,n_q", [(64, 1), (8, 1), (2, 16)])
+def test_stacked_projections(batch, n_q):
+    """mla_append_absorb_q (at these token counts one weight stream for
+    W_DQ, W_DKV and W_KR, and one epilogue for c_Q and the cache rows)
+    against mla_append_cache + mla_absorb_q on the same inputs: the
+    appended rows and the queries differ only by the order of fp32 sums
+    (about one bf16 step), and the stacked step matches the oracle."""
+    base = W.workload("b1_ctx4k")
+    rng = np.random.default_rng(1000 * batch + n_q)
+    ctx = tuple(int(x) for x in rng.integers(64, 700, size=batch))
+    wl = dataclasses.replace(base, name=f"stacked{batch}x{n_q}", batch=batch,
+                             ctx=ctx, n_q=n_q, seed=21, permuted=True)
+    log(f"case DeepSeek-V2 dims, {batch * n_q} tokens, stacked vs separate")
+    layer, w = layer_for(wl)
+    st_s = flow.prepare(wl, layer)
+    out_s = flow.run_step(st_s, stacked=True)
+    st_p = flow.prepare(wl, layer)
+    out_p = flow.run_step(st_p, stacked=False)
+    torch.cuda.synchronize()
+    q_s = out_s.q.float().cpu().numpy()
+    q_p = out_p.q.float().cpu().numpy()
+    assert np.isfinite(q_s).all()
+    assert_reordered("q", q_s, q_p)
+    rows_s = np.stack([flow.gather_rows(st_s, b, wl.ctx[b], n_q)
+                       for b in range(batch)])
+    rows_p = np.stack([flow.gather_rows(st_p, b, wl.ctx[b], n_q)
+                       for b in range(batch)])
+    assert_reordered("appended rows", rows_s, rows_p)
+    for b in sorted({0, batch - 1}):
+        ref = oracle_sequence(wl, w, b)
+        check_new_rows(wl, st_s, ref, b)
+        check_sequence(wl, out_s, ref, b)
+
+
 def test_b64_var():
     wl = W.workload("b64_var")
     log(f"case {wl.name}: B=64 ctx U[1024,8192] permuted table bf16")
