@@ -183,10 +183,11 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
  * c_KV = W_DKV h and the RoPE key RoPE(W_KR h) on one side, the query latent
  * c_Q = W_DQ h on the other ('MLA：潜在表示压缩与解耦 RoPE', section 3, joint
  * compression of keys/values and of queries; section 6, the decoupled RoPE
- * key).  For decode batches (bf16 layers, token counts past the
- * matrix-vector path, up to 64) the three weights are streamed as one
- * stacked projection [W_DQ; W_DKV; W_KR] h, and one epilogue launch sums its
- * K parts into both the cache rows and c_Q; the query path then continues as
+ * key).  With bf16 layers the three weights are streamed as one stacked
+ * projection [W_DQ; W_DKV; W_KR] h: for one or two tokens (the matrix-vector
+ * path) one launch writes both c_Q and the cache rows; for decode batches
+ * of 5 to 64 tokens one weight-streaming GEMM is followed by one epilogue
+ * launch that sums its K parts into both.  The query path then continues as
  * in mla_absorb_q.  Other shapes run the two calls' own paths in sequence.
  * The cache rows and q_out equal those of mla_append_cache followed by
  * mla_absorb_q up to the order of the fp32 sums of each projection.

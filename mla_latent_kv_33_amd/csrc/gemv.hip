@@ -218,15 +218,14 @@ __device__ __forceinline__ void rope_pair(float x1, float x2, int p, int j,
 // task < d_c / 2: rows 2 task, 2 task + 1 of W_DKV; then k_R task
 // j = task - d_c / 2: rows j and j + d_r/2 of W_KR (one RoPE pair).
 template <int T>
-__global__ __launch_bounds__(64) void gemv_append_kernel(
-    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_dkv,
+__device__ __forceinline__ void append_task(
+    int task, const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_dkv,
     const uint16_t* __restrict__ w_kr, int d, int d_c, int d_r,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
     const float* __restrict__ rcos, const float* __restrict__ rsin,
     int max_pos, const int32_t* __restrict__ block_table, int max_blocks,
     int block_size, uint16_t* __restrict__ cache) {
   const int lane = threadIdx.x;
-  const int task = blockIdx.x;
   const int width = d_c + d_r, half = d_r / 2;
   const bool is_kv = task < d_c / 2;
   const int c0 = is_kv ? 2 * task : task - d_c / 2;
@@ -255,6 +254,51 @@ __global__ __launch_bounds__(64) void gemv_append_kernel(
       row[d_c + c1] = f2bf(y2);
     }
   }
+}
+
+template <int T>
+__global__ __launch_bounds__(64) void gemv_append_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_dkv,
+    const uint16_t* __restrict__ w_kr, int d, int d_c, int d_r,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
+    const float* __restrict__ rcos, const float* __restrict__ rsin,
+    int max_pos, const int32_t* __restrict__ block_table, int max_blocks,
+    int block_size, uint16_t* __restrict__ cache) {
+  append_task<T>(blockIdx.x, h, w_dkv, w_kr, d, d_c, d_r, seq_idx, pos, rcos,
+                 rsin, max_pos, block_table, max_blocks, block_size, cache);
+}
+
+// ---- the three down-projections of h in one launch ----------------------
+// [W_DQ; W_DKV; W_KR] h: tasks < d_cq / 2 take rows 2 task, 2 task + 1 of
+// W_DQ and write c_Q as hi|lo pairs (ldcq values per token row) for the
+// query up-projection; the next d_c / 2 + d_r / 2 tasks are the append's.
+template <int T>
+__global__ __launch_bounds__(64) void gemv_down_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w_dq,
+    int d_cq, uint16_t* __restrict__ cq, const uint16_t* __restrict__ w_dkv,
+    const uint16_t* __restrict__ w_kr, int d, int d_c, int d_r,
+    const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
+    const float* __restrict__ rcos, const float* __restrict__ rsin,
+    int max_pos, const int32_t* __restrict__ block_table, int max_blocks,
+    int block_size, uint16_t* __restrict__ cache) {
+  const int nq = d_cq / 2;
+  if ((int)blockIdx.x >= nq) {
+    append_task<T>(blockIdx.x - nq, h, w_dkv, w_kr, d, d_c, d_r, seq_idx, pos,
+                   rcos, rsin, max_pos, block_table, max_blocks, block_size,
+                   cache);
+    return;
+  }
+  const int lane = threadIdx.x;
+  const int n0 = 2 * blockIdx.x;
+  const uint16_t* w[2] = {w_dq + (size_t)n0 * d, w_dq + (size_t)(n0 + 1) * d};
+  float acc[T][2];
+  gemv_rows<T, 2, XB16, GV_U_D>(w, h, d, d, lane, acc);
+  // lane 2 t + r writes (t, row r)
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      if (lane == 2 * t + r) store_hl(cq, d_cq, t, n0 + r, acc[t][r]);
 }
 
 // ---- plain rows: y[t][n] = W[n] . x[t] ----------------------------------
@@ -481,6 +525,17 @@ hipError_t launch_gemv_query(const mla_dims& d, int T, const void* h,
                      h, (long)d.d, 0, 0L, (void*)cq, (long)d.d_cq)
   MLA_GV_T2(T, MLA_DQ)
 #undef MLA_DQ
+  return launch_gemv_query_tail(d, T, w_uq, w_qr, w_uk, pos, rope_cos,
+                                rope_sin, max_pos, cq, qc, q_out, stream);
+}
+
+hipError_t launch_gemv_query_tail(const mla_dims& d, int T, const void* w_uq,
+                                  const void* w_qr, const void* w_uk,
+                                  const int32_t* pos, const float* rope_cos,
+                                  const float* rope_sin, int max_pos,
+                                  const float* cq, float* qc, void* q_out,
+                                  hipStream_t stream) {
+  if (T < 1 || T > GV_QO_MAXT) return hipErrorInvalidValue;
   // q_C (fp32) and RoPE(q_R) into the query rows
   const int t2 = d.n_h * d.d_h / 4 + d.n_h * (d.d_r / 4);
 #define MLA_UQ(TT)                                                           \
@@ -499,6 +554,27 @@ hipError_t launch_gemv_query(const mla_dims& d, int T, const void* h,
                      (uint16_t*)q_out)
   MLA_GV_T2(T, MLA_AB)
 #undef MLA_AB
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_down(const mla_dims& d, int T, const void* h,
+                            const void* w_dq, const void* w_dkv,
+                            const void* w_kr, const int32_t* seq_idx,
+                            const int32_t* pos, const float* rope_cos,
+                            const float* rope_sin, int max_pos,
+                            const int32_t* block_table, int max_blocks,
+                            void* cache, float* cq, hipStream_t stream) {
+  if (T < 1 || T > GV_QO_MAXT || d.d_cq % 2) return hipErrorInvalidValue;
+  const int tasks = d.d_cq / 2 + d.d_c / 2 + d.d_r / 2;
+#define MLA_DN(TT)                                                           \
+  hipLaunchKernelGGL(gemv_down_kernel<TT>, dim3(tasks), dim3(64), 0, stream, \
+                     (const uint16_t*)h, (const uint16_t*)w_dq, d.d_cq,       \
+                     (uint16_t*)cq, (const uint16_t*)w_dkv,                  \
+                     (const uint16_t*)w_kr, d.d, d.d_c, d.d_r, seq_idx, pos,  \
+                     rope_cos, rope_sin, max_pos, block_table, max_blocks,   \
+                     d.block_size, (uint16_t*)cache)
+  MLA_GV_T2(T, MLA_DN)
+#undef MLA_DN
   return hipGetLastError();
 }
 

@@ -522,6 +522,20 @@ mla_status mla_append_absorb_q(
   if (!ws || ws_bytes < mla_append_absorb_workspace_bytes(dims, T))
     return MLA_ERR_WORKSPACE;
   const mla_dims& d = *dims;
+  hipStream_t s = (hipStream_t)stream;
+  if (d.dtype == MLA_BF16 && gemv_supported(d, T, GV_QO_MAXT) &&
+      d.d_cq % 2 == 0) {
+    // one or two tokens: the three down-projections as one matrix-vector
+    // launch, then the query path's own (c_Q and q_C at the start of the
+    // workspace, as in mla_absorb_q)
+    float* cq = (float*)ws;
+    float* qc = cq + (size_t)T * d.d_cq;
+    MLA_TRY(launch_gemv_down(d, T, h, w_dq, w_dkv, w_kr, seq_idx, pos,
+                             rope_cos, rope_sin, max_pos, block_table,
+                             max_blocks, cache, cq, s));
+    return dev(launch_gemv_query_tail(d, T, w_uq, w_qr, w_uk, pos, rope_cos,
+                                      rope_sin, max_pos, cq, qc, q_out, s));
+  }
   if (!stacked_down(d, T)) {
     // the two calls' own paths, one after the other on the stream (the
     // workspace is free again once the append's kernels have run)
@@ -532,7 +546,6 @@ mla_status mla_append_absorb_q(
     return mla_absorb_q(dims, T, h, pos, w_dq, w_uq, w_qr, w_uk, rope_cos,
                         rope_sin, max_pos, q_out, ws, ws_bytes, stream);
   }
-  hipStream_t s = (hipStream_t)stream;
   const StackedWs w = stacked_layout(d, T, ws);
   GemmArgs g = down_gemm(d, T);
   g.A = h;

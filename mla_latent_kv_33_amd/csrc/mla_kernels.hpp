@@ -81,6 +81,23 @@ hipError_t launch_gemv_query(const mla_dims& d, int T, const void* h,
                              const int32_t* pos, const float* rope_cos,
                              const float* rope_sin, int max_pos, float* cq,
                              float* qc, void* q_out, hipStream_t stream);
+// The query path from c_Q on (cq as bf16 hi|lo pairs): q_C -> qc, then
+// q_out as launch_gemv_query.
+hipError_t launch_gemv_query_tail(const mla_dims& d, int T, const void* w_uq,
+                                  const void* w_qr, const void* w_uk,
+                                  const int32_t* pos, const float* rope_cos,
+                                  const float* rope_sin, int max_pos,
+                                  const float* cq, float* qc, void* q_out,
+                                  hipStream_t stream);
+// [W_DQ; W_DKV; W_KR] h in one launch (up to GV_QO_MAXT tokens): c_Q -> cq
+// as bf16 hi|lo pairs, and the append's cache rows as launch_gemv_append.
+hipError_t launch_gemv_down(const mla_dims& d, int T, const void* h,
+                            const void* w_dq, const void* w_dkv,
+                            const void* w_kr, const int32_t* seq_idx,
+                            const int32_t* pos, const float* rope_cos,
+                            const float* rope_sin, int max_pos,
+                            const int32_t* block_table, int max_blocks,
+                            void* cache, float* cq, hipStream_t stream);
 // v [T][n_h d_h] = W_UV_h o_lat_h as bf16 hi|lo pairs (4 bytes per value),
 // then u [T][d] bf16 = W_O v.
 hipError_t launch_gemv_out(const mla_dims& d, int T, const float* o_lat,

@@ -193,11 +193,13 @@ def assert_reordered(name, a, b):
          f"{b[at]:.6g}, rms {rms:.3g}), rel-Frobenius {rel:.3g}")
 
 
-@pytest.mark.parametrize("batch,n_q", [(64, 1), (8, 1), (2, 16)])
+@pytest.mark.parametrize("batch,n_q", [(64, 1), (8, 1), (2, 16), (1, 1),
+                                       (2, 1)])
 def test_stacked_projections(batch, n_q):
     """mla_append_absorb_q (at these token counts one weight stream for
-    W_DQ, W_DKV and W_KR, and one epilogue for c_Q and the cache rows)
-    against mla_append_cache + mla_absorb_q on the same inputs: the
+    W_DQ, W_DKV and W_KR: a matrix-vector launch for 1 and 2 tokens, a GEMM
+    and one epilogue for c_Q and the cache rows beyond) against
+    mla_append_cache + mla_absorb_q on the same inputs: the
     appended rows and the queries differ only by the order of fp32 sums
     (about one bf16 step), and the stacked step matches the oracle."""
     base = W.workload("b1_ctx4k")
