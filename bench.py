@@ -93,6 +93,10 @@ def parse():
                          "call (the down-projections W_DQ, W_DKV, W_KR of h "
                          "stacked into one weight stream) or as "
                          "mla_append_cache followed by mla_absorb_q")
+    ap.add_argument("--unbound", action="store_true",
+                    help="check and marshal every library call's arguments "
+                         "on every step (by default the step's calls are "
+                         "bound once: binding.BoundCall)")
     ap.add_argument("--graph", action="store_true",
                     help="timed steps replay HIP graphs (captured once after "
                          "the warmup: append + query, attention, output) "
@@ -257,8 +261,12 @@ def main():
         return [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
                 for _ in range(n)]
 
+    bound = None   # the step's library calls, bound once (set below)
+
     def attention():
-        if mha:
+        if bound is not None:
+            bound.attention()
+        elif mha:
             layer.prefill_mha(out.q, st.cache, st.table, st.kv_lens,
                               st.max_kv_len, o_v=out.o_v, lse=out.lse)
         else:
@@ -284,6 +292,17 @@ def main():
             B.lib().mla_absorb_merged_workspace_bytes(
                 ctypes.byref(layer.cdims), st.h_new.shape[0]),
             dtype=torch.uint8, device="cuda")
+
+    # The default path issues its library calls bound (binding.BoundCall):
+    # the tensor checks and the marshalling of the arguments run once here
+    # instead of on every step.  At B = 1 they took as long as the GPU's
+    # step (about 85 us per step on the host).
+    # (not under --graph: a bound call keeps the stream it was bound on,
+    # while capture runs on a capture stream)
+    if (not mha and merged is None and side is None and not args.unbound
+            and not args.graph):
+        bound = flow.bind_step(st, out, n_split, stacked=(
+            args.project == "stacked"))
 
     def query_path():
         if merged is not None:
@@ -313,6 +332,14 @@ def main():
             join.record(side)
             query_path()
             stream.wait_event(join)
+        elif bound is not None:
+            # stacked: one call (e[0] and e[1] around it; the absorb stage
+            # is empty); separate: the append, then the query path
+            if rec_all: e[0].record(stream)
+            bound.pre[0]()
+            if rec_all: e[1].record(stream)
+            for c in bound.pre[1:]:
+                c()
         elif stacked:
             # e[0] and e[1] together: the append stage is part of the call
             if rec_all:
@@ -329,7 +356,9 @@ def main():
         if rec_dec: e[2].record(stream)
         attention()
         if rec_dec: e[3].record(stream)
-        if mha:
+        if bound is not None:
+            bound.out()
+        elif mha:
             layer.out_values(out.o_v.view(-1, d.n_h * d.d_h), u=out.u)
         else:
             layer.out(out.o_lat.view(-1, d.n_h, d.d_c), u=out.u)
@@ -553,6 +582,8 @@ def main():
         "streams": ("append on a second stream, concurrent with the query "
                     "path" if side is not None else "one stream"),
         "query": args.query,
+        "calls": ("bound once (binding.BoundCall)" if bound is not None
+                  else "arguments checked on every call"),
         "projections": ("one mla_append_absorb_q call (W_DQ, W_DKV, W_KR "
                         "stacked)" if stacked else
                         "mla_append_cache, then the query call"),

@@ -197,6 +197,35 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+class BoundCall:
+    """One library call whose tensor arguments were checked and whose
+    ctypes arguments were built once (bind=True on a wrapper below).
+    Calling it issues the same call again with the same pointers, sizes and
+    stream, so the tensors must stay alive and in place; the library still
+    checks its scalar arguments on every call.  A serving loop (or a timed
+    benchmark) that reuses its buffers step after step pays the argument
+    checks once instead of on every call."""
+    __slots__ = ("name", "fn", "args")
+
+    def __init__(self, name: str, args):
+        self.name = name
+        self.fn = getattr(lib(), name)
+        self.args = tuple(args)
+
+    def __call__(self) -> None:
+        status = self.fn(*self.args)
+        if status != 0:
+            _check(self.name, status)
+
+
+def _call(name: str, args, bind: bool):
+    """Issue a library call, or return it as a BoundCall."""
+    if bind:
+        return BoundCall(name, args)
+    _check(name, getattr(lib(), name)(*args))
+    return None
+
+
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
     if nbytes == 0:
         return ws, 0 if ws is None else ws.numel() * ws.element_size()
@@ -316,7 +345,8 @@ def _attention_args(dims, q, cache, block_table, kv_lens, qwidth):
 
 
 def mla_append_cache(dims: MlaDims, h, seq_idx, pos, w_dkv, w_kr, rope_cos,
-                     rope_sin, block_table, cache, ws=None, stream=None):
+                     rope_sin, block_table, cache, ws=None, stream=None,
+                     bind: bool = False):
     """c_KV = W_DKV h and k_R = RoPE(W_KR h) for T = h.shape[0] tokens,
     written into the paged cache (see include/mla.h)."""
     T = h.shape[0]
@@ -324,10 +354,10 @@ def mla_append_cache(dims: MlaDims, h, seq_idx, pos, w_dkv, w_kr, rope_cos,
                             rope_sin, block_table, cache))
     ws, wsb = _workspace(mla_append_workspace_bytes(dims, T) if T else 0,
                          h.device, ws)
-    _check("mla_append_cache", lib().mla_append_cache(
+    return _call("mla_append_cache", (
         ctypes.byref(dims), T, *p[:7], rope_cos.shape[0], p[7],
         block_table.shape[1], p[8], cache.shape[0], _ptr(ws, "ws"), wsb,
-        _stream(stream)))
+        _stream(stream)), bind)
 
 
 def mla_append_cache_rmsnorm(dims: MlaDims, h, seq_idx, pos, w_dkv, w_kr,
@@ -348,7 +378,7 @@ def mla_append_cache_rmsnorm(dims: MlaDims, h, seq_idx, pos, w_dkv, w_kr,
 
 
 def mla_absorb_q(dims: MlaDims, h, pos, w_dq, w_uq, w_qr, w_uk, rope_cos,
-                 rope_sin, q_out, ws=None, stream=None):
+                 rope_sin, q_out, ws=None, stream=None, bind: bool = False):
     """q_out[t, h] = [W_UK_h^T q_C | RoPE(W_QR c_Q)_h] (see include/mla.h)."""
     T = h.shape[0]
     lt = _layer_dtype(dims)
@@ -359,14 +389,15 @@ def mla_absorb_q(dims: MlaDims, h, pos, w_dq, w_uq, w_qr, w_uk, rope_cos,
                  numel=T * dims.n_h * (dims.d_c + dims.d_r)))
     ws, wsb = _workspace(mla_absorb_workspace_bytes(dims, T) if T else 0,
                          h.device, ws)
-    _check("mla_absorb_q", lib().mla_absorb_q(
+    return _call("mla_absorb_q", (
         ctypes.byref(dims), T, *p[:5], p[7], p[5], p[6], rope_cos.shape[0],
-        p[8], _ptr(ws, "ws"), wsb, _stream(stream)))
+        p[8], _ptr(ws, "ws"), wsb, _stream(stream)), bind)
 
 
 def mla_append_absorb_q(dims: MlaDims, h, seq_idx, pos, w_dkv, w_kr, w_dq,
                         w_uq, w_qr, w_uk, rope_cos, rope_sin, block_table,
-                        cache, q_out, ws=None, stream=None):
+                        cache, q_out, ws=None, stream=None,
+                        bind: bool = False):
     """mla_append_cache and mla_absorb_q on the same tokens in one call (see
     include/mla.h)."""
     T = h.shape[0]
@@ -382,10 +413,10 @@ def mla_append_absorb_q(dims: MlaDims, h, seq_idx, pos, w_dkv, w_kr, w_dq,
     ws, wsb = _workspace(mla_append_absorb_workspace_bytes(dims, T) if T
                          else 0, h.device, ws)
     # p: h seq_idx pos w_dkv w_kr cos sin table cache w_dq w_uq w_qr w_uk q
-    _check("mla_append_absorb_q", lib().mla_append_absorb_q(
+    return _call("mla_append_absorb_q", (
         ctypes.byref(dims), T, *p[:5], p[9], p[10], p[11], p[12], p[5], p[6],
         rope_cos.shape[0], p[7], block_table.shape[1], p[8], cache.shape[0],
-        p[13], _ptr(ws, "ws"), wsb, _stream(stream)))
+        p[13], _ptr(ws, "ws"), wsb, _stream(stream)), bind)
 
 
 def mla_merge_uq_uk(dims: MlaDims, w_uq, w_uk, w_merged, stream=None):
@@ -418,7 +449,7 @@ def mla_absorb_q_merged(dims: MlaDims, h, pos, w_dq, w_merged, w_qr,
 
 def mla_decode(dims: MlaDims, q, cache, block_table, kv_lens, max_kv_len: int,
                o_lat, lse=None, causal: int = 1, n_split: int = 0, ws=None,
-               stream=None):
+               stream=None, bind: bool = False):
     """Latent attention of q [B, n_q, n_h, d_c + d_r] over the cache
     (see include/mla.h); writes o_lat [B, n_q, n_h, d_c] fp32 and lse."""
     B, n_q = q.shape[0], q.shape[1]
@@ -430,10 +461,10 @@ def mla_decode(dims: MlaDims, q, cache, block_table, kv_lens, max_kv_len: int,
     ws, wsb = _workspace(
         mla_decode_workspace_bytes(dims, B, n_q, max_kv_len, n_split),
         q.device, ws)
-    _check("mla_decode", lib().mla_decode(
+    return _call("mla_decode", (
         ctypes.byref(dims), B, n_q, p[0], p[1], cache.shape[0], p[2],
         block_table.shape[1], p[3], max_kv_len, causal, n_split, p[4], p[5],
-        _ptr(ws, "ws"), wsb, _stream(stream)))
+        _ptr(ws, "ws"), wsb, _stream(stream)), bind)
 
 
 def mla_decode_noalloc(dims: MlaDims, q, cache, block_table, kv_lens,
@@ -453,7 +484,8 @@ def mla_decode_noalloc(dims: MlaDims, q, cache, block_table, kv_lens,
         _stream(stream)))
 
 
-def mla_out(dims: MlaDims, o_lat, w_uv, w_o, u, ws=None, stream=None):
+def mla_out(dims: MlaDims, o_lat, w_uv, w_o, u, ws=None, stream=None,
+            bind: bool = False):
     """u = W_O [W_UV_h o_lat_h]_h for T = o_lat.shape[0] rows."""
     T = o_lat.shape[0]
     lt = _layer_dtype(dims)
@@ -463,8 +495,9 @@ def mla_out(dims: MlaDims, o_lat, w_uv, w_o, u, ws=None, stream=None):
               _a(u, "u", lt, numel=T * dims.d))
     ws, wsb = _workspace(mla_out_workspace_bytes(dims, T) if T else 0,
                          o_lat.device, ws)
-    _check("mla_out", lib().mla_out(
-        ctypes.byref(dims), T, *p, _ptr(ws, "ws"), wsb, _stream(stream)))
+    return _call("mla_out", (
+        ctypes.byref(dims), T, *p, _ptr(ws, "ws"), wsb, _stream(stream)),
+        bind)
 
 
 def mla_query_mha(dims: MlaDims, h, pos, w_dq, w_uq, w_qr, rope_cos, rope_sin,

@@ -127,6 +127,48 @@ def run_step(st: DeviceStep, n_split: Optional[int] = None, stream=None,
 
 
 @dataclasses.dataclass
+class BoundStep:
+    """The library calls of run_step with their arguments checked and
+    marshalled once (binding.BoundCall): `pre` (the append and the query
+    path: one stacked call, or the two calls), `attention` (mla_decode) and
+    `out` (mla_out), on the buffers of the StepOut given to bind_step."""
+    pre: list
+    attention: object
+    out: object
+
+    def __call__(self) -> None:
+        for c in self.pre:
+            c()
+        self.attention()
+        self.out()
+
+
+def bind_step(st: DeviceStep, out: StepOut, n_split: Optional[int] = None,
+              stream=None, stacked: bool = True) -> BoundStep:
+    """run_step(st, n_split, stream, out, stacked) as a BoundStep: each call
+    again writes into `out` and the same workspaces."""
+    wl, L = st.wl, st.layer
+    d = wl.dims
+    ns = wl.n_split if n_split is None else n_split
+    q_out = out.q.view(-1, d.n_h, d.d_c + d.d_r)
+    if stacked:
+        pre = [L.append_absorb(st.h_new, st.seq_idx, st.pos, st.table,
+                               st.cache, q_out=q_out, stream=stream,
+                               bind=True)]
+    else:
+        pre = [L.append(st.h_new, st.seq_idx, st.pos, st.table, st.cache,
+                        stream=stream, bind=True),
+               L.absorb(st.h_new, st.pos, q_out=q_out, stream=stream,
+                        bind=True)]
+    attention = L.decode(out.q, st.cache, st.table, st.kv_lens,
+                         st.max_kv_len, n_split=ns, o_lat=out.o_lat,
+                         lse=out.lse, stream=stream, bind=True)
+    o = L.out(out.o_lat.view(-1, d.n_h, d.d_c), u=out.u, stream=stream,
+              bind=True)
+    return BoundStep(pre=pre, attention=attention, out=o)
+
+
+@dataclasses.dataclass
 class PrefillOut:
     q: torch.Tensor       # [B, n_q, n_h, d_h + d_r]
     o_v: torch.Tensor     # [B, n_q, n_h, d_h] fp32

@@ -59,16 +59,20 @@ class MlaLayer:
         return ws
 
     # ---- the four steps ----------------------------------------------------
-    def append(self, h, seq_idx, pos, block_table, cache, stream=None):
+    # bind=True on the calls below: check and marshal the arguments, and
+    # return the call as a binding.BoundCall instead of issuing it.
+    def append(self, h, seq_idx, pos, block_table, cache, stream=None,
+               bind=False):
         T = h.shape[0]
         ws = self.workspace("append",
                             B.mla_append_workspace_bytes(self.cdims, T)) \
             if T else None
-        B.mla_append_cache(self.cdims, h, seq_idx, pos, self.w["w_dkv"],
-                           self.w["w_kr"], self.rope_cos, self.rope_sin,
-                           block_table, cache, ws=ws, stream=stream)
+        return B.mla_append_cache(self.cdims, h, seq_idx, pos,
+                                  self.w["w_dkv"], self.w["w_kr"],
+                                  self.rope_cos, self.rope_sin, block_table,
+                                  cache, ws=ws, stream=stream, bind=bind)
 
-    def absorb(self, h, pos, q_out=None, stream=None):
+    def absorb(self, h, pos, q_out=None, stream=None, bind=False):
         d = self.dims
         T = h.shape[0]
         if q_out is None:
@@ -77,13 +81,14 @@ class MlaLayer:
                                 device=self.device)
         ws = self.workspace("absorb",
                             B.mla_absorb_workspace_bytes(self.cdims, T))
-        B.mla_absorb_q(self.cdims, h, pos, self.w["w_dq"], self.w["w_uq"],
-                       self.w["w_qr"], self.w["w_uk"], self.rope_cos,
-                       self.rope_sin, q_out, ws=ws, stream=stream)
-        return q_out
+        call = B.mla_absorb_q(self.cdims, h, pos, self.w["w_dq"],
+                              self.w["w_uq"], self.w["w_qr"], self.w["w_uk"],
+                              self.rope_cos, self.rope_sin, q_out, ws=ws,
+                              stream=stream, bind=bind)
+        return call if bind else q_out
 
     def append_absorb(self, h, seq_idx, pos, block_table, cache, q_out=None,
-                      stream=None):
+                      stream=None, bind=False):
         """append and absorb of the same tokens as one library call."""
         d = self.dims
         T = h.shape[0]
@@ -95,15 +100,16 @@ class MlaLayer:
                             B.mla_append_absorb_workspace_bytes(self.cdims,
                                                                 T)) \
             if T else None
-        B.mla_append_absorb_q(self.cdims, h, seq_idx, pos, self.w["w_dkv"],
-                              self.w["w_kr"], self.w["w_dq"], self.w["w_uq"],
-                              self.w["w_qr"], self.w["w_uk"], self.rope_cos,
-                              self.rope_sin, block_table, cache, q_out, ws=ws,
-                              stream=stream)
-        return q_out
+        call = B.mla_append_absorb_q(
+            self.cdims, h, seq_idx, pos, self.w["w_dkv"], self.w["w_kr"],
+            self.w["w_dq"], self.w["w_uq"], self.w["w_qr"], self.w["w_uk"],
+            self.rope_cos, self.rope_sin, block_table, cache, q_out, ws=ws,
+            stream=stream, bind=bind)
+        return call if bind else q_out
 
     def decode(self, q, cache, block_table, kv_lens, max_kv_len: int,
-               n_split: int = 0, o_lat=None, lse=None, stream=None):
+               n_split: int = 0, o_lat=None, lse=None, stream=None,
+               bind=False):
         d = self.dims
         Bsz, n_q = q.shape[0], q.shape[1]
         if o_lat is None:
@@ -114,21 +120,21 @@ class MlaLayer:
                               device=self.device)
         ws = self.workspace("decode", B.mla_decode_workspace_bytes(
             self.cdims, Bsz, n_q, max_kv_len, n_split))
-        B.mla_decode(self.cdims, q, cache, block_table, kv_lens, max_kv_len,
-                     o_lat, lse, causal=1, n_split=n_split, ws=ws,
-                     stream=stream)
-        return o_lat, lse
+        call = B.mla_decode(self.cdims, q, cache, block_table, kv_lens,
+                            max_kv_len, o_lat, lse, causal=1,
+                            n_split=n_split, ws=ws, stream=stream, bind=bind)
+        return call if bind else (o_lat, lse)
 
-    def out(self, o_lat, u=None, stream=None):
+    def out(self, o_lat, u=None, stream=None, bind=False):
         d = self.dims
         T = o_lat.shape[0]
         if u is None:
             u = torch.empty((T, d.d), dtype=torch_dtype(self.dtype),
                             device=self.device)
         ws = self.workspace("out", B.mla_out_workspace_bytes(self.cdims, T))
-        B.mla_out(self.cdims, o_lat, self.w["w_uv"], self.w["w_o"], u, ws=ws,
-                  stream=stream)
-        return u
+        call = B.mla_out(self.cdims, o_lat, self.w["w_uv"], self.w["w_o"], u,
+                         ws=ws, stream=stream, bind=bind)
+        return call if bind else u
 
     # ---- MHA-path chunked prefill (explicit keys and values) ---------------
     def query_mha(self, h, pos, q_out=None, stream=None):

@@ -80,3 +80,31 @@ def test_step_graph_replays_match_eager(name, n_split):
             assert same, f"replay {rep}: {k} differs from the eager step"
         assert torch.equal(st.cache, ref["cache"]), \
             f"replay {rep}: cache differs from the eager step"
+
+
+@pytest.mark.parametrize("name,n_split,stacked", [("graph_b16", 0, True),
+                                                  ("graph_b16", -1, False),
+                                                  ("b1_ctx4k", 0, True)])
+def test_bound_step_matches_eager(name, n_split, stacked):
+    """flow.bind_step (the step's library calls with their arguments
+    checked and marshalled once, as bench.py runs them) reproduces the
+    eager step bit for bit, call after call."""
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    wl = _workload(name, n_split)
+    log(f"case {name} n_split={n_split} stacked={stacked}, bound calls")
+    layer = flow.make_layer(wl)
+    st = flow.prepare(wl, layer)
+    out = flow.run_step(st, stacked=stacked)
+    torch.cuda.synchronize()
+    ref = _snapshot(st, out)
+    step = flow.bind_step(st, out, stacked=stacked)
+    assert len(step.pre) == (1 if stacked else 2)
+    for rep in range(3):
+        for k in ("q", "o_lat", "lse", "u"):
+            getattr(out, k).fill_(float("nan"))
+        step()
+        torch.cuda.synchronize()
+        for k in ("q", "o_lat", "lse", "u"):
+            assert torch.equal(getattr(out, k), ref[k]), \
+                f"bound call {rep}: {k} differs from the eager step"
+        assert torch.equal(st.cache, ref["cache"])
