@@ -19,8 +19,9 @@
 // products grow with the token count, serve up to two (GV_QO_MAXT).
 //
 // The absorption q_lat_h = W_UK_h^T q_C_h reads W_UK_h [d_h][d_c] by rows:
-// one workgroup per head, each of its 8 waves accumulates 16 rows (lanes
-// own 8 latent columns each) and the waves' sums meet in LDS.
+// two workgroups per head (256 latent columns each), each of their 8 waves
+// accumulates 16 rows (lanes own 8 latent columns) and the sums meet in
+// LDS.
 
 #include "mla_common.hpp"
 #include "mla_kernels.hpp"
@@ -396,18 +397,24 @@ __global__ __launch_bounds__(64) void gemv_uq_kernel(
 }
 
 // ---- absorption: q_lat_h = W_UK_h^T q_C_h -------------------------------
-// Workgroup = head hh, 8 waves; wave w accumulates rows i = w, w + 8, ...
-// of W_UK_h (d_h rows of d_c), lane l owning latent columns
-// 8 l + 512 c (c = 0 .. d_c / 512 - 1); the waves' sums are added in LDS and
-// written as bf16 into the first d_c columns of each token's query row.
+// Workgroup = (head hh, 256 latent columns: blockIdx.y), 8 waves, so that
+// the 128 heads fill all compute units with two workgroups each.  Wave w
+// takes rows i = w, w + 8, ... of W_UK_h (d_h rows of d_c): lane half g
+// (lanes 32 g .. 32 g + 31) reads every other one of them, 512 contiguous
+// bytes per row and instruction, lane l owning latent columns
+// 256 y + 8 (l % 32) + 512 c (c = 0 .. d_c / 512 - 1).  The 16 partial sums
+// of a column (8 waves x 2 lane halves) are added in LDS and written as
+// bf16 into the first d_c columns of each token's query row.
 constexpr int AB_WAVES = 8;
+constexpr int AB_PARTS = 2 * AB_WAVES;  // partial sums per column
 template <int T>
 __global__ __launch_bounds__(64 * AB_WAVES) void gemv_absorb_kernel(
     const float* __restrict__ qc, const uint16_t* __restrict__ w_uk,
     int n_h, int d_h, int d_c, int d_r, uint16_t* __restrict__ q_out) {
-  extern __shared__ float red[];  // [AB_WAVES][T][d_c]
+  extern __shared__ float red[];  // [AB_PARTS][T][256]
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int g = lane >> 5;
   const int hh = blockIdx.x;
   const int nch = d_c / 512;  // 512-column chunks (d_c % 512 == 0)
   const uint16_t* wh = w_uk + (size_t)hh * d_h * d_c;
@@ -418,20 +425,21 @@ __global__ __launch_bounds__(64 * AB_WAVES) void gemv_absorb_kernel(
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[t][e] = 0.0f;
-    const int col = 512 * c + 8 * lane;
-    // all of the wave's rows in flight at once (16 for d_h = 128)
-    constexpr int AU = 16;
-    for (int i0 = wave; i0 < d_h; i0 += AB_WAVES * AU) {
+    const int col0 = 512 * c + 256 * blockIdx.y;
+    const int col = col0 + 8 * (lane & 31);
+    // all of the lane half's rows in flight at once (8 for d_h = 128)
+    constexpr int AU = 8;
+    for (int i0 = wave + AB_WAVES * g; i0 < d_h; i0 += AB_PARTS * AU) {
       u32x4 wv[AU];
 #pragma unroll
       for (int u = 0; u < AU; ++u) {
-        const int i = i0 + AB_WAVES * u;
+        const int i = i0 + AB_PARTS * u;
         wv[u] = i < d_h ? *(const u32x4*)(wh + (size_t)i * d_c + col)
                         : (u32x4){0, 0, 0, 0};
       }
 #pragma unroll
       for (int u = 0; u < AU; ++u) {
-        const int i = i0 + AB_WAVES * u;
+        const int i = i0 + AB_PARTS * u;
         if (i >= d_h) break;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
@@ -447,18 +455,19 @@ __global__ __launch_bounds__(64 * AB_WAVES) void gemv_absorb_kernel(
         }
       }
     }
+    const int part = 2 * wave + g;
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        red[((size_t)wave * T + t) * 512 + 8 * lane + e] = acc[t][e];
+        red[((size_t)part * T + t) * 256 + 8 * (lane & 31) + e] = acc[t][e];
     __syncthreads();
-    for (int k = threadIdx.x; k < T * 512; k += 64 * AB_WAVES) {
-      const int t = k / 512, cc = k % 512;
+    for (int k = threadIdx.x; k < T * 256; k += 64 * AB_WAVES) {
+      const int t = k / 256, cc = k % 256;
       float s = 0.0f;
 #pragma unroll
-      for (int w = 0; w < AB_WAVES; ++w) s += red[((size_t)w * T + t) * 512 + cc];
-      q_out[((size_t)t * n_h + hh) * (d_c + d_r) + 512 * c + cc] = f2bf(s);
+      for (int w = 0; w < AB_PARTS; ++w) s += red[((size_t)w * T + t) * 256 + cc];
+      q_out[((size_t)t * n_h + hh) * (d_c + d_r) + col0 + cc] = f2bf(s);
     }
     __syncthreads();
   }
@@ -548,8 +557,8 @@ hipError_t launch_gemv_query_tail(const mla_dims& d, int T, const void* w_uq,
 #undef MLA_UQ
   // q_lat_h = W_UK_h^T q_C_h
 #define MLA_AB(TT)                                                          \
-  hipLaunchKernelGGL(gemv_absorb_kernel<TT>, dim3(d.n_h),                   \
-                     dim3(64 * AB_WAVES), AB_WAVES * TT * 512 * 4, stream, qc, \
+  hipLaunchKernelGGL(gemv_absorb_kernel<TT>, dim3(d.n_h, 2),                \
+                     dim3(64 * AB_WAVES), AB_PARTS * TT * 256 * 4, stream, qc, \
                      (const uint16_t*)w_uk, d.n_h, d.d_h, d.d_c, d.d_r,      \
                      (uint16_t*)q_out)
   MLA_GV_T2(T, MLA_AB)
