@@ -95,8 +95,10 @@ __global__ __launch_bounds__(256) void absorb_kernel(
     for (int c = 0; c < 8; ++c) {
       const int j = 4 * c + wave;
       const int cg = j / 8, kg = 8 * s + j % 8;
-      dma16(l0 + 1024 * (16 * cg + kg),
-            (const char*)(wh + (size_t)8 * kg * d_c + 64 * cg), wvo[kg & 1]);
+      // W_UK is read once per step: non-temporal
+      dma16<true>(l0 + 1024 * (16 * cg + kg),
+                  (const char*)(wh + (size_t)8 * kg * d_c + 64 * cg),
+                  wvo[kg & 1]);
     }
 
   // ---- fragment offsets -------------------------------------------------

@@ -156,7 +156,7 @@ typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 // The lane's byte offset depends on k only through k % 4 (the token group)
 // and k / 4 (128 bytes per chunk group, the copy's immediate offset), so a
 // half needs at most four lane offsets, computed once per half.
-template <int NW>
+template <int NW, bool NTC>
 struct HalfCopy {
   static constexpr int PER = Cfg<NW>::PER_HALF;
   static constexpr int NQ = NW >= 4 ? 1 : 4 / NW;  // distinct k % 4 per wave
@@ -187,7 +187,8 @@ struct HalfCopy {
     // group k = I NW + wave; k / 4 = (I NW) / 4 since wave < NW <= 4 and
     // (I NW) % 4 + wave < 4 for every wave when NW divides 4.
     constexpr int CG = (I * NW) / 4;
-    dma16_off<CG * 128>(lds_buf + (I * NW + wave) * 1024, blk, lane_off[Q]);
+    dma16_off<CG * 128, NTC>(lds_buf + (I * NW + wave) * 1024, blk,
+                             lane_off[Q]);
   }
 };
 
@@ -304,7 +305,7 @@ __device__ BalWork balanced_work(const int32_t* __restrict__ kv_lens,
   return {-1, 0, 0, 0};
 }
 
-template <int NW>
+template <int NW, bool NTC>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64),
                           amdgpu_waves_per_eu(1, 1))) void
 decode_mfma_kernel(
@@ -390,7 +391,7 @@ decode_mfma_kernel(
   // The copies of half j from cache block `bid`.
   auto half_copy = [&](int j, int bid) __attribute__((always_inline)) {
     const int ts = tok0 + HT * j;
-    return HalfCopy<NW>(cache + (size_t)bid * BLOCK_BYTES, j & 1,
+    return HalfCopy<NW, NTC>(cache + (size_t)bid * BLOCK_BYTES, j & 1,
                         lds0 + (j & (NBUF - 1)) * HALF_BYTES,
                         min(HT, visible - ts), wave, lane);
   };
@@ -398,7 +399,7 @@ decode_mfma_kernel(
     return bt[(tok0 + HT * j) / BS];
   };
   auto issue = [&](int j) __attribute__((always_inline)) {
-    const HalfCopy<NW> hc = half_copy(j, block_of(j));
+    const HalfCopy<NW, NTC> hc = half_copy(j, block_of(j));
     CopyAll<0, PER>::run(hc, wave);
   };
 
@@ -551,7 +552,7 @@ decode_mfma_kernel(
   // copies of half j+3 go with the groups of part A.  Scores of the step
   // after the last half are computed on stale buffer contents and fully
   // masked by the caller's lim (0 there).
-  auto step = [&](int j, Half& H, int lim, const HalfCopy<NW>& hc,
+  auto step = [&](int j, Half& H, int lim, const HalfCopy<NW, NTC>& hc,
                   bool copying) __attribute__((always_inline)) {
     constexpr int AR = C::AR;
     constexpr int NPV = 2 * MTW * NW;  // value MFMAs per half: 32
@@ -702,7 +703,7 @@ decode_mfma_kernel(
     for (int j = 0; j < n_half; ++j) {
       barrier();
       const bool copying = j + 3 < n_half;
-      const HalfCopy<NW> hc = half_copy(j + 3, bid_next);
+      const HalfCopy<NW, NTC> hc = half_copy(j + 3, bid_next);
       if (j + 4 < n_half) bid_next = block_of(j + 4);
       const bool next = j + 1 < n_half;
       Half h;
@@ -845,7 +846,7 @@ decode_mfma_kernel(
   }
 }
 
-template <int NW>
+template <int NW, bool NTC = false>
 hipError_t launch_nw(const mla_dims& d, int B, int n_q, const void* q,
                      const void* cache, const int32_t* block_table,
                      int max_blocks, const int32_t* kv_lens, int n_split,
@@ -858,14 +859,15 @@ hipError_t launch_nw(const mla_dims& d, int B, int n_q, const void* q,
   static std::atomic<unsigned long long> lds_set{0};
   {
     const hipError_t e = set_lds_limit_once(
-        (const void*)decode_mfma_kernel<NW>, (int)lds, lds_set);
+        (const void*)decode_mfma_kernel<NW, NTC>, (int)lds, lds_set);
     if (e != hipSuccess) return e;
   }
   const int rows = B * n_q;
   const int slots = bal.plan ? BAL_SLOTS : rows * n_split;
   const dim3 grid(bal.plan ? BAL_SLOTS : rows, bal.plan ? 1 : n_split,
                   d.n_h / (NW * 32));
-  hipLaunchKernelGGL(decode_mfma_kernel<NW>, grid, dim3(NW * 64), lds, stream,
+  hipLaunchKernelGGL((decode_mfma_kernel<NW, NTC>), grid, dim3(NW * 64), lds,
+                     stream,
                      (const uint16_t*)q, (const char*)cache, block_table,
                      max_blocks, kv_lens, n_q, d.n_h, n_split, rows, slots,
                      bal.plan, scale_log2, o_part, m_part, l_part, o_final,
@@ -887,7 +889,8 @@ hipError_t launch_decode_mfma(const mla_dims& d, int B, int n_q,
                               const int32_t* kv_lens, int n_split,
                               const DecodeBalance& balance, float* o_part,
                               float* m_part, float* l_part, float* o_final,
-                              float* lse_final, hipStream_t stream) {
+                              float* lse_final, bool cache_nt,
+                              hipStream_t stream) {
   if (balance.plan && B * n_q > BAL_SLOTS) return hipErrorInvalidValue;
 #define MLA_DECODE_ARGS                                                     \
   d, B, n_q, q, cache, block_table, max_blocks, kv_lens, n_split, balance, \
@@ -900,6 +903,9 @@ hipError_t launch_decode_mfma(const mla_dims& d, int B, int n_q,
     // identical.
     const long wgs = balance.plan ? balance.est_wgs : (long)B * n_q * n_split;
     if (wgs * (d.n_h / 128) <= 128) return launch_nw<2>(MLA_DECODE_ARGS);
+    // Cache rows read once per call (see the caller) are copied with
+    // non-temporal loads.
+    if (cache_nt) return launch_nw<4, true>(MLA_DECODE_ARGS);
     return launch_nw<4>(MLA_DECODE_ARGS);
   }
   if (d.n_h == 64) return launch_nw<2>(MLA_DECODE_ARGS);

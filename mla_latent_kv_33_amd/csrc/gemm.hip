@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
     const uint16_t* __restrict__ B, const uint16_t* __restrict__ B2, int nb1,
     const uint16_t* __restrict__ B3, int nb2,
     long ldb, long b_bs, float* __restrict__ C, long ldc, long c_bs, long c_ks,
-    int M, int N, int K, int k_chunk, int m_split, int c_hl) {
+    int M, int N, int K, int k_chunk, int m_split, int c_hl, int w_nt) {
   static_assert(!HL || AF32, "pre-split A uses the fp32 layout");
   using L = LdsCfg<MT, NTW, AF32>;
   constexpr int NBUF = L::NBUF;
@@ -199,12 +199,22 @@ __global__ __launch_bounds__(256) void gemm_lds_kernel(
     for (int a = 0; a < L::A_PER; ++a)
       dma16(slot + (wave * L::A_PER + a) * 1024, a_base + (size_t)ks_ * L::RB,
             a_off[a]);
+    // weights: non-temporal when w_nt (a uniform branch around the copies)
+    if (w_nt) {
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt)
+      for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        dma16(slot + L::B_OFF + (wave * NTW + nt) * 4096 + q * 1024,
-              b_base[nt] + (size_t)ks_ * 128, b_off[nt][q]);
+        for (int q = 0; q < 4; ++q)
+          dma16<true>(slot + L::B_OFF + (wave * NTW + nt) * 4096 + q * 1024,
+                      b_base[nt] + (size_t)ks_ * 128, b_off[nt][q]);
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          dma16(slot + L::B_OFF + (wave * NTW + nt) * 4096 + q * 1024,
+                b_base[nt] + (size_t)ks_ * 128, b_off[nt][q]);
+    }
   };
 
   // ---- per-lane read offsets inside a slot
@@ -754,7 +764,7 @@ hipError_t launch_lds(const GemmArgs& g, dim3 grid, int k_chunk,
                      stream, g.A, g.lda, g.a_bs, (const uint16_t*)g.B,
                      (const uint16_t*)g.B2, g.nb1, (const uint16_t*)g.B3,
                      g.nb2, g.ldb, g.b_bs, g.C, g.ldc, g.c_bs, g.c_ks, g.M,
-                     g.N, g.K, k_chunk, g.m_split, g.c_hl);
+                     g.N, g.K, k_chunk, g.m_split, g.c_hl, g.w_nt);
   return hipGetLastError();
 }
 

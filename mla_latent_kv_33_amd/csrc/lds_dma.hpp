@@ -25,6 +25,10 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 // addresses are wave-uniform; readfirstlane makes that explicit so that they
 // sit in scalar registers.  readfirstlane returns a signed int: converting
 // through uint32_t zero-extends the low word into the 64-bit address.
+// NT: a non-temporal load, for data read once per step (streamed weights,
+// the cache rows of a large decode), which then does not displace what the
+// Infinity Cache holds.
+template <bool NT = false>
 __device__ __forceinline__ void dma16(uint32_t lds_addr, const void* sbase,
                                       uint32_t voff) {
   const uint64_t b = (uint64_t)sbase;
@@ -32,20 +36,26 @@ __device__ __forceinline__ void dma16(uint32_t lds_addr, const void* sbase,
   const uint32_t hi =
       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
   const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %1"
-      :
-      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"((const char*)sb),
-        "v"(voff)
-      : "memory", "m0");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %1 nt"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"((const char*)sb),
+          "v"(voff)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %1"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"((const char*)sb),
+          "v"(voff)
+        : "memory", "m0");
 }
-// dma16 with a constant added to the global address through the
-// instruction's offset field (0 .. 4095).  The offset field is added to the
-// LDS destination as well, so it is subtracted from M0 here: the data still
-// lands at lds_addr + 16 * lane.
-template <int IMM>
+template <int IMM, bool NT = false>
 __device__ __forceinline__ void dma16_off(uint32_t lds_addr, const void* sbase,
                                           uint32_t voff) {
   static_assert(IMM >= 0 && IMM < 4096, "offset field range");
@@ -55,14 +65,24 @@ __device__ __forceinline__ void dma16_off(uint32_t lds_addr, const void* sbase,
   const uint32_t hi =
       (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
   const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %1 offset:%3"
-      :
-      : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"((const char*)sb),
-        "v"(voff), "n"(IMM)
-      : "memory", "m0");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %1 offset:%3 nt"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"((const char*)sb),
+          "v"(voff), "n"(IMM)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %2, %1 offset:%3"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"((const char*)sb),
+          "v"(voff), "n"(IMM)
+        : "memory", "m0");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {

@@ -62,6 +62,7 @@ mla_status dev(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_DEVICE;
 // ---- GEMM argument builders (shared by sizing and launching) ----
 GemmArgs append_gemm(const mla_dims& d, int T) {
   GemmArgs g;
+  g.w_nt = 1;  // read once per step, not kept in the Infinity Cache
   g.lda = d.d;
   g.nb1 = d.d_c;
   g.ldb = d.d;
@@ -75,6 +76,7 @@ GemmArgs append_gemm(const mla_dims& d, int T) {
 }
 GemmArgs cq_gemm(const mla_dims& d, int T) {
   GemmArgs g;
+  g.w_nt = 1;  // read once per step, not kept in the Infinity Cache
   g.lda = d.d;
   g.ldb = d.d;
   g.ldc = d.d_cq;
@@ -87,6 +89,9 @@ GemmArgs cq_gemm(const mla_dims& d, int T) {
 }
 GemmArgs qcr_gemm(const mla_dims& d, int T) {
   GemmArgs g;
+  // W_UQ / W_QR and W_O keep ordinary loads: together (243.5 MB at
+  // DeepSeek-V2 dims) they fit the 256 MB Infinity Cache, and the other
+  // streams of a step are non-temporal
   g.a_f32 = 1;
   g.lda = d.d_cq;
   g.nb1 = d.n_h * d.d_h;
@@ -118,6 +123,7 @@ GemmArgs absorb_gemm(const mla_dims& d, int T) {
 }
 GemmArgs uv_gemm(const mla_dims& d, int T) {
   GemmArgs g;
+  g.w_nt = 1;  // read once per step, not kept in the Infinity Cache
   g.a_f32 = 1;
   g.lda = (long)d.n_h * d.d_c;
   g.a_bs = d.d_c;
@@ -450,6 +456,7 @@ namespace {
 // stacked as one weight of d_cq + d_c + d_r rows.
 GemmArgs down_gemm(const mla_dims& d, int T) {
   GemmArgs g;
+  g.w_nt = 1;  // read once per step, not kept in the Infinity Cache
   g.lda = d.d;
   g.ldb = d.d;
   g.nb1 = d.d_cq;
@@ -703,6 +710,15 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, int32_t n_q,
   hipStream_t s = (hipStream_t)stream;
   const bool mfma = decode_mfma_supported(d);
   const int rows = B * n_q;
+  // One query per sequence reads each cache row once per call: beyond a
+  // quarter of the 256 MB Infinity Cache the rows are copied with
+  // non-temporal loads, so that they do not push out the weights it holds
+  // between steps (B = 64 at 8K context, 604 MB of rows: 293-294 -> 287-288
+  // us per step together with the weights' policy, same box).  Causal
+  // chunks (n_q > 1) reread every row for each query and keep ordinary
+  // loads.
+  const bool cache_nt = n_q == 1 && (double)B * max_kv_len *
+                                        (d.d_c + d.d_r) * 2.0 > 64.0 * 1048576;
   if (balanced_mode(d, B, n_q, n_split)) {
     Carve c(ws);
     const size_t prow = (size_t)BAL_SLOTS * d.n_h;
@@ -715,7 +731,7 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, int32_t n_q,
     bal.est_wgs = (int)std::min((long)BAL_SLOTS, (long)rows * per_row);
     MLA_TRY(launch_decode_mfma(d, B, n_q, q, cache, block_table, max_blocks,
                                kv_lens, 1, bal, o_part, m_part, l_part, o_lat,
-                               lse, s));
+                               lse, cache_nt, s));
     MLA_TRY(launch_combine(d, rows, 1, o_part, true, m_part, l_part, o_lat,
                            lse, s, bal.plan, BAL_SLOTS));
     return MLA_OK;
@@ -732,7 +748,7 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, int32_t n_q,
   if (mfma)
     MLA_TRY(launch_decode_mfma(d, B, n_q, q, cache, block_table, max_blocks,
                                kv_lens, ns, DecodeBalance(), o_part, m_part,
-                               l_part, o_lat, lse, s));
+                               l_part, o_lat, lse, cache_nt, s));
   else
     MLA_TRY(launch_decode_simt(d, B, n_q, q, cache, block_table, max_blocks,
                                kv_lens, ns, o_part, m_part, l_part, o_lat,

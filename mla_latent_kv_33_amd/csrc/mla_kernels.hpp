@@ -38,7 +38,8 @@ hipError_t launch_decode_mfma(const mla_dims& d, int B, int n_q,
                               const int32_t* kv_lens, int n_split,
                               const DecodeBalance& balance, float* o_part,
                               float* m_part, float* l_part, float* o_final,
-                              float* lse_final, hipStream_t stream);
+                              float* lse_final, bool cache_nt,
+                              hipStream_t stream);
 hipError_t launch_decode_simt(const mla_dims& d, int B, int n_q,
                               const void* q, const void* cache,
                               const int32_t* block_table, int max_blocks,
@@ -189,6 +190,9 @@ struct GemmArgs {
   // it (LDS-staged kernel, one K chunk).
   int a_hl = 0;
   int c_hl = 0;
+  // LDS-staged kernel: read the weights with non-temporal loads (weights
+  // that are not meant to stay in the Infinity Cache between steps)
+  int w_nt = 0;
 };
 hipError_t launch_gemm(const mla_dims& d, const GemmArgs& g,
                        hipStream_t stream);
