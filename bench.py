@@ -68,12 +68,12 @@ def parse():
                     help="with --timed-events decode: record the pair of "
                          "events around the decode call in every N-th timed "
                          "step (the decode duration is their median)")
-    # The GPU's power management runs the first tens of milliseconds of a
-    # sustained load in a transient (here the decode kernel first runs at
-    # ~155 us, slows to ~190 us over the next ~30 steps, then settles near
-    # ~160 us).  Untimed steps for this long come before the warmup steps,
-    # so that the timed steps see the sustained state whatever W is.
-    ap.add_argument("--settle-ms", type=float, default=300.0,
+    # The GPU's power management runs the start of a sustained load in a
+    # transient (the decode kernel first runs at ~155 us, slows to ~190-200
+    # us, then settles near ~160 us).  Untimed steps for this long come
+    # before the warmup steps, so that the timed steps see the sustained
+    # state whatever W is (see the settle loop below).
+    ap.add_argument("--settle-ms", type=float, default=1500.0,
                     help="untimed steps for at least this long (wall clock) "
                          "before the warmup steps")
     ap.add_argument("--streams", type=int, choices=(1, 2), default=1,
@@ -364,13 +364,30 @@ def main():
             layer.out(out.o_lat.view(-1, d.n_h, d.d_c), u=out.u)
         if rec_all: e[4].record(stream)
 
+    # The timed steps' events, and the one garbage collection, come before
+    # the untimed steps, so that the GPU does not sit idle between the last
+    # warmup step and the first timed one.
+    ev = new_events(args.steps)
+    every = 1 if args.timed_events == "all" else max(1, args.event_every)
+    sampled = [i for i in range(args.steps) if i % every == 0]
+    # No garbage collection from here to the end of the timed region: the
+    # first bench process on a freshly started box once spent 34.6 ms of its
+    # first timed step in a full collection over the workload's host arrays
+    # (B = 64 with varying contexts: 408 us per step against 229 us for the
+    # next process).
+    gc.collect()
+    gc.disable()
+
     # settle phase (untimed), then the W warmup steps
     t_settle = time.perf_counter()
     settle_steps = 0
+    # Long groups between synchronisations: the transient comes with
+    # continuous load, and with a synchronisation every 8 steps (2 ms of
+    # work) it had not run its course when the timed steps began.
     while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
-        for _ in range(8):
+        for _ in range(64):
             step()
-        settle_steps += 8
+        settle_steps += 64
         torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
@@ -409,15 +426,6 @@ def main():
             for g in graphs:
                 g.replay()
         torch.cuda.synchronize()
-    ev = new_events(args.steps)
-    every = 1 if args.timed_events == "all" else max(1, args.event_every)
-    sampled = [i for i in range(args.steps) if i % every == 0]
-    # No garbage collection inside the timed region: the first bench process
-    # on a freshly started box once spent 34.6 ms of its first timed step in
-    # a full collection over the workload's host arrays (B = 64 with varying
-    # contexts: 408 us per step against 229 us for the next process).
-    gc.collect()
-    gc.disable()
     t0 = time.perf_counter()
     if graphs is not None:
         for i in range(args.steps):
