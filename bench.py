@@ -93,6 +93,14 @@ def parse():
                          "call (the down-projections W_DQ, W_DKV, W_KR of h "
                          "stacked into one weight stream) or as "
                          "mla_append_cache followed by mla_absorb_q")
+    ap.add_argument("--out-call", choices=("auto", "fused", "separate"),
+                    default="auto",
+                    help="the decode and the output projection as one "
+                         "mla_decode_out call (fused; its event pair then "
+                         "brackets both) or as mla_decode followed by "
+                         "mla_out; auto: fused for one or two query rows, "
+                         "where the library merges the split combine into "
+                         "the W_UV kernel")
     ap.add_argument("--unbound", action="store_true",
                     help="check and marshal every library call's arguments "
                          "on every step (by default the step's calls are "
@@ -263,8 +271,8 @@ def main():
 
     bound = None   # the step's library calls, bound once (set below)
 
-    def attention():
-        if bound is not None:
+    def attention(alone=False):
+        if bound is not None and not (alone and fuse_out):
             bound.attention()
         elif mha:
             layer.prefill_mha(out.q, st.cache, st.table, st.kv_lens,
@@ -299,10 +307,16 @@ def main():
     # step (about 85 us per step on the host).
     # (not under --graph: a bound call keeps the stream it was bound on,
     # while capture runs on a capture stream)
+    # One or two query rows: the decode and the output projection as one
+    # mla_decode_out call, which fuses the split combine with W_UV.
+    fuse_out = (not mha and merged is None and side is None and
+                not args.unbound and not args.graph and
+                (args.out_call == "fused" or
+                 (args.out_call == "auto" and wl.batch * wl.n_q <= 2)))
     if (not mha and merged is None and side is None and not args.unbound
             and not args.graph):
         bound = flow.bind_step(st, out, n_split, stacked=(
-            args.project == "stacked"))
+            args.project == "stacked"), fuse_out=fuse_out)
 
     def query_path():
         if merged is not None:
@@ -464,6 +478,10 @@ def main():
     if stacked:
         stage_ms = {"append+absorb": stage_ms["append"] + stage_ms["absorb"],
                     "decode": stage_ms["decode"], "out": stage_ms["out"]}
+    if fuse_out:
+        # the out stage is empty: mla_decode_out ran it
+        stage_ms = {("decode+out" if k == "decode" else k): v
+                    for k, v in stage_ms.items() if k != "out"}
     # The attention stage alone, outside the step, medians of 10 calls each:
     # right after writing a 512 MiB scratch buffer, right after reading one
     # (either evicts L2 and the 256 MB Infinity Cache, so the cache rows come
@@ -482,7 +500,7 @@ def main():
             elif k == "read":
                 sink.append(scratch.amax())
             ev_fl[k][r][0].record(stream)
-            attention()
+            attention(alone=True)
             ev_fl[k][r][1].record(stream)
     torch.cuda.synchronize()
     del scratch, sink
@@ -512,6 +530,12 @@ def main():
         olat_bytes = queries * d.n_h * d.d_c * 4
         alg_bytes = cache_bytes + q_bytes + olat_bytes
         flops = d.n_h * pairs * (2 * (d.d_c + d.d_r) + 2 * d.d_c)
+        if fuse_out:
+            # mla_decode_out: the output projection's weights read and u
+            # written, and its products
+            nv = d.n_h * d.d_h
+            alg_bytes += (nv * d.d_c + d.d * nv) * 2 + queries * d.d * 2
+            flops += 2.0 * queries * (nv * d.d_c + d.d * nv)
     t_dec = t_dec_ms * 1e-3
     achieved = alg_bytes / t_dec / 1e9
     tflops = flops / t_dec / 1e12
@@ -521,6 +545,9 @@ def main():
         stored_traffic(alg_bytes)
     stage_kernel = ("mla_prefill_mha: gather_rows_kernel + gemm_big_kernel "
                     "(k_C, v_C up-projection) + " + PREFILL_KERNEL if mha else
+                    "mla_decode_out: " + DECODE_KERNEL + " + combine_uv_kernel"
+                    " (split combine and W_UV) + gemv_plain_kernel (W_O)"
+                    if fuse_out else
                     "mla_decode: " + DECODE_KERNEL + " + combine_rows_kernel")
     result = {
         "metric": METRIC,
@@ -592,6 +619,9 @@ def main():
         "query": args.query,
         "calls": ("bound once (binding.BoundCall)" if bound is not None
                   else "arguments checked on every call"),
+        "out_call": ("mla_decode_out (decode, then the combine fused with "
+                     "W_UV, then W_O); decode_us covers all of it"
+                     if fuse_out else "mla_decode, then mla_out"),
         "projections": ("one mla_append_absorb_q call (W_DQ, W_DKV, W_KR "
                         "stacked)" if stacked else
                         "mla_append_cache, then the query call"),

@@ -423,6 +423,37 @@ mla_status mla_out(const mla_dims* dims, int32_t T, const float* o_lat,
                    const void* w_uv, const void* w_o, void* u, void* ws,
                    size_t ws_bytes, mla_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * mla_decode_out - mla_decode followed by mla_out on its rows, in one call.
+ *
+ * The output projection takes the decode's o_lat as it stands: v_h =
+ * W_UV_h o_lat_h, u = W_O v for the T = B n_q query rows ('MLA：潜在表示
+ * 压缩与解耦 RoPE', section 4: the values are up-projected after the
+ * weighted sum over the latent rows; section 7).  For one or two query
+ * rows with split keys on the bf16 matrix-core path (d_c = 512, d_h = 128,
+ * uniform splits) the split combine and the W_UV product run as one
+ * kernel, whose weight reads overlap the combine's; every other shape runs
+ * the two calls' own paths.
+ *
+ *   arguments of mla_decode, then w_uv, w_o and u of mla_out; o_lat and
+ *   lse are written as by mla_decode (lse may be NULL)
+ *   ws    at least mla_decode_out_workspace_bytes(dims, B, n_q,
+ *         max_kv_len, n_split)
+ * Results equal those of the two calls up to the order of fp32 sums.
+ * Errors: those of either call, all checked before anything is launched.
+ * ---------------------------------------------------------------------- */
+size_t mla_decode_out_workspace_bytes(const mla_dims* dims, int32_t B,
+                                      int32_t n_q, int32_t max_kv_len,
+                                      int32_t n_split);
+mla_status mla_decode_out(const mla_dims* dims, int32_t B, int32_t n_q,
+                          const void* q, const void* cache,
+                          int32_t num_blocks, const int32_t* block_table,
+                          int32_t max_blocks, const int32_t* kv_lens,
+                          int32_t max_kv_len, int32_t causal, int32_t n_split,
+                          const void* w_uv, const void* w_o, float* o_lat,
+                          float* lse, void* u, void* ws, size_t ws_bytes,
+                          mla_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

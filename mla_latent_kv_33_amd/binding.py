@@ -78,6 +78,9 @@ _SIGNATURES = {
     "mla_prefill_mha_workspace_bytes": (_S, [_DP, _I, _I]),
     "mla_prefill_mha": (_I, [_DP, _I, _I, _P, _P, _I, _P, _I, _P, _I, _I, _P,
                              _P, _P, _P, _P, _S, _P]),
+    "mla_decode_out_workspace_bytes": (_S, [_DP, _I, _I, _I, _I]),
+    "mla_decode_out": (_I, [_DP, _I, _I, _P, _P, _I, _P, _I, _P, _I, _I, _I,
+                            _P, _P, _P, _P, _P, _P, _S, _P]),
     "mla_out_values": (_I, [_DP, _I, _P, _P, _P, _P, _S, _P]),
     "mla_out_workspace_bytes": (_S, [_DP, _I]),
     "mla_out": (_I, [_DP, _I, _P, _P, _P, _P, _P, _S, _P]),
@@ -465,6 +468,37 @@ def mla_decode(dims: MlaDims, q, cache, block_table, kv_lens, max_kv_len: int,
         ctypes.byref(dims), B, n_q, p[0], p[1], cache.shape[0], p[2],
         block_table.shape[1], p[3], max_kv_len, causal, n_split, p[4], p[5],
         _ptr(ws, "ws"), wsb, _stream(stream)), bind)
+
+
+def mla_decode_out_workspace_bytes(dims: MlaDims, B: int, n_q: int,
+                                   max_kv_len: int, n_split: int) -> int:
+    return lib().mla_decode_out_workspace_bytes(ctypes.byref(dims), B, n_q,
+                                                max_kv_len, n_split)
+
+
+def mla_decode_out(dims: MlaDims, q, cache, block_table, kv_lens,
+                   max_kv_len: int, w_uv, w_o, o_lat, u, lse=None,
+                   causal: int = 1, n_split: int = 0, ws=None, stream=None,
+                   bind: bool = False):
+    """mla_decode, then mla_out on its B * n_q rows, in one call (see
+    include/mla.h): writes o_lat, lse and u [B * n_q, d]."""
+    B, n_q = q.shape[0], q.shape[1]
+    lt = _layer_dtype(dims)
+    p = _ptrs(*_attention_args(dims, q, cache, block_table, kv_lens,
+                               dims.d_c + dims.d_r),
+              _a(w_uv, "w_uv", lt, (dims.n_h * dims.d_h, dims.d_c)),
+              _a(w_o, "w_o", lt, (dims.d, dims.n_h * dims.d_h)),
+              _a(o_lat, "o_lat", _F32,
+                 numel=B * n_q * dims.n_h * dims.d_c),
+              _a(lse, "lse", _F32, numel=B * n_q * dims.n_h),
+              _a(u, "u", lt, numel=B * n_q * dims.d))
+    ws, wsb = _workspace(
+        mla_decode_out_workspace_bytes(dims, B, n_q, max_kv_len, n_split),
+        q.device, ws)
+    return _call("mla_decode_out", (
+        ctypes.byref(dims), B, n_q, p[0], p[1], cache.shape[0], p[2],
+        block_table.shape[1], p[3], max_kv_len, causal, n_split, p[4], p[5],
+        p[6], p[7], p[8], _ptr(ws, "ws"), wsb, _stream(stream)), bind)
 
 
 def mla_decode_noalloc(dims: MlaDims, q, cache, block_table, kv_lens,

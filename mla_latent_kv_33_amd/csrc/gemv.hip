@@ -352,6 +352,193 @@ __global__ __launch_bounds__(64) void gemv_plain_kernel(
       }
 }
 
+// ---- split combine fused with v_h = W_UV_h o_lat_h (one or two rows) ---
+// For a decode of one or two query rows whose keys were split by the
+// matrix-core decode (scaled fp16 partials, m and l per split):
+// workgroup (head h, half z) first issues its 64 rows of W_UV_h (wave w:
+// rows 64 z + 16 w .. + 15; lane l: latent columns 8 l .. 8 l + 7 of
+// each), then merges the head's splits for every query row with the split
+// combine's formula (wave w takes a quarter of the splits, lane l the same
+// 8 columns; the quarters meet in LDS), keeps the merged o_lat_h row in
+// LDS and takes its rows' dot products with it.  The weight stream thus
+// runs under the combine's loads instead of after them in a second kernel.
+// Half 0 also writes o_lat and lse.  The two workgroups of a head are n_h
+// apart in launch order, so with n_h % 8 == 0 they run on one XCD and the
+// second finds the partials in its L2.  Shapes: d_c = 512, d_h = 128.
+constexpr int CU_DC = 512, CU_DH = 128, CU_RW = 16, CU_CS = 16;
+
+// Wave totals of 16 values per lane in 17 exchanges instead of 16 x 6: at
+// each of the offsets 32, 16, 8, 4 a lane keeps the half of its values
+// whose row bit matches its lane bit and adds the partner's copy of that
+// half, then the last two offsets sum plainly.  Lane l ends with the total
+// of value (l >> 2) & 15.
+__device__ __forceinline__ float wave_sum16(const float (&a)[16], int lane) {
+  float b[8];
+  const bool p5 = lane & 32, p4 = lane & 16, p3 = lane & 8, p2 = lane & 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    b[i] = (p5 ? a[i + 8] : a[i]) + __shfl_xor(p5 ? a[i] : a[i + 8], 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    b[i] = (p4 ? b[i + 4] : b[i]) + __shfl_xor(p4 ? b[i] : b[i + 4], 16);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    b[i] = (p3 ? b[i + 2] : b[i]) + __shfl_xor(p3 ? b[i] : b[i + 2], 8);
+  float c = (p2 ? b[1] : b[0]) + __shfl_xor(p2 ? b[0] : b[1], 4);
+  c += __shfl_xor(c, 2);
+  c += __shfl_xor(c, 1);
+  return c;
+}
+
+template <int T>
+__global__ __launch_bounds__(256) void combine_uv_kernel(
+    int n_h, int n_split, const uint16_t* __restrict__ o_part,
+    const float* __restrict__ m_part, const float* __restrict__ l_part,
+    const uint16_t* __restrict__ w_uv, float* __restrict__ o_lat,
+    float* __restrict__ lse, uint16_t* __restrict__ v) {
+  static_assert(CU_RW == 16 && T <= 4, "wave_sum16 and the store lanes");
+  const int h = blockIdx.x, z = blockIdx.y;
+  const int lane = threadIdx.x % 64;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  // this wave's rows of W_UV_h, one 16-byte piece per lane and row (read
+  // once per step: non-temporal)
+  const int r0 = z * (CU_DH / 2) + wv * CU_RW;
+  const uint16_t* wb = w_uv + ((size_t)h * CU_DH + r0) * CU_DC + 8 * lane;
+  u32x4 wr[CU_RW];
+#pragma unroll
+  for (int k = 0; k < CU_RW; ++k)
+    wr[k] = __builtin_nontemporal_load((const u32x4*)(wb + (size_t)k * CU_DC));
+
+  __shared__ float sm_ml[4][2];
+  __shared__ f32x4 sm_o[4][64][2];
+  __shared__ f32x4 xs[T][64][2];
+  // the scales follow the T n_split n_h fp16 partial rows
+  const float* sc_part =
+      (const float*)(o_part + (size_t)T * n_split * n_h * CU_DC);
+  const int per = (n_split + 3) / 4;
+  const int j_lo = min(wv * per, n_split);
+  const int j_hi = min(j_lo + per, n_split);
+  for (int t = 0; t < T; ++t) {
+    const size_t row0 = (size_t)t * n_split * n_h + h;  // + j n_h
+    float M = -INFINITY, L = 0.0f;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    for (int j0 = j_lo; j0 < j_hi; j0 += CU_CS) {
+      // every load from an in-range split (clamped), masked afterwards, so
+      // that all of them are in flight together
+      float m[CU_CS], l[CU_CS], ps[CU_CS];
+      u32x4 raw[CU_CS];
+#pragma unroll
+      for (int u = 0; u < CU_CS; ++u) {
+        const size_t r = row0 + (size_t)min(j0 + u, j_hi - 1) * n_h;
+        m[u] = m_part[r];
+        l[u] = l_part[r];
+        ps[u] = sc_part[r];
+        raw[u] = *(const u32x4*)(o_part + r * CU_DC + 8 * lane);
+      }
+      float mc = M;
+#pragma unroll
+      for (int u = 0; u < CU_CS; ++u) {
+        m[u] = j0 + u < j_hi ? m[u] : -INFINITY;
+        mc = fmaxf(mc, m[u]);
+      }
+      if (mc == -INFINITY) continue;  // only empty splits so far
+      const float sc = M == -INFINITY ? 0.0f : exp2f(M - mc);
+      L *= sc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= sc;
+#pragma unroll
+      for (int u = 0; u < CU_CS; ++u) {
+        const bool live = m[u] != -INFINITY;
+        const float w = live ? exp2f(m[u] - mc) : 0.0f;
+        const float wl = w * l[u];
+        L += live ? wl : 0.0f;
+        const float wp = wl * ps[u];  // weight of the stored partial
+        const f32x8 f = __builtin_convertvector(
+            __builtin_bit_cast(f16x8, raw[u]), f32x8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[e] = live ? __builtin_fmaf(wp, f[e], acc[e]) : acc[e];
+      }
+      M = mc;
+    }
+    // waves 1..3 hand (M, L, columns) to wave 0, which merges them as one
+    // more chunk of splits (a wave without splits has M = -inf)
+    if (wv > 0) {
+      sm_o[wv][lane][0] = (f32x4){acc[0], acc[1], acc[2], acc[3]};
+      sm_o[wv][lane][1] = (f32x4){acc[4], acc[5], acc[6], acc[7]};
+      if (lane == 0) {
+        sm_ml[wv][0] = M;
+        sm_ml[wv][1] = L;
+      }
+    }
+    __syncthreads();
+    if (wv == 0) {
+      float mc = M;
+#pragma unroll
+      for (int g = 1; g < 4; ++g) mc = fmaxf(mc, sm_ml[g][0]);
+      const float sc = M == -INFINITY ? 0.0f : exp2f(M - mc);
+      L *= sc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= sc;
+#pragma unroll
+      for (int g = 1; g < 4; ++g) {
+        const float mg = sm_ml[g][0];
+        const bool live = mg != -INFINITY;
+        const float w = live ? exp2f(mg - mc) : 0.0f;
+        L += live ? w * sm_ml[g][1] : 0.0f;
+        const f32x4 a0 = sm_o[g][lane][0], a1 = sm_o[g][lane][1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[e] = live ? __builtin_fmaf(w, a0[e], acc[e]) : acc[e];
+          acc[e + 4] = live ? __builtin_fmaf(w, a1[e], acc[e + 4]) : acc[e + 4];
+        }
+      }
+      const float il = 1.0f / L;
+      const f32x4 o0 = {acc[0] * il, acc[1] * il, acc[2] * il, acc[3] * il};
+      const f32x4 o1 = {acc[4] * il, acc[5] * il, acc[6] * il, acc[7] * il};
+      xs[t][lane][0] = o0;
+      xs[t][lane][1] = o1;
+      if (z == 0) {
+        float* dst = o_lat + ((size_t)t * n_h + h) * CU_DC + 8 * lane;
+        *(f32x4*)dst = o0;
+        *(f32x4*)(dst + 4) = o1;
+        if (lane == 0 && lse)
+          lse[(size_t)t * n_h + h] = (mc + log2f(L)) * 0.69314718055994531f;
+      }
+    }
+    // publishes xs[t]; sm_o and sm_ml are free again for the next row
+    __syncthreads();
+  }
+  // v rows: the wave's rows of W_UV_h times the merged rows, fp32 products
+  // of the bf16 weights (as the matrix-vector W_UV with fp32 activations)
+  float a[T][CU_RW];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const f32x4 x0 = xs[t][lane][0], x1 = xs[t][lane][1];
+    const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+    for (int k = 0; k < CU_RW; ++k) {
+      float s = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s = __builtin_fmaf(__uint_as_float(wr[k][e] << 16), x[2 * e], s);
+        s = __builtin_fmaf(__uint_as_float(wr[k][e] & 0xFFFF0000u), x[2 * e + 1], s);
+      }
+      a[t][k] = s;
+    }
+  }
+  // lane 4 k + t writes (t, row r0 + k), pre-split for the W_O kernel
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const float tot = wave_sum16(a[t], lane);
+    if ((lane & 3) == t)
+      store_hl(v, (long)n_h * CU_DH, t, (long)h * CU_DH + r0 + (lane >> 2),
+               tot);
+  }
+}
+
 // ---- query up-projection: q_C rows (fp32 out) and q_R pairs (rotated,
 // bf16 into the query row), from c_Q in pre-split pairs ------------------
 // task < n_h d_h / 4: rows 4 task .. + 3 of W_UQ -> qc[t][n]; then task
@@ -617,6 +804,15 @@ hipError_t launch_gemv_out(const mla_dims& d, int T, const float* o_lat,
                      (long)d.d_c, (void*)v, (long)nv)
   MLA_GV_T2(T, MLA_UV)
 #undef MLA_UV
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_gemv_wo(d, T, v, w_o, u, stream);
+}
+
+hipError_t launch_gemv_wo(const mla_dims& d, int T, const float* v,
+                          const void* w_o, void* u, hipStream_t stream) {
+  if (T < 1 || T > GV_QO_MAXT) return hipErrorInvalidValue;
+  const int nv = d.n_h * d.d_h;
   // u = W_O v (bf16)
 #define MLA_O(TT)                                                            \
   hipLaunchKernelGGL((gemv_plain_kernel<TT, XHL, YB16, 4, GV_U_WIDE, false>), \
@@ -625,6 +821,26 @@ hipError_t launch_gemv_out(const mla_dims& d, int T, const float* o_lat,
                      (const void*)v, (long)nv, 0, 0L, u, (long)d.d)
   MLA_GV_T2(T, MLA_O)
 #undef MLA_O
+  return hipGetLastError();
+}
+
+bool combine_uv_supported(const mla_dims& d, int T) {
+  return d.dtype == MLA_BF16 && d.d_c == CU_DC && d.d_h == CU_DH && T >= 1 &&
+         T <= GV_QO_MAXT;
+}
+
+hipError_t launch_combine_uv(const mla_dims& d, int T, int n_split,
+                             const float* o_part, const float* m_part,
+                             const float* l_part, const void* w_uv,
+                             float* o_lat, float* lse, float* v,
+                             hipStream_t stream) {
+  if (!combine_uv_supported(d, T) || n_split < 2) return hipErrorInvalidValue;
+#define MLA_CUV(TT)                                                          \
+  hipLaunchKernelGGL(combine_uv_kernel<TT>, dim3(d.n_h, 2), dim3(256), 0,    \
+                     stream, d.n_h, n_split, (const uint16_t*)o_part, m_part, \
+                     l_part, (const uint16_t*)w_uv, o_lat, lse, (uint16_t*)v)
+  MLA_GV_T2(T, MLA_CUV)
+#undef MLA_CUV
   return hipGetLastError();
 }
 

@@ -686,6 +686,23 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t B, int32_t n_q,
   return align_up(rows * d.d_c * sizeof(float)) + 2 * align_up(rows * sizeof(float));
 }
 
+}  // extern "C"
+
+namespace {
+// One query per sequence reads each cache row once per call: beyond a
+// quarter of the 256 MB Infinity Cache the rows are copied with
+// non-temporal loads, so that they do not push out the weights it holds
+// between steps (B = 64 at 8K context, 604 MB of rows: 293-294 -> 287-288
+// us per step together with the weights' policy, same box).  Causal chunks
+// (n_q > 1) reread every row for each query and keep ordinary loads.
+bool decode_cache_nt(const mla_dims& d, int B, int n_q, int max_kv_len) {
+  return n_q == 1 &&
+         (double)B * max_kv_len * (d.d_c + d.d_r) * 2.0 > 64.0 * 1048576;
+}
+}  // namespace
+
+extern "C" {
+
 mla_status mla_decode(const mla_dims* dims, int32_t B, int32_t n_q,
                       const void* q, const void* cache, int32_t num_blocks,
                       const int32_t* block_table, int32_t max_blocks,
@@ -710,15 +727,7 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, int32_t n_q,
   hipStream_t s = (hipStream_t)stream;
   const bool mfma = decode_mfma_supported(d);
   const int rows = B * n_q;
-  // One query per sequence reads each cache row once per call: beyond a
-  // quarter of the 256 MB Infinity Cache the rows are copied with
-  // non-temporal loads, so that they do not push out the weights it holds
-  // between steps (B = 64 at 8K context, 604 MB of rows: 293-294 -> 287-288
-  // us per step together with the weights' policy, same box).  Causal
-  // chunks (n_q > 1) reread every row for each query and keep ordinary
-  // loads.
-  const bool cache_nt = n_q == 1 && (double)B * max_kv_len *
-                                        (d.d_c + d.d_r) * 2.0 > 64.0 * 1048576;
+  const bool cache_nt = decode_cache_nt(d, B, n_q, max_kv_len);
   if (balanced_mode(d, B, n_q, n_split)) {
     Carve c(ws);
     const size_t prow = (size_t)BAL_SLOTS * d.n_h;
@@ -757,6 +766,77 @@ mla_status mla_decode(const mla_dims* dims, int32_t B, int32_t n_q,
     MLA_TRY(launch_combine(d, rows, ns, o_part, mfma, m_part, l_part, o_lat,
                            lse, s));
   return MLA_OK;
+}
+
+size_t mla_decode_out_workspace_bytes(const mla_dims* dims, int32_t B,
+                                      int32_t n_q, int32_t max_kv_len,
+                                      int32_t n_split) {
+  if (!dims_ok(dims) || B <= 0 || n_q <= 0 || max_kv_len <= 0 ||
+      n_split < MLA_SPLIT_BALANCED || (int64_t)B * n_q > INT32_MAX)
+    return 0;
+  return align_up(mla_decode_workspace_bytes(dims, B, n_q, max_kv_len,
+                                             n_split)) +
+         mla_out_workspace_bytes(dims, B * n_q);
+}
+
+mla_status mla_decode_out(const mla_dims* dims, int32_t B, int32_t n_q,
+                          const void* q, const void* cache,
+                          int32_t num_blocks, const int32_t* block_table,
+                          int32_t max_blocks, const int32_t* kv_lens,
+                          int32_t max_kv_len, int32_t causal, int32_t n_split,
+                          const void* w_uv, const void* w_o, float* o_lat,
+                          float* lse, void* u, void* ws, size_t ws_bytes,
+                          mla_stream_t stream) {
+  // every check of both calls before anything is launched
+  if (!dims) return MLA_ERR_NULL;
+  if (!dims_ok(dims) || B <= 0 || n_q <= 0 || max_kv_len <= 0 ||
+      num_blocks <= 0 || max_blocks <= 0 || n_split < MLA_SPLIT_BALANCED ||
+      (int64_t)B * n_q > INT32_MAX)
+    return MLA_ERR_SHAPE;
+  if (!dims_supported(dims)) return MLA_ERR_UNSUPPORTED;
+  if (!q || !cache || !block_table || !kv_lens || !o_lat || !w_uv || !w_o ||
+      !u)
+    return MLA_ERR_NULL;
+  const mla_dims& d = *dims;
+  if (n_q > max_kv_len) return MLA_ERR_SHAPE;
+  if (n_q > 1 && causal != 1) return MLA_ERR_UNSUPPORTED;
+  const int nblk = decode_nblk(d, max_kv_len);
+  if (nblk > max_blocks || n_split > nblk) return MLA_ERR_RANGE;
+  const size_t dec_bytes =
+      align_up(mla_decode_workspace_bytes(dims, B, n_q, max_kv_len, n_split));
+  const size_t need =
+      mla_decode_out_workspace_bytes(dims, B, n_q, max_kv_len, n_split);
+  if (!ws || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  void* ws_out = (char*)ws + dec_bytes;
+  const int T = B * n_q;
+  hipStream_t s = (hipStream_t)stream;
+  const int ns = balanced_mode(d, B, n_q, n_split)
+                     ? 0
+                     : uniform_request(d, B, n_q, max_kv_len, n_split);
+  if (ns > 1 && decode_mfma_supported(d) &&
+      gemv_supported(d, T, GV_QO_MAXT) && combine_uv_supported(d, T)) {
+    // decode, then the split combine fused with W_UV, then W_O
+    Carve c(ws);
+    const size_t prow = (size_t)T * ns * d.n_h;
+    float* o_part = c.take(prow * d.d_c);
+    float* m_part = c.take(prow);
+    float* l_part = c.take(prow);
+    MLA_TRY(launch_decode_mfma(d, B, n_q, q, cache, block_table, max_blocks,
+                               kv_lens, ns, DecodeBalance(), o_part, m_part,
+                               l_part, o_lat, lse,
+                               decode_cache_nt(d, B, n_q, max_kv_len), s));
+    float* v = (float*)ws_out;
+    MLA_TRY(launch_combine_uv(d, T, ns, o_part, m_part, l_part, w_uv, o_lat,
+                              lse, v, s));
+    return dev(launch_gemv_wo(d, T, v, w_o, u, s));
+  }
+  const mla_status st =
+      mla_decode(dims, B, n_q, q, cache, num_blocks, block_table, max_blocks,
+                 kv_lens, max_kv_len, causal, n_split, o_lat, lse, ws,
+                 dec_bytes, stream);
+  if (st != MLA_OK) return st;
+  return mla_out(dims, T, o_lat, w_uv, w_o, u, ws_out, ws_bytes - dec_bytes,
+                 stream);
 }
 
 mla_status mla_validate_block_table(const int32_t* block_table, int32_t B,

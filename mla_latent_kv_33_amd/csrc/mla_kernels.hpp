@@ -104,6 +104,19 @@ hipError_t launch_gemv_down(const mla_dims& d, int T, const void* h,
 hipError_t launch_gemv_out(const mla_dims& d, int T, const float* o_lat,
                            const void* w_uv, const void* w_o, float* v,
                            void* u, hipStream_t stream);
+// u [T][d] bf16 = W_O v from v as launch_gemv_out writes it.
+hipError_t launch_gemv_wo(const mla_dims& d, int T, const float* v,
+                          const void* w_o, void* u, hipStream_t stream);
+// The split combine of a matrix-core decode of T (1 or 2) query rows with
+// n_split >= 2 uniform splits, fused with v = W_UV_h o_lat_h: writes o_lat,
+// lse (may be null) and v as launch_gemv_out does.  bf16, d_c = 512,
+// d_h = 128.
+bool combine_uv_supported(const mla_dims& d, int T);
+hipError_t launch_combine_uv(const mla_dims& d, int T, int n_split,
+                             const float* o_part, const float* m_part,
+                             const float* l_part, const void* w_uv,
+                             float* o_lat, float* lse, float* v,
+                             hipStream_t stream);
 
 // ---- pre-merged absorption (merged.hip) ---------------------------------
 // out [n_h][d_c][d_cq] = W_UK_h^T W_UQ_h per head, in the weight dtype.

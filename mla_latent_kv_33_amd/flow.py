@@ -100,11 +100,14 @@ class StepOut:
 
 
 def run_step(st: DeviceStep, n_split: Optional[int] = None, stream=None,
-             out: Optional[StepOut] = None, stacked: bool = True) -> StepOut:
+             out: Optional[StepOut] = None, stacked: bool = True,
+             fuse_out: bool = False) -> StepOut:
     """One pass of the hot path: append the new tokens, absorb their
     queries, decode over the cache, project the output.  stacked: the
     append and the query path as one mla_append_absorb_q call (else
-    mla_append_cache, then mla_absorb_q)."""
+    mla_append_cache, then mla_absorb_q).  fuse_out: the decode and the
+    output projection as one mla_decode_out call (else mla_decode, then
+    mla_out)."""
     wl, L = st.wl, st.layer
     d = wl.dims
     ns = wl.n_split if n_split is None else n_split
@@ -117,6 +120,13 @@ def run_step(st: DeviceStep, n_split: Optional[int] = None, stream=None,
                  stream=stream)
         q = L.absorb(st.h_new, st.pos, q_out=q_out, stream=stream)
     q4 = q.view(wl.batch, wl.n_q, d.n_h, d.d_c + d.d_r)
+    if fuse_out:
+        o_lat, lse, u = L.decode_out(
+            q4, st.cache, st.table, st.kv_lens, st.max_kv_len, n_split=ns,
+            o_lat=None if out is None else out.o_lat,
+            lse=None if out is None else out.lse,
+            u=None if out is None else out.u, stream=stream)
+        return StepOut(q=q4, o_lat=o_lat, lse=lse, u=u)
     o_lat, lse = L.decode(q4, st.cache, st.table, st.kv_lens, st.max_kv_len,
                           n_split=ns,
                           o_lat=None if out is None else out.o_lat,
@@ -130,8 +140,9 @@ def run_step(st: DeviceStep, n_split: Optional[int] = None, stream=None,
 class BoundStep:
     """The library calls of run_step with their arguments checked and
     marshalled once (binding.BoundCall): `pre` (the append and the query
-    path: one stacked call, or the two calls), `attention` (mla_decode) and
-    `out` (mla_out), on the buffers of the StepOut given to bind_step."""
+    path: one stacked call, or the two calls), `attention` (mla_decode, or
+    mla_decode_out) and `out` (mla_out, or nothing after mla_decode_out),
+    on the buffers of the StepOut given to bind_step."""
     pre: list
     attention: object
     out: object
@@ -143,10 +154,16 @@ class BoundStep:
         self.out()
 
 
+def _nothing() -> None:
+    pass
+
+
 def bind_step(st: DeviceStep, out: StepOut, n_split: Optional[int] = None,
-              stream=None, stacked: bool = True) -> BoundStep:
-    """run_step(st, n_split, stream, out, stacked) as a BoundStep: each call
-    again writes into `out` and the same workspaces."""
+              stream=None, stacked: bool = True,
+              fuse_out: bool = False) -> BoundStep:
+    """run_step(st, n_split, stream, out, stacked, fuse_out) as a
+    BoundStep: each call again writes into `out` and the same
+    workspaces."""
     wl, L = st.wl, st.layer
     d = wl.dims
     ns = wl.n_split if n_split is None else n_split
@@ -160,6 +177,12 @@ def bind_step(st: DeviceStep, out: StepOut, n_split: Optional[int] = None,
                         stream=stream, bind=True),
                L.absorb(st.h_new, st.pos, q_out=q_out, stream=stream,
                         bind=True)]
+    if fuse_out:
+        attention = L.decode_out(out.q, st.cache, st.table, st.kv_lens,
+                                 st.max_kv_len, n_split=ns, o_lat=out.o_lat,
+                                 lse=out.lse, u=out.u, stream=stream,
+                                 bind=True)
+        return BoundStep(pre=pre, attention=attention, out=_nothing)
     attention = L.decode(out.q, st.cache, st.table, st.kv_lens,
                          st.max_kv_len, n_split=ns, o_lat=out.o_lat,
                          lse=out.lse, stream=stream, bind=True)

@@ -125,6 +125,29 @@ class MlaLayer:
                             n_split=n_split, ws=ws, stream=stream, bind=bind)
         return call if bind else (o_lat, lse)
 
+    def decode_out(self, q, cache, block_table, kv_lens, max_kv_len: int,
+                   n_split: int = 0, o_lat=None, lse=None, u=None,
+                   stream=None, bind=False):
+        """decode, then out on its rows, as one library call."""
+        d = self.dims
+        Bsz, n_q = q.shape[0], q.shape[1]
+        if o_lat is None:
+            o_lat = torch.empty((Bsz, n_q, d.n_h, d.d_c), dtype=torch.float32,
+                                device=self.device)
+        if lse is None:
+            lse = torch.empty((Bsz, n_q, d.n_h), dtype=torch.float32,
+                              device=self.device)
+        if u is None:
+            u = torch.empty((Bsz * n_q, d.d), dtype=torch_dtype(self.dtype),
+                            device=self.device)
+        ws = self.workspace("decode_out", B.mla_decode_out_workspace_bytes(
+            self.cdims, Bsz, n_q, max_kv_len, n_split))
+        call = B.mla_decode_out(self.cdims, q, cache, block_table, kv_lens,
+                                max_kv_len, self.w["w_uv"], self.w["w_o"],
+                                o_lat, u, lse=lse, causal=1, n_split=n_split,
+                                ws=ws, stream=stream, bind=bind)
+        return call if bind else (o_lat, lse, u)
+
     def out(self, o_lat, u=None, stream=None, bind=False):
         d = self.dims
         T = o_lat.shape[0]

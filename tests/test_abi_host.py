@@ -184,6 +184,47 @@ def test_decode_validation():
     assert call_decode(d, n_split=2, ws_bytes=64) == WS
 
 
+def call_decode_out(dims, B_=2, n_q=1, max_kv=100, causal=1, n_split=0,
+                    max_blocks=2, ws=FAKE, ws_bytes=1 << 30, q=FAKE,
+                    w_uv=FAKE, w_o=FAKE, u=FAKE):
+    return B.lib().mla_decode_out(
+        ctypes.byref(dims), B_, n_q, q, FAKE, 4, FAKE, max_blocks, FAKE,
+        max_kv, causal, n_split, w_uv, w_o, FAKE, None, u, ws, ws_bytes,
+        None)
+
+
+def test_decode_out_validation():
+    """mla_decode_out checks every argument of mla_decode and mla_out
+    before it enqueues anything; its workspace holds both calls'."""
+    d = ds_dims()
+    for B_, n_q, kv, ns in ((1, 1, 4097, 0), (2, 1, 100, 2), (1, 2, 4097, 5),
+                            (64, 1, 8193, 0), (4, 1, 1000, -1)):
+        need = B.mla_decode_out_workspace_bytes(d, B_, n_q, kv, ns)
+        dec = B.mla_decode_workspace_bytes(d, B_, n_q, kv, ns)
+        out = B.mla_out_workspace_bytes(d, B_ * n_q)
+        assert need == -(-dec // 256) * 256 + out, (B_, n_q, kv, ns)
+    assert B.mla_decode_out_workspace_bytes(d, 0, 1, 100, 0) == 0
+    assert B.mla_decode_out_workspace_bytes(d, 1, 1, 100, -2) == 0
+    assert call_decode_out(d, q=None) == NULL
+    assert call_decode_out(d, w_uv=None) == NULL
+    assert call_decode_out(d, w_o=None) == NULL
+    assert call_decode_out(d, u=None) == NULL
+    assert call_decode_out(d, B_=0) == SHAPE
+    assert call_decode_out(d, n_q=0) == SHAPE
+    assert call_decode_out(d, n_q=200, max_kv=100) == SHAPE
+    assert call_decode_out(d, n_q=4, causal=0) == UNSUP
+    assert call_decode_out(ds_dims(d_cq=1552)) == UNSUP
+    assert call_decode_out(d, max_blocks=1) == RANGE
+    assert call_decode_out(d, n_split=3) == RANGE
+    assert call_decode_out(d, n_split=-2) == SHAPE
+    assert call_decode_out(d, ws=None) == WS
+    assert call_decode_out(d, ws_bytes=B.mla_decode_out_workspace_bytes(
+        d, 2, 1, 100, 0) - 1) == WS
+    assert call_decode_out(d, B_=1, n_split=2, ws_bytes=
+                           B.mla_decode_out_workspace_bytes(d, 1, 1, 100, 2)
+                           - 1) == WS
+
+
 def test_header_cites_pages_and_names_callers():
     text = open(os.path.join(ROOT, "include", "mla.h")).read()
     assert "MLA：潜在表示压缩与解耦 RoPE" in text

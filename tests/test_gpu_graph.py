@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 def _workload(name, n_split):
     if name == "b1_ctx4k":
-        # the single-sequence step (1 x 4096 context + 1 token): 32 splits
+        # the single-sequence step (1 x 4096 context + 1 token): 64 splits
         # of 64 heads each, the combine for few query rows
         return dataclasses.replace(W.workload("b1_ctx4k"), n_split=n_split)
     # 16 sequences, ragged contexts (partial last blocks), permuted table,
@@ -82,22 +82,26 @@ def test_step_graph_replays_match_eager(name, n_split):
             f"replay {rep}: cache differs from the eager step"
 
 
-@pytest.mark.parametrize("name,n_split,stacked", [("graph_b16", 0, True),
-                                                  ("graph_b16", -1, False),
-                                                  ("b1_ctx4k", 0, True)])
-def test_bound_step_matches_eager(name, n_split, stacked):
+@pytest.mark.parametrize("name,n_split,stacked,fuse_out",
+                         [("graph_b16", 0, True, False),
+                          ("graph_b16", -1, False, False),
+                          ("b1_ctx4k", 0, True, False),
+                          ("b1_ctx4k", 0, True, True)])
+def test_bound_step_matches_eager(name, n_split, stacked, fuse_out):
     """flow.bind_step (the step's library calls with their arguments
     checked and marshalled once, as bench.py runs them) reproduces the
-    eager step bit for bit, call after call."""
+    eager step bit for bit, call after call (fuse_out: the decode and the
+    output projection as one mla_decode_out call)."""
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     wl = _workload(name, n_split)
-    log(f"case {name} n_split={n_split} stacked={stacked}, bound calls")
+    log(f"case {name} n_split={n_split} stacked={stacked} "
+        f"fuse_out={fuse_out}, bound calls")
     layer = flow.make_layer(wl)
     st = flow.prepare(wl, layer)
-    out = flow.run_step(st, stacked=stacked)
+    out = flow.run_step(st, stacked=stacked, fuse_out=fuse_out)
     torch.cuda.synchronize()
     ref = _snapshot(st, out)
-    step = flow.bind_step(st, out, stacked=stacked)
+    step = flow.bind_step(st, out, stacked=stacked, fuse_out=fuse_out)
     assert len(step.pre) == (1 if stacked else 2)
     for rep in range(3):
         for k in ("q", "o_lat", "lse", "u"):

@@ -229,6 +229,45 @@ def test_stacked_projections(batch, n_q):
         check_sequence(wl, out_s, ref, b)
 
 
+@pytest.mark.parametrize("batch,n_q,n_split", [(1, 1, 0), (2, 1, 0),
+                                               (1, 2, 0), (1, 1, 5),
+                                               (1, 1, 1), (4, 1, 0)])
+def test_decode_out(batch, n_q, n_split):
+    """mla_decode_out against mla_decode + mla_out on the same queries and
+    cache.  With one or two query rows and split keys the split combine and
+    W_UV run as one kernel (5 uniform splits leave one of its four split
+    groups empty); with one split, or four rows, the call takes the two
+    calls' own paths.  o_lat and lse differ from the separate calls only by
+    the order of fp32 sums, u by that and its bf16 rounding; the fused step
+    matches the oracle on every sequence."""
+    base = W.workload("b1_ctx4k")
+    rng = np.random.default_rng(500 + 10 * batch + n_q)
+    ctx = tuple(int(x) for x in rng.integers(300, 3000, size=batch))
+    wl = dataclasses.replace(base, name=f"decout{batch}x{n_q}", batch=batch,
+                             ctx=ctx, n_q=n_q, seed=23, permuted=True)
+    d = wl.dims
+    log(f"case DeepSeek-V2 dims, mla_decode_out: ctx={ctx} n_q={n_q} "
+        f"n_split={n_split}")
+    layer, w = layer_for(wl)
+    st = flow.prepare(wl, layer)
+    out = flow.run_step(st, n_split=n_split, fuse_out=True)
+    o_lat2, lse2 = layer.decode(out.q, st.cache, st.table, st.kv_lens,
+                                st.max_kv_len, n_split=n_split)
+    u2 = layer.out(o_lat2.view(-1, d.n_h, d.d_c))
+    torch.cuda.synchronize()
+    for name, a, b in (("o_lat", out.o_lat, o_lat2), ("lse", out.lse, lse2)):
+        a = a.cpu().numpy().astype(np.float64)
+        b = b.cpu().numpy().astype(np.float64)
+        assert np.isfinite(a).all(), name
+        rel = float(np.linalg.norm(a - b) / np.linalg.norm(b))
+        worst = float(np.max(np.abs(a - b)) / np.max(np.abs(b)))
+        assert rel <= 1e-5 and worst <= 1e-5, (name, rel, worst)
+    assert_reordered("u", out.u.float().cpu().numpy(),
+                     u2.float().cpu().numpy())
+    for b in range(batch):
+        check_sequence(wl, out, oracle_sequence(wl, w, b), b)
+
+
 def test_b64_var():
     wl = W.workload("b64_var")
     log(f"case {wl.name}: B=64 ctx U[1024,8192] permuted table bf16")
