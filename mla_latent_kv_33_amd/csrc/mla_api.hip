@@ -329,6 +329,7 @@ mla_status mla_append_cache_rmsnorm(
 }
 
 // ------------------------------------------------------------------ absorb
+extern "C++" {  // helpers below keep C++ linkage
 namespace {
 struct AbsorbWs {
   float *cq_parts, *cq, *qcr_parts, *qcr;
@@ -346,7 +347,9 @@ AbsorbWs absorb_layout(const mla_dims& d, int T, void* base) {
   return w;
 }
 }  // namespace
+}  // extern "C++"
 
+extern "C++" {  // helpers below keep C++ linkage
 namespace {
 // The query path from c_Q on (fp32, or pre-split hi|lo when cq_hl): q_C and
 // q_R = W_UQ c_Q, W_QR c_Q, then RoPE(q_R) and q_lat_h = W_UK_h^T q_C_h into
@@ -392,6 +395,7 @@ mla_status query_from_cq(const mla_dims& d, int T, const float* cq,
   return MLA_OK;
 }
 }  // namespace
+}  // extern "C++"
 
 size_t mla_absorb_workspace_bytes(const mla_dims* dims, int32_t T) {
   if (!dims_ok(dims) || T <= 0) return 0;
@@ -451,6 +455,7 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t T, const void* h,
 
 
 // ---------------------------------------- append and query in one call
+extern "C++" {  // helpers below keep C++ linkage
 namespace {
 // [W_DQ; W_DKV; W_KR] h: the three down-projections of the new tokens
 // stacked as one weight of d_cq + d_c + d_r rows.
@@ -496,6 +501,7 @@ StackedWs stacked_layout(const mla_dims& d, int T, void* base) {
   return w;
 }
 }  // namespace
+}  // extern "C++"
 
 size_t mla_append_absorb_workspace_bytes(const mla_dims* dims, int32_t T) {
   if (!dims_ok(dims) || T <= 0) return 0;
@@ -569,6 +575,7 @@ mla_status mla_append_absorb_q(
 }
 
 // ------------------------------------------------- pre-merged absorption
+extern "C++" {  // helpers below keep C++ linkage
 namespace {
 GemmArgs merged_gemm(const mla_dims& d, int T) {
   GemmArgs g;
@@ -599,6 +606,7 @@ MergedWs merged_layout(const mla_dims& d, int T, void* base) {
   return w;
 }
 }  // namespace
+}  // extern "C++"
 
 mla_status mla_merge_uq_uk(const mla_dims* dims, const void* w_uq,
                            const void* w_uk, void* w_merged,
