@@ -12,6 +12,7 @@ Prints one JSON line (see the keys below).  `--gpus N` with N > 1 exits: this
 build measures one GPU.
 """
 import argparse
+import dataclasses
 import gc
 import hashlib
 import json
@@ -53,6 +54,15 @@ def parse():
                          "mla_out), or explicit per-head keys and values for "
                          "chunked prefill (mla_query_mha, mla_prefill_mha, "
                          "mla_out_values)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="with --context: sequences of the uniform workload "
+                         "(default: the named workload's batch)")
+    ap.add_argument("--context", type=int, default=0,
+                    help="uniform prior context for every sequence instead "
+                         "of the named workload's lengths (a sweep over it "
+                         "separates the decode's per-key cost from its fixed "
+                         "per-launch cost); the line is then marked as not "
+                         "the headline configuration")
     ap.add_argument("--cpu-sample", type=int, default=24,
                     help="sequences of the workload the CPU oracle times")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -246,6 +256,14 @@ def main():
 
     B.lib()   # fail loudly if the library is not built
     wl = W.workload(args.workload)
+    if args.context > 0 or args.batch > 0:
+        if args.context <= 0:
+            raise SystemExit("--batch needs --context")
+        nb = args.batch if args.batch > 0 else wl.batch
+        wl = dataclasses.replace(
+            wl, name=f"{wl.name}@B{nb}xctx{args.context}", batch=nb,
+            ctx=(args.context,) * nb,
+            n_split=0 if wl.n_split < 0 else wl.n_split)
     d = wl.dims
     torch.cuda.set_device(0)
     layer = flow.make_layer(wl)
